@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the W4A16 path.
+
+This module only draws random inputs; it holds none of the method's
+arithmetic (no decode, no product, no transform), so both the GPU path's tests
+and the CPU oracle can take their inputs from it.
+
+Distributions (the same for every workload):
+  * packed code words: uniform uint32, i.e. eight i.i.d. uniform 4-bit codes
+    0..15 per word, canonical order (element k of a row in word k/8, bits
+    [4*(k%8), +4));
+  * scales: 0.02*|N(0,1)| + 1e-3 computed in fp32, rounded to bf16 (nearest,
+    ties to even), one per (row, K-group);
+  * activations: N(0,1) in fp32 rounded to bf16; optionally a fraction of the
+    elements (exactly round(frac*M*K), drawn without replacement) multiplied
+    by a factor before rounding (outliers).
+Draw order per matrix from one ``numpy.random.default_rng(seed)`` (PCG64):
+words, then scales, then activations.
+
+Workloads are a stand-in for batch-1 decode of a Gemma-4-E2B-sized model
+(hidden 1536, 35 decoder layers, vocabulary 262144), the shapes the pages'
+model has; no trained weights are used.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+HIDDEN = 1536
+N_LAYERS = 35
+VOCAB = 262144
+
+# (name, N, K) of one decoder layer's fused projections, in decode order.
+LAYER_SHAPES = (
+    ("qkv", 2048 + 256 + 256, HIDDEN),
+    ("o", HIDDEN, 2048),
+    ("gate_up", 2 * 6144, HIDDEN),
+    ("down", HIDDEN, 6144),
+)
+LM_HEAD_SHAPE = ("lm_head", VOCAB, HIDDEN)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16
+    bit patterns.  Inputs are finite."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(h, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def draw_weights(rng: np.random.Generator, N: int, K: int, group: int):
+    """Canonical packed words P[N][K/8] (uint32) and bf16 scales
+    S[N][K/group] (uint16 bit patterns)."""
+    assert K % 8 == 0 and K % group == 0
+    P = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint32)
+    z = rng.standard_normal(size=(N, K // group), dtype=np.float32)
+    s = np.abs(z) * np.float32(0.02) + np.float32(1e-3)
+    return P, f32_to_bf16_bits(s)
+
+
+def draw_activations(rng: np.random.Generator, M: int, K: int,
+                     outlier_frac: float = 0.0, outlier_mult: float = 20.0):
+    """bf16 activations X[M][K] (uint16 bit patterns)."""
+    x = rng.standard_normal(size=(M, K), dtype=np.float32)
+    if outlier_frac > 0.0:
+        count = int(round(outlier_frac * M * K))
+        idx = rng.choice(M * K, size=count, replace=False)
+        flat = x.reshape(-1)
+        flat[idx] *= np.float32(outlier_mult)
+    return f32_to_bf16_bits(x)
+
+
+@dataclass
+class GemvCase:
+    name: str
+    N: int
+    K: int
+    group: int
+    M: int
+    P: np.ndarray        # uint32 [N, K/8] canonical packed codes
+    S: np.ndarray        # uint16 [N, K/group] bf16 scales
+    X: np.ndarray        # uint16 [M, K] bf16 activations
+    out_dtype: str       # "f32" or "bf16"
+    seed: int
+    hadamard_block: int = 0
+
+    @property
+    def weight_bytes(self) -> int:
+        """Algorithmic weight bytes: 4-bit codes plus one bf16 scale per group."""
+        return self.N * self.K // 2 + self.N * (self.K // self.group) * 2
+
+
+def make_case(name, N, K, group, M, seed, out_dtype, outlier_frac=0.0,
+              hadamard_block=0) -> GemvCase:
+    rng = np.random.default_rng(seed)
+    P, S = draw_weights(rng, N, K, group)
+    X = draw_activations(rng, M, K, outlier_frac=outlier_frac)
+    return GemvCase(name, N, K, group, M, P, S, X, out_dtype, seed,
+                    hadamard_block)
+
+
+def layer_seed(layer: int, j: int) -> int:
+    return 1 + 4 * layer + j
+
+
+def single_gemv_small() -> GemvCase:
+    """M=1, N=256, K=512, group 32, fp32 out, seed 0."""
+    return make_case("gemv_256x512", 256, 512, 32, 1, 0, "f32")
+
+
+def decoder_layer(layer: int = 0):
+    """The four fused projections of one decoder layer, bf16 out."""
+    return [make_case(name, N, K, 32, 1, layer_seed(layer, j), "bf16")
+            for j, (name, N, K) in enumerate(LAYER_SHAPES)]
+
+
+def lm_head(seed: int = 0) -> GemvCase:
+    """Tied embedding / lm_head GEMV: N=262144, K=1536, group 32, fp32 logits."""
+    name, N, K = LM_HEAD_SHAPE
+    return make_case(name, N, K, 32, 1, seed, "f32")
+
+
+def decode_sweep():
+    """One decode step's weights: 35 x {qkv, o, gate_up, down} then lm_head,
+    a fresh seed per matrix, each with its own activation vector."""
+    cases = []
+    for layer in range(N_LAYERS):
+        cases.extend(decoder_layer(layer))
+    cases.append(lm_head(seed=1 + 4 * N_LAYERS))
+    return cases
+
+
+def prefill_g256(M: int) -> GemvCase:
+    """Prefill-shaped GEMM: group 256, N=12288, K=1536; activations with 1%
+    outliers x20; a 512-point Hadamard rotation along K is applied at run time
+    (weights are drawn directly as the stored rotated weights)."""
+    return make_case("prefill_g256_M%d" % M, 2 * 6144, HIDDEN, 256, M,
+                     1000 + M, "bf16", outlier_frac=0.01, hadamard_block=512)

@@ -1,0 +1,154 @@
+"""Oracle for the W4A16 path -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, scalar fp64 CPU implementation (``oracle.c``) of what the GPU
+library computes, written from the pages' definitions and sharing no code with
+the GPU path.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import this package; the product path never does.
+
+Functions follow:
+  * [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp",
+    the paragraph introducing the compressed-tensors W4A16 checkpoint (groups
+    of 32, bf16 step per group) and the paragraph on the w4gemv.py kernel
+    (packed 4-bit words, value = code - 8, exact);
+  * [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI",
+    section "What is in the file" (W' = W H^T with a runtime fast
+    Walsh-Hadamard transform of the activation; int4 groups of 256).
+
+Every function here is pinned by a CPU test to something other than itself
+(hand-typed tables, closed forms, brute force with library matmul, invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_OUT_DIR = os.path.join(_HERE, "_build")
+_LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2, no explicit SIMD, OpenMP over rows)."""
+    os.makedirs(_OUT_DIR, exist_ok=True)
+    stale = (not os.path.exists(_LIB_PATH)
+             or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC))
+    if force or stale:
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99",
+               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            i = ctypes.c_int
+            lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+            lib.oracle_bf16_to_f64.restype = ctypes.c_double
+            lib.oracle_bf16_array_to_f64.argtypes = [P, P, ctypes.c_size_t]
+            lib.oracle_code.argtypes = [P, i, i, i]
+            lib.oracle_code.restype = i
+            lib.oracle_codes.argtypes = [P, i, i, P]
+            lib.oracle_weight.argtypes = [P, P, i, i, i, i]
+            lib.oracle_weight.restype = ctypes.c_double
+            lib.oracle_dequant.argtypes = [P, P, i, i, i, P]
+            lib.oracle_gemm.argtypes = [P, P, i, i, i, P, i, i, P, P, i]
+            lib.oracle_fwht.argtypes = [P, P, i, i, i]
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def bf16_to_f64(h) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, dtype=np.float64)
+    _load().oracle_bf16_array_to_f64(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def code(P, K: int, n: int, k: int) -> int:
+    P = _c(P, np.uint32)
+    return int(_load().oracle_code(_ptr(P), K, n, k))
+
+
+def codes(P, N: int, K: int) -> np.ndarray:
+    """All 4-bit codes (0..15) of the canonical packed matrix, N x K int8."""
+    P = _c(P, np.uint32)
+    assert P.size == N * (K // 8)
+    out = np.empty((N, K), dtype=np.int8)
+    _load().oracle_codes(_ptr(P), N, K, _ptr(out))
+    return out
+
+
+def weight(P, S, K: int, group: int, n: int, k: int) -> float:
+    P = _c(P, np.uint32)
+    S = _c(S, np.uint16)
+    return float(_load().oracle_weight(_ptr(P), _ptr(S), K, group, n, k))
+
+
+def dequant(P, S, N: int, K: int, group: int) -> np.ndarray:
+    """Dense fp64 W[n][k] = (code - 8) * scale (exact)."""
+    P = _c(P, np.uint32)
+    S = _c(S, np.uint16)
+    assert P.size == N * (K // 8) and S.size == N * (K // group)
+    W = np.empty((N, K), dtype=np.float64)
+    _load().oracle_dequant(_ptr(P), _ptr(S), N, K, group, _ptr(W))
+    return W
+
+
+def gemm(P, S, N: int, K: int, group: int, X, threads: int = 1):
+    """Y[m][n] = sum_k w(n,k) X[m][k] in fp64, sequential k; also
+    A[m][n] = sum_k |w(n,k) X[m][k]|.  X is float64 (M x K) or (K,)."""
+    P = _c(P, np.uint32)
+    S = _c(S, np.uint16)
+    X = _c(X, np.float64)
+    squeeze = X.ndim == 1
+    X2 = X.reshape(1, K) if squeeze else X
+    M = X2.shape[0]
+    assert X2.shape[1] == K
+    assert P.size == N * (K // 8) and S.size == N * (K // group)
+    Y = np.empty((M, N), dtype=np.float64)
+    A = np.empty((M, N), dtype=np.float64)
+    _load().oracle_gemm(_ptr(P), _ptr(S), N, K, group, _ptr(X2), M, K,
+                        _ptr(Y), _ptr(A), int(threads))
+    if squeeze:
+        return Y[0], A[0]
+    return Y, A
+
+
+def gemm_bf16(P, S, N: int, K: int, group: int, Xbf16, threads: int = 1):
+    """gemm() with bf16 activations (uint16 bit patterns), widened exactly."""
+    return gemm(P, S, N, K, group, bf16_to_f64(Xbf16), threads)
+
+
+def fwht(X, block: int) -> np.ndarray:
+    """Blockwise orthonormal Sylvester-order FWHT along the last axis (fp64)."""
+    X = _c(X, np.float64)
+    squeeze = X.ndim == 1
+    X2 = X.reshape(1, -1) if squeeze else X
+    M, K = X2.shape
+    assert block > 0 and block & (block - 1) == 0 and K % block == 0
+    out = np.empty_like(X2)
+    _load().oracle_fwht(_ptr(X2), _ptr(out), M, K, block)
+    return out[0] if squeeze else out

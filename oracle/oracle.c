@@ -1,0 +1,145 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, scalar CPU reference for the W4A16 group-quantized
+ * matrix-vector / matrix-matrix product and the blockwise Walsh-Hadamard
+ * transform of activations.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the GPU library: everything below is written
+ * from the definitions on the pages, in fp64, in the order they state.
+ *
+ * Sources (pages as published on the web):
+ *  [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp":
+ *       - paragraph introducing the compressed-tensors W4A16 checkpoint:
+ *         4-bit weights in groups of 32, one 16-bit (bf16) step per group,
+ *         16-bit activations;
+ *       - paragraph on the w4gemv.py kernel: decoding one token multiplies one
+ *         vector by every weight matrix; the kernel reads the packed 4-bit
+ *         words and multiplies, and each 4-bit value becomes a float as
+ *         (value - 8), exactly.
+ *  [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI",
+ *       section "What is in the file": weights rotated along K by an orthogonal
+ *       Hadamard matrix H, W' = W H^T, and a fast Walsh-Hadamard transform of
+ *       the activation at run time gives the same product; FFN weights are
+ *       int4 with groups of 256.
+ *
+ * Readings where the pages are silent (each is also listed in the design
+ * notes of the repository):
+ *  - nibble order: element k of a row sits in word k/8, bits [4*(k%8), +4),
+ *    least significant nibble first;
+ *  - sign convention: offset binary, value = (code - 8) * scale (not two's
+ *    complement int4);
+ *  - scales: S[n][k / group], row-major, bf16, no zero point;
+ *  - Hadamard: Sylvester (natural) order, orthonormal factor block^-1/2,
+ *    contiguous blocks along K; Sylvester H is symmetric, so H^T = H.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/* bf16 is the top 16 bits of an IEEE binary32; widening is exact. */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+void oracle_bf16_array_to_f64(const uint16_t* in, double* out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f64(in[i]);
+}
+
+/* The 4-bit code of element (n, k) of an N x K matrix whose canonical packed
+ * form is P[N][K/8] (uint32), integer arithmetic only. */
+int oracle_code(const uint32_t* P, int K, int n, int k)
+{
+    const uint32_t word = P[(size_t)n * (size_t)(K / 8) + (size_t)(k / 8)];
+    const int shift = 4 * (k % 8);
+    return (int)((word >> shift) & 0xFu);
+}
+
+/* All codes, row-major N x K, as small integers 0..15. */
+void oracle_codes(const uint32_t* P, int N, int K, int8_t* out)
+{
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            out[(size_t)n * K + k] = (int8_t)oracle_code(P, K, n, k);
+}
+
+/* Dequantized weight value (code - 8) * scale, exact in fp64
+ * (a 4-bit integer times an 8-significant-bit scale). */
+double oracle_weight(const uint32_t* P, const uint16_t* S, int K, int group, int n, int k)
+{
+    const int v = oracle_code(P, K, n, k) - 8;
+    const double s = oracle_bf16_to_f64(S[(size_t)n * (size_t)(K / group) + (size_t)(k / group)]);
+    return (double)v * s;
+}
+
+void oracle_dequant(const uint32_t* P, const uint16_t* S, int N, int K, int group, double* W)
+{
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            W[(size_t)n * K + k] = oracle_weight(P, S, K, group, n, k);
+}
+
+/*
+ * Y[m][n] = sum_{k=0..K-1} w(n,k) * X[m][k], summed in order of increasing k
+ * in fp64; A[m][n] = sum_k |w(n,k) * X[m][k]| (the scale of the acceptance
+ * bound).  X is fp64 (the caller widens bf16 activations exactly, or passes a
+ * Hadamard-transformed activation).  Rows of X are ldx apart.
+ * nthreads > 1 splits the independent output rows n over OpenMP threads; the
+ * arithmetic of each output is unchanged.
+ */
+void oracle_gemm(const uint32_t* P, const uint16_t* S, int N, int K, int group,
+                 const double* X, int M, int ldx, double* Y, double* A, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    for (int m = 0; m < M; ++m) {
+        const double* x = X + (size_t)m * (size_t)ldx;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+        for (int n = 0; n < N; ++n) {
+            double y = 0.0, a = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double t = oracle_weight(P, S, K, group, n, k) * x[k];
+                y += t;
+                a += fabs(t);
+            }
+            Y[(size_t)m * N + n] = y;
+            if (A) A[(size_t)m * N + n] = a;
+        }
+    }
+}
+
+/*
+ * Blockwise fast Walsh-Hadamard transform along K, one row of X at a time:
+ * every contiguous block of `block` (a power of two) elements is replaced by
+ * H_block times that block, H_block the Sylvester-ordered Hadamard matrix
+ * scaled by block^-1/2 (orthonormal).  Butterfly stages of span 1, 2, 4, ...
+ * (a, b) -> (a + b, a - b), then one scaling.  K must be a multiple of block.
+ */
+void oracle_fwht(const double* X, double* Xout, int M, int K, int block)
+{
+    const double norm = 1.0 / sqrt((double)block);
+    for (int m = 0; m < M; ++m) {
+        const double* x = X + (size_t)m * K;
+        double* y = Xout + (size_t)m * K;
+        for (int k = 0; k < K; ++k) y[k] = x[k];
+        for (int b0 = 0; b0 < K; b0 += block) {
+            double* v = y + b0;
+            for (int h = 1; h < block; h *= 2) {
+                for (int i = 0; i < block; i += 2 * h) {
+                    for (int j = i; j < i + h; ++j) {
+                        const double a = v[j];
+                        const double b = v[j + h];
+                        v[j] = a + b;
+                        v[j + h] = a - b;
+                    }
+                }
+            }
+            for (int j = 0; j < block; ++j) v[j] *= norm;
+        }
+    }
+}
