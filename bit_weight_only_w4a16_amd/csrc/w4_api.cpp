@@ -1,0 +1,286 @@
+// w4_api.cpp -- the C ABI: validation, dispatch, errors.
+//
+// Every entry point validates its arguments before its first HIP call, so the
+// error paths run on a machine without a GPU.  No HIP call happens when the
+// library is loaded.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "w4_dispatch.h"
+
+namespace w4 {
+
+static thread_local char g_err[512];
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    if (e == hipSuccess) return W4_OK;
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return W4_ERR_HIP;
+}
+
+static bool aligned(const void* p, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Largest sizes served (indices stay far from overflow).
+constexpr int kMaxN = 1 << 26;
+constexpr int kMaxK = 1 << 20;
+
+static int check_weight_shape(int N, int K, int group) {
+    if (group != 32 && group != 256)
+        return fail(W4_ERR_SHAPE, "group must be 32 or 256 (got %d)", group);
+    if (N < 1 || N > kMaxN) return fail(W4_ERR_SHAPE, "N out of range (got %d)", N);
+    if (K < group || K > kMaxK || K % group != 0)
+        return fail(W4_ERR_SHAPE, "K must be a positive multiple of group %d (got %d)",
+                    group, K);
+    return W4_OK;
+}
+
+static int check_dtype(int ydt) {
+    if (ydt != W4_F32 && ydt != W4_BF16)
+        return fail(W4_ERR_DTYPE, "output dtype must be W4_F32 or W4_BF16 (got %d)", ydt);
+    return W4_OK;
+}
+
+static int check_out_ptr(const void* y, int ydt, const char* name) {
+    if (!y) return fail(W4_ERR_ARG, "%s is NULL", name);
+    if (!aligned(y, ydt == W4_F32 ? 4 : 2))
+        return fail(W4_ERR_ALIGN, "%s misaligned for its dtype", name);
+    return W4_OK;
+}
+
+static int check_in16(const void* p, const char* name) {
+    if (!p) return fail(W4_ERR_ARG, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(W4_ERR_ALIGN, "%s must be 16-byte aligned", name);
+    return W4_OK;
+}
+
+}  // namespace w4
+
+using namespace w4;
+
+#define W4_TRY(expr)                 \
+    do {                             \
+        const int _st = (expr);      \
+        if (_st != W4_OK) return _st; \
+    } while (0)
+
+extern "C" {
+
+const char* w4_status_str(int status) {
+    switch (status) {
+        case W4_OK: return "ok";
+        case W4_ERR_ARG: return "invalid argument";
+        case W4_ERR_SHAPE: return "invalid shape";
+        case W4_ERR_ALIGN: return "misaligned pointer or stride";
+        case W4_ERR_DTYPE: return "invalid dtype";
+        case W4_ERR_UNSUPPORTED: return "unsupported";
+        case W4_ERR_HIP: return "HIP runtime error";
+        case W4_ERR_NOMEM: return "out of memory";
+        case W4_ERR_ARCH: return "device is not gfx950";
+        case W4_ERR_TIMEOUT: return "in-kernel wait timed out";
+        default: return "unknown status";
+    }
+}
+
+const char* w4_last_error(void) { return g_err; }
+
+int w4_device_check(void) {
+    int dev = 0;
+    W4_TRY(hip_fail(hipGetDevice(&dev), "hipGetDevice"));
+    hipDeviceProp_t prop;
+    W4_TRY(hip_fail(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties"));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(W4_ERR_ARCH, "device %d is %s, this library is built for gfx950",
+                    dev, prop.gcnArchName);
+    return W4_OK;
+}
+
+const char* w4_build_info(void) {
+    return "abi=1 arch=gfx950 kernels=gemv,gemv_generic,smallm,fwht,mfma_gemm,sweep_graph,"
+           "sweep_persistent,pack,probe";
+}
+
+size_t w4_packed_bytes(int N, int K, int group) {
+    if (check_weight_shape(N, K, group) != W4_OK) return 0;
+    return packed_bytes(N, K, group);
+}
+
+int w4_pack(const uint32_t* P, const uint16_t* S, int N, int K, int group,
+            void* out, void* stream) {
+    W4_TRY(check_weight_shape(N, K, group));
+    if (!P || !S || !out) return fail(W4_ERR_ARG, "w4_pack: NULL pointer");
+    if (!aligned(P, 4) || !aligned(S, 2) || !aligned(out, 16))
+        return fail(W4_ERR_ALIGN, "w4_pack: P 4-, S 2-, out 16-byte alignment required");
+    return launch_pack(P, S, N, K, group, out, static_cast<hipStream_t>(stream));
+}
+
+int w4_pack_host(const uint32_t* P, const uint16_t* S, int N, int K, int group,
+                 void* out) {
+    W4_TRY(check_weight_shape(N, K, group));
+    if (!P || !S || !out) return fail(W4_ERR_ARG, "w4_pack_host: NULL pointer");
+    uint8_t* base = static_cast<uint8_t*>(out);
+    uint32_t* codes = reinterpret_cast<uint32_t*>(base);
+    const size_t n_words = (size_t)N * (size_t)(K / 8);
+    for (size_t i = 0; i < n_words; ++i) codes[i] = word_to_device(P[i]);
+    const size_t off = scale_offset(N, K);
+    memset(base + n_words * 4, 0, off - n_words * 4);
+    const size_t n_scales = (size_t)N * (size_t)(K / group);
+    memcpy(base + off, S, n_scales * 2);
+    const size_t total = packed_bytes(N, K, group);
+    memset(base + off + n_scales * 2, 0, total - off - n_scales * 2);
+    return W4_OK;
+}
+
+int w4_unpack_host(const void* packed, int N, int K, int group, uint32_t* P,
+                   uint16_t* S) {
+    W4_TRY(check_weight_shape(N, K, group));
+    if (!packed || !P || !S) return fail(W4_ERR_ARG, "w4_unpack_host: NULL pointer");
+    const uint8_t* base = static_cast<const uint8_t*>(packed);
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>(base);
+    const size_t n_words = (size_t)N * (size_t)(K / 8);
+    for (size_t i = 0; i < n_words; ++i) P[i] = word_from_device(codes[i]);
+    memcpy(S, base + scale_offset(N, K), (size_t)N * (size_t)(K / group) * 2);
+    return W4_OK;
+}
+
+int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
+               void* y, int ydt, void* stream) {
+    W4_TRY(check_weight_shape(N, K, group));
+    W4_TRY(check_dtype(ydt));
+    W4_TRY(check_in16(packed, "packed"));
+    W4_TRY(check_in16(x, "x"));
+    W4_TRY(check_out_ptr(y, ydt, "y"));
+    const GemvTile t = pick_gemv_tile(N, K, group);
+    return launch_gemv(t, packed, N, K, group, x, y, ydt,
+                       static_cast<hipStream_t>(stream));
+}
+
+int w4a16_gemm_smallM(const void* packed, int N, int K, int group, int M,
+                      const uint16_t* X, int ldx, void* Y, int ldy, int ydt,
+                      void* stream) {
+    W4_TRY(check_weight_shape(N, K, group));
+    W4_TRY(check_dtype(ydt));
+    if (M < 2 || M > 16) return fail(W4_ERR_SHAPE, "smallM: M must be in 2..16 (got %d)", M);
+    if (ldx < K || ldy < N) return fail(W4_ERR_SHAPE, "smallM: ldx >= K and ldy >= N required");
+    if (ldx % 8 != 0) return fail(W4_ERR_ALIGN, "smallM: ldx must be a multiple of 8");
+    W4_TRY(check_in16(packed, "packed"));
+    W4_TRY(check_in16(X, "X"));
+    W4_TRY(check_out_ptr(Y, ydt, "Y"));
+    return launch_smallm(packed, N, K, group, M, X, ldx, Y, ldy, ydt,
+                         static_cast<hipStream_t>(stream));
+}
+
+int w4_fwht(const uint16_t* X, int ldx, uint16_t* Xo, int ldo, int M, int K,
+            int block, void* stream) {
+    if (block < 2 || block > 1024 || (block & (block - 1)) != 0)
+        return fail(W4_ERR_SHAPE, "fwht: block must be a power of two in 2..1024 (got %d)", block);
+    if (M < 1 || K < block || K % block != 0 || K > kMaxK)
+        return fail(W4_ERR_SHAPE, "fwht: K must be a positive multiple of block");
+    if (ldx < K || ldo < K) return fail(W4_ERR_SHAPE, "fwht: ldx, ldo >= K required");
+    if (ldx % 8 != 0 || ldo % 8 != 0)
+        return fail(W4_ERR_ALIGN, "fwht: ldx and ldo must be multiples of 8");
+    W4_TRY(check_in16(X, "X"));
+    W4_TRY(check_in16(Xo, "Xout"));
+    if (X == Xo && ldx != ldo) return fail(W4_ERR_ARG, "fwht: in place needs ldo == ldx");
+    return launch_fwht(X, ldx, Xo, ldo, M, K, block, static_cast<hipStream_t>(stream));
+}
+
+size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block) {
+    if (had_block == 0 || M < 1 || K < 1) return 0;
+    return align_up((size_t)M * (size_t)K * 2, kAlign);
+}
+
+int w4a16_gemm(const void* packed, int N, int K, int group, int M,
+               const uint16_t* X, int ldx, int had_block, void* workspace,
+               size_t ws_bytes, void* Y, int ldy, int ydt, void* stream) {
+    W4_TRY(check_weight_shape(N, K, group));
+    W4_TRY(check_dtype(ydt));
+    if (M < 1 || M > (1 << 20)) return fail(W4_ERR_SHAPE, "gemm: M out of range (got %d)", M);
+    if (K % 256 != 0) return fail(W4_ERR_SHAPE, "gemm: K must be a multiple of 256");
+    if (ldx < K || ldy < N) return fail(W4_ERR_SHAPE, "gemm: ldx >= K and ldy >= N required");
+    if (ldx % 8 != 0) return fail(W4_ERR_ALIGN, "gemm: ldx must be a multiple of 8");
+    if (had_block != 0 &&
+        (had_block < 2 || had_block > 1024 || (had_block & (had_block - 1)) != 0 ||
+         K % had_block != 0))
+        return fail(W4_ERR_SHAPE, "gemm: had_block must be 0 or a power of two dividing K");
+    W4_TRY(check_in16(packed, "packed"));
+    W4_TRY(check_in16(X, "X"));
+    W4_TRY(check_out_ptr(Y, ydt, "Y"));
+    const size_t need = w4a16_gemm_workspace_bytes(M, K, had_block);
+    if (need) {
+        if (ws_bytes < need)
+            return fail(W4_ERR_SHAPE, "gemm: workspace of %zu bytes needed (got %zu)", need,
+                        ws_bytes);
+        W4_TRY(check_in16(workspace, "workspace"));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* Xin = X;
+    int ld_in = ldx;
+    if (had_block) {
+        uint16_t* Xr = static_cast<uint16_t*>(workspace);
+        W4_TRY(launch_fwht(X, ldx, Xr, K, M, K, had_block, s));
+        Xin = Xr;
+        ld_in = K;
+    }
+    // decode-shaped row counts stay on the vector-ALU kernels; M > 16 goes to
+    // the matrix cores ([P2] "fastgemma": below 16 rows a GEMM is decode-shaped)
+    if (M == 1) {
+        const GemvTile t = pick_gemv_tile(N, K, group);
+        return launch_gemv(t, packed, N, K, group, Xin, Y, ydt, s);
+    }
+    if (M <= 16) return launch_smallm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
+    return launch_mfma_gemm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
+}
+
+int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) {
+    W4_TRY(check_weight_shape(N, K, group));
+    if (!buf || len == 0) return fail(W4_ERR_ARG, "describe: empty buffer");
+    if (M < 1) return fail(W4_ERR_SHAPE, "describe: M must be >= 1");
+    if (M == 1) {
+        const GemvTile t = pick_gemv_tile(N, K, group);
+        snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d", t.generic ? "_generic" : "",
+                 t.L, t.U, t.waves, t.grid);
+    } else if (M <= 16) {
+        describe_smallm(M, N, K, group, buf, len);
+    } else {
+        if (K % 256 != 0) return fail(W4_ERR_SHAPE, "describe: gemm needs K % 256 == 0");
+        describe_mfma(M, N, K, group, buf, len);
+    }
+    return W4_OK;
+}
+
+int w4_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    W4_TRY(check_in16(buf, "buf"));
+    if (!out) return fail(W4_ERR_ARG, "probe: out is NULL");
+    if (!aligned(out, 4)) return fail(W4_ERR_ALIGN, "probe: out must be 4-byte aligned");
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(W4_ERR_SHAPE, "probe: bytes must be a positive multiple of 16");
+    return launch_probe_read(buf, bytes, out, static_cast<hipStream_t>(stream));
+}
+
+int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    W4_TRY(check_in16(src, "src"));
+    W4_TRY(check_in16(dst, "dst"));
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(W4_ERR_SHAPE, "probe: bytes must be a positive multiple of 16");
+    return launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

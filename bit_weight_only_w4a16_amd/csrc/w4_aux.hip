@@ -1,0 +1,99 @@
+// w4_aux.hip -- the packer and the memory probes.
+//
+// Packer: [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI",
+// section "What is in the file": weights are packed once into the order the
+// kernel loads them, so nothing is repacked at run time.  Here that order is
+// the canonical row-major code layout with each word's nibbles regrouped
+// (even elements in the low half-word, odd in the high) so one and-or per
+// element pair yields a bf16 operand pair; scales follow at a 256-byte
+// boundary.
+//
+// Probes: [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than
+// llama.cpp", the summary line of the w4gemv.py kernel compares the kernel
+// with a plain sum over memory; the copy kernel calibrates byte counters.
+#include "w4_dispatch.h"
+
+namespace w4 {
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint32_t* __restrict__ P,
+                                                   const uint16_t* __restrict__ S,
+                                                   uint32_t* __restrict__ codes,
+                                                   uint16_t* __restrict__ scales,
+                                                   size_t n_words, size_t n_scales) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride)
+        codes[i] = word_to_device(P[i]);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_scales; i += stride)
+        scales[i] = S[i];
+}
+
+int launch_pack(const uint32_t* P, const uint16_t* S, int N, int K, int group,
+                void* out, hipStream_t s) {
+    const size_t n_words = (size_t)N * (size_t)(K / 8);
+    const size_t n_scales = (size_t)N * (size_t)(K / group);
+    uint8_t* base = static_cast<uint8_t*>(out);
+    size_t blocks = (n_words + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    pack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        P, S, reinterpret_cast<uint32_t*>(base),
+        reinterpret_cast<uint16_t*>(base + scale_offset(N, K)), n_words, n_scales);
+    return hip_fail(hipGetLastError(), "pack launch");
+}
+
+__global__ void zero_u32_kernel(uint32_t* p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0u;
+}
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ buf,
+                                                         size_t n16, uint32_t* out) {
+    uint32_t acc = 0u;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // four independent loads in flight per lane per step
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = nt_load(buf + i);
+        const u32x4 b = nt_load(buf + i + stride);
+        const u32x4 c = nt_load(buf + i + 2 * stride);
+        const u32x4 d = nt_load(buf + i + 3 * stride);
+        acc += (a[0] + a[1] + a[2] + a[3]) + (b[0] + b[1] + b[2] + b[3]) +
+               (c[0] + c[1] + c[2] + c[3]) + (d[0] + d[1] + d[2] + d[3]);
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = nt_load(buf + i);
+        acc += a[0] + a[1] + a[2] + a[3];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if ((threadIdx.x & 63) == 0) atomicAdd(out, acc);
+}
+
+int launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s) {
+    zero_u32_kernel<<<1, 64, 0, s>>>(out);
+    const size_t n16 = bytes / 16;
+    size_t blocks = (n16 + 255) / 256;
+    const size_t cap = (size_t)kNumCUs * 8;
+    if (blocks > cap) blocks = cap;
+    probe_read_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(buf), n16, out);
+    return hip_fail(hipGetLastError(), "probe read launch");
+}
+
+__global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst,
+                                                         size_t n16) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        __builtin_nontemporal_store(nt_load(src + i), dst + i);
+}
+
+int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    size_t blocks = (n16 + 255) / 256;
+    const size_t cap = (size_t)kNumCUs * 8;
+    if (blocks > cap) blocks = cap;
+    probe_copy_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
+        static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+    return hip_fail(hipGetLastError(), "probe copy launch");
+}
+
+}  // namespace w4

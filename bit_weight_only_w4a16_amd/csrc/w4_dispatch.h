@@ -1,0 +1,46 @@
+// w4_dispatch.h -- tile selection and kernel launchers (internal).
+#pragma once
+
+#include "w4_common.h"
+
+namespace w4 {
+
+constexpr int kNumCUs = 256;        // MI355X: 8 XCDs x 32 CUs
+constexpr int kMaxU = 8;            // 32-element chunks held per lane
+
+// Batch-1 GEMV tiling: L lanes share one row (each lane owns U chunks of K,
+// chunk index lane + L*u), a wave covers 64/L rows per step, `waves` waves per
+// workgroup, `grid` workgroups; generic = chunks re-read per row (huge K).
+struct GemvTile {
+    int L = 16;
+    int U = 3;
+    int waves = 4;
+    int grid = 1;
+    bool generic = false;
+};
+
+GemvTile pick_gemv_tile(int N, int K, int group);
+int launch_gemv(const GemvTile& t, const void* packed, int N, int K, int group,
+                const uint16_t* x, void* y, int ydt, hipStream_t s);
+
+int launch_pack(const uint32_t* P, const uint16_t* S, int N, int K, int group,
+                void* out, hipStream_t s);
+
+int launch_smallm(const void* packed, int N, int K, int group, int M,
+                  const uint16_t* X, int ldx, void* Y, int ldy, int ydt,
+                  hipStream_t s);
+void describe_smallm(int M, int N, int K, int group, char* buf, size_t len);
+
+int launch_fwht(const uint16_t* X, int ldx, uint16_t* Xo, int ldo, int M,
+                int K, int block, hipStream_t s);
+
+int launch_mfma_gemm(const void* packed, int N, int K, int group, int M,
+                     const uint16_t* X, int ldx, void* Y, int ldy, int ydt,
+                     hipStream_t s);
+void describe_mfma(int M, int N, int K, int group, char* buf, size_t len);
+
+int launch_probe_read(const void* buf, size_t bytes, uint32_t* out,
+                      hipStream_t s);
+int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace w4

@@ -1,0 +1,254 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so, an MI355X (gfx950) library for the W4A16
+ * group-quantized matrix-vector product of batch-1 decode.
+ *
+ * Sources the operations follow (pages as published on the web):
+ *  [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp"
+ *       - the paragraph introducing the compressed-tensors W4A16 checkpoint:
+ *         4-bit weights in groups of 32 with one 16-bit step (bf16) per group,
+ *         16-bit activations;
+ *       - the paragraph on the w4gemv.py kernel: decoding one token multiplies
+ *         one vector by every weight matrix, so the speed limit is how fast
+ *         the weights are read; the kernel reads the packed 4-bit words,
+ *         unpacks them in registers and multiplies, never writing a 16-bit
+ *         copy; each 4-bit value becomes the exact float (value - 8); each
+ *         weight shape gets its own fixed tiling;
+ *       - the paragraph on the decode step as one captured graph (launching
+ *         hundreds of small kernels one at a time costs more than running
+ *         them) and the paragraph on concatenated gate|up and q|k|v matrices;
+ *       - the summary line of the kernel: GB/s counted from packed weight
+ *         bytes, compared with a plain-sum read of memory.
+ *  [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI"
+ *       - section "What is in the file": int4 weights in groups of 256,
+ *         rotated along K by an orthogonal Hadamard matrix (W' = W H^T) with a
+ *         run-time fast Walsh-Hadamard transform of the activation; weights
+ *         pre-packed once into the kernel's operand order;
+ *       - section "Why AMX for GEMM but not for attention": a weight GEMM
+ *         reuses each weight byte across all M activation rows.
+ *
+ * Conventions for every call:
+ *  - Status: 0 (W4_OK) on success, a negative W4_ERR_* otherwise.  No call
+ *    throws.  On a validation error nothing is launched and no output byte is
+ *    written; w4_last_error() then holds a message for the calling thread.
+ *  - Validation (shapes, group, dtype, null pointers, alignment) happens before
+ *    any HIP call, so every error path can be exercised without a GPU.
+ *  - Pointers named "device" are device (HBM) addresses, e.g. from hipMalloc or
+ *    torch; "host" pointers are ordinary CPU memory.  The caller owns every
+ *    buffer; the library never allocates on a compute call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    are stream-ordered and asynchronous: a launch failure returns W4_ERR_HIP,
+ *    a fault shows at the caller's next synchronization.
+ *  - Stateless calls are thread-safe.  A sweep handle is used by one thread.
+ *
+ * Weight format (canonical, what callers hold):
+ *  - codes P[N][K/8] uint32: element (n, k) is the 4-bit code in word
+ *    P[n][k/8], bits [4*(k%8), 4*(k%8)+4) (least significant nibble first);
+ *  - scales S[N][K/group] bf16 (uint16 bit patterns), row-major;
+ *  - weight value w(n,k) = (code - 8) * S[n][k/group] (offset binary, symmetric,
+ *    no zero point).  A matrix is N x K like a linear layer's (out x in).
+ * Device layout ("packed"), produced only by w4_pack / w4_pack_host and read
+ * by every compute call: w4_packed_bytes(N, K, group) bytes holding the codes
+ * (N*K/2 bytes, row-major, each word's nibbles reordered so that the codes of
+ * elements 2j and 2j+1 sit at bits [4j, 4j+4) and [16+4j, 20+4j)), then, at the
+ * next 256-byte boundary, the scales unchanged.  Callers treat it as opaque.
+ * Activations X[M][K] are bf16, row stride ldx elements.  Outputs are fp32 or
+ * bf16 (round to nearest even from the fp32 accumulator).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4_ABI_VERSION 1
+
+enum w4_status {
+    W4_OK = 0,
+    W4_ERR_ARG = -1,          /* null pointer, bad enum, bad handle          */
+    W4_ERR_SHAPE = -2,        /* N, K, M, group, block or size out of range  */
+    W4_ERR_ALIGN = -3,        /* pointer or leading dimension misaligned     */
+    W4_ERR_DTYPE = -4,        /* output dtype not W4_F32 / W4_BF16           */
+    W4_ERR_UNSUPPORTED = -5,  /* valid request this build does not serve     */
+    W4_ERR_HIP = -6,          /* a HIP runtime call failed                   */
+    W4_ERR_NOMEM = -7,        /* allocation failed (sweep creation only)     */
+    W4_ERR_ARCH = -8,         /* current device is not gfx950                */
+    W4_ERR_TIMEOUT = -9       /* a bounded in-kernel wait gave up            */
+};
+
+enum w4_dtype { W4_F32 = 0, W4_BF16 = 1 };
+
+/* Text for a status code (static storage). */
+const char* w4_status_str(int status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* w4_last_error(void);
+
+/* W4_OK if the current HIP device is gfx950, W4_ERR_ARCH otherwise,
+ * W4_ERR_HIP if no device can be queried. */
+int w4_device_check(void);
+
+/* Library build information: "<abi version> <offload arch> <kernel set>". */
+const char* w4_build_info(void);
+
+/*
+ * Bytes of the device layout for an N x K matrix (0 when the shape is
+ * invalid: N < 1, K < 1, group not 32 or 256, K % group != 0).
+ */
+size_t w4_packed_bytes(int N, int K, int group);
+
+/*
+ * Canonical (P, S) -> device layout, on the device.  P_canon: device,
+ * N*K/8 uint32.  S_bf16: device, N*(K/group) uint16.  packed_out: device,
+ * w4_packed_bytes(N, K, group) bytes, 16-byte aligned; must not overlap the
+ * inputs.  [P2] "What is in the file": weights are packed once into the
+ * kernel's load order so nothing is repacked at run time.
+ */
+int w4_pack(const uint32_t* P_canon, const uint16_t* S_bf16, int N, int K,
+            int group, void* packed_out, void* stream);
+
+/* Same transform on host memory (all three pointers host). */
+int w4_pack_host(const uint32_t* P_canon, const uint16_t* S_bf16, int N,
+                 int K, int group, void* packed_out);
+
+/* Inverse of w4_pack_host: device layout (host copy) -> canonical P and S. */
+int w4_unpack_host(const void* packed, int N, int K, int group,
+                   uint32_t* P_canon, uint16_t* S_bf16);
+
+/*
+ * y = W x for one activation vector (M = 1): y[n] = sum_k w(n,k) x[k], fp32
+ * accumulation, any summation order but bitwise run-to-run deterministic.
+ * [P1] paragraph on the w4gemv.py kernel.
+ *  packed: device layout of W (N x K, group 32 or 256), 16-byte aligned.
+ *  x: device, K bf16, 16-byte aligned.
+ *  y: device, N elements of y_dtype (4-byte aligned for fp32, 2 for bf16).
+ * N >= 1; K >= 32 and K % group == 0.
+ */
+int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
+               void* y, int y_dtype, void* stream);
+
+/*
+ * Y = X W^T for 2 <= M <= 16 activation rows, reading each weight byte once
+ * for all M rows ([P2] "Why AMX for GEMM but not for attention": a weight GEMM
+ * reuses each byte across all M rows).
+ *  X: device, M rows of K bf16, row stride ldx >= K elements (ldx % 8 == 0),
+ *     16-byte aligned.
+ *  Y: device, M rows of N y_dtype elements, row stride ldy >= N elements.
+ */
+int w4a16_gemm_smallM(const void* packed, int N, int K, int group, int M,
+                      const uint16_t* X, int ldx, void* Y, int ldy,
+                      int y_dtype, void* stream);
+
+/*
+ * Blockwise fast Walsh-Hadamard transform of activations along K ([P2]
+ * "What is in the file"): every contiguous block of `block` elements of each
+ * row is multiplied by the Sylvester-ordered Hadamard matrix of that size
+ * scaled by block^-1/2 (orthonormal).  fp32 arithmetic, bf16 result (round to
+ * nearest even).  block is a power of two, 2 <= block <= 1024, K % block == 0.
+ *  X: device, M x K bf16, stride ldx (>= K, % 8 == 0).  Xout: device, stride
+ *  ldo.  Xout may equal X (in place) when ldo == ldx.
+ */
+int w4_fwht(const uint16_t* X, int ldx, uint16_t* Xout, int ldo, int M, int K,
+            int block, void* stream);
+
+/* Workspace bytes w4a16_gemm needs (0 when had_block == 0). */
+size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block);
+
+/*
+ * Y = X' W'^T, the prefill-shaped product on the matrix cores (bf16 MFMA,
+ * fp32 accumulation): X' = X when had_block == 0, else X' is the blockwise
+ * FWHT of X (block had_block, computed into `workspace`, M*K bf16) and W' is
+ * stored pre-rotated.  Codes enter the matrix cores as exact bf16 integers;
+ * each K-group's partial product is multiplied by its fp32 scale.
+ *  group must be 256 (the rotated prefill format of [P2]) or 32.
+ *  M >= 1, K % 256 == 0.  Row counts of 16 or fewer are decode-shaped and run
+ *  on the vector-ALU kernels (M = 1: the GEMV, 2..16: the small-M product)
+ *  after the same transform; M > 16 runs on the matrix cores.
+ *  X: device, stride ldx (% 8 == 0).  Y: device, stride ldy.
+ *  workspace: device, >= w4a16_gemm_workspace_bytes(M, K, had_block) bytes,
+ *  16-byte aligned (may be NULL when that size is 0).
+ */
+int w4a16_gemm(const void* packed, int N, int K, int group, int M,
+               const uint16_t* X, int ldx, int had_block, void* workspace,
+               size_t ws_bytes, void* Y, int ldy, int y_dtype, void* stream);
+
+/*
+ * A decode step's worth of GEMVs replayed as one unit ([P1] paragraph on the
+ * decode step captured once as a graph and replayed per token).
+ * Each op is one w4a16_gemv (M = 1).  The handle owns its graph, its
+ * executable graph and a small device buffer (op table, counters, flags); it
+ * BORROWS every pointer in `ops`, which must stay valid while the handle
+ * lives.  Ops run in array order.
+ * Modes:
+ *  W4_SWEEP_GRAPH      one GEMV kernel per op captured into a hipGraph;
+ *                      op i+1 starts after op i has finished (stream order).
+ *  W4_SWEEP_PERSISTENT one persistent kernel walks all ops in order; weight
+ *                      tiles are prefetched ahead across op boundaries, but no
+ *                      output of op i+1 is computed (and no activation of op
+ *                      i+1 is read) before every output of op i is written:
+ *                      the same ordering as a decode step.  Bounded waits:
+ *                      a wait that exceeds its limit ends the kernel and is
+ *                      reported by w4_decode_sweep_check as W4_ERR_TIMEOUT.
+ *  W4_SWEEP_STREAM     the persistent kernel without the op-to-op ordering
+ *                      (ops treated as independent); an upper bound.
+ * Persistent modes are captured into a hipGraph as well.
+ */
+typedef struct w4_gemv_op {
+    const void* packed;      /* device layout of this op's weights   */
+    int N, K, group;         /* shape; group 32 or 256               */
+    const uint16_t* x;       /* device, K bf16, 16-byte aligned      */
+    void* y;                 /* device, N elements of y_dtype        */
+    int y_dtype;             /* W4_F32 or W4_BF16                    */
+} w4_gemv_op;
+
+enum w4_sweep_mode {
+    W4_SWEEP_GRAPH = 0,
+    W4_SWEEP_PERSISTENT = 1,
+    W4_SWEEP_STREAM = 2
+};
+
+typedef struct w4_sweep w4_sweep;
+
+/* Validates every op, builds and instantiates the graph on `stream`. */
+int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode,
+                           void* stream, w4_sweep** out);
+/* One replay: a single hipGraphLaunch on `stream`. */
+int w4_decode_sweep_launch(w4_sweep* h, void* stream);
+/* Synchronizes `stream` and reports a timed-out wait of a persistent replay
+ * since the last check (W4_ERR_TIMEOUT), else W4_OK. */
+int w4_decode_sweep_check(w4_sweep* h, void* stream);
+/* Number of ops, total algorithmic weight bytes, kernels per replay. */
+int w4_decode_sweep_info(const w4_sweep* h, int* n_ops, size_t* weight_bytes,
+                         int* kernels_per_replay);
+int w4_decode_sweep_destroy(w4_sweep* h);
+
+/*
+ * The kernel and tile the dispatcher picks for (M, N, K, group), as text
+ * (e.g. "gemv L=16 U=3 W=4 grid=512"), written NUL-terminated into buf.
+ * [P1] paragraph on the w4gemv.py kernel: each weight shape gets its own
+ * fixed tiling.
+ */
+int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
+                         size_t len);
+
+/*
+ * Plain-sum read of `bytes` of device memory (the measurement the summary line
+ * of [P1]'s kernel compares against): *out = sum of the buffer's 32-bit words
+ * as unsigned integers modulo 2^32 (integer sum, so the result does not depend
+ * on the order of reads).  buf: device, 16-byte aligned, bytes % 16 == 0,
+ * bytes > 0.  out: device, one uint32, 4-byte aligned.
+ */
+int w4_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
+/* Plain copy of `bytes` (16-byte aligned pointers, bytes % 16 == 0): the
+ * reference kernel for calibrating hardware byte counters. */
+int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

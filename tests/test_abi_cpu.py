@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol its
+header declares, rejects bad arguments before any HIP call, and the host
+packer is the documented bijection."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_weight_only_w4a16_amd as w4
+from bit_weight_only_w4a16_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(w4.LIB_PATH):
+        from bit_weight_only_w4a16_amd import build
+        build.build(verbose=False)
+    return w4.lib()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(w4[a-z0-9_A-Z]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(w4.EXPORTS) == names
+
+
+def test_status_strings(L):
+    for code, name in w4.STATUS.items():
+        s = L.w4_status_str(code).decode()
+        assert s and s != "unknown status", (code, name)
+    assert L.w4_status_str(-1000).decode() == "unknown status"
+
+
+def test_packed_bytes(L):
+    assert w4.packed_bytes(256, 512, 32) == 65536 + 8192
+    # codes then scales, each padded to 256 bytes
+    assert w4.packed_bytes(1, 32, 32) == 256 + 256
+    assert w4.packed_bytes(262144, 1536, 32) == 201326592 + 25165824
+    assert w4.packed_bytes(12288, 1536, 256) == 9437184 + 147456
+    for bad in [(0, 512, 32), (16, 48, 32), (16, 512, 64), (16, 256, 512), (-1, 32, 32)]:
+        assert w4.packed_bytes(*bad) == 0
+
+
+VP = ctypes.c_void_p
+A16 = VP(0x10000)   # aligned, never dereferenced: validation fails first
+A2 = VP(0x10002)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A16, 256, 512, 64, A16, A16, 0), -2),       # group
+    ((A16, 0, 512, 32, A16, A16, 0), -2),         # N
+    ((A16, 256, 500, 32, A16, A16, 0), -2),       # K % group
+    ((A16, 256, 512, 32, A16, A16, 7), -4),       # dtype
+    ((VP(0), 256, 512, 32, A16, A16, 0), -1),     # null packed
+    ((A16, 256, 512, 32, VP(0), A16, 0), -1),     # null x
+    ((A16, 256, 512, 32, A16, VP(0), 0), -1),     # null y
+    ((A2, 256, 512, 32, A16, A16, 0), -3),        # misaligned packed
+    ((A16, 256, 512, 32, A2, A16, 0), -3),        # misaligned x
+    ((A16, 256, 512, 32, A16, A2, 0), -3),        # fp32 y misaligned
+])
+def test_gemv_validation(L, args, status):
+    st = L.w4a16_gemv(*args, VP(0))
+    assert st == status, w4.last_error()
+    assert w4.last_error()
+
+
+def test_smallm_validation(L):
+    f = L.w4a16_gemm_smallM
+    assert f(A16, 64, 512, 32, 1, A16, 512, A16, 64, 1, VP(0)) == -2   # M < 2
+    assert f(A16, 64, 512, 32, 17, A16, 512, A16, 64, 1, VP(0)) == -2  # M > 16
+    assert f(A16, 64, 512, 32, 4, A16, 500, A16, 64, 1, VP(0)) == -2   # ldx < K
+    assert f(A16, 64, 512, 32, 4, A16, 516, A16, 64, 1, VP(0)) == -3   # ldx % 8
+    assert f(A16, 64, 512, 32, 4, A16, 512, A16, 60, 1, VP(0)) == -2   # ldy < N
+
+
+def test_fwht_validation(L):
+    f = L.w4_fwht
+    assert f(A16, 1536, A16, 1536, 4, 1536, 384, VP(0)) == -2    # not a power of 2
+    assert f(A16, 1536, A16, 1536, 4, 1536, 2048, VP(0)) == -2   # too large
+    assert f(A16, 1536, A16, 1536, 4, 1000, 512, VP(0)) == -2    # K % block
+    assert f(A16, 1536, A16, 1544, 4, 1536, 512, VP(0)) == -1    # in place, strides differ
+    assert f(A2, 1536, A16, 1536, 4, 1536, 512, VP(0)) == -3
+
+
+def test_gemm_validation(L):
+    f = L.w4a16_gemm
+    assert f(A16, 64, 1536, 256, 64, A16, 1536, 384, A16, 1 << 20, A16, 64, 1, VP(0)) == -2
+    assert f(A16, 64, 1536, 256, 64, A16, 1536, 512, A16, 100, A16, 64, 1, VP(0)) == -2
+    assert f(A16, 64, 1536, 256, 0, A16, 1536, 0, VP(0), 0, A16, 64, 1, VP(0)) == -2
+    assert f(A16, 64, 1536, 256, 64, A16, 1536, 512, A2, 1 << 20, A16, 64, 1, VP(0)) == -3
+    assert w4.gemm_workspace_bytes(512, 1536, 512) == 512 * 1536 * 2
+    assert w4.gemm_workspace_bytes(512, 1536, 0) == 0
+
+
+def test_sweep_validation(L):
+    ops = (w4.GemvOp * 2)()
+    ops[0] = w4.GemvOp(0x10000, 64, 512, 32, 0x10000, 0x10000, 0)
+    ops[1] = w4.GemvOp(0x10000, 64, 512, 48, 0x10000, 0x10000, 0)
+    h = ctypes.c_void_p()
+    assert L.w4_decode_sweep_create(ops, 2, 0, VP(0), ctypes.byref(h)) == -2
+    assert "op 1" in w4.last_error()
+    ops[1] = w4.GemvOp(0x10002, 64, 512, 32, 0x10000, 0x10000, 0)
+    assert L.w4_decode_sweep_create(ops, 2, 0, VP(0), ctypes.byref(h)) == -3
+    assert L.w4_decode_sweep_create(ops, 2, 9, VP(0), ctypes.byref(h)) == -1
+    assert L.w4_decode_sweep_create(ops, 0, 0, VP(0), ctypes.byref(h)) == -1
+    assert L.w4_decode_sweep_launch(VP(0), VP(0)) == -1
+    assert L.w4_decode_sweep_destroy(VP(0)) == -1
+
+
+def test_probe_validation(L):
+    assert L.w4_probe_read(A16, 0, A16, VP(0)) == -2
+    assert L.w4_probe_read(A16, 24, A16, VP(0)) == -2
+    assert L.w4_probe_read(A2, 32, A16, VP(0)) == -3
+    assert L.w4_probe_copy(A16, A2, 32, VP(0)) == -3
+
+
+def test_describe_dispatch_tile_table(L):
+    # one fixed tiling per weight shape
+    assert w4.describe_dispatch(1, 12288, 1536, 32).startswith("gemv L=16 U=3")
+    assert w4.describe_dispatch(1, 262144, 1536, 32).startswith("gemv L=16 U=3")
+    assert w4.describe_dispatch(1, 1536, 6144, 32).startswith("gemv L=64 U=3")
+    assert w4.describe_dispatch(1, 2560, 1536, 32).startswith("gemv L=16 U=3")
+    assert w4.describe_dispatch(1, 256, 512, 32).startswith("gemv L=16 U=1")
+    assert w4.describe_dispatch(1, 100, 96, 32).startswith("gemv L=8 U=1")
+    assert w4.describe_dispatch(1, 100, 20000, 32).startswith("gemv_generic")
+    assert w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm")
+    assert w4.describe_dispatch(64, 12288, 1536, 256).startswith("mfma")
+    with pytest.raises(w4.W4Error):
+        w4.describe_dispatch(1, 12288, 1500, 32)
+
+
+# ---------------------------------------------------------- host packer ---
+
+def test_device_word_order_hand_typed(L):
+    # canonical word 0x76543210 holds elements 0..7 = codes 0..7; the device
+    # word keeps even elements (0, 2, 4, 6) in the low half-word and odd ones
+    # (1, 3, 5, 7) in the high half-word, in order.
+    cases = {0x76543210: 0x75316420, 0x88888888: 0x88888888,
+             0xFEDCBA98: 0xFDB9ECA8, 0x0000000F: 0x0000000F,
+             0x000000F0: 0x000F0000, 0xF0000000: 0xF0000000}
+    for canon, dev in cases.items():
+        P = np.array([[canon]], dtype=np.uint32)
+        S = np.array([[0x3F80]], dtype=np.uint16)
+        P4 = np.array([[canon, 0, 0, 0]], dtype=np.uint32)
+        buf = w4.pack_host(P4, S, 1, 32, 32)
+        assert int(buf[:4].view(np.uint32)[0]) == dev, hex(canon)
+        assert int(buf[256:258].view(np.uint16)[0]) == 0x3F80
+
+
+@pytest.mark.parametrize("N,K,group", [(1, 32, 32), (33, 96, 32), (7, 512, 256),
+                                       (65, 1536, 32)])
+def test_host_pack_round_trip(L, N, K, group):
+    rng = np.random.default_rng(N * K)
+    P, S = synth.draw_weights(rng, N, K, group)
+    buf = w4.pack_host(P, S, N, K, group)
+    assert buf.size == w4.packed_bytes(N, K, group)
+    P2, S2 = w4.unpack_host(buf, N, K, group)
+    assert np.array_equal(P, P2) and np.array_equal(S, S2)
+
+
+def test_library_load_makes_no_gpu_call(L):
+    # no device on this host: the build info is static, device_check fails cleanly
+    assert "gfx950" in w4.build_info()

@@ -1,0 +1,125 @@
+"""GPU parity of the blockwise FWHT (w4_fwht), the small-M product
+(w4a16_gemm_smallM) and the prefill entry point (w4a16_gemm) against the fp64
+oracle.  The prefill workload is group 256, N=12288, K=1536 with a 512-point
+Hadamard rotation along K and activations with 1% outliers x20."""
+import numpy as np
+import pytest
+
+import bit_weight_only_w4a16_amd as w4
+from bit_weight_only_w4a16_amd import synth
+
+from _util import (assert_within, bf16_ulp, device, from_dev, note, to_dev_bf16,
+                   upload_packed)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    device()
+    w4.device_check()
+
+
+# ------------------------------------------------------------------ FWHT ---
+
+@pytest.mark.parametrize("M,K,block", [(8, 1536, 512), (64, 1536, 512), (512, 1536, 512),
+                                       (3, 1024, 1024), (5, 256, 2), (7, 96, 32),
+                                       (2, 512, 64), (9, 384, 128), (1, 4096, 256)])
+def test_fwht_vs_oracle(oracle_mod, M, K, block):
+    note("fwht M=%d K=%d block=%d" % (M, K, block))
+    rng = np.random.default_rng(M * K + block)
+    Xb = synth.draw_activations(rng, M, K, outlier_frac=0.01)
+    X = to_dev_bf16(Xb)
+    got = from_dev(w4.fwht(X, block)).astype(np.float64)
+    ref = oracle_mod.fwht(oracle_mod.bf16_to_f64(Xb), block)
+    # bf16 rounding of the fp32 result (half an ulp) plus fp32 butterfly error
+    absx = np.abs(oracle_mod.bf16_to_f64(Xb)).reshape(M, K // block, block).sum(-1)
+    fp32_err = np.repeat(absx, block, axis=1) * (np.log2(block) + 2) * 2.0 ** -24
+    err = np.abs(got - ref)
+    assert np.all(err <= 0.5 * bf16_ulp(ref) * 1.0001 + fp32_err + 1e-30), err.max()
+
+
+def test_fwht_in_place_and_strided(oracle_mod):
+    import torch
+    M, K, block = 6, 1536, 512
+    rng = np.random.default_rng(2)
+    Xb = synth.draw_activations(rng, M, K)
+    big = torch.zeros((M, K + 64), dtype=torch.bfloat16, device=device())
+    big[:, :K] = to_dev_bf16(Xb)
+    view = big[:, :K]
+    ref = from_dev(w4.fwht(to_dev_bf16(Xb), block))
+    w4.fwht(view, block, out=view)
+    assert np.array_equal(from_dev(view), ref)
+    assert np.all(from_dev(big[:, K:]) == 0.0)
+
+
+def test_fwht_twice_is_identity_within_rounding():
+    M, K, block = 4, 1536, 512
+    rng = np.random.default_rng(9)
+    Xb = synth.draw_activations(rng, M, K)
+    X = to_dev_bf16(Xb)
+    back = from_dev(w4.fwht(w4.fwht(X, block), block))
+    x = synth.bf16_bits_to_f32(Xb)
+    assert np.all(np.abs(back - x) <= 4 * bf16_ulp(x) + 1e-2 * np.abs(x).max() * 2 ** -7)
+
+
+# --------------------------------------------------------------- small M ---
+
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8, 11, 16])
+@pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (97, 288, 32), (1536, 6144, 32),
+                                   (33, 16384, 32), (65, 1024, 256)])
+def test_smallm_vs_oracle(oracle_mod, M, N, K, g):
+    note("smallM M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    case = synth.make_case("smallm", N, K, g, M, 10 * M + N + K, "bf16")
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    for out_dtype in ("bf16", "f32"):
+        Y = from_dev(w4.gemm_smallM(packed, N, K, g, X, out_dtype))
+        Yr, A = oracle_mod.gemm_bf16(case.P, case.S, N, K, g, case.X, threads=16)
+        assert_within(Y, Yr, A, out_dtype, "smallM M=%d" % M)
+
+
+def test_smallm_rows_equal_gemv_bitwise():
+    """Each row of the small-M product equals the batch-1 GEMV of that row
+    within fp32 rounding of a different summation order; row m only depends
+    on X[m]."""
+    import torch
+    N, K, g, M = 2560, 1536, 32, 5
+    case = synth.make_case("rows", N, K, g, M, 77, "f32")
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    Y = from_dev(w4.gemm_smallM(packed, N, K, g, X, "f32"))
+    X2 = X.clone()
+    X2[3] = 0
+    Y2 = from_dev(w4.gemm_smallM(packed, N, K, g, X2, "f32"))
+    assert np.array_equal(Y[[0, 1, 2, 4]], Y2[[0, 1, 2, 4]])
+    assert np.all(Y2[3] == 0.0)
+    del torch
+
+
+# ---------------------------------------------------- prefill (group 256) ---
+
+@pytest.mark.parametrize("M", [8, 64, 512])
+def test_prefill_g256_hadamard(oracle_mod, M):
+    """The prefill workload: W' stored (drawn directly as the rotated weights),
+    x' = FWHT_512(x) at run time.  The oracle uses the exact fp64 transform;
+    the GPU rounds x' to bf16 before the product (within the tolerance)."""
+    case = synth.prefill_g256(M)
+    N, K, g = case.N, case.K, case.group
+    note("prefill M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    try:
+        Y = from_dev(w4.gemm(packed, N, K, g, X, had_block=512, out_dtype="bf16"))
+    except w4.W4Error as e:
+        if e.status == -5:
+            pytest.skip("matrix-core tile not built: %s" % e)
+        raise
+    xr = oracle_mod.fwht(oracle_mod.bf16_to_f64(case.X), 512)
+    if M > 64:
+        rows = np.random.default_rng(0).choice(M, 48, replace=False)
+        Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr[rows], threads=16)
+        assert_within(Y[rows], Yr, A, "bf16", "prefill M=%d (sampled rows)" % M)
+    else:
+        Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr, threads=16)
+        assert_within(Y, Yr, A, "bf16", "prefill M=%d" % M)

@@ -1,0 +1,75 @@
+"""GPU parity of the decode-step sweep: 35 layers x {qkv, o, gate_up, down}
+plus the lm_head, every matrix with its own seed and activation, replayed as
+one graph.  Every one of the 141 outputs is checked against the oracle, and a
+second replay must give identical bits."""
+import numpy as np
+import pytest
+
+import bit_weight_only_w4a16_amd as w4
+from bit_weight_only_w4a16_amd import synth
+
+from _util import assert_within, device, from_dev, note, to_dev_bf16, upload_packed
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sweep_data(oracle_mod):
+    import torch
+    device()
+    w4.device_check()
+    cases = synth.decode_sweep()
+    ops, refs = [], []
+    for c in cases:
+        packed = upload_packed(c.P, c.S, c.N, c.K, c.group)
+        x = to_dev_bf16(c.X[0])
+        dt = torch.float32 if c.out_dtype == "f32" else torch.bfloat16
+        y = torch.full((c.N,), float("nan"), dtype=dt, device=device())
+        ops.append((packed, c.N, c.K, c.group, x, y))
+    torch.cuda.synchronize()
+    return cases, ops
+
+
+def _check_all(oracle_mod, cases, ops, what):
+    worst = 0.0
+    for c, op in zip(cases, ops):
+        Y, A = oracle_mod.gemm_bf16(c.P, c.S, c.N, c.K, c.group, c.X[0], threads=16)
+        worst = max(worst, assert_within(from_dev(op[5]), Y, A, c.out_dtype,
+                                         "%s %s seed %d" % (what, c.name, c.seed)))
+    return worst
+
+
+MODES = [("graph", w4.W4_SWEEP_GRAPH), ("persistent", w4.W4_SWEEP_PERSISTENT),
+         ("stream", w4.W4_SWEEP_STREAM)]
+
+
+@pytest.mark.parametrize("name,mode", MODES)
+def test_sweep_all_outputs(oracle_mod, sweep_data, name, mode):
+    import torch
+    cases, ops = sweep_data
+    note("sweep mode=%s ops=%d" % (name, len(ops)))
+    for op in ops:
+        op[5].fill_(float("nan"))
+    try:
+        sw = w4.DecodeSweep(ops, mode)
+    except w4.W4Error as e:
+        if e.status == -5:
+            pytest.skip("mode not built: %s" % e)
+        raise
+    info = sw.info()
+    assert info["n_ops"] == 141
+    assert info["weight_bytes"] == 923_222_016
+    sw.launch()
+    sw.check()
+    torch.cuda.synchronize()
+    worst = _check_all(oracle_mod, cases, ops, name)
+    note("  worst err/bound = %.3g" % worst)
+    first = [from_dev(op[5]).copy() for op in ops]
+    for _ in range(3):
+        sw.launch()
+    sw.check()
+    torch.cuda.synchronize()
+    for a, op in zip(first, ops):
+        b = from_dev(op[5])
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    sw.close()
