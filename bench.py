@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark: W4A16 GEMV effective HBM GB/s and ms per decode-step sweep.
+
+One step = one replay of a decode step's weight sweep on one GPU: 35 decoder
+layers x {qkv 2560x1536, o 1536x2048, gate_up 12288x1536, down 1536x6144}
+plus the lm_head 262144x1536, int4 codes with bf16 scales per group of 32,
+M = 1, 923,222,016 weight bytes, synthetic seeded weights and activations
+(no trained weights).  Inputs are resident in HBM before timing.  GB/s counts
+weight bytes with 1 GB = 1e9 B, the accounting of the pages' own figures
+([P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp",
+summary line of the w4gemv.py kernel).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--mode stream]
+
+Prints one JSON line.  The timed mode (default "stream") replays the 141
+independent GEMVs as one persistent kernel captured in a graph; the other
+modes (one kernel per GEMV in a graph; decode-ordered persistent kernel) and a
+plain-sum read of a 4 GiB buffer are measured alongside and reported under
+"extra".  The CPU baseline times the fp64 oracle on one full sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV effective HBM GB/s (% of peak) + ms per 35-layer+lm_head sweep"
+PEAK_HBM_GBPS = 8000.0
+MODES = {"graph": 0, "persistent": 1, "stream": 2}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sweep_stream.json")
+KERNEL_SOURCES = ("bit_weight_only_w4a16_amd/csrc/w4_persist.hip",
+                  "bit_weight_only_w4a16_amd/csrc/w4_persist.h",
+                  "bit_weight_only_w4a16_amd/csrc/w4_common.h")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(weight_bytes: int):
+    """HBM bytes per launch of the stream kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def upload_sweep(torch, w4, synth, dev):
+    cases = synth.decode_sweep()
+    ops = []
+    for c in cases:
+        import numpy as np
+        P = torch.from_numpy(c.P.view(np.int32)).to(dev)
+        S = torch.from_numpy(c.S.view(np.int16)).to(dev)
+        packed = w4.pack(P, S, c.N, c.K, c.group)
+        del P, S
+        x = torch.from_numpy(c.X[0].view(np.int16)).to(dev).view(torch.bfloat16)
+        dt = torch.float32 if c.out_dtype == "f32" else torch.bfloat16
+        y = torch.empty(c.N, dtype=dt, device=dev)
+        ops.append((packed, c.N, c.K, c.group, x, y))
+    torch.cuda.synchronize()
+    return cases, ops
+
+
+def time_sweep(torch, sw, steps, warmup):
+    for _ in range(warmup):
+        sw.launch()
+    sw.check()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        sw.launch()
+    e1.record()
+    torch.cuda.synchronize()
+    sw.check()
+    return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def probe_read(torch, w4, dev, nbytes=4 << 30, reps=10):
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    out = torch.empty(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        w4.probe_read(buf, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        w4.probe_read(buf, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def cpu_baseline(cases, max_threads=16, min_seconds=2.0, max_passes=4):
+    """The fp64 oracle over whole decode-step sweeps (all 141 GEMVs), OpenMP
+    over rows, repeated until min_seconds of wall time (at most max_passes)."""
+    import oracle
+    oracle.build()
+    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    total = 0
+    passes = 0
+    t0 = time.perf_counter()
+    while passes < max_passes:
+        for c in cases:
+            oracle.gemm_bf16(c.P, c.S, c.N, c.K, c.group, c.X[0], threads=threads)
+            total += c.weight_bytes
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": total / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full decode-step sweep(s) (141 GEMVs, %d weight bytes each) in "
+                      "%.1f s with the scalar fp64 oracle" % (passes, total // passes, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=sorted(MODES), default="stream")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_only_w4a16_amd as w4
+    from bit_weight_only_w4a16_amd import synth
+
+    dev = torch.device("cuda:0")
+    w4.device_check()
+    log("generating and packing the sweep")
+    cases, ops = upload_sweep(torch, w4, synth, dev)
+    weight_bytes = sum(c.weight_bytes for c in cases)
+    io_bytes = sum(c.K * 2 + c.N * (4 if c.out_dtype == "f32" else 2) for c in cases)
+
+    extra = {}
+    results = {}
+    order = [args.mode] + ([m for m in ("stream", "graph", "persistent") if m != args.mode]
+                           if not args.no_extra else [])
+    for name in order:
+        sw = w4.DecodeSweep(ops, MODES[name])
+        steps = args.steps if name == args.mode else max(5, min(args.steps, 20))
+        warm = args.warmup if name == args.mode else 3
+        ms = time_sweep(torch, sw, steps, warm)
+        info = sw.info()
+        results[name] = {"ms_per_sweep": ms, "GBps": weight_bytes / (ms * 1e-3) / 1e9,
+                         "kernels_per_sweep": info["kernels"]}
+        log("%-10s %.1f us/sweep  %.1f GB/s" % (name, ms * 1e3, results[name]["GBps"]))
+        sw.close()
+    ms = results[args.mode]["ms_per_sweep"]
+    value = weight_bytes / (ms * 1e-3) / 1e9
+
+    if not args.no_extra:
+        probe = probe_read(torch, w4, dev)
+        extra = {
+            "pct_of_8TBps_spec": value / PEAK_HBM_GBPS * 100,
+            "probe_read_4GiB_GBps": probe,
+            "pct_of_probe_read": value / probe * 100,
+            "GBps_incl_x_y": (weight_bytes + io_bytes) / (ms * 1e-3) / 1e9,
+            "ms_per_1222.8MiB_at_this_rate": 1282203648 / (value * 1e9) * 1e3,
+            "modes": results,
+        }
+
+    # roofline of the dominant (only) kernel of the timed step
+    kernels = results[args.mode]["kernels_per_sweep"]
+    achieved = weight_bytes / kernels / (ms / kernels * 1e-3) / 1e9 if kernels == 1 else None
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": (achieved / PEAK_HBM_GBPS) if achieved else None,
+                "traffic": load_traffic(weight_bytes),
+                "kernel": "w4::stream_kernel" if args.mode == "stream" else args.mode}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one sweep")
+        cpu = cpu_baseline(cases)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode-step weight sweep: 35 x {qkv 2560x1536, o 1536x2048, "
+                        "gate_up 12288x1536, down 1536x6144} + lm_head 262144x1536, "
+                        "int4 group-32 bf16 scales, M=1, fresh seed per matrix",
+            "weight_bytes": weight_bytes,
+            "ops": len(cases),
+            "mode": args.mode,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -114,13 +114,15 @@ __device__ __forceinline__ uint32_t decode_pair(uint32_t w, int j, const DecodeC
     return ((w >> (4 * j)) & k.mask) | k.magic;
 }
 
-// One 32-element chunk: init + sum over the chunk of (128 + c_k) * x_k, with q
-// the chunk's 4 device words and xr its 16 bf16 activation pairs (pair i
-// holds elements 2i, 2i+1).  Passing init = -136 * sum(x) yields
-// sum (c_k - 8) * x_k.
-__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr, float init,
+// One 32-element chunk: sum over the chunk of (128 + c_k) * x_k, with q the
+// chunk's 4 device words and xr its 16 bf16 activation pairs (pair i holds
+// elements 2i, 2i+1).  Two accumulation chains (even / odd pairs), each
+// started at zero, in the same order as chunk_bias: for a chunk whose codes
+// are all 8 the decoded pairs equal the offset pair (136, 136), both
+// computations round identically, and the chunk contributes exactly zero.
+__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr,
                                            const DecodeConsts& k) {
-    float a0 = init, a1 = 0.f;
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t w = q[d];
@@ -133,7 +135,7 @@ __device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr, float in
 }
 
 // 136 * sum of the chunk's 32 activations (the bias of chunk_dot plus the
-// code offset 8), fp32.
+// code offset 8), fp32, accumulated exactly like chunk_dot.
 __device__ __forceinline__ float chunk_bias(const uint32_t* xr) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll

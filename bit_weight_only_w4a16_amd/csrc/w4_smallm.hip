@@ -105,6 +105,7 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmallMArgs a) {
                             }
                             xb = chunk_bias(xr);
                         }
+                        // same chain order as chunk_bias (exact zero for code 8)
                         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
                         for (int i = 0; i < 16; i += 2) {

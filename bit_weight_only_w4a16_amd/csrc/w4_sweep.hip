@@ -1,4 +1,6 @@
-// w4_sweep.hip -- one decode step's GEMVs replayed as a single graph.
+// w4_sweep.hip -- one decode step's GEMVs replayed as a single graph: one
+// GEMV kernel per op (W4_SWEEP_GRAPH) or one persistent kernel for all ops
+// (W4_SWEEP_PERSISTENT, W4_SWEEP_STREAM; see w4_persist.hip).
 //
 // [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp",
 // paragraph on the decode step: hundreds of small kernels launched one at a
@@ -8,15 +10,19 @@
 #include <new>
 #include <vector>
 
-#include "w4_dispatch.h"
+#include "w4_persist.h"
 
 struct w4_sweep {
     int mode = 0;
     std::vector<w4_gemv_op> ops;
     size_t weight_bytes = 0;
     int kernels = 0;
+    int grid = 0;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
+    void* dev = nullptr;              // persistent modes: op table, ranges, control block
+    w4::SweepCtl* ctl = nullptr;
+    int* range = nullptr;             // STREAM: first tile of each wave (waves + 1)
 };
 
 namespace w4 {
@@ -50,9 +56,125 @@ static int capture_graph_nodes(w4_sweep* h, hipStream_t cs) {
     return W4_OK;
 }
 
+// Lanes per row for the persistent kernel: the smallest of 16, 32, 64 that
+// keeps every lane within kPwMaxU chunks of a row.
+static int persist_lanes(int C) {
+    if (C <= 16 * kPwMaxU) return 16;
+    if (C <= 32 * kPwMaxU) return 32;
+    return 64;
+}
+
+static int blocks_per_cu_override() {
+    const char* e = getenv("W4_SWEEP_BLOCKS_PER_CU");
+    const int v = e ? atoi(e) : 0;
+    return (v >= 1 && v <= 16) ? v : 0;
+}
+
+static int setup_persistent(w4_sweep* h) {
+    const bool dep = h->mode == W4_SWEEP_PERSISTENT;
+    int occ = 0;
+    int st = persist_occupancy(dep, &occ);
+    if (st != W4_OK) return st;
+    if (occ < 1) return fail(W4_ERR_UNSUPPORTED, "sweep: persistent kernel does not fit a CU");
+    int bpc = blocks_per_cu_override();
+    if (bpc == 0) bpc = dep ? 1 : 4;
+    if (bpc > occ) bpc = occ;  // every workgroup must be resident at once
+    int ncu = kNumCUs;
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0)
+            ncu = prop.multiProcessorCount;
+    }
+    h->grid = ncu * bpc;
+    const int GW = h->grid * kPwWaves;
+
+    const int n = (int)h->ops.size();
+    std::vector<SweepOp> tab(n);
+    long long tiles_before = 0;
+    for (int i = 0; i < n; ++i) {
+        const w4_gemv_op& o = h->ops[i];
+        SweepOp& t = tab[i];
+        t.codes = static_cast<const u32x4*>(o.packed);
+        t.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(o.packed) +
+                                                     scale_offset(o.N, o.K));
+        t.x = static_cast<const u32x4*>(static_cast<const void*>(o.x));
+        t.y = o.y;
+        t.N = o.N;
+        t.C = o.K / 32;
+        t.G = o.K / o.group;
+        t.gshift = ilog2(o.group / 32);
+        t.ydt = o.y_dtype;
+        if (dep) {
+            t.L = persist_lanes(t.C);
+            t.cfg = kCfgGeneric;
+        } else {
+            t.cfg = stream_cfg(t.C, &t.L);
+        }
+        t.lshift = ilog2(t.L);
+        t.U = (t.C + t.L - 1) / t.L;
+        t.R = 64 / t.L;
+        t.NG = (o.N + t.R - 1) / t.R;
+        t.rot = (int)(tiles_before % GW);
+        t.base = (int)tiles_before;
+        tiles_before += t.NG;
+    }
+    if (tiles_before >= (1LL << 31)) return fail(W4_ERR_SHAPE, "sweep: too many tiles");
+
+    // STREAM partition: wave b starts at the first tile whose starting byte
+    // offset reaches b * total / waves (tiles of one op are equal-sized)
+    const int parts = GW;
+    std::vector<int> range(parts + 1);
+    {
+        double total_bytes = 0.0;
+        for (const w4_gemv_op& o : h->ops)
+            total_bytes += (double)o.N * o.K / 2 + (double)o.N * (o.K / o.group) * 2;
+        int b = 0;
+        double at = 0.0;  // byte offset of the current tile
+        for (int i = 0; i < n && b <= parts; ++i) {
+            const w4_gemv_op& o = h->ops[i];
+            const double tile = (double)tab[i].R * ((double)o.K / 2 + (double)(o.K / o.group) * 2);
+            for (int t = 0; t < tab[i].NG; ++t) {
+                while (b <= parts && at >= total_bytes * b / parts) range[b++] = tab[i].base + t;
+                at += tile;
+            }
+        }
+        while (b <= parts) range[b++] = (int)tiles_before;
+        range[0] = 0;
+        range[parts] = (int)tiles_before;
+    }
+
+    const size_t tab_bytes = align_up(sizeof(SweepOp) * (size_t)n, kAlign);
+    const size_t range_bytes = align_up(sizeof(int) * (size_t)(parts + 1), kAlign);
+    const size_t total = tab_bytes + range_bytes + sweep_ctl_bytes(h->grid);
+    st = hip_fail(hipMalloc(&h->dev, total), "sweep device buffer");
+    if (st != W4_OK) {
+        h->dev = nullptr;
+        return W4_ERR_NOMEM;
+    }
+    h->range = reinterpret_cast<int*>(static_cast<uint8_t*>(h->dev) + tab_bytes);
+    h->ctl = reinterpret_cast<SweepCtl*>(static_cast<uint8_t*>(h->dev) + tab_bytes + range_bytes);
+    st = hip_fail(hipMemcpy(h->dev, tab.data(), sizeof(SweepOp) * (size_t)n,
+                            hipMemcpyHostToDevice), "sweep op table");
+    if (st != W4_OK) return st;
+    st = hip_fail(hipMemcpy(h->range, range.data(), sizeof(int) * (size_t)(parts + 1),
+                            hipMemcpyHostToDevice), "sweep ranges");
+    if (st != W4_OK) return st;
+    st = hip_fail(hipMemset(h->ctl, 0, sweep_ctl_bytes(h->grid)), "sweep control block");
+    if (st != W4_OK) return st;
+    return hip_fail(hipDeviceSynchronize(), "sweep setup");
+}
+
+static int capture_persistent(w4_sweep* h, hipStream_t cs) {
+    h->kernels = 1;
+    return launch_persist(h->mode == W4_SWEEP_PERSISTENT, static_cast<const SweepOp*>(h->dev),
+                          (int)h->ops.size(), h->ctl, h->range, h->grid, cs);
+}
+
 static void release(w4_sweep* h) {
     if (h->exec) (void)hipGraphExecDestroy(h->exec);
     if (h->graph) (void)hipGraphDestroy(h->graph);
+    if (h->dev) (void)hipFree(h->dev);
     delete h;
 }
 
@@ -74,8 +196,13 @@ int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode, void* str
         const int st = check_op(ops[i], i);
         if (st != W4_OK) return st;
     }
-    if (mode != W4_SWEEP_GRAPH)
-        return fail(W4_ERR_UNSUPPORTED, "sweep: persistent modes are not built yet");
+    if (mode != W4_SWEEP_GRAPH) {
+        for (int i = 0; i < n_ops; ++i)
+            if (ops[i].K / 32 > kPwMaxC)
+                return fail(W4_ERR_UNSUPPORTED,
+                            "sweep op %d: persistent modes serve K <= %d (got %d)", i,
+                            kPwMaxC * 32, ops[i].K);
+    }
     w4_sweep* h = new (std::nothrow) w4_sweep;
     if (!h) return fail(W4_ERR_NOMEM, "sweep: host allocation failed");
     h->mode = mode;
@@ -89,9 +216,15 @@ int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode, void* str
         release(h);
         return st;
     }
-    st = hip_fail(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal), "begin capture");
+    // persistent modes: the op table and control block are allocated and
+    // filled before capture; the capture records only kernel launches.
+    if (mode != W4_SWEEP_GRAPH) st = setup_persistent(h);
+    if (st == W4_OK)
+        st = hip_fail(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal),
+                      "begin capture");
     if (st == W4_OK) {
-        const int cst = capture_graph_nodes(h, cs);
+        const int cst = mode == W4_SWEEP_GRAPH ? capture_graph_nodes(h, cs)
+                                               : capture_persistent(h, cs);
         const int est = hip_fail(hipStreamEndCapture(cs, &h->graph), "end capture");
         st = cst != W4_OK ? cst : est;
     }
@@ -114,7 +247,18 @@ int w4_decode_sweep_launch(w4_sweep* h, void* stream) {
 
 int w4_decode_sweep_check(w4_sweep* h, void* stream) {
     if (!h) return fail(W4_ERR_ARG, "sweep: bad handle");
-    return hip_fail(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "sweep sync");
+    int st = hip_fail(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "sweep sync");
+    if (st != W4_OK || !h->ctl) return st;
+    unsigned err = 0;
+    st = hip_fail(hipMemcpy(&err, &h->ctl->error, sizeof err, hipMemcpyDeviceToHost),
+                  "sweep error word");
+    if (st != W4_OK) return st;
+    if (err != 0) {
+        const unsigned zero = 0;
+        (void)hipMemcpy(&h->ctl->error, &zero, sizeof zero, hipMemcpyHostToDevice);
+        return fail(W4_ERR_TIMEOUT, "sweep: a bounded in-kernel wait gave up");
+    }
+    return W4_OK;
 }
 
 int w4_decode_sweep_info(const w4_sweep* h, int* n_ops, size_t* weight_bytes,
