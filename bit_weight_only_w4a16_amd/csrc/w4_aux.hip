@@ -44,35 +44,44 @@ __global__ void zero_u32_kernel(uint32_t* p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0u;
 }
 
+// Each wave sums its own contiguous slice of the buffer, 1 KB per load
+// instruction, 8 non-temporal loads in flight per lane (the access pattern
+// that reads fastest on gfx950); the remainder is summed grid-stride.
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ buf,
                                                          size_t n16, uint32_t* out) {
+    constexpr int kUnroll = 8;
+    const int lane = threadIdx.x & 63;
+    const size_t nw = (size_t)gridDim.x * (blockDim.x >> 6);
+    const size_t gw = (size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const size_t per = n16 / nw / (64 * kUnroll) * (64 * kUnroll);  // per wave
     uint32_t acc = 0u;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // four independent loads in flight per lane per step
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 a = nt_load(buf + i);
-        const u32x4 b = nt_load(buf + i + stride);
-        const u32x4 c = nt_load(buf + i + 2 * stride);
-        const u32x4 d = nt_load(buf + i + 3 * stride);
-        acc += (a[0] + a[1] + a[2] + a[3]) + (b[0] + b[1] + b[2] + b[3]) +
-               (c[0] + c[1] + c[2] + c[3]) + (d[0] + d[1] + d[2] + d[3]);
+    const u32x4* p = buf + gw * per + lane;
+    for (size_t j = 0; j < per; j += 64 * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = nt_load(p + j + 64 * u);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc += v[u][0] + v[u][1] + v[u][2] + v[u][3];
     }
-    for (; i < n16; i += stride) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = per * nw + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += stride) {
         const u32x4 a = nt_load(buf + i);
         acc += a[0] + a[1] + a[2] + a[3];
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if ((threadIdx.x & 63) == 0) atomicAdd(out, acc);
+    if (lane == 0) atomicAdd(out, acc);
 }
 
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* out, hipStream_t s) {
     zero_u32_kernel<<<1, 64, 0, s>>>(out);
     const size_t n16 = bytes / 16;
-    size_t blocks = (n16 + 255) / 256;
-    const size_t cap = (size_t)kNumCUs * 8;
+    // up to 2048 waves (8 per CU); fewer for small buffers
+    size_t blocks = (n16 + 256 * 8 - 1) / (256 * 8);
+    const size_t cap = (size_t)kNumCUs * 2;
     if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
     probe_read_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
         static_cast<const u32x4*>(buf), n16, out);
     return hip_fail(hipGetLastError(), "probe read launch");

@@ -55,13 +55,14 @@ __device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
 // Row groups rg0, rg0 + step, ... (< rg1) of one matrix for one wave.
 // FULLC: L * U == C.  Otherwise lanes past the row end read a clamped, valid
 // chunk and multiply it by a zero activation slice.  Rows past N are clamped
-// to row N - 1 and not stored, so the loop has no divergent branches.  Two
-// register stages alternate: the next row group is in flight while the
+// to row N - 1 and not stored, so the loop has no divergent branches.
+// STAGES register sets rotate: STAGES - 1 row groups are in flight while the
 // current one is decoded.  Lane partials are summed in a fixed order, so the
 // result is bitwise deterministic.
-template <int L, int U, bool FULLC>
+template <int L, int U, bool FULLC, int STAGES = 2>
 __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, int step,
                                           int lane, const DecodeConsts& k) {
+    static_assert(STAGES == 2 || STAGES == 3, "register stages");
     constexpr int R = 64 / L;
     const int lk = lane % L;
     const int lr = lane / L;
@@ -102,18 +103,40 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
     };
 
     int rg = rg0;
-    u32x4 qa[U], qb[U];
-    uint32_t sa[U], sb[U];
-    load(rg, qa, sa);
-    while (true) {
+    if (STAGES == 2) {
+        u32x4 qa[U], qb[U];
+        uint32_t sa[U], sb[U];
+        load(rg, qa, sa);
+        while (true) {
+            if (rg + step < rg1) load(rg + step, qb, sb);
+            finish(rg, qa, sa);
+            rg += step;
+            if (rg >= rg1) break;
+            if (rg + step < rg1) load(rg + step, qa, sa);
+            finish(rg, qb, sb);
+            rg += step;
+            if (rg >= rg1) break;
+        }
+    } else {
+        // three stages: two row groups in flight while one is decoded
+        u32x4 qa[U], qb[U], qc[U];
+        uint32_t sa[U], sb[U], sc[U];
+        load(rg, qa, sa);
         if (rg + step < rg1) load(rg + step, qb, sb);
-        finish(rg, qa, sa);
-        rg += step;
-        if (rg >= rg1) break;
-        if (rg + step < rg1) load(rg + step, qa, sa);
-        finish(rg, qb, sb);
-        rg += step;
-        if (rg >= rg1) break;
+        while (true) {
+            if (rg + 2 * step < rg1) load(rg + 2 * step, qc, sc);
+            finish(rg, qa, sa);
+            rg += step;
+            if (rg >= rg1) break;
+            if (rg + 2 * step < rg1) load(rg + 2 * step, qa, sa);
+            finish(rg, qb, sb);
+            rg += step;
+            if (rg >= rg1) break;
+            if (rg + 2 * step < rg1) load(rg + 2 * step, qb, sb);
+            finish(rg, qc, sc);
+            rg += step;
+            if (rg >= rg1) break;
+        }
     }
 }
 

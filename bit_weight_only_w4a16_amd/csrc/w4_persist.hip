@@ -34,6 +34,13 @@
 namespace w4 {
 
 constexpr unsigned kSpinLimit = 1u << 18;
+#ifndef W4_STREAM_STAGES
+#define W4_STREAM_STAGES 2
+#endif
+#ifndef W4_STREAM_WAVES_PER_EU
+#define W4_STREAM_WAVES_PER_EU 4
+#endif
+constexpr int kStreamStages = W4_STREAM_STAGES;  // register stages per wave
 
 struct TileRegs {
     u32x4 q[kPwMaxU];
@@ -237,9 +244,12 @@ __global__ __launch_bounds__(kPwThreads) void ordered_kernel(const SweepOp* __re
 // into one contiguous, byte-balanced range per wave (range[w] .. range[w+1]),
 // so each wave streams about total/waves bytes, crossing only the few op
 // boundaries inside its range.  Within one op the wave runs the batch-1 GEMV
-// inner loop over consecutive row groups (activation slice in registers, two
-// register stages); there is no LDS, no barrier and no inter-wave
-// communication.  The op's tile shape (L, U) selects a compiled loop.
+// inner loop over consecutive row groups (activation slice in registers, next
+// row group in flight); there is no LDS, no barrier and no communication
+// between waves.  The op's tile shape (L, U) selects a compiled loop.
+// (Handing tiles out through a per-workgroup counter evens out the waves'
+// finishing times but measured slower: the counter sits between one tile's
+// compute and the next tile's loads.)
 template <int L, int U>
 __device__ __forceinline__ void stream_rows(const SweepOp& op, int rg0, int rg1, int lane,
                                             const DecodeConsts& k) {
@@ -254,13 +264,14 @@ __device__ __forceinline__ void stream_rows(const SweepOp& op, int rg0, int rg1,
     a.gshift = op.gshift;
     a.ydt = op.ydt;
     if (U > 0)
-        gemv_rows<L, (U > 0 ? U : 1), true>(a, rg0, rg1, 1, lane, k);
+        gemv_rows<L, (U > 0 ? U : 1), true, kStreamStages>(a, rg0, rg1, 1, lane, k);
     else
         gemv_rows_generic<L>(a, rg0, rg1, 1, lane, k);
 }
 
-// (at most 128 VGPRs: four waves per SIMD)
-__global__ __launch_bounds__(kPwThreads) __attribute__((amdgpu_waves_per_eu(4)))
+// (register budget for W4_STREAM_WAVES_PER_EU waves per SIMD: 4 -> 128 VGPRs)
+__global__ __launch_bounds__(kPwThreads)
+__attribute__((amdgpu_waves_per_eu(W4_STREAM_WAVES_PER_EU)))
 void stream_kernel(const SweepOp* __restrict__ ops, int n_ops, const int* __restrict__ range) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -77,7 +77,7 @@ static int setup_persistent(w4_sweep* h) {
     if (st != W4_OK) return st;
     if (occ < 1) return fail(W4_ERR_UNSUPPORTED, "sweep: persistent kernel does not fit a CU");
     int bpc = blocks_per_cu_override();
-    if (bpc == 0) bpc = dep ? 1 : 4;
+    if (bpc == 0) bpc = dep ? 1 : 5;
     if (bpc > occ) bpc = occ;  // every workgroup must be resident at once
     int ncu = kNumCUs;
     int dev = 0;
@@ -87,7 +87,7 @@ static int setup_persistent(w4_sweep* h) {
             ncu = prop.multiProcessorCount;
     }
     h->grid = ncu * bpc;
-    const int GW = h->grid * kPwWaves;
+    const int GW = h->grid * kPwWaves;  // waves of the decode-order kernel
 
     const int n = (int)h->ops.size();
     std::vector<SweepOp> tab(n);
