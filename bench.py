@@ -147,6 +147,10 @@ def main():
     ap.add_argument("--mode", choices=sorted(MODES), default="stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="for hardware-counter runs: only --steps replays of the timed "
+                         "mode, then three 1 GiB probe copies (the calibration kernel); "
+                         "prints nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU; this library has no multi-GPU path "
@@ -163,6 +167,19 @@ def main():
     cases, ops = upload_sweep(torch, w4, synth, dev)
     weight_bytes = sum(c.weight_bytes for c in cases)
     io_bytes = sum(c.K * 2 + c.N * (4 if c.out_dtype == "f32" else 2) for c in cases)
+
+    if args.kernel_only:
+        sw = w4.DecodeSweep(ops, MODES[args.mode])
+        for _ in range(args.steps):
+            sw.launch()
+        sw.check()
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            w4.probe_copy(src, dst)
+        torch.cuda.synchronize()
+        sw.close()
+        return
 
     extra = {}
     results = {}
