@@ -131,3 +131,47 @@ def test_prefill_g256_hadamard(oracle_mod, M):
     else:
         Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr, threads=16)
         assert_within(Y, Yr, A, "bf16", "prefill M=%d" % M)
+
+
+@pytest.mark.parametrize("M,N,K,g,had", [(17, 100, 256, 32, 0), (64, 12288, 1536, 32, 0),
+                                         (100, 513, 1536, 256, 512), (512, 300, 512, 256, 0),
+                                         (65, 1000, 2048, 256, 256), (33, 64, 256, 256, 0)])
+def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
+    """M > 16 runs on the matrix cores: ragged M and N, both group sizes,
+    with and without the run-time transform."""
+    note("mfma gemm M=%d N=%d K=%d g=%d had=%d" % (M, N, K, g, had))
+    case = synth.make_case("mfma", N, K, g, M, M * 31 + N + K, "bf16", outlier_frac=0.01)
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    x64 = oracle_mod.bf16_to_f64(case.X)
+    xr = oracle_mod.fwht(x64, had) if had else x64
+    rows = np.arange(M) if M <= 128 else np.random.default_rng(1).choice(M, 64, replace=False)
+    Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr[rows], threads=16)
+    for out_dtype in ("bf16", "f32"):
+        Y = from_dev(w4.gemm(packed, N, K, g, X, had_block=had, out_dtype=out_dtype))
+        assert_within(Y[rows], Yr, A, out_dtype, "mfma %s" % out_dtype)
+
+
+def test_matrix_core_code8_columns_exact_zero():
+    """Columns whose codes are all 8 are exactly zero through the matrix-core
+    path (the offset MFMA goes through the same arithmetic)."""
+    M, N, K, g = 64, 128, 1536, 256
+    rng = np.random.default_rng(4)
+    P, S = synth.draw_weights(rng, N, K, g)
+    P[5, :] = 0x88888888
+    P[77, :] = 0x88888888
+    packed = upload_packed(P, S, N, K, g)
+    X = to_dev_bf16(synth.draw_activations(rng, M, K, outlier_frac=0.01))
+    Y = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
+    assert np.all(Y[:, 5] == 0.0) and np.all(Y[:, 77] == 0.0)
+    assert np.all(Y[:, 6] != 0.0)
+
+
+def test_matrix_core_deterministic():
+    M, N, K, g = 512, 1024, 1536, 256
+    case = synth.make_case("det", N, K, g, M, 9, "bf16")
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    a = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
+    b = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
