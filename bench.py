@@ -117,6 +117,62 @@ def probe_read(torch, w4, dev, nbytes=4 << 30, reps=10):
     return gbps
 
 
+def time_calls(torch, fn, calls=20, reps=10):
+    """Microseconds per call of fn: `calls` calls captured in one graph,
+    replayed `reps` times between HIP events (no host overhead per call)."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * calls) * 1e3
+
+
+def time_prefill(torch, w4, synth, dev):
+    """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
+    run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
+    cores); also the transform alone and the product without it."""
+    import numpy as np
+    out = {}
+    for M in (8, 64, 512):
+        c = synth.prefill_g256(M)
+        P = torch.from_numpy(c.P.view(np.int32)).to(dev)
+        S = torch.from_numpy(c.S.view(np.int16)).to(dev)
+        packed = w4.pack(P, S, c.N, c.K, c.group)
+        X = torch.from_numpy(c.X.view(np.int16)).to(dev).view(torch.bfloat16)
+        Y = torch.empty((M, c.N), dtype=torch.bfloat16, device=dev)
+        Xr = torch.empty_like(X)
+        ws = torch.empty(max(1, w4.gemm_workspace_bytes(M, c.K, 512)), dtype=torch.uint8,
+                         device=dev)
+        res = {"kernel": w4.describe_dispatch(M, c.N, c.K, c.group)}
+        res["fwht_plus_gemm_us"] = time_calls(torch, lambda: w4.gemm(
+            packed, c.N, c.K, c.group, X, 512, "bf16", out=Y, workspace=ws))
+        res["gemm_us"] = time_calls(torch, lambda: w4.gemm(
+            packed, c.N, c.K, c.group, X, 0, "bf16", out=Y))
+        res["fwht_us"] = time_calls(torch, lambda: w4.fwht(X, 512, out=Xr))
+        flops = 2.0 * M * c.N * c.K
+        t = res["gemm_us"] * 1e-6
+        res["gemm_TFLOPs"] = flops / t / 1e12
+        res["gemm_pct_of_2.5PF_bf16"] = flops / t / 2.5e15 * 100
+        res["gemm_weight_GBps"] = c.weight_bytes / t / 1e9
+        out["M%d" % M] = res
+        del P, S, packed, X, Y, Xr, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cases, max_threads=16, min_seconds=2.0, max_passes=4):
     """The fp64 oracle over whole decode-step sweeps (all 141 GEMVs), OpenMP
     over rows, repeated until min_seconds of wall time (at most max_passes)."""
@@ -209,6 +265,7 @@ def main():
             "GBps_incl_x_y": (weight_bytes + io_bytes) / (ms * 1e-3) / 1e9,
             "ms_per_1222.8MiB_at_this_rate": 1282203648 / (value * 1e9) * 1e3,
             "modes": results,
+            "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
         }
 
     # roofline of the dominant (only) kernel of the timed step
