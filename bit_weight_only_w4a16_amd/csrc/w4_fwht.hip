@@ -29,8 +29,21 @@ __global__ __launch_bounds__(256) void fwht_kernel(const uint16_t* X, int ldx,
     const bool active = lane < lanes;
     const uint16_t* src = X + (size_t)m * ldx + (size_t)b * block + (size_t)lane * E;
     float v[E];
+    if (E >= 8) {
+        // E contiguous bf16 per lane, 16-byte aligned (ldx % 8 == 0)
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = active ? bf16_to_f32(src[e]) : 0.f;
+        for (int h = 0; h < E / 8; ++h) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(src)[h];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[8 * h + 2 * i] = __uint_as_float(w[i] << 16);
+                v[8 * h + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = active ? bf16_to_f32(src[e]) : 0.f;
+    }
     // spans inside a lane
 #pragma unroll
     for (int h = 1; h < E; h *= 2) {
@@ -54,8 +67,20 @@ __global__ __launch_bounds__(256) void fwht_kernel(const uint16_t* X, int ldx,
     }
     if (active) {
         uint16_t* dst = Xo + (size_t)m * ldo + (size_t)b * block + (size_t)lane * E;
+        if (E >= 8) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) dst[e] = (uint16_t)f32_to_bf16_rne(v[e] * scale);
+            for (int h = 0; h < E / 8; ++h) {
+                u32x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = f32_to_bf16_rne(v[8 * h + 2 * i] * scale) |
+                           (f32_to_bf16_rne(v[8 * h + 2 * i + 1] * scale) << 16);
+                reinterpret_cast<u32x4*>(dst)[h] = w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < E; ++e) dst[e] = (uint16_t)f32_to_bf16_rne(v[e] * scale);
+        }
     }
 }
 

@@ -5,12 +5,13 @@
 // byte across all M rows.  Each packed chunk is loaded and decoded to bf16
 // operand pairs once, then multiplied by every activation row.
 //
-// Work split as in the batch-1 GEMV: 16 lanes share a weight row (lane l owns
-// chunks l, l + 16, ...), a wave covers 4 rows per step.  The activation rows
-// and their per-chunk offset terms (136 * sum of the chunk's activations) are
-// staged once per workgroup in LDS when they fit; otherwise they are read
-// through the cache and the offset term is formed on the fly.  At this size
-// the kernel is bound by vector ALU work (one dot2 per two codes per row).
+// Work split as in the batch-1 GEMV: L lanes share a weight row (lane l owns
+// chunks l, l + L, ...), a wave covers 64/L rows per step.  The activation
+// rows and their per-chunk offset terms (136 * sum of the chunk's
+// activations) are staged once per workgroup in LDS when they fit; otherwise
+// (generic kernel) they are read through the cache and the offset term is
+// formed on the fly.  At this size the kernel is bound by vector ALU work
+// (one dot2 per two codes per row).
 #include <cstdio>
 
 #include "w4_dispatch.h"
@@ -130,14 +131,174 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmallMArgs a) {
     }
 }
 
+// Fast path: every lane owns exactly U chunks (C == L * U) and X fits LDS.
+// The row group's codes and scales for all U chunks are loaded at once, with
+// the next row group in flight (two register stages), so a wave pays one
+// memory latency per row group, not one per chunk.  Each chunk is decoded
+// once into 16 operand pairs and multiplied by the M activation rows read
+// from LDS (lanes of the same chunk read the same LDS words).  The M sums of
+// a row are reduced with DPP moves; lane m of the row then stores output m.
+template <int MT, int L, int U>
+__global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int R = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const int lk = lane % L;
+    const int lr = lane / L;
+    const DecodeConsts k = decode_consts();
+
+    // X in LDS, one 64-byte chunk per (row m, chunk c); quarter i of chunk c
+    // is stored at quarter (i + c/2) mod 4, so the 16-byte reads of eight
+    // consecutive chunks (one per lane of an 8-lane group) hit all 32 banks.
+    uint32_t* xs = reinterpret_cast<uint32_t*>(smem);                   // [M][C][16]
+    float* xbs = reinterpret_cast<float*>(smem + (size_t)a.M * a.K * 2);  // [M][C]
+    {
+        const int vec_per_row = a.K / 8;
+        for (int i = threadIdx.x; i < a.M * vec_per_row; i += blockDim.x) {
+            const int m = i / vec_per_row, v = i % vec_per_row;
+            const int c = v >> 2, q = v & 3;
+            reinterpret_cast<u32x4*>(xs)[((size_t)m * a.C + c) * 4 + ((q + (c >> 1)) & 3)] =
+                reinterpret_cast<const u32x4*>(a.X + (size_t)m * a.ldx)[v];
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < a.M * a.C; i += blockDim.x) {
+            const int c = i % a.C;
+            const u32x4* p = reinterpret_cast<const u32x4*>(xs) + (size_t)i * 4;
+            uint32_t xr[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 v = p[(q + (c >> 1)) & 3];
+                xr[4 * q + 0] = v[0];
+                xr[4 * q + 1] = v[1];
+                xr[4 * q + 2] = v[2];
+                xr[4 * q + 3] = v[3];
+            }
+            xbs[i] = chunk_bias(xr);
+        }
+        __syncthreads();
+    }
+
+    const int NG = (a.N + R - 1) / R;
+    const int stride = gridDim.x * nw;
+    int rg = blockIdx.x * nw + wave;
+    if (rg >= NG) return;
+
+    auto load = [&](int g, u32x4 (&q)[U], uint32_t (&sc)[U]) {
+        int n = g * R + lr;
+        n = n < a.N ? n : a.N - 1;
+        const u32x4* cp = a.codes + (size_t)n * a.C + lk;
+        const uint16_t* sp = a.scales + (size_t)n * a.G + (lk >> a.gshift);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            q[u] = nt_load(cp + L * u);
+            sc[u] = sp[(L * u) >> a.gshift];
+        }
+    };
+    auto finish = [&](int g, const u32x4 (&q)[U], const uint32_t (&sc)[U]) {
+        float acc[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = lk + L * u;
+            uint32_t d[16];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d[4 * w + j] = decode_pair(q[u][w], j, k);
+            const float s = bf16_to_f32(sc[u]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < a.M) {
+                    const u32x4* p =
+                        reinterpret_cast<const u32x4*>(xs) + ((size_t)m * a.C + c) * 4;
+                    uint32_t xr[16];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const u32x4 v = p[(i + (c >> 1)) & 3];
+                        xr[4 * i + 0] = v[0];
+                        xr[4 * i + 1] = v[1];
+                        xr[4 * i + 2] = v[2];
+                        xr[4 * i + 3] = v[3];
+                    }
+                    // same chain order as chunk_bias (exact zero for code 8)
+                    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; i += 2) {
+                        d0 = dot2(d[i], xr[i], d0);
+                        d1 = dot2(d[i + 1], xr[i + 1], d1);
+                    }
+                    acc[m] = fmaf(s, (d0 + d1) - xbs[m * a.C + c], acc[m]);
+                }
+            }
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float t = group_sum<L>(acc[m]);
+            if (lk == m) mine = t;
+        }
+        const int n = g * R + lr;
+        if (lk < a.M && n < a.N) store_out(a.Y, (size_t)lk * a.ldy + n, mine, a.ydt);
+    };
+
+    u32x4 qa[U], qb[U];
+    uint32_t sa[U], sb[U];
+    load(rg, qa, sa);
+    while (true) {
+        if (rg + stride < NG) load(rg + stride, qb, sb);
+        finish(rg, qa, sa);
+        rg += stride;
+        if (rg >= NG) break;
+        if (rg + stride < NG) load(rg + stride, qa, sa);
+        finish(rg, qb, sb);
+        rg += stride;
+        if (rg >= NG) break;
+    }
+}
+
 static size_t smallm_lds(int M, int K) {
     return (size_t)M * K * 2 + (size_t)M * (K / 32) * 4;
 }
 
-static int smallm_grid(int N) {
-    const int NG = (N + 3) / 4;
+static int smallm_grid(int N, int R = 4) {
+    const int NG = (N + R - 1) / R;
     const int waves = NG < kNumCUs * 8 ? NG : kNumCUs * 8;
     return (waves + 3) / 4;
+}
+
+// (L, U) of the fast path for C chunks per row, or 0 when it does not apply.
+static int smallm_fast_shape(int C, int* L) {
+    if (C == 16 || C == 32 || C == 48 || C == 64) {
+        *L = 16;
+        return C / 16;
+    }
+    if (C == 128 || C == 192) {
+        *L = 64;
+        return C / 64;
+    }
+    return 0;
+}
+
+template <int MT, int L>
+static void launch_fast_mt(int U, dim3 g, dim3 b, size_t shm, hipStream_t s, const SmallMArgs& a) {
+    switch (U) {
+        case 1: smallm_fast_kernel<MT, L, 1><<<g, b, shm, s>>>(a); break;
+        case 2: smallm_fast_kernel<MT, L, 2><<<g, b, shm, s>>>(a); break;
+        case 3: smallm_fast_kernel<MT, L, 3><<<g, b, shm, s>>>(a); break;
+        default: smallm_fast_kernel<MT, L, 4><<<g, b, shm, s>>>(a); break;
+    }
+}
+
+template <int MT>
+static void launch_fast(int L, int U, dim3 g, dim3 b, size_t shm, hipStream_t s,
+                        const SmallMArgs& a) {
+    if (L == 16)
+        launch_fast_mt<MT, 16>(U, g, b, shm, s, a);
+    else
+        launch_fast_mt<MT, 64>(U, g, b, shm, s, a);
 }
 
 template <int MT>
@@ -169,6 +330,18 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
     a.K = K;
     const size_t shm = smallm_lds(M, K);
     const bool lds = shm <= kSmLdsMax;
+    int L = 16;
+    const int U = smallm_fast_shape(K / 32, &L);
+    if (lds && U > 0) {
+        const dim3 g(smallm_grid(N, 64 / L)), b(256);
+        if (M <= 4)
+            launch_fast<4>(L, U, g, b, shm, s, a);
+        else if (M <= 8)
+            launch_fast<8>(L, U, g, b, shm, s, a);
+        else
+            launch_fast<16>(L, U, g, b, shm, s, a);
+        return hip_fail(hipGetLastError(), "smallM launch");
+    }
     const dim3 g(smallm_grid(N)), b(256);
     if (M <= 4)
         launch_mt<4>(lds, g, b, shm, s, a);
@@ -182,6 +355,13 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
 void describe_smallm(int M, int N, int K, int group, char* buf, size_t len) {
     (void)group;
     const size_t shm = smallm_lds(M, K);
+    int L = 16;
+    const int U = smallm_fast_shape(K / 32, &L);
+    if (shm <= kSmLdsMax && U > 0) {
+        snprintf(buf, len, "smallm MT=%d L=%d U=%d x=lds grid=%d", M <= 4 ? 4 : (M <= 8 ? 8 : 16),
+                 L, U, smallm_grid(N, 64 / L));
+        return;
+    }
     snprintf(buf, len, "smallm MT=%d L=%d x=%s grid=%d", M <= 4 ? 4 : (M <= 8 ? 8 : 16),
              kSmL, shm <= kSmLdsMax ? "lds" : "global", smallm_grid(N));
 }
