@@ -170,16 +170,48 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Global-memory accesses through pointers typed as global.  A pointer that
+// was read out of device memory (an op table) is generic to the compiler,
+// and generic (flat) loads hold the LDS counter as well as the vector-memory
+// counter: the wait before any LDS or cross-lane result would then also wait
+// for every weight load in flight.  Every operand these helpers touch is in
+// global memory.
+template <typename T>
+using global_t = __attribute__((address_space(1))) T;
+
 template <typename T>
 __device__ __forceinline__ T nt_load(const T* p) {
-    return __builtin_nontemporal_load(p);
+    return __builtin_nontemporal_load((const global_t<T>*)p);
+}
+
+template <typename T>
+__device__ __forceinline__ T gload(const T* p) {
+    return *(const global_t<T>*)p;
+}
+
+template <typename T>
+__device__ __forceinline__ void gstore(T* p, T v) {
+    *(global_t<T>*)p = v;
+}
+
+// Scales are read as the aligned dword that holds them (rows of an even
+// number of groups keep every row's scales dword-aligned); the bf16 is moved
+// into the high half of an fp32 with one byte permute at its use.  A 16-bit
+// load would need a conversion right after it, and the compiler places such
+// a conversion where it reuses the load's register, waiting for the load
+// there -- before the next row group's loads are issued.
+constexpr uint32_t kScaleSelLo = 0x01000C0Cu;  // bytes 1,0 -> 3,2; zeros below
+constexpr uint32_t kScaleSelHi = 0x03020C0Cu;  // bytes 3,2 -> 3,2; zeros below
+
+__device__ __forceinline__ float scale_from_word(uint32_t w, uint32_t sel) {
+    return __uint_as_float(__builtin_amdgcn_perm(0u, w, sel));
 }
 
 __device__ __forceinline__ void store_out(void* y, size_t i, float v, int ydt) {
     if (ydt == W4_BF16)
-        static_cast<uint16_t*>(y)[i] = (uint16_t)f32_to_bf16_rne(v);
+        gstore(static_cast<uint16_t*>(y) + i, (uint16_t)f32_to_bf16_rne(v));
     else
-        static_cast<float*>(y)[i] = v;
+        gstore(static_cast<float*>(y) + i, v);
 }
 
 }  // namespace w4

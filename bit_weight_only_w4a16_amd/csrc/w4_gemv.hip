@@ -81,7 +81,6 @@ static int waves_per_cu() {
 }
 
 GemvTile pick_gemv_tile(int N, int K, int group) {
-    (void)group;
     GemvTile t;
     const int C = K / 32;
     const int target = kNumCUs * waves_per_cu();
@@ -101,7 +100,9 @@ GemvTile pick_gemv_tile(int N, int K, int group) {
             }
             if (waste == best_waste) cand[nc++] = L;
         }
-        if (nc == 0) {
+        if (nc == 0 || ((K / group) & 1)) {
+            // a K with no tiling, or an odd number of groups per row (the
+            // tiled loop reads scales in dword pairs)
             t.L = 64;
             t.U = 0;
             t.generic = true;
@@ -116,7 +117,7 @@ GemvTile pick_gemv_tile(int N, int K, int group) {
             t.U = (C + L - 1) / L;
         }
         t.waves = 4;
-    } else if (t.L * t.U < C) {
+    } else if (t.L * t.U < C || ((K / group) & 1)) {
         t.generic = true;
     }
     const int R = 64 / t.L;

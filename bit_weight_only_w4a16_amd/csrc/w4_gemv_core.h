@@ -37,7 +37,7 @@ __device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
             const u32x4* p = reinterpret_cast<const u32x4*>(x + 16 * c);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const u32x4 v = p[i];
+                const u32x4 v = gload(p + i);
                 xr[u][4 * i + 0] = v[0];
                 xr[u][4 * i + 1] = v[1];
                 xr[u][4 * i + 2] = v[2];
@@ -53,13 +53,18 @@ __device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
 }
 
 // Row groups rg0, rg0 + step, ... (< rg1) of one matrix for one wave.
-// FULLC: L * U == C.  Otherwise lanes past the row end read a clamped, valid
+// Needs an even number of groups per row (G).  FULLC: L * U == C.  Otherwise lanes past the row end read a clamped, valid
 // chunk and multiply it by a zero activation slice.  Rows past N are clamped
 // to row N - 1 and not stored, so the loop has no divergent branches.
 // STAGES register sets rotate: STAGES - 1 row groups are in flight while the
 // current one is decoded.  Lane partials are summed in a fixed order, so the
 // result is bitwise deterministic.
-template <int L, int U, bool FULLC, int STAGES = 2>
+// BATCH (consecutive row groups, step == 1): outputs are gathered into one
+// register, lane i holding row b + i of the current 64-row block b, and the
+// block is written with one store when the walk leaves it (128 or 256
+// contiguous bytes instead of a few bytes per row group: small scattered
+// writes in a stream of reads cost HBM read bandwidth).
+template <int L, int U, bool FULLC, int STAGES = 2, bool BATCH = false>
 __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, int step,
                                           int lane, const DecodeConsts& k) {
     static_assert(STAGES == 2 || STAGES == 3, "register stages");
@@ -72,71 +77,108 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
     float xb[U];
     load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
 
+    // chunk offsets, scale dword offsets and scale half selectors per chunk
     int coff[U], soff[U];
+    uint32_t ssel[U];
+    const int sbase = (lk >> a.gshift) >> 1;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int c = lk + L * u;
         if (!FULLC && c >= a.C) c = a.C - 1;
+        const int cg = c >> a.gshift;
         coff[u] = c - lk;
-        soff[u] = (c >> a.gshift) - (lk >> a.gshift);
+        soff[u] = (cg >> 1) - sbase;
+        ssel[u] = (cg & 1) ? kScaleSelHi : kScaleSelLo;
     }
+    const uint32_t* swords = reinterpret_cast<const uint32_t*>(a.scales);
+    const int Gw = a.G >> 1;
+
+    float outv = 0.f;           // BATCH: lane i = row ob + i
+    int ob = -1, olo = 0, ohi = 0;  // block base row, lanes written so far
+    auto flush = [&]() {
+        const int n = ob + lane;
+        if (ob >= 0 && lane >= olo && lane < ohi && n < a.N) store_out(a.y, (size_t)n, outv, a.ydt);
+    };
 
     auto load = [&](int g, u32x4 (&q)[U], uint32_t (&sc)[U]) {
         int n = g * R + lr;
         n = n < a.N ? n : a.N - 1;
         const u32x4* cp = a.codes + (size_t)n * a.C + lk;
-        const uint16_t* sp = a.scales + (size_t)n * a.G + (lk >> a.gshift);
+        const uint32_t* sp = swords + (size_t)n * Gw + sbase;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             q[u] = nt_load(cp + coff[u]);
-            sc[u] = sp[soff[u]];
+            sc[u] = gload(sp + soff[u]);
         }
     };
     auto finish = [&](int g, const u32x4 (&q)[U], const uint32_t (&sc)[U]) {
         float acc = 0.f;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            acc = fmaf(bf16_to_f32(sc[u]), chunk_dot(q[u], xr[u], k) + xb[u], acc);
+            acc = fmaf(scale_from_word(sc[u], ssel[u]), chunk_dot(q[u], xr[u], k) + xb[u], acc);
         acc = group_sum<L>(acc);
-        const int n = g * R + lr;
-        if (lk == 0 && n < a.N) store_out(a.y, (size_t)n, acc, a.ydt);
+        if (BATCH) {
+            const int row0 = g * R;
+            const int blk = row0 & ~63;
+            if (blk != ob) {
+                flush();
+                ob = blk;
+                olo = row0 - blk;
+            }
+            const int slot = row0 - blk;
+            const int r = lane - slot;  // row of this tile held by this lane
+            const float v = R == 1 ? acc : __shfl(acc, (r & (R - 1)) * L, 64);
+            if (r >= 0 && r < R) outv = v;
+            ohi = slot + R;
+        } else {
+            const int n = g * R + lr;
+            if (lk == 0 && n < a.N) store_out(a.y, (size_t)n, acc, a.ydt);
+        }
     };
 
+    // The prefetch is never skipped: on the last row group it re-reads the
+    // current one (lines just fetched, so a cache hit) instead of branching.
+    // A load issued under a branch that rejoins would leave the wait-count
+    // pass the smaller of the two paths' counts, and the wait before decoding
+    // the current row group would then also wait for the prefetched one.
+    auto next = [&](int g, int d) { return g + d < rg1 ? g + d : g; };
     int rg = rg0;
     if (STAGES == 2) {
         u32x4 qa[U], qb[U];
         uint32_t sa[U], sb[U];
         load(rg, qa, sa);
         while (true) {
-            if (rg + step < rg1) load(rg + step, qb, sb);
+            load(next(rg, step), qb, sb);
             finish(rg, qa, sa);
             rg += step;
             if (rg >= rg1) break;
-            if (rg + step < rg1) load(rg + step, qa, sa);
+            load(next(rg, step), qa, sa);
             finish(rg, qb, sb);
             rg += step;
             if (rg >= rg1) break;
         }
+        if (BATCH) flush();
     } else {
         // three stages: two row groups in flight while one is decoded
         u32x4 qa[U], qb[U], qc[U];
         uint32_t sa[U], sb[U], sc[U];
         load(rg, qa, sa);
-        if (rg + step < rg1) load(rg + step, qb, sb);
+        load(next(rg, step), qb, sb);
         while (true) {
-            if (rg + 2 * step < rg1) load(rg + 2 * step, qc, sc);
+            load(next(rg, 2 * step), qc, sc);
             finish(rg, qa, sa);
             rg += step;
             if (rg >= rg1) break;
-            if (rg + 2 * step < rg1) load(rg + 2 * step, qa, sa);
+            load(next(rg, 2 * step), qa, sa);
             finish(rg, qb, sb);
             rg += step;
             if (rg >= rg1) break;
-            if (rg + 2 * step < rg1) load(rg + 2 * step, qb, sb);
+            load(next(rg, 2 * step), qb, sb);
             finish(rg, qc, sc);
             rg += step;
             if (rg >= rg1) break;
         }
+        if (BATCH) flush();
     }
 }
 
@@ -153,12 +195,12 @@ __device__ __forceinline__ void gemv_rows_generic(const GemvArgs& a, int rg0, in
         if (n < a.N) {
             for (int c = lk; c < a.C; c += L) {
                 const u32x4 q = nt_load(a.codes + (size_t)n * a.C + c);
-                const float s = bf16_to_f32(a.scales[(size_t)n * a.G + (c >> a.gshift)]);
+                const float s = bf16_to_f32(gload(a.scales + (size_t)n * a.G + (c >> a.gshift)));
                 uint32_t xr[16];
                 const u32x4* p = reinterpret_cast<const u32x4*>(a.x + 16 * c);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const u32x4 v = p[i];
+                    const u32x4 v = gload(p + i);
                     xr[4 * i + 0] = v[0];
                     xr[4 * i + 1] = v[1];
                     xr[4 * i + 2] = v[2];

@@ -74,7 +74,7 @@ __device__ __forceinline__ void load_tile(const SweepOp& op, int rg, int lane, T
             int c = lk + op.L * u;
             c = c < op.C ? c : op.C - 1;
             t.q[u] = nt_load(cp + c);
-            t.s[u] = sp[c >> op.gshift];
+            t.s[u] = gload(sp + (c >> op.gshift));
         }
     }
 }
@@ -131,7 +131,7 @@ __device__ __forceinline__ void put_chunk(const u32x4 (&v)[4], int t, uint32_t* 
 
 __device__ __forceinline__ void get_chunk(const SweepOp& op, int t, u32x4 (&v)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = op.x[4 * t + i];
+    for (int i = 0; i < 4; ++i) v[i] = gload(op.x + 4 * t + i);
 }
 
 __device__ __forceinline__ unsigned wave_min(unsigned v) {
@@ -264,7 +264,7 @@ __device__ __forceinline__ void stream_rows(const SweepOp& op, int rg0, int rg1,
     a.gshift = op.gshift;
     a.ydt = op.ydt;
     if (U > 0)
-        gemv_rows<L, (U > 0 ? U : 1), true, kStreamStages>(a, rg0, rg1, 1, lane, k);
+        gemv_rows<L, (U > 0 ? U : 1), true, kStreamStages, true>(a, rg0, rg1, 1, lane, k);
     else
         gemv_rows_generic<L>(a, rg0, rg1, 1, lane, k);
 }

@@ -110,6 +110,10 @@ static int setup_persistent(w4_sweep* h) {
             t.cfg = kCfgGeneric;
         } else {
             t.cfg = stream_cfg(t.C, &t.L);
+            if (t.G & 1) {  // the tiled loop reads scales in dword pairs
+                t.cfg = kCfgGeneric;
+                t.L = 16;  // the generic loop's lanes per row
+            }
         }
         t.lshift = ilog2(t.L);
         t.U = (t.C + t.L - 1) / t.L;

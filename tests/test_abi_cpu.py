@@ -136,7 +136,12 @@ def test_describe_dispatch_tile_table(L):
     assert w4.describe_dispatch(1, 1536, 6144, 32).startswith("gemv L=64 U=3")
     assert w4.describe_dispatch(1, 2560, 1536, 32).startswith("gemv L=16 U=3")
     assert w4.describe_dispatch(1, 256, 512, 32).startswith("gemv L=16 U=1")
-    assert w4.describe_dispatch(1, 100, 96, 32).startswith("gemv L=8 U=1")
+    # K = 128: 4 chunks, 8 lanes per row with half of them masked
+    assert w4.describe_dispatch(1, 100, 128, 32).startswith("gemv L=8 U=1")
+    # an odd number of groups per row (3) takes the generic loop: the tiled
+    # loop reads scales as dword pairs
+    assert w4.describe_dispatch(1, 100, 96, 32).startswith("gemv_generic")
+    assert w4.describe_dispatch(1, 100, 768, 256).startswith("gemv_generic")
     assert w4.describe_dispatch(1, 100, 20000, 32).startswith("gemv_generic")
     assert w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm")
     assert w4.describe_dispatch(64, 12288, 1536, 256).startswith("mfma")

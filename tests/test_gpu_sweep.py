@@ -77,3 +77,48 @@ def test_sweep_all_outputs(oracle_mod, sweep_data, name, mode):
             b = from_dev(op[5])
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (rep, op[1], op[2])
     sw.close()
+
+
+# Ragged shapes: row counts that end inside a 64-row output block, blocks
+# shared by several waves (more waves than tiles), every compiled tile shape
+# of the one-kernel modes, and K with an odd number of groups per row (the
+# generic loop).  Outputs past each op's N must stay untouched.
+RAGGED_OPS = [(33, 512, 32, "f32"), (100, 1536, 32, "bf16"), (1000, 2048, 32, "bf16"),
+              (4097, 1536, 32, "f32"), (65, 6144, 32, "bf16"), (130, 96, 32, "f32"),
+              (77, 768, 256, "bf16"), (5000, 1536, 32, "bf16"), (1, 1536, 32, "f32"),
+              (129, 3072, 32, "bf16"), (63, 1024, 32, "f32"), (31, 64, 32, "bf16"),
+              (50, 4096, 32, "f32")]
+
+
+@pytest.mark.parametrize("name,mode", MODES)
+def test_sweep_ragged_shapes(oracle_mod, name, mode):
+    import torch
+    device()
+    w4.device_check()
+    cases, ops, guards = [], [], []
+    for j, (N, K, g, odt) in enumerate(RAGGED_OPS):
+        c = synth.make_case("ragged%d" % j, N, K, g, 1, 500 + j, odt)
+        dt = torch.float32 if odt == "f32" else torch.bfloat16
+        # one extra element after the outputs, which nothing may write
+        ybuf = torch.full((N + 1,), float("nan"), dtype=dt, device=device())
+        guards.append(ybuf)
+        ops.append((upload_packed(c.P, c.S, N, K, g), N, K, g, to_dev_bf16(c.X[0]), ybuf[:N]))
+        cases.append(c)
+    note("ragged sweep mode=%s ops=%d" % (name, len(ops)))
+    try:
+        sw = w4.DecodeSweep(ops, mode)
+    except w4.W4Error as e:
+        if e.status == -5:
+            pytest.skip("mode not built: %s" % e)
+        raise
+    for rep in range(2):
+        for op in ops:
+            op[5].fill_(float("nan"))
+        torch.cuda.synchronize()
+        sw.launch()
+        sw.check()
+        torch.cuda.synchronize()
+        _check_all(oracle_mod, cases, ops, "%s rep %d" % (name, rep))
+        for gbuf in guards:
+            assert np.isnan(from_dev(gbuf[-1:]))[0], "write past N"
+    sw.close()
