@@ -21,7 +21,6 @@ plain-sum read of a 4 GiB buffer are measured alongside and reported under
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,33 +32,20 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMV effective HBM GB/s (% of peak) + ms per 35-layer+lm_head sweep"
 PEAK_HBM_GBPS = 8000.0
 MODES = {"graph": 0, "persistent": 1, "stream": 2}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sweep_stream.json")
-KERNEL_SOURCES = ("bit_weight_only_w4a16_amd/csrc/w4_persist.hip",
-                  "bit_weight_only_w4a16_amd/csrc/w4_persist.h",
-                  "bit_weight_only_w4a16_amd/csrc/w4_common.h")
-
-
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def load_traffic(weight_bytes: int):
     """HBM bytes per launch of the stream kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel source."""
+    from bit_weight_only_w4a16_amd import traffic
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic.OUT_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != traffic.kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -169,12 +169,6 @@ static int setup_persistent(w4_sweep* h) {
     return hip_fail(hipDeviceSynchronize(), "sweep setup");
 }
 
-static int capture_persistent(w4_sweep* h, hipStream_t cs) {
-    h->kernels = 1;
-    return launch_persist(h->mode == W4_SWEEP_PERSISTENT, static_cast<const SweepOp*>(h->dev),
-                          (int)h->ops.size(), h->ctl, h->range, h->grid, cs);
-}
-
 static void release(w4_sweep* h) {
     if (h->exec) (void)hipGraphExecDestroy(h->exec);
     if (h->graph) (void)hipGraphDestroy(h->graph);
@@ -220,21 +214,25 @@ int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode, void* str
         release(h);
         return st;
     }
-    // persistent modes: the op table and control block are allocated and
-    // filled before capture; the capture records only kernel launches.
-    if (mode != W4_SWEEP_GRAPH) st = setup_persistent(h);
-    if (st == W4_OK)
+    // GRAPH mode captures its per-op kernels into a graph.  The persistent
+    // modes are one kernel each: it is launched directly (a one-node graph
+    // launch costs more than the kernel launch it wraps); their op table and
+    // control block are allocated and filled here.
+    if (mode == W4_SWEEP_GRAPH) {
         st = hip_fail(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal),
                       "begin capture");
-    if (st == W4_OK) {
-        const int cst = mode == W4_SWEEP_GRAPH ? capture_graph_nodes(h, cs)
-                                               : capture_persistent(h, cs);
-        const int est = hip_fail(hipStreamEndCapture(cs, &h->graph), "end capture");
-        st = cst != W4_OK ? cst : est;
+        if (st == W4_OK) {
+            const int cst = capture_graph_nodes(h, cs);
+            const int est = hip_fail(hipStreamEndCapture(cs, &h->graph), "end capture");
+            st = cst != W4_OK ? cst : est;
+        }
+        if (st == W4_OK)
+            st = hip_fail(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0),
+                          "graph instantiate");
+    } else {
+        st = setup_persistent(h);
+        h->kernels = 1;
     }
-    if (st == W4_OK)
-        st = hip_fail(hipGraphInstantiate(&h->exec, h->graph, nullptr, nullptr, 0),
-                      "graph instantiate");
     (void)hipStreamDestroy(cs);
     if (st != W4_OK) {
         release(h);
@@ -245,8 +243,14 @@ int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode, void* str
 }
 
 int w4_decode_sweep_launch(w4_sweep* h, void* stream) {
-    if (!h || !h->exec) return fail(W4_ERR_ARG, "sweep: bad handle");
-    return hip_fail(hipGraphLaunch(h->exec, static_cast<hipStream_t>(stream)), "graph launch");
+    if (!h) return fail(W4_ERR_ARG, "sweep: bad handle");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (h->mode != W4_SWEEP_GRAPH)
+        return launch_persist(h->mode == W4_SWEEP_PERSISTENT,
+                              static_cast<const SweepOp*>(h->dev), (int)h->ops.size(), h->ctl,
+                              h->range, h->grid, s);
+    if (!h->exec) return fail(W4_ERR_ARG, "sweep: bad handle");
+    return hip_fail(hipGraphLaunch(h->exec, s), "graph launch");
 }
 
 int w4_decode_sweep_check(w4_sweep* h, void* stream) {

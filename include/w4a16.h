@@ -194,7 +194,7 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
  *                      reported by w4_decode_sweep_check as W4_ERR_TIMEOUT.
  *  W4_SWEEP_STREAM     the persistent kernel without the op-to-op ordering
  *                      (ops treated as independent); an upper bound.
- * Persistent modes are captured into a hipGraph as well.
+ * The persistent modes are one kernel launch per replay.
  */
 typedef struct w4_gemv_op {
     const void* packed;      /* device layout of this op's weights   */
@@ -212,10 +212,13 @@ enum w4_sweep_mode {
 
 typedef struct w4_sweep w4_sweep;
 
-/* Validates every op, builds and instantiates the graph on `stream`. */
+/* Validates every op and builds the replay: the graph of per-op kernels
+ * (GRAPH) or the persistent kernel's op table (other modes).  `stream` is
+ * unused (setup is synchronous). */
 int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode,
                            void* stream, w4_sweep** out);
-/* One replay: a single hipGraphLaunch on `stream`. */
+/* One replay on `stream`: one hipGraphLaunch (GRAPH) or one kernel launch
+ * (other modes).  May be recorded into a caller's graph capture. */
 int w4_decode_sweep_launch(w4_sweep* h, void* stream);
 /* Synchronizes `stream` and reports a timed-out wait of a persistent replay
  * since the last check (W4_ERR_TIMEOUT), else W4_OK. */
