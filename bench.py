@@ -230,6 +230,7 @@ def main():
     probe = probe_read(torch, w4, dev) if not args.no_extra else None
     order = ([m for m in ("graph", "persistent", "stream") if m != args.mode]
              if not args.no_extra else []) + [args.mode]
+    trials = None
     for name in order:
         sw = w4.DecodeSweep(ops, MODES[name])
         steps = args.steps if name == args.mode else max(5, min(args.steps, 20))
@@ -239,6 +240,11 @@ def main():
         results[name] = {"ms_per_sweep": ms, "GBps": weight_bytes / (ms * 1e-3) / 1e9,
                          "kernels_per_sweep": info["kernels"]}
         log("%-10s %.1f us/sweep  %.1f GB/s" % (name, ms * 1e3, results[name]["GBps"]))
+        if name == args.mode and not args.no_extra:
+            # run-to-run spread: five more timed regions of the same length
+            t = sorted(time_sweep(torch, sw, steps, 0) * 1e3 for _ in range(5))
+            trials = {"n": 5, "steps_each": steps, "median_us": t[2], "min_us": t[0],
+                      "max_us": t[-1], "spread_pct": (t[-1] - t[0]) / t[2] * 100}
         sw.close()
     ms = results[args.mode]["ms_per_sweep"]
     value = weight_bytes / (ms * 1e-3) / 1e9
@@ -251,6 +257,7 @@ def main():
             "GBps_incl_x_y": (weight_bytes + io_bytes) / (ms * 1e-3) / 1e9,
             "ms_per_1222.8MiB_at_this_rate": 1282203648 / (value * 1e9) * 1e3,
             "modes": results,
+            "trials_us": trials,
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
         }
 

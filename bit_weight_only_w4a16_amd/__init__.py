@@ -34,7 +34,7 @@ W4_SWEEP_STREAM = 2
 STATUS = {
     0: "W4_OK", -1: "W4_ERR_ARG", -2: "W4_ERR_SHAPE", -3: "W4_ERR_ALIGN",
     -4: "W4_ERR_DTYPE", -5: "W4_ERR_UNSUPPORTED", -6: "W4_ERR_HIP",
-    -7: "W4_ERR_NOMEM", -8: "W4_ERR_ARCH", -9: "W4_ERR_TIMEOUT",
+    -7: "W4_ERR_NOMEM", -8: "W4_ERR_ARCH", -9: "W4_ERR_TIMEOUT", -10: "W4_ERR_SELFTEST",
 }
 
 # every symbol include/w4a16.h declares
@@ -44,7 +44,7 @@ EXPORTS = (
     "w4a16_gemv", "w4a16_gemm_smallM", "w4_fwht", "w4a16_gemm_workspace_bytes",
     "w4a16_gemm", "w4_decode_sweep_create", "w4_decode_sweep_launch",
     "w4_decode_sweep_check", "w4_decode_sweep_info", "w4_decode_sweep_destroy",
-    "w4_describe_dispatch", "w4_probe_read", "w4_probe_copy",
+    "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
 )
 
 
@@ -107,6 +107,7 @@ def lib():
                                       ctypes.POINTER(i)], i),
             "w4_decode_sweep_destroy": ([vp], i),
             "w4_describe_dispatch": ([i, i, i, i, ctypes.c_char_p, sz], i),
+            "w4_selftest": ([vp], i),
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
         }
@@ -174,6 +175,11 @@ def describe_dispatch(M: int, N: int, K: int, group: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib().w4_describe_dispatch(M, N, K, group, buf, 256))
     return buf.value.decode()
+
+
+def selftest(stream=None) -> None:
+    """Runs the library's start-up check on the current GPU (raises W4Error)."""
+    _check(lib().w4_selftest(_stream(stream)))
 
 
 # --------------------------------------------------------------- packing ---

@@ -95,6 +95,7 @@ const char* w4_status_str(int status) {
         case W4_ERR_NOMEM: return "out of memory";
         case W4_ERR_ARCH: return "device is not gfx950";
         case W4_ERR_TIMEOUT: return "in-kernel wait timed out";
+        case W4_ERR_SELFTEST: return "self-test output mismatch";
         default: return "unknown status";
     }
 }

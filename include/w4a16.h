@@ -76,7 +76,8 @@ enum w4_status {
     W4_ERR_HIP = -6,          /* a HIP runtime call failed                   */
     W4_ERR_NOMEM = -7,        /* allocation failed (sweep creation only)     */
     W4_ERR_ARCH = -8,         /* current device is not gfx950                */
-    W4_ERR_TIMEOUT = -9       /* a bounded in-kernel wait gave up            */
+    W4_ERR_TIMEOUT = -9,      /* a bounded in-kernel wait gave up            */
+    W4_ERR_SELFTEST = -10     /* w4_selftest found a wrong output            */
 };
 
 enum w4_dtype { W4_F32 = 0, W4_BF16 = 1 };
@@ -236,6 +237,19 @@ int w4_decode_sweep_destroy(w4_sweep* h);
  */
 int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
                          size_t len);
+
+/*
+ * Start-up check of the compute paths on the current device ([P2] probes its
+ * machine at start-up before trusting a kernel path).  Runs the batch-1 GEMV
+ * (group 32 and 256), the small-M kernel (M = 8) and the matrix-core GEMM
+ * (M = 64) through the public entry points on built-in 100 x 512 matrices
+ * with one-hot activations, whose outputs are exactly (code - 8) * scale, and
+ * compares every output bitwise.  Allocates and frees about 1 MB of device
+ * memory and synchronizes `stream` (not for use inside a graph capture).
+ * W4_OK; W4_ERR_SELFTEST with the first wrong output in w4_last_error();
+ * W4_ERR_ARCH / W4_ERR_HIP / W4_ERR_NOMEM as for other calls.
+ */
+int w4_selftest(void* stream);
 
 /*
  * Plain-sum read of `bytes` of device memory (the measurement the summary line

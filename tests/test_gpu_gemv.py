@@ -155,3 +155,9 @@ def test_output_guard_regions(oracle_mod):
             assert np.array_equal(h[:G], before[:G]) and np.array_equal(h[G + N:], before[G + N:])
             Y, A = oracle_mod.gemm_bf16(case.P, case.S, N, K, 32, case.X[0])
             assert_within(h[G:G + N], Y, A, out_dtype, "guard")
+
+
+def test_selftest_passes():
+    """The library's own start-up check (closed-form one-hot outputs)."""
+    device()
+    w4.selftest()
