@@ -67,6 +67,9 @@ def _load():
             lib.oracle_dequant.argtypes = [P, P, i, i, i, P]
             lib.oracle_gemm.argtypes = [P, P, i, i, i, P, i, i, P, P, i]
             lib.oracle_fwht.argtypes = [P, P, i, i, i]
+            lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+            lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
+            lib.oracle_gather.argtypes = [P, P, i, i, i, P, i, i, P]
             _lib = lib
     return _lib
 
@@ -152,3 +155,23 @@ def fwht(X, block: int) -> np.ndarray:
     out = np.empty_like(X2)
     _load().oracle_fwht(_ptr(X2), _ptr(out), M, K, block)
     return out[0] if squeeze else out
+
+
+def f64_to_bf16(v: float) -> int:
+    """bf16 bit pattern of v, round to nearest even (v zero or bf16-normal)."""
+    return int(_load().oracle_f64_to_bf16(float(v)))
+
+
+def gather(P, S, N: int, K: int, group: int, ids, out_dtype: str = "f32") -> np.ndarray:
+    """Rows ids of the dequantized N x K table: float32 [B, K] (exact) or
+    uint16 bf16 bit patterns [B, K] (round to nearest even); NaN rows for
+    ids outside [0, N)."""
+    P = _c(P, np.uint32)
+    S = _c(S, np.uint16)
+    ids = _c(ids, np.int32)
+    B = ids.shape[0]
+    bf = out_dtype == "bf16"
+    out = np.empty((B, K), dtype=np.uint16 if bf else np.float32)
+    _load().oracle_gather(_ptr(P), _ptr(S), N, K, group, _ptr(ids), B, 1 if bf else 0,
+                          _ptr(out))
+    return out

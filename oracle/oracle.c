@@ -31,7 +31,14 @@
  *    complement int4);
  *  - scales: S[n][k / group], row-major, bf16, no zero point;
  *  - Hadamard: Sylvester (natural) order, orthonormal factor block^-1/2,
- *    contiguous blocks along K; Sylvester H is symmetric, so H^T = H.
+ *    contiguous blocks along K; Sylvester H is symmetric, so H^T = H;
+ *  - bf16 outputs: round to nearest, ties to even.
+ *
+ * Table gather: [P1], step 2 "Keep the Vocabulary Tables in 4-Bit": the
+ * token-embedding table (one copy, shared with the output layer) and the
+ * per-layer input table (a row of 35 x 256 values per token) are stored as
+ * 4-bit codes with one 16-bit step per group, and the row lookup runs on the
+ * GPU; a looked-up row is the dequantized row w(id, k), k = 0..K-1.
  */
 #include <math.h>
 #include <stddef.h>
@@ -140,6 +147,66 @@ void oracle_fwht(const double* X, double* Xout, int M, int K, int block)
                 }
             }
             for (int j = 0; j < block; ++j) v[j] *= norm;
+        }
+    }
+}
+
+/*
+ * fp64 -> bf16 bit pattern, round to nearest, ties to even, written from the
+ * definition: with |v| = m * 2^e (0.5 <= m < 1), bf16 keeps 8 significant
+ * bits, so the two neighbours of |v| are floor(m * 2^8) and that + 1, in units
+ * of 2^(e-8); the nearer is taken, and on a tie the even one.  v must be zero
+ * or have a magnitude in bf16's normal range (every value the gather makes
+ * from a normal bf16 scale does).
+ */
+uint16_t oracle_f64_to_bf16(double v)
+{
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+    int e;
+    const double m = frexp(fabs(v), &e);
+    const double t = ldexp(m, 8);          /* 128 <= t < 256 */
+    const double lo = floor(t);
+    const double dlo = t - lo, dhi = lo + 1.0 - t;
+    double r;
+    if (dlo < dhi)
+        r = lo;
+    else if (dhi < dlo)
+        r = lo + 1.0;
+    else
+        r = fmod(lo, 2.0) == 0.0 ? lo : lo + 1.0;
+    const float f = (float)ldexp(r, e - 8);  /* <= 8 significant bits: exact */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t h = (uint16_t)(u >> 16);
+    if (v < 0.0) h |= 0x8000u;
+    return h;
+}
+
+/*
+ * Rows ids[0..B-1] of an N x K table, dequantized: Y[b][k] = w(ids[b], k).
+ * out_bf16 = 0: Y is float[B][K], each value exact ((code - 8) * scale has at
+ * most 12 significant bits); out_bf16 = 1: Y is uint16[B][K], bf16 rounded to
+ * nearest even.  An id outside [0, N) gives a row of quiet NaNs.
+ */
+void oracle_gather(const uint32_t* P, const uint16_t* S, int N, int K, int group,
+                   const int32_t* ids, int B, int out_bf16, void* Y)
+{
+    for (int b = 0; b < B; ++b) {
+        const int id = ids[b];
+        for (int k = 0; k < K; ++k) {
+            const size_t at = (size_t)b * K + k;
+            if (id < 0 || id >= N) {
+                if (out_bf16)
+                    ((uint16_t*)Y)[at] = 0x7FC0u;
+                else
+                    ((float*)Y)[at] = (float)NAN;
+                continue;
+            }
+            const double w = oracle_weight(P, S, K, group, id, k);
+            if (out_bf16)
+                ((uint16_t*)Y)[at] = oracle_f64_to_bf16(w);
+            else
+                ((float*)Y)[at] = (float)w;
         }
     }
 }
