@@ -126,6 +126,30 @@ def time_calls(torch, fn, calls=20, reps=10):
     return e0.elapsed_time(e1) / (reps * calls) * 1e3
 
 
+def time_gather(torch, w4, synth, dev, embed_packed):
+    """Row lookup in the step's 4-bit tables, bf16 out: the token-embedding
+    table (the lm_head's packed copy, 262144 x 1536) and the per-layer input
+    table (262144 x 8960), for 1 token (decode) and 512 tokens (prefill)."""
+    import numpy as np
+    out = {}
+    ple = synth.ple_table()
+    P = torch.from_numpy(ple.P.view(np.int32)).to(dev)
+    S = torch.from_numpy(ple.S.view(np.int16)).to(dev)
+    ple_packed = w4.pack(P, S, ple.N, ple.K, ple.group)
+    del P, S
+    for name, packed, K in (("embed_262144x1536", embed_packed, synth.HIDDEN),
+                            ("ple_262144x8960", ple_packed, synth.PLE_WIDTH)):
+        for B in (1, 512):
+            ids = torch.from_numpy(synth.token_ids(B, 7)).to(dev)
+            Y = torch.empty((B, K), dtype=torch.bfloat16, device=dev)
+            us = time_calls(torch, lambda: w4.gather(packed, synth.VOCAB, K, 32, ids, "bf16",
+                                                     out=Y))
+            moved = B * (K // 2 + K // 32 * 2) + B * K * 2
+            out["%s_B%d" % (name, B)] = {"us": us, "GBps_read_plus_write": moved / us / 1e3}
+    del ple_packed
+    return out
+
+
 def time_prefill(torch, w4, synth, dev):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
@@ -259,6 +283,7 @@ def main():
             "modes": results,
             "trials_us": trials,
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
+            "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
         }
 
     # roofline of the dominant (only) kernel of the timed step

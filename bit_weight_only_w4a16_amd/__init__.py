@@ -44,7 +44,7 @@ EXPORTS = (
     "w4a16_gemv", "w4a16_gemm_smallM", "w4_fwht", "w4a16_gemm_workspace_bytes",
     "w4a16_gemm", "w4_decode_sweep_create", "w4_decode_sweep_launch",
     "w4_decode_sweep_check", "w4_decode_sweep_info", "w4_decode_sweep_destroy",
-    "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
+    "w4_gather", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
 )
 
 
@@ -108,6 +108,7 @@ def lib():
             "w4_decode_sweep_destroy": ([vp], i),
             "w4_describe_dispatch": ([i, i, i, i, ctypes.c_char_p, sz], i),
             "w4_selftest": ([vp], i),
+            "w4_gather": ([vp, i, i, i, vp, i, vp, i, i, vp], i),
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
         }
@@ -175,6 +176,20 @@ def describe_dispatch(M: int, N: int, K: int, group: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib().w4_describe_dispatch(M, N, K, group, buf, 256))
     return buf.value.decode()
+
+
+def gather(packed, N: int, K: int, group: int, ids, out_dtype: str = "bf16", out=None,
+           stream=None):
+    """Dequantized rows ids (int32 device tensor [B]) of the packed N x K
+    table -> [B, K] fp32 or bf16 tensor (NaN rows for ids outside [0, N))."""
+    import torch
+    B = int(ids.numel())
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
+                          device=ids.device)
+    _check(lib().w4_gather(_ptr(packed), N, K, group, _ptr(ids), B, _ptr(out), out.stride(0),
+                           _dt(out_dtype), _stream(stream)))
+    return out
 
 
 def selftest(stream=None) -> None:

@@ -115,7 +115,7 @@ int w4_device_check(void) {
 
 const char* w4_build_info(void) {
     return "abi=1 arch=gfx950 kernels=gemv,gemv_generic,smallm,fwht,mfma_gemm,sweep_graph,"
-           "sweep_persistent,pack,probe";
+           "sweep_persistent,pack,gather,probe";
 }
 
 size_t w4_packed_bytes(int N, int K, int group) {
@@ -248,6 +248,23 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
     }
     if (M <= 16) return launch_smallm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
     return launch_mfma_gemm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
+}
+
+int w4_gather(const void* packed, int N, int K, int group, const int32_t* ids, int B,
+              void* Y, int ldy, int ydt, void* stream) {
+    W4_TRY(check_weight_shape(N, K, group));
+    W4_TRY(check_in16(packed, "packed"));
+    W4_TRY(check_dtype(ydt));
+    if (B < 0 || B > (1 << 24)) return fail(W4_ERR_SHAPE, "gather: B out of range (got %d)", B);
+    if (B == 0) return W4_OK;
+    if (!ids) return fail(W4_ERR_ARG, "gather: ids is NULL");
+    if (!aligned(ids, 4)) return fail(W4_ERR_ALIGN, "gather: ids must be 4-byte aligned");
+    W4_TRY(check_in16(Y, "Y"));
+    if (ldy < K) return fail(W4_ERR_SHAPE, "gather: ldy %d < K %d", ldy, K);
+    if (ldy % (ydt == W4_F32 ? 4 : 8) != 0)
+        return fail(W4_ERR_ALIGN, "gather: rows of Y must start 16-byte aligned (ldy %d)", ldy);
+    return launch_gather(packed, N, K, group, ids, B, Y, ldy, ydt,
+                         static_cast<hipStream_t>(stream));
 }
 
 int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) {

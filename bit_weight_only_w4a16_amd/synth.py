@@ -38,6 +38,9 @@ LAYER_SHAPES = (
     ("down", HIDDEN, 6144),
 )
 LM_HEAD_SHAPE = ("lm_head", VOCAB, HIDDEN)
+# Per-layer input table: a row of 35 x 256 values per token, 4-bit, group 32.
+PLE_WIDTH = N_LAYERS * 256
+PLE_SHAPE = ("ple", VOCAB, PLE_WIDTH)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -141,3 +144,16 @@ def prefill_g256(M: int) -> GemvCase:
     (weights are drawn directly as the stored rotated weights)."""
     return make_case("prefill_g256_M%d" % M, 2 * 6144, HIDDEN, 256, M,
                      1000 + M, "bf16", outlier_frac=0.01, hadamard_block=512)
+
+
+def ple_table(seed: int = 142) -> GemvCase:
+    """Per-layer input table, 262144 x 8960 (35 x 256), group 32 (1.32 GB
+    packed).  Its X row is drawn but unused."""
+    name, N, K = PLE_SHAPE
+    return make_case(name, N, K, 32, 1, seed, "bf16")
+
+
+def token_ids(B: int, seed: int, vocab: int = VOCAB) -> np.ndarray:
+    """B token ids drawn uniformly from [0, vocab) (repeats allowed), int32."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, vocab, B, dtype=np.int64).astype(np.int32)

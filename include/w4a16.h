@@ -230,6 +230,25 @@ int w4_decode_sweep_info(const w4_sweep* h, int* n_ops, size_t* weight_bytes,
 int w4_decode_sweep_destroy(w4_sweep* h);
 
 /*
+ * Row lookup in a 4-bit table, dequantized:
+ *   Y[b][k] = (code(ids[b], k) - 8) * scale(ids[b], k / group),  b < B, k < K.
+ * [P1] step 2 "Keep the Vocabulary Tables in 4-Bit": the token-embedding
+ * table (the same copy serves as the output layer, whose GEMV is w4a16_gemv)
+ * and the per-layer input table (a row of 35 x 256 values per token) are
+ * 4-bit codes with a 16-bit step per group, looked up on the GPU.
+ *  packed: device layout (w4_pack) of the N x K table, 16-byte aligned.
+ *  ids:    device, B int32 row indices, 4-byte aligned; duplicates allowed.
+ *          An id outside [0, N) reads nothing and yields a row of quiet NaNs.
+ *  Y:      device, B rows of ldy elements (ldy >= K), 16-byte aligned, each
+ *          row 16-byte aligned (ldy % 4 == 0 for fp32, % 8 for bf16).
+ *  ydt:    W4_F32 (exact: the values have at most 12 significant bits) or
+ *          W4_BF16 (round to nearest even).
+ * B = 0 is a no-op; B <= 2^24.
+ */
+int w4_gather(const void* packed, int N, int K, int group, const int32_t* ids,
+              int B, void* Y, int ldy, int ydt, void* stream);
+
+/*
  * The kernel and tile the dispatcher picks for (M, N, K, group), as text
  * (e.g. "gemv L=16 U=3 W=4 grid=512"), written NUL-terminated into buf.
  * [P1] paragraph on the w4gemv.py kernel: each weight shape gets its own

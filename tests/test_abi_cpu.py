@@ -88,6 +88,22 @@ def test_smallm_validation(L):
     assert f(A16, 64, 512, 32, 4, A16, 512, A16, 60, 1, VP(0)) == -2   # ldy < N
 
 
+def test_gather_validation(L):
+    f = L.w4_gather
+    assert f(A16, 64, 512, 48, A16, 4, A16, 512, 1, VP(0)) == -2     # group
+    assert f(A2, 64, 512, 32, A16, 4, A16, 512, 1, VP(0)) == -3      # packed alignment
+    assert f(A16, 64, 512, 32, A16, -1, A16, 512, 1, VP(0)) == -2    # B < 0
+    assert f(A16, 64, 512, 32, VP(0), 4, A16, 512, 1, VP(0)) == -1   # ids NULL
+    assert f(A16, 64, 512, 32, A2, 4, A16, 512, 1, VP(0)) == -3      # ids alignment
+    assert f(A16, 64, 512, 32, A16, 4, A2, 512, 1, VP(0)) == -3      # Y alignment
+    assert f(A16, 64, 512, 32, A16, 4, A16, 500, 1, VP(0)) == -2     # ldy < K
+    assert f(A16, 64, 512, 32, A16, 4, A16, 516, 1, VP(0)) == -3     # bf16 rows misaligned
+    assert f(A16, 64, 512, 32, A16, 4, A16, 514, 0, VP(0)) == -3     # fp32 rows misaligned
+    assert f(A16, 64, 512, 32, A16, 4, A16, 512, 7, VP(0)) == -4     # dtype
+    # B = 0 launches nothing
+    assert f(A16, 64, 512, 32, VP(0), 0, VP(0), 512, 1, VP(0)) == 0
+
+
 def test_fwht_validation(L):
     f = L.w4_fwht
     assert f(A16, 1536, A16, 1536, 4, 1536, 384, VP(0)) == -2    # not a power of 2
