@@ -157,3 +157,16 @@ def token_ids(B: int, seed: int, vocab: int = VOCAB) -> np.ndarray:
     """B token ids drawn uniformly from [0, vocab) (repeats allowed), int32."""
     rng = np.random.default_rng(seed)
     return rng.integers(0, vocab, B, dtype=np.int64).astype(np.int32)
+
+
+def outlier_weights(N: int, K: int, seed: int, frac: float = 0.005,
+                    factor: float = 20.0) -> np.ndarray:
+    """Dense fp32 weights with outlier input channels, the kind a Hadamard
+    rotation helps: N(0, 1) entries, then exactly max(1, round(frac * K))
+    columns, drawn without replacement, multiplied by `factor`."""
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((N, K), dtype=np.float32)
+    n_out = max(1, int(round(frac * K)))
+    cols = rng.choice(K, size=n_out, replace=False)
+    W[:, cols] *= np.float32(factor)
+    return W

@@ -70,6 +70,7 @@ def _load():
             lib.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
             lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
             lib.oracle_gather.argtypes = [P, P, i, i, i, P, i, i, P]
+            lib.oracle_quantize.argtypes = [P, i, i, i, i, i, P, P]
             _lib = lib
     return _lib
 
@@ -175,3 +176,16 @@ def gather(P, S, N: int, K: int, group: int, ids, out_dtype: str = "f32") -> np.
     _load().oracle_gather(_ptr(P), _ptr(S), N, K, group, _ptr(ids), B, 1 if bf else 0,
                           _ptr(out))
     return out
+
+
+def quantize(W, group: int, block: int = 0):
+    """Rotate (block > 0: orthonormal FWHT per block along K, fp32) and
+    quantize the fp32 matrix W [N, K] -> (canonical codes P [N, K/8] uint32,
+    bf16 scales S [N, K/group] uint16)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    assert K % group == 0 and (block == 0 or K % block == 0)
+    P = np.empty((N, K // 8), dtype=np.uint32)
+    S = np.empty((N, K // group), dtype=np.uint16)
+    _load().oracle_quantize(_ptr(W), N, K, K, group, block, _ptr(P), _ptr(S))
+    return P, S

@@ -34,6 +34,14 @@
  *    contiguous blocks along K; Sylvester H is symmetric, so H^T = H;
  *  - bf16 outputs: round to nearest, ties to even.
  *
+ * Rotate-and-quantize: [P2] section "What is in the file": every linear
+ * weight is rotated along K by the orthogonal Hadamard matrix, W' = W H^T,
+ * and stored as int4 with one scale per group; the pages do not give the
+ * scale rule.  Reading taken: symmetric, s = bf16(max|w'| / 7) per group,
+ * q = clamp(round_half_even(w' / s), -8, 7), code = q + 8; all-zero groups
+ * get s = 0 and code 8.  The rotation and the rounding decisions are made in
+ * fp32, the kernel's precision, so that both sides decide every code alike.
+ *
  * Table gather: [P1], step 2 "Keep the Vocabulary Tables in 4-Bit": the
  * token-embedding table (one copy, shared with the output layer) and the
  * per-layer input table (a row of 35 x 256 values per token) are stored as
@@ -43,6 +51,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 /* bf16 is the top 16 bits of an IEEE binary32; widening is exact. */
@@ -209,4 +218,61 @@ void oracle_gather(const uint32_t* P, const uint16_t* S, int N, int K, int group
                 ((float*)Y)[at] = (float)w;
         }
     }
+}
+
+/*
+ * Rotate (optionally) and quantize an N x K fp32 matrix W (rows ldw apart)
+ * into canonical codes P[N][K/8] and bf16 scales S[N][K/group].
+ * block = 0: no rotation; otherwise each contiguous block of `block` elements
+ * of a row becomes H_block times it, computed in fp32 by butterfly stages of
+ * span 1, 2, 4, ... ((a, b) -> (a + b, a - b)) and one multiplication by
+ * (float)(block^-1/2).  Then per group of `group` elements:
+ *   a = max |w'| (fp32), s = a / 7 (fp32 division), sb = bf16 of s (nearest
+ *   even), sf = sb widened; q = sf == 0 ? 0 : rint(w' / sf) (fp32 division,
+ *   round half to even), clamped to [-8, 7]; code = q + 8.
+ * Scales must come out zero or bf16-normal (true for any W whose group maxima
+ * exceed 7 * 2^-126).
+ */
+void oracle_quantize(const float* W, int N, int K, int ldw, int group, int block,
+                     uint32_t* P, uint16_t* S)
+{
+    float* v = (float*)malloc(sizeof(float) * (size_t)K);
+    const float norm = block ? (float)(1.0 / sqrt((double)block)) : 1.0f;
+    for (int n = 0; n < N; ++n) {
+        for (int k = 0; k < K; ++k) v[k] = W[(size_t)n * ldw + k];
+        if (block) {
+            for (int b0 = 0; b0 < K; b0 += block) {
+                float* x = v + b0;
+                for (int h = 1; h < block; h *= 2)
+                    for (int i = 0; i < block; i += 2 * h)
+                        for (int j = i; j < i + h; ++j) {
+                            const float a = x[j], b = x[j + h];
+                            x[j] = a + b;
+                            x[j + h] = a - b;
+                        }
+                for (int j = 0; j < block; ++j) x[j] = x[j] * norm;
+            }
+        }
+        for (int k = 0; k < K / 8; ++k) P[(size_t)n * (K / 8) + k] = 0u;
+        for (int g0 = 0; g0 < K; g0 += group) {
+            float a = 0.0f;
+            for (int k = g0; k < g0 + group; ++k)
+                if (fabsf(v[k]) > a) a = fabsf(v[k]);
+            const float sc = a / 7.0f;
+            const uint16_t sb = oracle_f64_to_bf16((double)sc);
+            const float sf = (float)oracle_bf16_to_f64(sb);
+            S[(size_t)n * (K / group) + g0 / group] = sb;
+            for (int k = g0; k < g0 + group; ++k) {
+                float q = 0.0f;
+                if (sf != 0.0f) {
+                    q = rintf(v[k] / sf);
+                    if (q < -8.0f) q = -8.0f;
+                    if (q > 7.0f) q = 7.0f;
+                }
+                const uint32_t code = (uint32_t)((int)q + 8);
+                P[(size_t)n * (K / 8) + k / 8] |= code << (4 * (k % 8));
+            }
+        }
+    }
+    free(v);
 }
