@@ -150,6 +150,18 @@ def time_gather(torch, w4, synth, dev, embed_packed):
     return out
 
 
+def time_quantize(torch, w4, synth, dev):
+    """Offline rotate-and-quantize of the prefill-shaped weight (12288 x 1536
+    fp32 with outlier channels -> 512-point rotation, int4 group 256)."""
+    N, K = 2 * 6144, synth.HIDDEN
+    W = torch.from_numpy(synth.outlier_weights(N, K, 13)).to(dev)
+    out = torch.empty(w4.packed_bytes(N, K, 256), dtype=torch.uint8, device=dev)
+    us = time_calls(torch, lambda: w4.quantize(W, 256, 512, out=out))
+    moved = N * K * 4 + w4.packed_bytes(N, K, 256)
+    return {"shape": "12288x1536 fp32 -> g256, had_block 512", "us": us,
+            "GBps_read_plus_write": moved / us / 1e3}
+
+
 def time_prefill(torch, w4, synth, dev):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
@@ -284,6 +296,7 @@ def main():
             "trials_us": trials,
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
+            "quantize_rotate": time_quantize(torch, w4, synth, dev),
         }
 
     # roofline of the dominant (only) kernel of the timed step

@@ -44,7 +44,7 @@ EXPORTS = (
     "w4a16_gemv", "w4a16_gemm_smallM", "w4_fwht", "w4a16_gemm_workspace_bytes",
     "w4a16_gemm", "w4_decode_sweep_create", "w4_decode_sweep_launch",
     "w4_decode_sweep_check", "w4_decode_sweep_info", "w4_decode_sweep_destroy",
-    "w4_gather", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
+    "w4_gather", "w4_quantize", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
 )
 
 
@@ -109,6 +109,7 @@ def lib():
             "w4_describe_dispatch": ([i, i, i, i, ctypes.c_char_p, sz], i),
             "w4_selftest": ([vp], i),
             "w4_gather": ([vp, i, i, i, vp, i, vp, i, i, vp], i),
+            "w4_quantize": ([vp, i, i, i, i, i, i, vp, vp], i),
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
         }
@@ -189,6 +190,21 @@ def gather(packed, N: int, K: int, group: int, ids, out_dtype: str = "bf16", out
                           device=ids.device)
     _check(lib().w4_gather(_ptr(packed), N, K, group, _ptr(ids), B, _ptr(out), out.stride(0),
                            _dt(out_dtype), _stream(stream)))
+    return out
+
+
+def quantize(W, group: int, had_block: int = 0, out=None, stream=None):
+    """Dense fp32 or bf16 weights W [N, K] on the device -> packed uint8 tensor
+    (rotated along K by the orthonormal Hadamard blocks of had_block when
+    had_block > 0, then int4 with one scale per group)."""
+    import torch
+    N, K = W.shape
+    nb = packed_bytes(N, K, group)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    wdt = W4_F32 if W.dtype == torch.float32 else (W4_BF16 if W.dtype == torch.bfloat16 else -1)
+    _check(lib().w4_quantize(_ptr(W), wdt, W.stride(0), N, K, group, had_block, _ptr(out),
+                             _stream(stream)))
     return out
 
 

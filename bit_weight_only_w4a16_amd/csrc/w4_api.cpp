@@ -115,7 +115,7 @@ int w4_device_check(void) {
 
 const char* w4_build_info(void) {
     return "abi=1 arch=gfx950 kernels=gemv,gemv_generic,smallm,fwht,mfma_gemm,sweep_graph,"
-           "sweep_persistent,pack,gather,probe";
+           "sweep_persistent,pack,gather,quantize,probe";
 }
 
 size_t w4_packed_bytes(int N, int K, int group) {
@@ -265,6 +265,26 @@ int w4_gather(const void* packed, int N, int K, int group, const int32_t* ids, i
         return fail(W4_ERR_ALIGN, "gather: rows of Y must start 16-byte aligned (ldy %d)", ldy);
     return launch_gather(packed, N, K, group, ids, B, Y, ldy, ydt,
                          static_cast<hipStream_t>(stream));
+}
+
+int w4_quantize(const void* W, int w_dtype, int ldw, int N, int K, int group, int had_block,
+                void* packed, void* stream) {
+    W4_TRY(check_weight_shape(N, K, group));
+    if (w_dtype != W4_F32 && w_dtype != W4_BF16)
+        return fail(W4_ERR_DTYPE, "quantize: W dtype must be W4_F32 or W4_BF16 (got %d)", w_dtype);
+    if (had_block != 0 && had_block != 64 && had_block != 128 && had_block != 256 &&
+        had_block != 512)
+        return fail(W4_ERR_SHAPE, "quantize: had_block must be 0, 64, 128, 256 or 512 (got %d)",
+                    had_block);
+    if (had_block && K % had_block != 0)
+        return fail(W4_ERR_SHAPE, "quantize: K %d not a multiple of had_block %d", K, had_block);
+    W4_TRY(check_in16(W, "W"));
+    W4_TRY(check_in16(packed, "packed"));
+    if (ldw < K) return fail(W4_ERR_SHAPE, "quantize: ldw %d < K %d", ldw, K);
+    if (ldw % (w_dtype == W4_F32 ? 4 : 8) != 0)
+        return fail(W4_ERR_ALIGN, "quantize: rows of W must start 16-byte aligned (ldw %d)", ldw);
+    return launch_quantize(W, w_dtype, ldw, N, K, group, had_block, packed,
+                           static_cast<hipStream_t>(stream));
 }
 
 int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) {

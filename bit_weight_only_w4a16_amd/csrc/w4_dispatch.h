@@ -42,6 +42,9 @@ void describe_mfma(int M, int N, int K, int group, char* buf, size_t len);
 int launch_gather(const void* packed, int N, int K, int group, const int32_t* ids, int B,
                   void* Y, int ldy, int ydt, hipStream_t s);
 
+int launch_quantize(const void* W, int wdt, int ldw, int N, int K, int group, int block,
+                    void* packed, hipStream_t s);
+
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* out,
                       hipStream_t s);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

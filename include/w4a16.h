@@ -230,6 +230,30 @@ int w4_decode_sweep_info(const w4_sweep* h, int* n_ops, size_t* weight_bytes,
 int w4_decode_sweep_destroy(w4_sweep* h);
 
 /*
+ * Rotate-and-quantize: dense weights -> the device layout, on the GPU.
+ * [P2] section "What is in the file": every linear weight is rotated along K
+ * by an orthogonal Hadamard matrix, W' = W H^T, and stored as int4 with one
+ * scale per group (group 256 there); with the run-time transform of the
+ * activation (w4_fwht, or had_block of w4a16_gemm) the product is unchanged,
+ * and groups with outliers quantize with less error.  The page gives no
+ * scale rule; the rule here is symmetric per group:
+ *   s = bf16(max|w'| / 7)  (round to nearest even),
+ *   q = clamp(round_half_even(w' / s), -8, 7),  code = q + 8,
+ * with s = 0 and code 8 for an all-zero group; the rotation (butterfly
+ * stages of span 1, 2, 4, ..., then one fp32 scaling by block^-1/2) and every
+ * rounding decision are fp32, so the output is a deterministic function of W.
+ *  W:        device, N rows of ldw elements (ldw >= K), fp32 or bf16
+ *            (w_dtype W4_F32 / W4_BF16), 16-byte aligned, each row 16-byte
+ *            aligned (ldw % 4 == 0 for fp32, % 8 for bf16); finite values.
+ *  had_block: 0 (no rotation) or 64, 128, 256, 512 (Sylvester order,
+ *            orthonormal, contiguous blocks along K; K % had_block == 0).
+ *  packed:   device, w4_packed_bytes(N, K, group) bytes, 16-byte aligned;
+ *            written completely (codes and scales).
+ */
+int w4_quantize(const void* W, int w_dtype, int ldw, int N, int K, int group,
+                int had_block, void* packed, void* stream);
+
+/*
  * Row lookup in a 4-bit table, dequantized:
  *   Y[b][k] = (code(ids[b], k) - 8) * scale(ids[b], k / group),  b < B, k < K.
  * [P1] step 2 "Keep the Vocabulary Tables in 4-Bit": the token-embedding

@@ -104,6 +104,21 @@ def test_gather_validation(L):
     assert f(A16, 64, 512, 32, VP(0), 0, VP(0), 512, 1, VP(0)) == 0
 
 
+def test_quantize_validation(L):
+    f = L.w4_quantize
+    assert f(A16, 0, 512, 64, 512, 48, 0, A16, VP(0)) == -2      # group
+    assert f(A16, 2, 512, 64, 512, 32, 0, A16, VP(0)) == -4      # W dtype
+    assert f(A16, 0, 512, 64, 512, 32, 384, A16, VP(0)) == -2    # had_block
+    assert f(A16, 0, 1536, 64, 1536, 32, 1024, A16, VP(0)) == -2  # had_block > 512
+    assert f(A16, 0, 768, 64, 768, 32, 512, A16, VP(0)) == -2    # K % had_block
+    assert f(A2, 0, 512, 64, 512, 32, 0, A16, VP(0)) == -3       # W alignment
+    assert f(A16, 0, 512, 64, 512, 32, 0, A2, VP(0)) == -3       # packed alignment
+    assert f(A16, 0, 500, 64, 512, 32, 0, A16, VP(0)) == -2      # ldw < K
+    assert f(A16, 0, 514, 64, 512, 32, 0, A16, VP(0)) == -3      # fp32 rows misaligned
+    assert f(A16, 1, 516, 64, 512, 32, 0, A16, VP(0)) == -3      # bf16 rows misaligned
+    assert f(VP(0), 0, 512, 64, 512, 32, 0, A16, VP(0)) == -1    # W NULL
+
+
 def test_fwht_validation(L):
     f = L.w4_fwht
     assert f(A16, 1536, A16, 1536, 4, 1536, 384, VP(0)) == -2    # not a power of 2
