@@ -71,6 +71,8 @@ def _load():
             lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
             lib.oracle_gather.argtypes = [P, P, i, i, i, P, i, i, P]
             lib.oracle_quantize.argtypes = [P, i, i, i, i, i, P, P]
+            lib.oracle_attn_decode.argtypes = [P, P, P, P, i, i, i, i, i, ctypes.c_double,
+                                               P, P]
             _lib = lib
     return _lib
 
@@ -189,3 +191,23 @@ def quantize(W, group: int, block: int = 0):
     S = np.empty((N, K // group), dtype=np.uint16)
     _load().oracle_quantize(_ptr(W), N, K, K, group, block, _ptr(P), _ptr(S))
     return P, S
+
+
+def attn_decode(q, K, V, scale: float, pos=None, cur: int = 0, window: int = 0):
+    """Decode attention over T cache slots: q [H, D], K and V [T, D] as bf16
+    bit patterns (uint16); pos: None (every slot valid) or int32 [T] slot
+    positions (valid: 0 <= pos <= cur and, window > 0, pos > cur - window).
+    Returns (out [H, D], absout [H, D]) in fp64."""
+    q = _c(q, np.uint16)
+    K = _c(K, np.uint16)
+    V = _c(V, np.uint16)
+    H, D = q.shape
+    T = K.shape[0]
+    assert K.shape == (T, D) and V.shape == (T, D)
+    pp = None if pos is None else _c(pos, np.int32)
+    out = np.empty((H, D))
+    absout = np.empty((H, D))
+    _load().oracle_attn_decode(_ptr(q), _ptr(K), _ptr(V),
+                               None if pp is None else _ptr(pp), H, T, D, cur, window,
+                               float(scale), _ptr(out), _ptr(absout))
+    return out, absout

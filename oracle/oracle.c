@@ -42,6 +42,14 @@
  * get s = 0 and code 8.  The rotation and the rounding decisions are made in
  * fp32, the kernel's precision, so that both sides decide every code alike.
  *
+ * Decode attention: [P1] paragraph on w4attn.py: one key/value head is shared
+ * by eight query heads; every cached key and value is read once for all
+ * eight heads and the softmax runs over the cache; paragraph on the cache:
+ * full layers hold one slot per position, sliding layers a 512-slot ring that
+ * records each slot's position, and masks come from positions.  The oracle is
+ * the definition: scores s_t = scale * q.k_t over the valid slots, softmax,
+ * output sum_t p_t v_t, in fp64.
+ *
  * Table gather: [P1], step 2 "Keep the Vocabulary Tables in 4-Bit": the
  * token-embedding table (one copy, shared with the output layer) and the
  * per-layer input table (a row of 35 x 256 values per token) are stored as
@@ -275,4 +283,61 @@ void oracle_quantize(const float* W, int N, int K, int ldw, int group, int block
         }
     }
     free(v);
+}
+
+/*
+ * Decode attention, one KV head, H query heads, head width D, T cache slots:
+ *   valid(t) = pos == NULL ? 1
+ *              : pos[t] >= 0 && pos[t] <= cur && (window <= 0 || pos[t] > cur - window)
+ *   s_t = scale * sum_d q[h][d] K[t][d]   (valid t), m = max_t s_t,
+ *   p_t = exp(s_t - m), out[h][d] = sum_t p_t V[t][d] / sum_t p_t,
+ *   absout[h][d] = sum_t p_t |V[t][d]| / sum_t p_t  (scale of the acceptance bound).
+ * q, K, V are bf16 bit patterns (row-major, rows of D), widened exactly; all
+ * sums in fp64, in order of increasing t.  No valid slot: NaN outputs.
+ */
+void oracle_attn_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                        const int32_t* pos, int H, int T, int D, int cur, int window,
+                        double scale, double* out, double* absout)
+{
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int h = 0; h < H; ++h) {
+        double m = -INFINITY;
+        int any = 0;
+        for (int t = 0; t < T; ++t) {
+            int ok = 1;
+            if (pos) ok = pos[t] >= 0 && pos[t] <= cur && (window <= 0 || pos[t] > cur - window);
+            if (!ok) {
+                sc[t] = -INFINITY;
+                continue;
+            }
+            double d = 0.0;
+            for (int k = 0; k < D; ++k)
+                d += oracle_bf16_to_f64(q[(size_t)h * D + k]) *
+                     oracle_bf16_to_f64(K[(size_t)t * D + k]);
+            sc[t] = scale * d;
+            if (sc[t] > m) m = sc[t];
+            any = 1;
+        }
+        for (int k = 0; k < D; ++k) {
+            out[(size_t)h * D + k] = any ? 0.0 : NAN;
+            if (absout) absout[(size_t)h * D + k] = any ? 0.0 : NAN;
+        }
+        if (!any) continue;
+        double l = 0.0;
+        for (int t = 0; t < T; ++t) {
+            if (sc[t] == -INFINITY) continue;
+            const double p = exp(sc[t] - m);
+            l += p;
+            for (int k = 0; k < D; ++k) {
+                const double v = oracle_bf16_to_f64(V[(size_t)t * D + k]);
+                out[(size_t)h * D + k] += p * v;
+                if (absout) absout[(size_t)h * D + k] += p * fabs(v);
+            }
+        }
+        for (int k = 0; k < D; ++k) {
+            out[(size_t)h * D + k] /= l;
+            if (absout) absout[(size_t)h * D + k] /= l;
+        }
+    }
+    free(sc);
 }
