@@ -162,6 +162,37 @@ def time_quantize(torch, w4, synth, dev):
             "GBps_read_plus_write": moved / us / 1e3}
 
 
+def time_attention(torch, w4, dev):
+    """Split-K decode attention, 8 query heads on one KV head: full-length
+    caches (head width 512) at 4096 / 32768 / 131072 slots, and a sliding
+    layer's 512-slot ring (width 256).  Bytes = K and V of the slots scanned."""
+    import numpy as np
+    out = {}
+    rng = np.random.default_rng(5)
+    cases = [("full_D512_T4096", 512, 4096, False), ("full_D512_T32768", 512, 32768, False),
+             ("full_D512_T131072", 512, 131072, False), ("ring_D256_S512", 256, 512, True)]
+    for name, D, T, ring in cases:
+        K = torch.randn((T, D), device=dev).to(torch.bfloat16)
+        V = torch.randn((T, D), device=dev).to(torch.bfloat16)
+        q = torch.randn((8, D), device=dev).to(torch.bfloat16)
+        Vt = w4.attn_pack_v(V)
+        pos = None
+        cur = T - 1
+        if ring:
+            cur = 5000
+            pos = torch.from_numpy(np.array([cur - ((cur - s) % T) for s in range(T)],
+                                            dtype=np.int32)).to(dev)
+        ws = torch.empty(w4.attn_workspace_bytes(T, D), dtype=torch.uint8, device=dev)
+        o = torch.empty((8, D), dtype=torch.bfloat16, device=dev)
+        us = time_calls(torch, lambda: w4.attn_decode(q, K, Vt, T, 1.0 / D ** 0.5, pos=pos,
+                                                      cur=cur, window=512 if ring else 0,
+                                                      out_dtype="bf16", out=o, workspace=ws))
+        kv = 2 * T * D * 2
+        out[name] = {"us": us, "kv_GBps": kv / us / 1e3, "pct_of_8TBps": kv / us / 1e3 / 80.0}
+        del K, V, Vt, ws
+    return out
+
+
 def time_prefill(torch, w4, synth, dev):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
@@ -297,6 +328,7 @@ def main():
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
             "quantize_rotate": time_quantize(torch, w4, synth, dev),
+            "attention_decode": time_attention(torch, w4, dev),
         }
 
     # roofline of the dominant (only) kernel of the timed step

@@ -44,7 +44,8 @@ EXPORTS = (
     "w4a16_gemv", "w4a16_gemm_smallM", "w4_fwht", "w4a16_gemm_workspace_bytes",
     "w4a16_gemm", "w4_decode_sweep_create", "w4_decode_sweep_launch",
     "w4_decode_sweep_check", "w4_decode_sweep_info", "w4_decode_sweep_destroy",
-    "w4_gather", "w4_quantize", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
+    "w4_gather", "w4_quantize", "w4_attn_workspace_bytes", "w4_attn_decode",
+    "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
 )
 
 
@@ -110,6 +111,11 @@ def lib():
             "w4_selftest": ([vp], i),
             "w4_gather": ([vp, i, i, i, vp, i, vp, i, i, vp], i),
             "w4_quantize": ([vp, i, i, i, i, i, i, vp, vp], i),
+            "w4_attn_workspace_bytes": ([i, i], sz),
+            "w4_attn_decode": ([vp, vp, i, vp, vp, i, i, i, i, ctypes.c_float, vp, sz, vp, i,
+                                vp], i),
+            "w4_attn_pack_v": ([vp, i, i, i, vp, vp], i),
+            "w4_attn_store_kv": ([vp, vp, i, vp, i, vp, i, vp], i),
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
         }
@@ -205,6 +211,46 @@ def quantize(W, group: int, had_block: int = 0, out=None, stream=None):
     wdt = W4_F32 if W.dtype == torch.float32 else (W4_BF16 if W.dtype == torch.bfloat16 else -1)
     _check(lib().w4_quantize(_ptr(W), wdt, W.stride(0), N, K, group, had_block, _ptr(out),
                              _stream(stream)))
+    return out
+
+
+def attn_workspace_bytes(T: int, D: int) -> int:
+    return int(lib().w4_attn_workspace_bytes(T, D))
+
+
+def attn_pack_v(V, T: int = None, out=None, stream=None):
+    """Row-major bf16 V [T, D] (device) -> the blocked layout w4_attn_decode
+    reads (a flat bf16 tensor of ceil(T/32)*32*D elements)."""
+    import torch
+    T = V.shape[0] if T is None else T
+    D = V.shape[1]
+    if out is None:
+        out = torch.empty(((T + 31) // 32) * 32 * D, dtype=torch.bfloat16, device=V.device)
+    _check(lib().w4_attn_pack_v(_ptr(V), V.stride(0), T, D, _ptr(out), _stream(stream)))
+    return out
+
+
+def attn_store_kv(k, v, slot: int, K, Vt, stream=None):
+    """Writes one slot: K[slot] = k and V slot `slot` = v (blocked layout)."""
+    D = K.shape[1]
+    _check(lib().w4_attn_store_kv(_ptr(k), _ptr(v), slot, _ptr(K), K.stride(0), _ptr(Vt), D,
+                                  _stream(stream)))
+
+
+def attn_decode(q, K, Vt, T: int, scale: float, pos=None, cur: int = 0, window: int = 0,
+                out_dtype: str = "f32", out=None, workspace=None, stream=None):
+    """Decode attention of 8 query heads q [8, D] over T slots of one KV head
+    (K [>=T, D] row-major, Vt blocked); pos: None or int32 [T] positions."""
+    import torch
+    D = q.shape[1]
+    if out is None:
+        out = _empty_out((8, D), out_dtype, q.device)
+    ws = attn_workspace_bytes(T, D)
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    _check(lib().w4_attn_decode(_ptr(q), _ptr(K), K.stride(0), _ptr(Vt), _ptr(pos), T, D, cur,
+                                window, float(scale), _ptr(workspace), ws, _ptr(out),
+                                _dt(out_dtype), _stream(stream)))
     return out
 
 

@@ -115,7 +115,7 @@ int w4_device_check(void) {
 
 const char* w4_build_info(void) {
     return "abi=1 arch=gfx950 kernels=gemv,gemv_generic,smallm,fwht,mfma_gemm,sweep_graph,"
-           "sweep_persistent,pack,gather,quantize,probe";
+           "sweep_persistent,pack,gather,quantize,attn_decode,probe";
 }
 
 size_t w4_packed_bytes(int N, int K, int group) {
@@ -285,6 +285,60 @@ int w4_quantize(const void* W, int w_dtype, int ldw, int N, int K, int group, in
         return fail(W4_ERR_ALIGN, "quantize: rows of W must start 16-byte aligned (ldw %d)", ldw);
     return launch_quantize(W, w_dtype, ldw, N, K, group, had_block, packed,
                            static_cast<hipStream_t>(stream));
+}
+
+static int check_attn_shape(int T, int D) {
+    if (D != 256 && D != 512) return fail(W4_ERR_SHAPE, "attention: D must be 256 or 512 (got %d)", D);
+    if (T < 1 || T > (1 << 24)) return fail(W4_ERR_SHAPE, "attention: T out of range (got %d)", T);
+    return W4_OK;
+}
+
+size_t w4_attn_workspace_bytes(int T, int D) {
+    if (check_attn_shape(T, D) != W4_OK) return 0;
+    return attn_workspace_bytes(T, D);
+}
+
+int w4_attn_decode(const uint16_t* q, const uint16_t* K, int ldk, const uint16_t* Vt,
+                   const int32_t* pos, int T, int D, int cur, int window, float scale,
+                   void* workspace, size_t ws_bytes, void* out, int out_dtype, void* stream) {
+    W4_TRY(check_attn_shape(T, D));
+    W4_TRY(check_dtype(out_dtype));
+    W4_TRY(check_in16(q, "q"));
+    W4_TRY(check_in16(K, "K"));
+    W4_TRY(check_in16(Vt, "Vt"));
+    W4_TRY(check_in16(workspace, "workspace"));
+    W4_TRY(check_in16(out, "out"));
+    if (ldk < D || ldk % 8 != 0)
+        return fail(W4_ERR_ALIGN, "attention: ldk must be >= D and a multiple of 8 (got %d)", ldk);
+    if (pos && !aligned(pos, 4)) return fail(W4_ERR_ALIGN, "attention: pos must be 4-byte aligned");
+    if (window < 0) return fail(W4_ERR_ARG, "attention: window < 0");
+    if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+        return fail(W4_ERR_ARG, "attention: scale must be finite");
+    if (ws_bytes < attn_workspace_bytes(T, D))
+        return fail(W4_ERR_SHAPE, "attention: workspace %zu bytes < %zu", ws_bytes,
+                    attn_workspace_bytes(T, D));
+    return launch_attn_decode(q, K, ldk, Vt, pos, T, D, cur, window, scale, workspace, out,
+                              out_dtype, static_cast<hipStream_t>(stream));
+}
+
+int w4_attn_pack_v(const uint16_t* V, int ldv, int T, int D, uint16_t* Vt, void* stream) {
+    W4_TRY(check_attn_shape(T, D));
+    if (!V) return fail(W4_ERR_ARG, "attention: V is NULL");
+    if (!aligned(V, 2)) return fail(W4_ERR_ALIGN, "attention: V must be 2-byte aligned");
+    W4_TRY(check_in16(Vt, "Vt"));
+    if (ldv < D) return fail(W4_ERR_SHAPE, "attention: ldv %d < D %d", ldv, D);
+    return launch_attn_pack_v(V, ldv, T, D, Vt, static_cast<hipStream_t>(stream));
+}
+
+int w4_attn_store_kv(const uint16_t* k, const uint16_t* v, int slot, uint16_t* K, int ldk,
+                     uint16_t* Vt, int D, void* stream) {
+    W4_TRY(check_attn_shape(1, D));
+    if (!k || !v || !K || !Vt) return fail(W4_ERR_ARG, "attention: NULL pointer");
+    if (!aligned(k, 2) || !aligned(v, 2) || !aligned(K, 2) || !aligned(Vt, 2))
+        return fail(W4_ERR_ALIGN, "attention: pointers must be 2-byte aligned");
+    if (slot < 0 || slot >= (1 << 24)) return fail(W4_ERR_SHAPE, "attention: slot out of range");
+    if (ldk < D) return fail(W4_ERR_SHAPE, "attention: ldk %d < D %d", ldk, D);
+    return launch_attn_store_kv(k, v, slot, K, ldk, Vt, D, static_cast<hipStream_t>(stream));
 }
 
 int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) {

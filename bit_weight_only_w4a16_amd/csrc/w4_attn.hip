@@ -1,0 +1,381 @@
+// w4_attn.hip -- split-K decode attention: one key/value head, eight query heads.
+//
+// [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp",
+// paragraph on w4attn.py: the model has one key/value head shared by eight
+// query heads, so each cached key and value is read once for all eight heads,
+// the cache is split into slices, and the slices are combined with an online
+// softmax; paragraph on the cache: full layers hold one slot per position
+// (head width 512), sliding layers a 512-slot ring that records each slot's
+// position, and masks are built from positions.
+//
+// MI355X shape of it.  Per 32-slot tile, both products run on the matrix
+// cores (v_mfma_f32_16x16x32_bf16, heads padded to 16):
+//   S^T = K Q^T   A = 16 key rows x 32 dims, B = Q^T (dims x heads),
+//   O^T += V^T P^T  A = 16 dims x 32 slots of V^T, B = P^T (slots x heads).
+// Key rows are read in their natural layout; the score tile leaves every lane
+// with one head and 8 slots, which is exactly the B operand of the second
+// product, so P needs no transpose.  V is stored in 32-slot blocks, each D
+// rows of 32 slots (the blocked layout w4_attn_pack_v writes), so the A
+// operand of the second product is one 16-byte load per lane.
+// The four waves of a workgroup split the head width D into quarters: each
+// computes partial scores over its quarter, the partials are summed through
+// LDS in a fixed order (identical in every wave), the softmax bookkeeping is
+// repeated in every wave, and each wave accumulates O for its quarter of D
+// only.  A workgroup walks a contiguous range of tiles and writes one partial
+// (running max, running sum, unnormalised O); a second kernel merges the
+// partials of all workgroups.
+#include "w4_dispatch.h"
+
+namespace w4 {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kAttnHeads = 8;
+constexpr int kAttnTile = 32;
+constexpr int kAttnMaxWG = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+    const uint16_t* q;    // [8][D]
+    const uint16_t* K;    // [T][ldk]
+    const uint16_t* Vt;   // blocked: tile b, dim d, slot c at ((b * D + d) * 32 + c)
+    const int32_t* pos;   // nullptr or [T]
+    float* part;          // per workgroup: m[16], l[16], O[8][D]
+    int ldk, T, cur, window, tiles, nwg;
+    float scale2;         // scale * log2(e): scores in base 2
+};
+
+__device__ __forceinline__ int part_stride(int D) { return 32 + kAttnHeads * D; }
+
+// Slot c is attended iff c < T and, with positions, the slot's position p is
+// in (cur - window, cur] (window 0: no lower bound).
+__device__ __forceinline__ bool slot_valid(const AttnArgs& a, int c, int p) {
+    if (c >= a.T) return false;
+    if (!a.pos) return true;
+    return p >= 0 && p <= a.cur && (a.window <= 0 || p > a.cur - a.window);
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_split_kernel(AttnArgs a) {
+    constexpr int DQ = D / 4;   // dims per wave
+    constexpr int KS = DQ / 32; // score k-steps per wave
+    constexpr int DT = DQ / 16; // output tiles (16 dims) per wave
+    __shared__ float sx[2][4][8][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15;  // head (columns of both products)
+    const int g = lane >> 4;  // k-group of the operands, row group of the results
+    const int d0 = wave * DQ;
+    const int tb = (int)((long long)a.tiles * blockIdx.x / a.nwg);
+    const int te = (int)((long long)a.tiles * (blockIdx.x + 1) / a.nwg);
+
+    // B operand of S^T = K Q^T: head i, dims d0 + 32 s + 8 g .. + 7 (zero for padded heads)
+    u32x4 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (i < kAttnHeads)
+            qf[s] = gload(reinterpret_cast<const u32x4*>(a.q + (size_t)i * D + d0 + 32 * s + 8 * g));
+        else
+            qf[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+
+    f32x4 acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -__builtin_inff(), l_run = 0.f;
+
+    struct TileRegs {
+        u32x4 ka[KS], kb[KS], vf[DT];
+        int pos[8];  // positions of this lane's slots (ring caches)
+    };
+    // Loads of tile tau: score tile a row r is slot p0 + 8 (r / 4) + r % 4, tile b
+    // that + 4, so result row 4 g + j holds slot p0 + 8 g + j (tile a, j < 4) or
+    // + 4 (tile b); V^T rows are dims d0 + 16 t + i, slots 8 g .. 8 g + 7.
+    auto load_tile = [&](int tau, TileRegs& r) {
+        const int p0 = tau * kAttnTile;
+        const int ra = p0 + 8 * (i >> 2) + (i & 3);
+        const int rb = ra + 4;
+        const uint16_t* kra = a.K + (size_t)(ra < a.T ? ra : a.T - 1) * a.ldk + d0 + 8 * g;
+        const uint16_t* krb = a.K + (size_t)(rb < a.T ? rb : a.T - 1) * a.ldk + d0 + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            r.ka[s] = gload(reinterpret_cast<const u32x4*>(kra + 32 * s));
+            r.kb[s] = gload(reinterpret_cast<const u32x4*>(krb + 32 * s));
+        }
+        const uint16_t* vb =
+            a.Vt + (size_t)tau * D * kAttnTile + (size_t)(d0 + i) * kAttnTile + 8 * g;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+            r.vf[t] = gload(reinterpret_cast<const u32x4*>(vb + (size_t)16 * t * kAttnTile));
+        if (a.pos) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = p0 + 8 * g + j;
+                r.pos[j] = c < a.T ? gload(a.pos + c) : -1;
+            }
+        }
+    };
+
+    auto process = [&](int tau, const TileRegs& r) {
+        const int p0 = tau * kAttnTile;
+        bool valid[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) valid[j] = slot_valid(a, p0 + 8 * g + j, a.pos ? r.pos[j] : 0);
+
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sa = mma(r.ka[s], qf[s], sa);
+            sb = mma(r.kb[s], qf[s], sb);
+        }
+        // partial scores of the four dim quarters: summed in wave order 0..3
+        float* buf = &sx[tau & 1][0][0][0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            buf[(wave * 8 + q) * 64 + lane] = sa[q];
+            buf[(wave * 8 + 4 + q) * 64 + lane] = sb[q];
+        }
+        __syncthreads();
+        float t8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float s = ((buf[(0 * 8 + j) * 64 + lane] + buf[(1 * 8 + j) * 64 + lane]) +
+                             buf[(2 * 8 + j) * 64 + lane]) +
+                            buf[(3 * 8 + j) * 64 + lane];
+            t8[j] = valid[j] ? s * a.scale2 : -__builtin_inff();
+        }
+        // online softmax of head i over the tile's 32 slots (4 lanes x 8)
+        float mt = t8[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mt = fmaxf(mt, t8[j]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        const bool none = m_new == -__builtin_inff();
+        const float alpha = none ? 1.f : exp2f(m_run - m_new);
+        uint32_t pb[8];
+        float ls = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float p = none ? 0.f : exp2f(t8[j] - m_new);
+            pb[j] = f32_to_bf16_rne(p);
+            ls += bf16_to_f32(pb[j]);  // the sum uses the weights the product uses
+        }
+        ls += __shfl_xor(ls, 16, 64);
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = alpha * l_run + ls;
+        m_run = m_new;
+
+        const u32x4 pf = u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16),
+                               pb[4] | (pb[5] << 16), pb[6] | (pb[7] << 16)};
+        // V of slots that are not attended may hold anything (a never-written
+        // ring slot, slots past T): zero them so 0 * NaN never reaches O
+        u32x4 vmask;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            vmask[w] = (valid[2 * w] ? 0x0000FFFFu : 0u) | (valid[2 * w + 1] ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+            acc[t] = acc[t] * alpha;
+            acc[t] = mma(r.vf[t] & vmask, pf, acc[t]);
+        }
+    };
+
+    // two register sets: the next tile's loads are in flight while this one
+    // is computed (the last step re-loads the current tile instead of
+    // branching, so every wait counts exactly)
+    TileRegs ta, tb2;
+    int tau = tb;
+    load_tile(tau, ta);
+    while (true) {
+        load_tile(tau + 1 < te ? tau + 1 : tau, tb2);
+        process(tau, ta);
+        if (++tau >= te) break;
+        load_tile(tau + 1 < te ? tau + 1 : tau, ta);
+        process(tau, tb2);
+        if (++tau >= te) break;
+    }
+
+    // partial of this workgroup: m and l of each head (base 2), unnormalised O
+    float* part = a.part + (size_t)blockIdx.x * part_stride(D);
+    if (wave == 0 && g == 0 && i < kAttnHeads) {
+        gstore(part + i, m_run);
+        gstore(part + 16 + i, l_run);
+    }
+    if (i < kAttnHeads) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                gstore(part + 32 + i * D + d0 + 16 * t + 4 * g + r, acc[t][r]);
+    }
+}
+
+// Workgroup-wide reductions over the merge kernel's threads in a fixed tree
+// order (the same on every run).
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeWaves = kMergeThreads / 64;
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+    red[threadIdx.x] = v;
+    __syncthreads();
+    for (int k = kMergeThreads / 2; k > 0; k >>= 1) {
+        if ((int)threadIdx.x < k) {
+            const float o = red[threadIdx.x + k];
+            red[threadIdx.x] = is_max ? fmaxf(red[threadIdx.x], o) : red[threadIdx.x] + o;
+        }
+        __syncthreads();
+    }
+    const float r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// out[h][d] = sum_w O_w[h][d] e_w / sum_w l_w e_w, e_w = 2^(m_w - M), M = max_w m_w
+// (e_w = 0 for a partial that attended nothing); NaN when no slot was attended.
+// Workgroup (h, 64-dim block) of 16 waves: the weights e_w are computed once
+// into LDS; wave k sums the partials w = k, k + 16, ... for its 64 dims, eight
+// loads in flight and no branches, and the 16 wave sums are added in order.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* __restrict__ part,
+                                                                  int nwg,
+                                                                  void* __restrict__ out,
+                                                                  int odt) {
+    __shared__ float ew[kAttnMaxWG];
+    __shared__ float red[kMergeThreads];
+    __shared__ float wsum[kMergeWaves][64];
+    const int h = blockIdx.x;
+    const int d = blockIdx.y * 64 + (threadIdx.x & 63);
+    const int wave = threadIdx.x >> 6;
+    const int ps = part_stride(D);
+
+    float mloc = -__builtin_inff();
+    for (int w = threadIdx.x; w < nwg; w += kMergeThreads)
+        mloc = fmaxf(mloc, gload(part + (size_t)w * ps + h));
+    const float M = block_reduce(mloc, red, true);
+    float lloc = 0.f;
+    for (int w = threadIdx.x; w < nwg; w += kMergeThreads) {
+        const float mw = gload(part + (size_t)w * ps + h);
+        const float e = mw == -__builtin_inff() ? 0.f : exp2f(mw - M);
+        ew[w] = e;
+        lloc += gload(part + (size_t)w * ps + 16 + h) * e;
+    }
+    const float L = block_reduce(lloc, red, false);  // ends with a barrier: ew[] complete
+
+    constexpr int S = kMergeWaves;
+    float o = 0.f;
+    const float* col = part + 32 + (size_t)h * D + d;
+    int w = wave;
+    for (; w + 7 * S < nwg; w += 8 * S) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = gload(col + (size_t)(w + u * S) * ps);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o += v[u] * ew[w + u * S];
+    }
+    for (; w < nwg; w += S) o += gload(col + (size_t)w * ps) * ew[w];
+    wsum[wave][threadIdx.x & 63] = o;
+    __syncthreads();
+    if (wave == 0) {
+        const int t = threadIdx.x;
+        float tot = wsum[0][t];
+#pragma unroll
+        for (int k = 1; k < kMergeWaves; ++k) tot += wsum[k][t];
+        const float v = M == -__builtin_inff() ? __builtin_nanf("") : tot / L;
+        store_out(out, (size_t)h * D + d, v, odt);
+    }
+}
+
+// Blocked V: tile b, dim d, slot c at ((b * D + d) * 32 + c); slots past T are 0.
+__global__ __launch_bounds__(256) void attn_pack_v_kernel(const uint16_t* __restrict__ V, int ldv,
+                                                         int T, int D,
+                                                         uint16_t* __restrict__ Vt) {
+    const long long row = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // (b, d)
+    const int tiles = (T + kAttnTile - 1) / kAttnTile;
+    if (row >= (long long)tiles * D) return;
+    const int b = (int)(row / D), d = (int)(row - (long long)b * D);
+    uint32_t w[16];
+#pragma unroll
+    for (int c = 0; c < kAttnTile; c += 2) {
+        const int t0 = b * kAttnTile + c;
+        const uint32_t lo = t0 < T ? gload(V + (size_t)t0 * ldv + d) : 0u;
+        const uint32_t hi = t0 + 1 < T ? gload(V + (size_t)(t0 + 1) * ldv + d) : 0u;
+        w[c / 2] = lo | (hi << 16);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(Vt + (size_t)row * kAttnTile);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        gstore(dst + k, u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]});
+}
+
+// One decode step's cache write: key row `slot` and value column `slot`.
+__global__ __launch_bounds__(256) void attn_store_kv_kernel(const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v, int slot,
+                                                           uint16_t* __restrict__ K, int ldk,
+                                                           uint16_t* __restrict__ Vt, int D) {
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        gstore(K + (size_t)slot * ldk + d, gload(k + d));
+        gstore(Vt + ((size_t)(slot / kAttnTile) * D + d) * kAttnTile + slot % kAttnTile,
+               gload(v + d));
+    }
+}
+
+size_t attn_workspace_bytes(int T, int D) {
+    const int tiles = (T + kAttnTile - 1) / kAttnTile;
+    const int nwg = tiles < kAttnMaxWG ? tiles : kAttnMaxWG;
+    return (size_t)nwg * (size_t)(32 + kAttnHeads * D) * sizeof(float);
+}
+
+int launch_attn_decode(const uint16_t* q, const uint16_t* K, int ldk, const uint16_t* Vt,
+                       const int32_t* pos, int T, int D, int cur, int window, float scale,
+                       void* ws, void* out, int odt, hipStream_t s) {
+    AttnArgs a;
+    a.q = q;
+    a.K = K;
+    a.Vt = Vt;
+    a.pos = pos;
+    a.part = static_cast<float*>(ws);
+    a.ldk = ldk;
+    a.T = T;
+    a.cur = cur;
+    a.window = window;
+    a.tiles = (T + kAttnTile - 1) / kAttnTile;
+    a.nwg = a.tiles < kAttnMaxWG ? a.tiles : kAttnMaxWG;
+    a.scale2 = scale * kLog2e;
+    if (D == 512) {
+        attn_split_kernel<512><<<dim3(a.nwg), dim3(256), 0, s>>>(a);
+        attn_merge_kernel<512><<<dim3(kAttnHeads, 512 / 64), dim3(kMergeThreads), 0, s>>>(
+            a.part, a.nwg, out, odt);
+    } else {
+        attn_split_kernel<256><<<dim3(a.nwg), dim3(256), 0, s>>>(a);
+        attn_merge_kernel<256><<<dim3(kAttnHeads, 256 / 64), dim3(kMergeThreads), 0, s>>>(
+            a.part, a.nwg, out, odt);
+    }
+    return hip_fail(hipGetLastError(), "attention launch");
+}
+
+int launch_attn_pack_v(const uint16_t* V, int ldv, int T, int D, uint16_t* Vt, hipStream_t s) {
+    const long long rows = (long long)((T + kAttnTile - 1) / kAttnTile) * D;
+    attn_pack_v_kernel<<<dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s>>>(V, ldv, T, D, Vt);
+    return hip_fail(hipGetLastError(), "attention V pack launch");
+}
+
+int launch_attn_store_kv(const uint16_t* k, const uint16_t* v, int slot, uint16_t* K, int ldk,
+                         uint16_t* Vt, int D, hipStream_t s) {
+    attn_store_kv_kernel<<<dim3(1), dim3(256), 0, s>>>(k, v, slot, K, ldk, Vt, D);
+    return hip_fail(hipGetLastError(), "attention cache store launch");
+}
+
+}  // namespace w4

@@ -45,6 +45,14 @@ int launch_gather(const void* packed, int N, int K, int group, const int32_t* id
 int launch_quantize(const void* W, int wdt, int ldw, int N, int K, int group, int block,
                     void* packed, hipStream_t s);
 
+size_t attn_workspace_bytes(int T, int D);
+int launch_attn_decode(const uint16_t* q, const uint16_t* K, int ldk, const uint16_t* Vt,
+                       const int32_t* pos, int T, int D, int cur, int window, float scale,
+                       void* ws, void* out, int odt, hipStream_t s);
+int launch_attn_pack_v(const uint16_t* V, int ldv, int T, int D, uint16_t* Vt, hipStream_t s);
+int launch_attn_store_kv(const uint16_t* k, const uint16_t* v, int slot, uint16_t* K, int ldk,
+                         uint16_t* Vt, int D, hipStream_t s);
+
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* out,
                       hipStream_t s);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

@@ -254,6 +254,47 @@ int w4_quantize(const void* W, int w_dtype, int ldw, int N, int K, int group,
                 int had_block, void* packed, void* stream);
 
 /*
+ * Split-K decode attention: one key/value head shared by 8 query heads.
+ * [P1] paragraph on w4attn.py: each cached key and value is read once for
+ * all eight query heads, the cache is split into slices and the slices are
+ * combined with an online softmax; paragraph on the cache: full layers hold
+ * one slot per position (head width 512), sliding layers a 512-slot ring
+ * recording each slot's position, masks built from positions.
+ *   valid(t) = t < T and (pos == NULL or (pos[t] >= 0 and pos[t] <= cur and
+ *              (window == 0 or pos[t] > cur - window)))
+ *   s_t = scale * q_h . K[t],  out[h] = sum_t softmax_t(s) V[t]  over valid t.
+ *  q:   device, [8][D] bf16, 16-byte aligned.
+ *  K:   device, T rows of ldk bf16 (ldk >= D, ldk % 8 == 0), 16-byte aligned.
+ *  Vt:  device, V in the blocked layout: ceil(T/32) blocks of 32 slots, block
+ *       b holding D rows of 32 bf16; slot t, dim d at Vt[((t/32)*D + d)*32 +
+ *       t%32].  w4_attn_pack_v writes it from row-major V; w4_attn_store_kv
+ *       writes one slot.  Slots that are not valid may hold any bits.
+ *  pos: NULL (slots 0..T-1 all valid: a full-length cache) or device int32
+ *       [T] slot positions (-1 = empty), e.g. a ring of 512 slots.
+ *  D:   256 or 512.  T: 1 .. 2^24 slots scanned.  window >= 0.  scale finite.
+ *  workspace: device, >= w4_attn_workspace_bytes(T, D) bytes, 16-byte aligned
+ *       (per-slice partials; overwritten).
+ *  out: device, [8][D] fp32 or bf16 (nearest even), 16-byte aligned.  A head
+ *       with no valid slot gets NaN.
+ * Products on the matrix cores (bf16 operands, fp32 accumulation); the
+ * softmax weights enter the value product as bf16 (nearest even) and the
+ * normaliser sums those same weights.  Two launches (split, merge).
+ */
+size_t w4_attn_workspace_bytes(int T, int D);
+int w4_attn_decode(const uint16_t* q, const uint16_t* K, int ldk,
+                   const uint16_t* Vt, const int32_t* pos, int T, int D,
+                   int cur, int window, float scale, void* workspace,
+                   size_t ws_bytes, void* out, int out_dtype, void* stream);
+/* Row-major V (T rows of ldv bf16, ldv >= D) -> the blocked layout above
+ * (ceil(T/32)*32*D bf16; slots past T written as 0).  Vt 16-byte aligned. */
+int w4_attn_pack_v(const uint16_t* V, int ldv, int T, int D, uint16_t* Vt,
+                   void* stream);
+/* One decode step's cache write: K[slot] = k (D bf16), V slot `slot` = v,
+ * in the blocked layout. */
+int w4_attn_store_kv(const uint16_t* k, const uint16_t* v, int slot,
+                     uint16_t* K, int ldk, uint16_t* Vt, int D, void* stream);
+
+/*
  * Row lookup in a 4-bit table, dequantized:
  *   Y[b][k] = (code(ids[b], k) - 8) * scale(ids[b], k / group),  b < B, k < K.
  * [P1] step 2 "Keep the Vocabulary Tables in 4-Bit": the token-embedding

@@ -119,6 +119,40 @@ def test_quantize_validation(L):
     assert f(VP(0), 0, 512, 64, 512, 32, 0, A16, VP(0)) == -1    # W NULL
 
 
+def test_attention_validation(L):
+    f = L.w4_attn_decode
+    F = ctypes.c_float
+    ws = L.w4_attn_workspace_bytes(1000, 512)
+    assert ws == 32 * (32 + 8 * 512) * 4                   # ceil(1000/32) = 32 slices
+    assert L.w4_attn_workspace_bytes(1000, 384) == 0
+    assert L.w4_attn_workspace_bytes(1 << 20, 256) == 512 * (32 + 8 * 256) * 4
+    ok = (A16, A16, 512, A16, VP(0), 1000, 512, 999, 0, F(0.04), A16, ws, A16, 0, VP(0))
+
+    def call(**kw):
+        args = list(ok)
+        names = ["q", "K", "ldk", "Vt", "pos", "T", "D", "cur", "window", "scale", "ws",
+                 "ws_bytes", "out", "odt", "s"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(D=384) == -2
+    assert call(T=0) == -2
+    assert call(q=A2) == -3
+    assert call(Vt=A2) == -3
+    assert call(ldk=500) == -3
+    assert call(ldk=516) == -3
+    assert call(pos=A2) == -3
+    assert call(window=-1) == -1
+    assert call(scale=F(float("nan"))) == -1
+    assert call(ws_bytes=ws - 1) == -2
+    assert call(odt=5) == -4
+    assert L.w4_attn_pack_v(A16, 500, 100, 512, A16, VP(0)) == -2     # ldv < D
+    assert L.w4_attn_pack_v(A16, 512, 100, 512, A2, VP(0)) == -3
+    assert L.w4_attn_store_kv(A16, A16, -1, A16, 512, A16, 512, VP(0)) == -2
+    assert L.w4_attn_store_kv(A16, A16, 3, A16, 100, A16, 512, VP(0)) == -2
+
+
 def test_fwht_validation(L):
     f = L.w4_fwht
     assert f(A16, 1536, A16, 1536, 4, 1536, 384, VP(0)) == -2    # not a power of 2
