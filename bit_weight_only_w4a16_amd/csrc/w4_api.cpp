@@ -43,8 +43,8 @@ constexpr int kMaxN = 1 << 26;
 constexpr int kMaxK = 1 << 20;
 
 static int check_weight_shape(int N, int K, int group) {
-    if (group != 32 && group != 256)
-        return fail(W4_ERR_SHAPE, "group must be 32 or 256 (got %d)", group);
+    if (group != 32 && group != 256 && group != 512)
+        return fail(W4_ERR_SHAPE, "group must be 32, 256 or 512 (got %d)", group);
     if (N < 1 || N > kMaxN) return fail(W4_ERR_SHAPE, "N out of range (got %d)", N);
     if (K < group || K > kMaxK || K % group != 0)
         return fail(W4_ERR_SHAPE, "K must be a positive multiple of group %d (got %d)",

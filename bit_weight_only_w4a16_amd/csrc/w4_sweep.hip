@@ -30,8 +30,8 @@ namespace w4 {
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 static int check_op(const w4_gemv_op& op, int i) {
-    if (op.group != 32 && op.group != 256)
-        return fail(W4_ERR_SHAPE, "sweep op %d: group must be 32 or 256", i);
+    if (op.group != 32 && op.group != 256 && op.group != 512)
+        return fail(W4_ERR_SHAPE, "sweep op %d: group must be 32, 256 or 512", i);
     if (op.N < 1 || op.K < op.group || op.K % op.group != 0 || op.K > (1 << 20) ||
         op.N > (1 << 26))
         return fail(W4_ERR_SHAPE, "sweep op %d: bad shape N=%d K=%d", i, op.N, op.K);

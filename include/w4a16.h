@@ -97,7 +97,7 @@ const char* w4_build_info(void);
 
 /*
  * Bytes of the device layout for an N x K matrix (0 when the shape is
- * invalid: N < 1, K < 1, group not 32 or 256, K % group != 0).
+ * invalid: N < 1, K < 1, group not 32, 256 or 512, K % group != 0).
  */
 size_t w4_packed_bytes(int N, int K, int group);
 
@@ -123,7 +123,7 @@ int w4_unpack_host(const void* packed, int N, int K, int group,
  * y = W x for one activation vector (M = 1): y[n] = sum_k w(n,k) x[k], fp32
  * accumulation, any summation order but bitwise run-to-run deterministic.
  * [P1] paragraph on the w4gemv.py kernel.
- *  packed: device layout of W (N x K, group 32 or 256), 16-byte aligned.
+ *  packed: device layout of W (N x K, group 32, 256 or 512), 16-byte aligned.
  *  x: device, K bf16, 16-byte aligned.
  *  y: device, N elements of y_dtype (4-byte aligned for fp32, 2 for bf16).
  * N >= 1; K >= 32 and K % group == 0.
@@ -199,7 +199,7 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
  */
 typedef struct w4_gemv_op {
     const void* packed;      /* device layout of this op's weights   */
-    int N, K, group;         /* shape; group 32 or 256               */
+    int N, K, group;         /* shape; group 32, 256 or 512          */
     const uint16_t* x;       /* device, K bf16, 16-byte aligned      */
     void* y;                 /* device, N elements of y_dtype        */
     int y_dtype;             /* W4_F32 or W4_BF16                    */

@@ -63,6 +63,8 @@ A2 = VP(0x10002)
 
 @pytest.mark.parametrize("args,status", [
     ((A16, 256, 512, 64, A16, A16, 0), -2),       # group
+    ((A16, 256, 1024, 1024, A16, A16, 0), -2),    # group 1024
+    ((A16, 256, 768, 512, A16, A16, 0), -2),      # K % 512
     ((A16, 0, 512, 32, A16, A16, 0), -2),         # N
     ((A16, 256, 500, 32, A16, A16, 0), -2),       # K % group
     ((A16, 256, 512, 32, A16, A16, 7), -4),       # dtype

@@ -43,7 +43,8 @@ def _check(oracle_mod, c, packed, ids, dtype, what):
         what, len(bad), tuple(bad[0]), g[tuple(bad[0])], wb[tuple(bad[0])])
 
 
-SHAPES = [(1000, 1536, 32), (700, 8960, 32), (513, 512, 256), (97, 96, 32), (5, 32, 32)]
+SHAPES = [(1000, 1536, 32), (700, 8960, 32), (513, 512, 256), (97, 96, 32), (5, 32, 32),
+          (300, 1536, 512)]
 
 
 @pytest.mark.parametrize("N,K,g", SHAPES)

@@ -75,7 +75,7 @@ def test_fwht_twice_is_identity_within_rounding():
 
 @pytest.mark.parametrize("M", [2, 3, 4, 5, 8, 11, 16])
 @pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (97, 288, 32), (1536, 6144, 32),
-                                   (33, 16384, 32), (65, 1024, 256)])
+                                   (33, 16384, 32), (65, 1024, 256), (129, 1536, 512)])
 def test_smallm_vs_oracle(oracle_mod, M, N, K, g):
     note("smallM M=%d N=%d K=%d g=%d" % (M, N, K, g))
     case = synth.make_case("smallm", N, K, g, M, 10 * M + N + K, "bf16")
@@ -135,7 +135,8 @@ def test_prefill_g256_hadamard(oracle_mod, M):
 
 @pytest.mark.parametrize("M,N,K,g,had", [(17, 100, 256, 32, 0), (64, 12288, 1536, 32, 0),
                                          (100, 513, 1536, 256, 512), (512, 300, 512, 256, 0),
-                                         (65, 1000, 2048, 256, 256), (33, 64, 256, 256, 0)])
+                                         (65, 1000, 2048, 256, 256), (33, 64, 256, 256, 0),
+                                         (64, 12288, 1536, 512, 512), (40, 300, 1024, 512, 0)])
 def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
     """M > 16 runs on the matrix cores: ragged M and N, both group sizes,
     with and without the run-time transform."""

@@ -87,7 +87,7 @@ RAGGED_OPS = [(33, 512, 32, "f32"), (100, 1536, 32, "bf16"), (1000, 2048, 32, "b
               (4097, 1536, 32, "f32"), (65, 6144, 32, "bf16"), (130, 96, 32, "f32"),
               (77, 768, 256, "bf16"), (5000, 1536, 32, "bf16"), (1, 1536, 32, "f32"),
               (129, 3072, 32, "bf16"), (63, 1024, 32, "f32"), (31, 64, 32, "bf16"),
-              (50, 4096, 32, "f32")]
+              (50, 4096, 32, "f32"), (70, 1536, 512, "bf16"), (40, 1024, 512, "f32")]
 
 
 @pytest.mark.parametrize("name,mode", MODES)

@@ -50,7 +50,7 @@ def test_all_zero_group(oracle_mod):
     assert c[1, 40] == 1                          # -3 is the group max -> -7
 
 
-@pytest.mark.parametrize("group", [32, 256])
+@pytest.mark.parametrize("group", [32, 256, 512])
 def test_grid_values_round_trip(oracle_mod, group):
     rng = np.random.default_rng(group)
     N, K = 5, 512
