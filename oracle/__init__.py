@@ -71,6 +71,8 @@ def _load():
             lib.oracle_f64_to_bf16.restype = ctypes.c_uint16
             lib.oracle_gather.argtypes = [P, P, i, i, i, P, i, i, P]
             lib.oracle_quantize.argtypes = [P, i, i, i, i, i, P, P]
+            lib.oracle_quantize_rows_i8.argtypes = [P, i, i, i, i, P, P]
+            lib.oracle_gemm_i8.argtypes = [P, P, P, P, i, i, i, P]
             lib.oracle_attn_decode.argtypes = [P, P, P, P, i, i, i, i, i, ctypes.c_double,
                                                P, P]
             _lib = lib
@@ -211,3 +213,28 @@ def attn_decode(q, K, V, scale: float, pos=None, cur: int = 0, window: int = 0):
                                None if pp is None else _ptr(pp), H, T, D, cur, window,
                                float(scale), _ptr(out), _ptr(absout))
     return out, absout
+
+
+def quantize_rows_i8(W, block: int = 0):
+    """Per-row symmetric int8 of the fp32 matrix W [N, K] after an optional
+    fp32 rotation (block > 0) -> (Q int8 [N, K], S fp32 [N])."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    assert block == 0 or K % block == 0
+    Q = np.empty((N, K), dtype=np.int8)
+    S = np.empty(N, dtype=np.float32)
+    _load().oracle_quantize_rows_i8(_ptr(W), N, K, K, block, _ptr(Q), _ptr(S))
+    return Q, S
+
+
+def gemm_i8(Xq, xs, Wq, ws) -> np.ndarray:
+    """(Xq Wq^T) * xs[m] * ws[n]: exact integer sums, fp64 scaling."""
+    Xq = _c(Xq, np.int8)
+    Wq = _c(Wq, np.int8)
+    xs = _c(xs, np.float32)
+    ws = _c(ws, np.float32)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    Y = np.empty((M, N))
+    _load().oracle_gemm_i8(_ptr(Xq), _ptr(xs), _ptr(Wq), _ptr(ws), M, N, K, _ptr(Y))
+    return Y

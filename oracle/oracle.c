@@ -42,6 +42,16 @@
  * get s = 0 and code 8.  The rotation and the rounding decisions are made in
  * fp32, the kernel's precision, so that both sides decide every code alike.
  *
+ * int8 twin: [P2] section "What is in the file": the FFN weights are also
+ * stored as an int8 twin (per output channel), and prefill runs on int8
+ * ("selected automatically at >= 16 rows", the auto:M switch), decode on
+ * int4.  Both operands of the pages' int8 product are int8, so the
+ * activations are quantized at run time too.  Reading taken (the rule is not
+ * given): every row (of W', and of the rotated activations x') is quantized
+ * symmetrically with its own fp32 scale s = max|v| / 127,
+ * q = clamp(round_half_even(v / s), -127, 127); the product is the exact
+ * integer sum times both scales.
+ *
  * Decode attention: [P1] paragraph on w4attn.py: one key/value head is shared
  * by eight query heads; every cached key and value is read once for all
  * eight heads and the softmax runs over the cache; paragraph on the cache:
@@ -340,4 +350,65 @@ void oracle_attn_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
         }
     }
     free(sc);
+}
+
+/*
+ * Per-row symmetric int8: each of the N rows of the fp32 matrix W (rows ldw
+ * apart) is optionally rotated (block > 0: the same fp32 butterfly FWHT per
+ * block as oracle_quantize), then a = max |v| (fp32), s = a / 127 (fp32
+ * division), q = s == 0 ? 0 : clamp(rint(v / s), -127, 127).  Q is [N][K]
+ * int8, S[N] the fp32 scales.
+ */
+void oracle_quantize_rows_i8(const float* W, int N, int K, int ldw, int block, int8_t* Q,
+                             float* S)
+{
+    float* v = (float*)malloc(sizeof(float) * (size_t)K);
+    const float norm = block ? (float)(1.0 / sqrt((double)block)) : 1.0f;
+    for (int n = 0; n < N; ++n) {
+        for (int k = 0; k < K; ++k) v[k] = W[(size_t)n * ldw + k];
+        if (block) {
+            for (int b0 = 0; b0 < K; b0 += block) {
+                float* x = v + b0;
+                for (int h = 1; h < block; h *= 2)
+                    for (int i = 0; i < block; i += 2 * h)
+                        for (int j = i; j < i + h; ++j) {
+                            const float a = x[j], b = x[j + h];
+                            x[j] = a + b;
+                            x[j + h] = a - b;
+                        }
+                for (int j = 0; j < block; ++j) x[j] = x[j] * norm;
+            }
+        }
+        float a = 0.0f;
+        for (int k = 0; k < K; ++k)
+            if (fabsf(v[k]) > a) a = fabsf(v[k]);
+        const float sc = a / 127.0f;
+        S[n] = sc;
+        for (int k = 0; k < K; ++k) {
+            float q = 0.0f;
+            if (sc != 0.0f) {
+                q = rintf(v[k] / sc);
+                if (q < -127.0f) q = -127.0f;
+                if (q > 127.0f) q = 127.0f;
+            }
+            Q[(size_t)n * K + k] = (int8_t)q;
+        }
+    }
+    free(v);
+}
+
+/*
+ * Y[m][n] = (sum_k Xq[m][k] * Wq[n][k]) * xs[m] * ws[n]: the integer sum is
+ * exact (64-bit), the scaling fp64.
+ */
+void oracle_gemm_i8(const int8_t* Xq, const float* xs, const int8_t* Wq, const float* ws,
+                    int M, int N, int K, double* Y)
+{
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            long long acc = 0;
+            for (int k = 0; k < K; ++k)
+                acc += (long long)Xq[(size_t)m * K + k] * (long long)Wq[(size_t)n * K + k];
+            Y[(size_t)m * N + n] = (double)acc * (double)xs[m] * (double)ws[n];
+        }
 }
