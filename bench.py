@@ -193,6 +193,39 @@ def time_attention(torch, w4, dev):
     return out
 
 
+def time_twin(torch, w4, synth, dev):
+    """The auto:M switch on the prefill-shaped weight (12288 x 1536, rotated
+    along K with 512-point blocks): int4 group 256 (w4a16_gemm with the
+    run-time transform) against the int8 twin (activations rotated and
+    quantized at run time, int8 matrix cores), bf16 out."""
+    import numpy as np
+    N, K = 2 * 6144, synth.HIDDEN
+    W = torch.from_numpy(synth.outlier_weights(N, K, 13)).to(dev)
+    packed4 = w4.quantize(W, 256, 512)
+    W8, ws8 = w4.quantize_rows_i8(W, 512)
+    del W
+    out = {}
+    for M in (8, 16, 64, 512):
+        X = torch.from_numpy(synth.draw_activations(np.random.default_rng(M), M, K)
+                             .view(np.int16)).to(dev).view(torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws4 = torch.empty(max(1, w4.gemm_workspace_bytes(M, K, 512)), dtype=torch.uint8,
+                          device=dev)
+        ws8b = torch.empty(max(1, int(w4.lib().w4a16_gemm_twin_workspace_bytes(M, K, 512, 1))),
+                           dtype=torch.uint8, device=dev)
+        int4_us = time_calls(torch, lambda: w4.gemm(packed4, N, K, 256, X, 512, "bf16", out=Y,
+                                                    workspace=ws4))
+        int8_us = time_calls(torch, lambda: w4.gemm_twin(packed4, W8, ws8, N, K, 256, X, 512, 1,
+                                                         "bf16", out=Y, workspace=ws8b))
+        auto_us = int8_us if M >= 16 else int4_us
+        ops = 2.0 * M * N * K
+        out["M%d" % M] = {"int4_us": int4_us, "int8_twin_us": int8_us,
+                          "auto16_picks": "int8" if M >= 16 else "int4", "auto16_us": auto_us,
+                          "int8_TOPS": ops / int8_us / 1e6,
+                          "int8_pct_of_5POPS": ops / int8_us / 1e6 / 5000 * 100}
+    return out
+
+
 def time_prefill(torch, w4, synth, dev):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
@@ -328,6 +361,7 @@ def main():
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
             "quantize_rotate": time_quantize(torch, w4, synth, dev),
+            "int8_twin_auto16": time_twin(torch, w4, synth, dev),
             "attention_decode": time_attention(torch, w4, dev),
         }
 

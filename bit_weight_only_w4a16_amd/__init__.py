@@ -44,7 +44,9 @@ EXPORTS = (
     "w4a16_gemv", "w4a16_gemm_smallM", "w4_fwht", "w4a16_gemm_workspace_bytes",
     "w4a16_gemm", "w4_decode_sweep_create", "w4_decode_sweep_launch",
     "w4_decode_sweep_check", "w4_decode_sweep_info", "w4_decode_sweep_destroy",
-    "w4_gather", "w4_quantize", "w4_attn_workspace_bytes", "w4_attn_decode",
+    "w4_gather", "w4_quantize", "w4_quantize_rows_i8", "w4_gemm_i8",
+    "w4a16_gemm_twin_workspace_bytes", "w4a16_gemm_twin", "w4_attn_workspace_bytes",
+    "w4_attn_decode",
     "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
 )
 
@@ -111,6 +113,11 @@ def lib():
             "w4_selftest": ([vp], i),
             "w4_gather": ([vp, i, i, i, vp, i, vp, i, i, vp], i),
             "w4_quantize": ([vp, i, i, i, i, i, i, vp, vp], i),
+            "w4_quantize_rows_i8": ([vp, i, i, i, i, i, vp, i, vp, vp], i),
+            "w4_gemm_i8": ([vp, i, vp, vp, i, vp, i, i, i, vp, i, i, vp], i),
+            "w4a16_gemm_twin_workspace_bytes": ([i, i, i, i], sz),
+            "w4a16_gemm_twin": ([vp, vp, i, vp, i, i, i, i, vp, i, i, i, vp, sz, vp, i, i,
+                                 vp], i),
             "w4_attn_workspace_bytes": ([i, i], sz),
             "w4_attn_decode": ([vp, vp, i, vp, vp, i, i, i, i, ctypes.c_float, vp, sz, vp, i,
                                 vp], i),
@@ -211,6 +218,51 @@ def quantize(W, group: int, had_block: int = 0, out=None, stream=None):
     wdt = W4_F32 if W.dtype == torch.float32 else (W4_BF16 if W.dtype == torch.bfloat16 else -1)
     _check(lib().w4_quantize(_ptr(W), wdt, W.stride(0), N, K, group, had_block, _ptr(out),
                              _stream(stream)))
+    return out
+
+
+def quantize_rows_i8(X, had_block: int = 0, Q=None, S=None, stream=None):
+    """Per-row symmetric int8 of X [N, K] (fp32 or bf16, device) after an
+    optional rotation -> (Q int8 [N, K], S fp32 [N])."""
+    import torch
+    N, K = X.shape
+    if Q is None:
+        Q = torch.empty((N, K), dtype=torch.int8, device=X.device)
+    if S is None:
+        S = torch.empty(N, dtype=torch.float32, device=X.device)
+    xdt = W4_F32 if X.dtype == torch.float32 else (W4_BF16 if X.dtype == torch.bfloat16 else -1)
+    _check(lib().w4_quantize_rows_i8(_ptr(X), xdt, X.stride(0), N, K, had_block, _ptr(Q),
+                                     Q.stride(0), _ptr(S), _stream(stream)))
+    return Q, S
+
+
+def gemm_i8(Xq, xs, Wq, ws, out_dtype: str = "bf16", out=None, stream=None):
+    """(Xq Wq^T) * xs[m] * ws[n] on the int8 matrix cores."""
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if out is None:
+        out = _empty_out((M, N), out_dtype, Xq.device)
+    _check(lib().w4_gemm_i8(_ptr(Xq), Xq.stride(0), _ptr(xs), _ptr(Wq), Wq.stride(0), _ptr(ws),
+                            M, N, K, _ptr(out), out.stride(0), _dt(out_dtype), _stream(stream)))
+    return out
+
+
+def gemm_twin(packed4, W8, ws8, N: int, K: int, group: int, X, had_block: int = 0,
+              switch_rows: int = 16, out_dtype: str = "bf16", out=None, workspace=None,
+              stream=None):
+    """The auto:M switch: int4 product below switch_rows rows, the int8 twin
+    (activations quantized at run time) at or above."""
+    import torch
+    M = X.shape[0]
+    if out is None:
+        out = _empty_out((M, N), out_dtype, X.device)
+    ws = int(lib().w4a16_gemm_twin_workspace_bytes(M, K, had_block, switch_rows))
+    if workspace is None and ws:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=X.device)
+    _check(lib().w4a16_gemm_twin(_ptr(packed4), _ptr(W8), W8.stride(0), _ptr(ws8), N, K, group,
+                                 M, _ptr(X), X.stride(0), had_block, switch_rows,
+                                 _ptr(workspace), ws, _ptr(out), out.stride(0), _dt(out_dtype),
+                                 _stream(stream)))
     return out
 
 

@@ -115,7 +115,7 @@ int w4_device_check(void) {
 
 const char* w4_build_info(void) {
     return "abi=1 arch=gfx950 kernels=gemv,gemv_generic,smallm,fwht,mfma_gemm,sweep_graph,"
-           "sweep_persistent,pack,gather,quantize,attn_decode,probe";
+           "sweep_persistent,pack,gather,quantize,attn_decode,int8_twin,probe";
 }
 
 size_t w4_packed_bytes(int N, int K, int group) {
@@ -285,6 +285,92 @@ int w4_quantize(const void* W, int w_dtype, int ldw, int N, int K, int group, in
         return fail(W4_ERR_ALIGN, "quantize: rows of W must start 16-byte aligned (ldw %d)", ldw);
     return launch_quantize(W, w_dtype, ldw, N, K, group, had_block, packed,
                            static_cast<hipStream_t>(stream));
+}
+
+static int check_had_block(int K, int had_block, const char* what) {
+    if (had_block != 0 && had_block != 64 && had_block != 128 && had_block != 256 &&
+        had_block != 512)
+        return fail(W4_ERR_SHAPE, "%s: had_block must be 0, 64, 128, 256 or 512 (got %d)", what,
+                    had_block);
+    if (had_block && K % had_block != 0)
+        return fail(W4_ERR_SHAPE, "%s: K %d not a multiple of had_block %d", what, K, had_block);
+    return W4_OK;
+}
+
+int w4_quantize_rows_i8(const void* X, int x_dtype, int ldx, int N, int K, int had_block,
+                        int8_t* Q, int ldq, float* S, void* stream) {
+    if (x_dtype != W4_F32 && x_dtype != W4_BF16)
+        return fail(W4_ERR_DTYPE, "int8 quantize: dtype must be W4_F32 or W4_BF16 (got %d)",
+                    x_dtype);
+    if (N < 1 || N > kMaxN) return fail(W4_ERR_SHAPE, "int8 quantize: N out of range (got %d)", N);
+    if (K < 8 || K > kMaxK || K % 8 != 0)
+        return fail(W4_ERR_SHAPE, "int8 quantize: K must be a positive multiple of 8 (got %d)", K);
+    W4_TRY(check_had_block(K, had_block, "int8 quantize"));
+    W4_TRY(check_in16(X, "X"));
+    W4_TRY(check_in16(Q, "Q"));
+    if (!S) return fail(W4_ERR_ARG, "int8 quantize: S is NULL");
+    if (!aligned(S, 4)) return fail(W4_ERR_ALIGN, "int8 quantize: S must be 4-byte aligned");
+    if (ldx < K || ldx % (x_dtype == W4_F32 ? 4 : 8) != 0)
+        return fail(W4_ERR_ALIGN, "int8 quantize: ldx must be >= K with 16-byte aligned rows");
+    if (ldq < K || ldq % 8 != 0)
+        return fail(W4_ERR_ALIGN, "int8 quantize: ldq must be >= K and a multiple of 8");
+    return launch_quantize_rows_i8(X, x_dtype, ldx, N, K, had_block, Q, ldq, S,
+                                   static_cast<hipStream_t>(stream));
+}
+
+int w4_gemm_i8(const int8_t* Xq, int ldx, const float* xs, const int8_t* Wq, int ldw,
+               const float* ws, int M, int N, int K, void* Y, int ldy, int ydt, void* stream) {
+    if (M < 1 || M > kMaxN || N < 1 || N > kMaxN)
+        return fail(W4_ERR_SHAPE, "int8 gemm: M or N out of range (%d, %d)", M, N);
+    if (K < 128 || K > kMaxK || K % 128 != 0)
+        return fail(W4_ERR_SHAPE, "int8 gemm: K must be a positive multiple of 128 (got %d)", K);
+    W4_TRY(check_dtype(ydt));
+    W4_TRY(check_in16(Xq, "Xq"));
+    W4_TRY(check_in16(Wq, "Wq"));
+    if (!xs || !ws) return fail(W4_ERR_ARG, "int8 gemm: scales NULL");
+    if (!aligned(xs, 4) || !aligned(ws, 4))
+        return fail(W4_ERR_ALIGN, "int8 gemm: scales must be 4-byte aligned");
+    if (ldx < K || ldx % 16 != 0 || ldw < K || ldw % 16 != 0)
+        return fail(W4_ERR_ALIGN, "int8 gemm: ldx and ldw must be >= K and multiples of 16");
+    W4_TRY(check_out_ptr(Y, ydt, "Y"));
+    if (ldy < N) return fail(W4_ERR_SHAPE, "int8 gemm: ldy %d < N %d", ldy, N);
+    return launch_gemm_i8(Xq, ldx, xs, Wq, ldw, ws, M, N, K, Y, ldy, ydt,
+                          static_cast<hipStream_t>(stream));
+}
+
+size_t w4a16_gemm_twin_workspace_bytes(int M, int K, int had_block, int switch_rows) {
+    if (M < 1 || K < 1) return 0;
+    if (M < switch_rows) return w4a16_gemm_workspace_bytes(M, K, had_block);
+    return align_up((size_t)M * (size_t)K, kAlign) + (size_t)M * sizeof(float);
+}
+
+int w4a16_gemm_twin(const void* packed4, const int8_t* W8, int ldw8, const float* ws8, int N,
+                    int K, int group, int M, const uint16_t* X, int ldx, int had_block,
+                    int switch_rows, void* workspace, size_t ws_bytes, void* Y, int ldy, int ydt,
+                    void* stream) {
+    if (switch_rows < 1) return fail(W4_ERR_ARG, "twin: switch_rows must be >= 1");
+    if (M < switch_rows)
+        return w4a16_gemm(packed4, N, K, group, M, X, ldx, had_block, workspace, ws_bytes, Y, ldy,
+                          ydt, stream);
+    W4_TRY(check_weight_shape(N, K, group));
+    W4_TRY(check_had_block(K, had_block, "twin"));
+    if (K % 128 != 0) return fail(W4_ERR_SHAPE, "twin: K must be a multiple of 128 (got %d)", K);
+    const size_t need = w4a16_gemm_twin_workspace_bytes(M, K, had_block, switch_rows);
+    W4_TRY(check_in16(workspace, "workspace"));
+    if (ws_bytes < need)
+        return fail(W4_ERR_SHAPE, "twin: workspace %zu bytes < %zu", ws_bytes, need);
+    if (!W8 || !ws8) return fail(W4_ERR_ARG, "twin: int8 twin NULL");
+    int8_t* Xq = static_cast<int8_t*>(workspace);
+    float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                         align_up((size_t)M * (size_t)K, kAlign));
+    // validate the product's arguments before the first launch
+    if (ldw8 < K || ldw8 % 16 != 0 || !aligned(W8, 16) || !aligned(ws8, 4))
+        return fail(W4_ERR_ALIGN, "twin: W8 rows must be 16-byte aligned (ldw8 >= K, %% 16)");
+    W4_TRY(check_dtype(ydt));
+    W4_TRY(check_out_ptr(Y, ydt, "Y"));
+    if (ldy < N) return fail(W4_ERR_SHAPE, "twin: ldy %d < N %d", ldy, N);
+    W4_TRY(w4_quantize_rows_i8(X, W4_BF16, ldx, M, K, had_block, Xq, K, xs, stream));
+    return w4_gemm_i8(Xq, K, xs, W8, ldw8, ws8, M, N, K, Y, ldy, ydt, stream);
 }
 
 static int check_attn_shape(int T, int D) {

@@ -53,6 +53,13 @@ int launch_attn_pack_v(const uint16_t* V, int ldv, int T, int D, uint16_t* Vt, h
 int launch_attn_store_kv(const uint16_t* k, const uint16_t* v, int slot, uint16_t* K, int ldk,
                          uint16_t* Vt, int D, hipStream_t s);
 
+int launch_quantize_rows_i8(const void* W, int wdt, int ldw, int N, int K, int block, int8_t* Q,
+                            int ldq, float* S, hipStream_t s);
+int launch_gemm_i8(const int8_t* X, int ldx, const float* xs, const int8_t* W, int ldw,
+                   const float* ws, int M, int N, int K, void* Y, int ldy, int ydt,
+                   hipStream_t s);
+void describe_i8(int M, int N, int K, char* buf, size_t len);
+
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* out,
                       hipStream_t s);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

@@ -1,0 +1,358 @@
+// w4_int8.hip -- the int8 twin: per-row int8 quantization and the int8 GEMM.
+//
+// [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI",
+// section "What is in the file": every FFN weight is also stored as an int8
+// twin (twice the int4 bytes), and prefill runs on int8, selected
+// automatically at 16 rows or more (FGM_WEIGHTS=auto:16), decode on int4.
+// Both operands of that product are int8; on MI355X the int8 matrix cores
+// (v_mfma_i32_16x16x64_i8) run at twice the bf16 rate, which is the same
+// reason to keep the twin.  Quantization rule (not on the page; the reading
+// taken): each row -- of the rotated weight W', and at run time of the
+// rotated activations x' -- gets its own fp32 scale s = max|v| / 127 and
+// codes q = clamp(round_half_even(v / s), -127, 127); the product is the exact
+// integer sum times both scales.
+#include <cstdio>
+#include <cstdlib>
+
+#include "w4_dispatch.h"
+
+namespace w4 {
+
+namespace {
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 mma_i8(u32x4 a, u32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
+                                                 __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+}  // namespace
+
+// One workgroup (4 waves) per row; wave w takes the row's 512-element spans
+// w, w + 4, ... (lane l holds elements 8l .. 8l+7 of a span).  The spans are
+// rotated once (the butterfly FWHT of w4_quantize: spans 1, 2, 4 inside a
+// lane, 8 .. block/2 across lanes, then one fp32 scaling) and kept in
+// registers for rows of up to 4 * kQMaxSpans spans (recomputed, identically,
+// beyond); max |v| is reduced across the lanes and, through LDS, across the
+// waves; then the codes are written.
+constexpr int kQMaxSpans = 4;
+
+template <bool BF16IN>
+__global__ __launch_bounds__(256) void quant_rows_i8_kernel(const void* __restrict__ W, int ldw,
+                                                           int N, int K, int block, float hscale,
+                                                           int8_t* __restrict__ Q, int ldq,
+                                                           float* __restrict__ S) {
+    __shared__ float wmax[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int row = blockIdx.x;
+    const int spans = (K + 511) / 512;
+
+    auto span_vals = [&](int sp, float (&v)[8]) {
+        const int k0 = sp * 512 + 8 * lane;
+        if (k0 < K) {
+            if (BF16IN) {
+                const u32x4 w = gload(reinterpret_cast<const u32x4*>(
+                    static_cast<const uint16_t*>(W) + (size_t)row * ldw + k0));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = __uint_as_float(w[i] << 16);
+                    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                }
+            } else {
+                const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(W) +
+                                                                (size_t)row * ldw + k0);
+                const u32x4 a = gload(p), b = gload(p + 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = __uint_as_float(a[i]);
+                    v[4 + i] = __uint_as_float(b[i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+        if (block) {
+#pragma unroll
+            for (int h = 1; h < 8; h *= 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if ((e & h) == 0) {
+                        const float a = v[e], c = v[e + h];
+                        v[e] = a + c;
+                        v[e + h] = a - c;
+                    }
+                }
+            }
+            for (int d = 1; d < block / 8; d *= 2) {
+                const bool upper = (lane & d) != 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float o = __shfl_xor(v[e], d, 64);
+                    v[e] = upper ? (o - v[e]) : (v[e] + o);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * hscale;
+        }
+    };
+
+    float cache[kQMaxSpans][8];
+    float amax = 0.f;
+    for (int i = 0, sp = wave; sp < spans; ++i, sp += 4) {
+        float v[8];
+        span_vals(sp, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+        for (int c = 0; c < kQMaxSpans; ++c)
+            if (c == i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cache[c][e] = v[e];
+    }
+    for (int d = 1; d < 64; d *= 2) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    const float rmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float sc = rmax / 127.f;
+    if (threadIdx.x == 0) gstore(S + row, sc);
+
+    for (int i = 0, sp = wave; sp < spans; ++i, sp += 4) {
+        float v[8];
+        if (i < kQMaxSpans) {
+#pragma unroll
+            for (int c = 0; c < kQMaxSpans; ++c)
+                if (c == i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = cache[c][e];
+        } else {
+            span_vals(sp, v);
+        }
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float q = 0.f;
+            if (sc != 0.f) q = fminf(fmaxf(__builtin_rintf(v[e] / sc), -127.f), 127.f);
+            const uint32_t b = (uint32_t)(int)q & 0xFFu;
+            if (e < 4)
+                w0 |= b << (8 * e);
+            else
+                w1 |= b << (8 * (e - 4));
+        }
+        const int k0 = sp * 512 + 8 * lane;
+        if (k0 < K) {
+            uint32_t* dst = reinterpret_cast<uint32_t*>(Q + (size_t)row * ldq + k0);
+            gstore(dst, w0);
+            gstore(dst + 1, w1);
+        }
+    }
+}
+
+int launch_quantize_rows_i8(const void* W, int wdt, int ldw, int N, int K, int block, int8_t* Q,
+                            int ldq, float* S, hipStream_t s) {
+    const float hscale = block ? (float)(1.0 / __builtin_sqrt((double)block)) : 1.f;
+    const dim3 g((unsigned)N), b(256);
+    if (wdt == W4_BF16)
+        quant_rows_i8_kernel<true><<<g, b, 0, s>>>(W, ldw, N, K, block, hscale, Q, ldq, S);
+    else
+        quant_rows_i8_kernel<false><<<g, b, 0, s>>>(W, ldw, N, K, block, hscale, Q, ldq, S);
+    return hip_fail(hipGetLastError(), "int8 quantize launch");
+}
+
+// ---------------------------------------------------------------- GEMM ---
+//
+// Y[m][n] = (sum_k Xq[m][k] Wq[n][k]) * xs[m] * ws[n], on v_mfma_i32_16x16x64_i8
+// (A 16x64, B 64x16, D 16x16; lane l holds A[l%16][16(l/16) + j] and
+// B[16(l/16) + j][l%16] for j = 0..15, and D[4(l/16) + r][l%16] for r = 0..3,
+// checked on the hardware).  B is W^T, so a lane's B bytes are 16 consecutive
+// codes of weight row n = l%16, like its A bytes of activation row l%16.
+// A 256-thread workgroup (2 x 2 waves) computes a BM x BN block; K advances in
+// 128-wide stages copied into padded LDS rows, the next stage's tiles in
+// flight in registers while the current one is multiplied (one barrier per
+// stage).  Blocks are numbered so that all M blocks of an N block run on one
+// XCD, which then reads those weight rows once.
+constexpr int kI8StageK = 128;
+constexpr int kI8Row = kI8StageK + 16;  // LDS bytes per row (padded)
+
+struct I8Args {
+    const int8_t* X;
+    const float* xs;
+    const int8_t* W;
+    const float* ws;
+    void* Y;
+    int M, N, K, ldx, ldw, ldy, ydt, m_blocks, n_blocks;
+};
+
+template <int MF, int NF>
+__global__ __launch_bounds__(256) void gemm_i8_kernel(I8Args a) {
+    constexpr int WN = 2;
+    constexpr int BM = 2 * MF * 16, BN = WN * NF * 16;
+    constexpr int CPR = kI8StageK / 16;  // 16-byte chunks per row and stage
+    constexpr int A_CHUNKS = BM * CPR / 256, B_CHUNKS = BN * CPR / 256;
+    static_assert(A_CHUNKS * 256 == BM * CPR && B_CHUNKS * 256 == BN * CPR, "tile split");
+    __shared__ __align__(16) int8_t As[2][BM * kI8Row];
+    __shared__ __align__(16) int8_t Bs[2][BN * kI8Row];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lk = lane >> 4;
+    const int wm = wave / WN, wn = wave % WN;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int mb = j % a.m_blocks;
+    const int nb = (j / a.m_blocks) * 8 + xcd;
+    if (nb >= a.n_blocks) return;
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int stages = a.K / kI8StageK;
+
+    // this thread's share of each stage's tiles (rows past M / N clamped to
+    // valid memory and never stored)
+    const int8_t* asrc[A_CHUNKS];
+    int aoff[A_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < A_CHUNKS; ++c) {
+        const int idx = tid + 256 * c, r = idx / CPR, q = idx % CPR;
+        const int m = m0 + r < a.M ? m0 + r : a.M - 1;
+        asrc[c] = a.X + (size_t)m * a.ldx + 16 * q;
+        aoff[c] = r * kI8Row + 16 * q;
+    }
+    const int8_t* bsrc[B_CHUNKS];
+    int boff[B_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < B_CHUNKS; ++c) {
+        const int idx = tid + 256 * c, r = idx / CPR, q = idx % CPR;
+        const int n = n0 + r < a.N ? n0 + r : a.N - 1;
+        bsrc[c] = a.W + (size_t)n * a.ldw + 16 * q;
+        boff[c] = r * kI8Row + 16 * q;
+    }
+    u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
+    auto fetch = [&](int st) {
+#pragma unroll
+        for (int c = 0; c < A_CHUNKS; ++c)
+            ra[c] = gload(reinterpret_cast<const u32x4*>(asrc[c] + (size_t)st * kI8StageK));
+#pragma unroll
+        for (int c = 0; c < B_CHUNKS; ++c)
+            rb[c] = nt_load(reinterpret_cast<const u32x4*>(bsrc[c] + (size_t)st * kI8StageK));
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < A_CHUNKS; ++c) *reinterpret_cast<u32x4*>(&As[buf][aoff[c]]) = ra[c];
+#pragma unroll
+        for (int c = 0; c < B_CHUNKS; ++c) *reinterpret_cast<u32x4*>(&Bs[buf][boff[c]]) = rb[c];
+    };
+
+    i32x4 acc[MF][NF];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) acc[mf][nf] = i32x4{0, 0, 0, 0};
+
+    const int arow0 = (wm * MF * 16 + li) * kI8Row + 16 * lk;
+    const int brow0 = (wn * NF * 16 + li) * kI8Row + 16 * lk;
+    fetch(0);
+    put(0);
+    __syncthreads();
+    for (int st = 0; st < stages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < stages) fetch(st + 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            u32x4 xa[MF], wb[NF];
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+                xa[mf] = *reinterpret_cast<const u32x4*>(&As[buf][arow0 + mf * 16 * kI8Row + 64 * t]);
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+                wb[nf] = *reinterpret_cast<const u32x4*>(&Bs[buf][brow0 + nf * 16 * kI8Row + 64 * t]);
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) acc[mf][nf] = mma_i8(xa[mf], wb[nf], acc[mf][nf]);
+        }
+        if (st + 1 < stages) {
+            // buffer buf ^ 1 was last read in stage st - 1, which every wave
+            // finished before the previous barrier
+            put(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) {
+        const int n = n0 + wn * NF * 16 + 16 * nf + li;
+        const float wsn = gload(a.ws + (n < a.N ? n : a.N - 1));
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * MF * 16 + 16 * mf + 4 * lk + r;
+                if (m < a.M && n < a.N) {
+                    const float y = ((float)acc[mf][nf][r] * gload(a.xs + m)) * wsn;
+                    store_out(a.Y, (size_t)m * a.ldy + n, y, a.ydt);
+                }
+            }
+    }
+}
+
+struct I8Plan {
+    int MF, NF, BM, BN, m_blocks, n_blocks, grid;
+};
+
+static I8Plan plan_i8(int M, int N) {
+    I8Plan p;
+    // measured on MI355X at N = 12288, K = 1536, M = 64..512: 64 x 64 blocks
+    // (four workgroups per CU) beat 64 x 128, 128 x 64 and 128 x 128 at every M
+    (void)M;
+    p.MF = 2;
+    p.NF = 2;
+    const char* e = getenv("W4_I8_TILE");  // tuning override "MF,NF" (2 or 4 each)
+    int mf = 0, nf = 0;
+    if (e && sscanf(e, "%d,%d", &mf, &nf) == 2 && (mf == 2 || mf == 4) && (nf == 2 || nf == 4)) {
+        p.MF = mf;
+        p.NF = nf;
+    }
+    p.BM = 2 * p.MF * 16;
+    p.BN = 2 * p.NF * 16;
+    p.m_blocks = (M + p.BM - 1) / p.BM;
+    p.n_blocks = (N + p.BN - 1) / p.BN;
+    p.grid = 8 * p.m_blocks * ((p.n_blocks + 7) / 8);
+    return p;
+}
+
+int launch_gemm_i8(const int8_t* X, int ldx, const float* xs, const int8_t* W, int ldw,
+                   const float* ws, int M, int N, int K, void* Y, int ldy, int ydt,
+                   hipStream_t s) {
+    const I8Plan p = plan_i8(M, N);
+    I8Args a;
+    a.X = X;
+    a.xs = xs;
+    a.W = W;
+    a.ws = ws;
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.ldx = ldx;
+    a.ldw = ldw;
+    a.ldy = ldy;
+    a.ydt = ydt;
+    a.m_blocks = p.m_blocks;
+    a.n_blocks = p.n_blocks;
+    if (p.MF == 2 && p.NF == 2)
+        gemm_i8_kernel<2, 2><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    else if (p.MF == 2)
+        gemm_i8_kernel<2, 4><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    else if (p.NF == 2)
+        gemm_i8_kernel<4, 2><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    else
+        gemm_i8_kernel<4, 4><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    return hip_fail(hipGetLastError(), "int8 gemm launch");
+}
+
+void describe_i8(int M, int N, int K, char* buf, size_t len) {
+    const I8Plan p = plan_i8(M, N);
+    snprintf(buf, len, "int8 mfma 16x16x64 block %dx%d waves 2x2 stage 128 grid=%d (K=%d)", p.BM,
+             p.BN, p.grid, K);
+}
+
+}  // namespace w4

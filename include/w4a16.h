@@ -254,6 +254,45 @@ int w4_quantize(const void* W, int w_dtype, int ldw, int N, int K, int group,
                 int had_block, void* packed, void* stream);
 
 /*
+ * The int8 twin ([P2] section "What is in the file": the FFN weights are
+ * also kept as int8, twice the int4 bytes; prefill runs on int8, selected
+ * automatically at 16 rows or more -- FGM_WEIGHTS=auto:16 -- decode on
+ * int4).  Both operands of the int8 product are int8: weights per output
+ * channel, activations per row at run time.  Rule (the page gives none):
+ * after an optional rotation (had_block, as w4_quantize), each row gets an
+ * fp32 scale s = max|v| / 127 and codes q = clamp(round_half_even(v / s),
+ * -127, 127), all in fp32.
+ *
+ * w4_quantize_rows_i8: N rows of X (fp32 or bf16, ldx >= K, 16-byte aligned
+ *   rows) -> Q int8 [N][ldq] (ldq >= K, ldq % 8 == 0, Q 16-byte aligned;
+ *   ldq % 16 == 0 for rows w4_gemm_i8 reads) and S fp32 [N].  K % 8 == 0.
+ *   Used offline for the weight twin and at run time for activations.
+ * w4_gemm_i8: Y[m][n] = (sum_k Xq[m][k] Wq[n][k]) * xs[m] * ws[n] on the int8
+ *   matrix cores (exact int32 sums; the int32 -> fp32 conversion and the two
+ *   scale multiplications round in fp32).  K % 128 == 0; Xq, Wq rows 16-byte
+ *   aligned (ldx, ldw >= K and % 16); Y fp32 or bf16 (nearest even), ldy >= N.
+ * w4a16_gemm_twin: the auto:M switch.  M < switch_rows (the page: 16): the
+ *   int4 product w4a16_gemm on packed4; otherwise the activations are
+ *   rotated and quantized into the workspace and multiplied by the int8
+ *   twin (W8 [N][ldw8], ws8 [N], quantized from the same weights with the
+ *   same had_block).  workspace >= w4a16_gemm_twin_workspace_bytes(M, K,
+ *   had_block, switch_rows), 16-byte aligned.
+ */
+int w4_quantize_rows_i8(const void* X, int x_dtype, int ldx, int N, int K,
+                        int had_block, int8_t* Q, int ldq, float* S,
+                        void* stream);
+int w4_gemm_i8(const int8_t* Xq, int ldx, const float* xs, const int8_t* Wq,
+               int ldw, const float* ws, int M, int N, int K, void* Y,
+               int ldy, int ydt, void* stream);
+size_t w4a16_gemm_twin_workspace_bytes(int M, int K, int had_block,
+                                       int switch_rows);
+int w4a16_gemm_twin(const void* packed4, const int8_t* W8, int ldw8,
+                    const float* ws8, int N, int K, int group, int M,
+                    const uint16_t* X, int ldx, int had_block, int switch_rows,
+                    void* workspace, size_t ws_bytes, void* Y, int ldy,
+                    int ydt, void* stream);
+
+/*
  * Split-K decode attention: one key/value head shared by 8 query heads.
  * [P1] paragraph on w4attn.py: each cached key and value is read once for
  * all eight query heads, the cache is split into slices and the slices are

@@ -155,6 +155,31 @@ def test_attention_validation(L):
     assert L.w4_attn_store_kv(A16, A16, 3, A16, 100, A16, 512, VP(0)) == -2
 
 
+def test_int8_validation(L):
+    q = L.w4_quantize_rows_i8
+    assert q(A16, 2, 512, 4, 512, 0, A16, 512, A16, VP(0)) == -4      # dtype
+    assert q(A16, 0, 512, 4, 100, 0, A16, 512, A16, VP(0)) == -2      # K % 8
+    assert q(A16, 0, 512, 4, 512, 384, A16, 512, A16, VP(0)) == -2    # had_block
+    assert q(A16, 0, 512, 4, 512, 0, A16, 516, A16, VP(0)) == -3      # ldq % 8
+    assert q(A16, 0, 512, 4, 512, 0, A16, 512, VP(0), VP(0)) == -1    # S NULL
+    assert q(A2, 0, 512, 4, 512, 0, A16, 512, A16, VP(0)) == -3       # X alignment
+    g = L.w4_gemm_i8
+    assert g(A16, 512, A16, A16, 512, A16, 4, 64, 500, A16, 64, 1, VP(0)) == -2   # K % 128
+    assert g(A16, 520, A16, A16, 512, A16, 4, 64, 512, A16, 64, 1, VP(0)) == -3   # ldx % 16
+    assert g(A16, 512, VP(0), A16, 512, A16, 4, 64, 512, A16, 64, 1, VP(0)) == -1  # xs NULL
+    assert g(A16, 512, A16, A16, 512, A16, 4, 64, 512, A16, 60, 1, VP(0)) == -2   # ldy < N
+    assert g(A16, 512, A16, A16, 512, A16, 0, 64, 512, A16, 64, 1, VP(0)) == -2   # M = 0
+    t = L.w4a16_gemm_twin
+    assert L.w4a16_gemm_twin_workspace_bytes(64, 1536, 512, 16) == 64 * 1536 + 64 * 4
+    assert L.w4a16_gemm_twin_workspace_bytes(8, 1536, 512, 16) == 8 * 1536 * 2
+    assert t(A16, A16, 1536, A16, 64, 1536, 256, 64, A16, 1536, 512, 0, A16, 1 << 20, A16, 64,
+             1, VP(0)) == -1                                            # switch_rows
+    assert t(A16, A16, 1536, A16, 64, 1536, 256, 64, A16, 1536, 512, 16, A16, 100, A16, 64,
+             1, VP(0)) == -2                                            # workspace
+    assert t(A16, VP(0), 1536, A16, 64, 1536, 256, 64, A16, 1536, 512, 16, A16, 1 << 20, A16,
+             64, 1, VP(0)) == -1                                        # twin NULL
+
+
 def test_fwht_validation(L):
     f = L.w4_fwht
     assert f(A16, 1536, A16, 1536, 4, 1536, 384, VP(0)) == -2    # not a power of 2
