@@ -154,6 +154,23 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// Sum over each 16-lane row; every lane of the row ends with the row's total
+// (the same fixed order as group_sum<16>).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0x128>(v);  // row_ror:8
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+    return v;
+}
+
+// DPP row broadcast (row_bcast:15 = 0x142, row_bcast:31 = 0x143) into the
+// rows of ROWMASK; the other rows get 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_row_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false));
+}
+
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
     static_assert(L == 8 || L == 16 || L == 32 || L == 64, "group size");

@@ -60,10 +60,14 @@ __device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
 // current one is decoded.  Lane partials are summed in a fixed order, so the
 // result is bitwise deterministic.
 // BATCH (consecutive row groups, step == 1): outputs are gathered into one
-// register, lane i holding row b + i of the current 64-row block b, and the
-// block is written with one store when the walk leaves it (128 or 256
-// contiguous bytes instead of a few bytes per row group: small scattered
-// writes in a stream of reads cost HBM read bandwidth).
+// register and each 64-row block is written with one store when the walk
+// leaves it (128 or 256 contiguous bytes instead of a few bytes per row
+// group: small scattered writes in a stream of reads cost HBM read
+// bandwidth).  Lane l holds row R * (l % L) + l / L of the block, i.e. row r
+// of the block's row group t sits in lane L r + t: after the 16-lane DPP row
+// sums every lane of a 16-lane row already holds its row's total, so a row
+// group's outputs are taken with one compare and no cross-lane move (32- and
+// 64-lane rows finish with DPP row broadcasts and one readlane per row).
 template <int L, int U, bool FULLC, int STAGES = 2, bool BATCH = false>
 __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, int step,
                                           int lane, const DecodeConsts& k) {
@@ -93,11 +97,12 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
     const uint32_t* swords = reinterpret_cast<const uint32_t*>(a.scales);
     const int Gw = a.G >> 1;
 
-    float outv = 0.f;           // BATCH: lane i = row ob + i
-    int ob = -1, olo = 0, ohi = 0;  // block base row, lanes written so far
+    float outv = 0.f;               // BATCH: lane l = row ob + R (l % L) + l / L
+    int ob = -1, olo = 0, ohi = 0;  // block base row, row groups written so far
     auto flush = [&]() {
-        const int n = ob + lane;
-        if (ob >= 0 && lane >= olo && lane < ohi && n < a.N) store_out(a.y, (size_t)n, outv, a.ydt);
+        const int t = lane % L;
+        const int n = ob + R * t + lane / L;
+        if (ob >= 0 && t >= olo && t < ohi && n < a.N) store_out(a.y, (size_t)n, outv, a.ydt);
     };
 
     auto load = [&](int g, u32x4 (&q)[U], uint32_t (&sc)[U]) {
@@ -116,21 +121,33 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
 #pragma unroll
         for (int u = 0; u < U; ++u)
             acc = fmaf(scale_from_word(sc[u], ssel[u]), chunk_dot(q[u], xr[u], k) + xb[u], acc);
-        acc = group_sum<L>(acc);
         if (BATCH) {
+            acc = row16_sum(acc);
             const int row0 = g * R;
             const int blk = row0 & ~63;
+            const int ti = (row0 - blk) / R;  // row group within the block
             if (blk != ob) {
                 flush();
                 ob = blk;
-                olo = row0 - blk;
+                olo = ti;
             }
-            const int slot = row0 - blk;
-            const int r = lane - slot;  // row of this tile held by this lane
-            const float v = R == 1 ? acc : __shfl(acc, (r & (R - 1)) * L, 64);
-            if (r >= 0 && r < R) outv = v;
-            ohi = slot + R;
+            if (L == 16) {
+                if ((lane & 15) == ti) outv = acc;
+            } else if (L == 32) {
+                acc += dpp_row_bcast<0x142, 0xA>(acc);  // rows 1, 3 += lanes 15, 47
+                const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 31));
+                const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 63));
+                if (lane == ti) outv = s0;
+                if (lane == 32 + ti) outv = s1;
+            } else {
+                acc += dpp_row_bcast<0x142, 0xA>(acc);  // rows 1, 3 += lanes 15, 47
+                acc += dpp_row_bcast<0x143, 0xC>(acc);  // rows 2, 3 += lane 31
+                const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), 63));
+                if (lane == ti) outv = s;
+            }
+            ohi = ti + 1;
         } else {
+            acc = group_sum<L>(acc);
             const int n = g * R + lr;
             if (lk == 0 && n < a.N) store_out(a.y, (size_t)n, acc, a.ydt);
         }
