@@ -39,6 +39,12 @@ int launch_mfma_gemm(const void* packed, int N, int K, int group, int M,
                      hipStream_t s);
 void describe_mfma(int M, int N, int K, int group, char* buf, size_t len);
 
+// DMA-ring prefill kernel (w4_prefill.hip): groups that are multiples of 64
+bool prefill_supported(int M, int N, int K, int group, int ldx);
+int launch_prefill(const void* packed, int N, int K, int group, int M, const uint16_t* X,
+                   int ldx, void* Y, int ldy, int ydt, hipStream_t s);
+void describe_prefill(int M, int N, int K, int group, char* buf, size_t len);
+
 int launch_gather(const void* packed, int N, int K, int group, const int32_t* ids, int B,
                   void* Y, int ldy, int ydt, hipStream_t s);
 

@@ -280,8 +280,17 @@ static void launch_cfg(bool super, dim3 g, hipStream_t s, const MfmaArgs& a) {
         mfma_gemm_kernel<WM, WN, MF, NF, false><<<g, dim3(256), 0, s>>>(a);
 }
 
+// W4_PREFILL=0 keeps every shape on the register-staged kernel below (A/B
+// comparisons); otherwise groups that are multiples of 64 take the DMA ring.
+static bool use_ring(int M, int N, int K, int group, int ldx) {
+    const char* e = getenv("W4_PREFILL");
+    if (e && e[0] == '0' && e[1] == 0) return false;
+    return prefill_supported(M, N, K, group, ldx);
+}
+
 int launch_mfma_gemm(const void* packed, int N, int K, int group, int M, const uint16_t* X,
                      int ldx, void* Y, int ldy, int ydt, hipStream_t s) {
+    if (use_ring(M, N, K, group, ldx)) return launch_prefill(packed, N, K, group, M, X, ldx, Y, ldy, ydt, s);
     const MfmaPlan p = plan_mfma(M, N);
     MfmaArgs a;
     a.codes = static_cast<const uint32_t*>(packed);
@@ -310,6 +319,7 @@ int launch_mfma_gemm(const void* packed, int N, int K, int group, int M, const u
 }
 
 void describe_mfma(int M, int N, int K, int group, char* buf, size_t len) {
+    if (use_ring(M, N, K, group, K)) return describe_prefill(M, N, K, group, buf, len);
     const MfmaPlan p = plan_mfma(M, N);
     snprintf(buf, len, "mfma 16x16x32 block %dx%d waves 2x2 %s grid=%d (K=%d g=%d)", p.BM, p.BN,
              group % kStageK == 0 ? "stage 128 permuted" : "stage 128 by group", p.grid, K, group);

@@ -1,0 +1,452 @@
+// w4_prefill.hip -- prefill-shaped W4A16 GEMM on the matrix cores, fed by an
+// LDS ring that the global-to-LDS DMA loads fill several stages ahead.
+//
+// [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI":
+// section "Why AMX for GEMM but not for attention" -- a weight GEMM reuses each
+// weight byte across all M activation rows, so at prefill row counts the
+// multiply units bound it; section "What is in the file" -- int4 weights in
+// groups of 256 (or 512), rotated along K.  Same product as w4_mfma.hip:
+// Y[m][n] = sum_g s[n][g] * sum_{k in g} (c[n][k] - 8) * x[m][k], fp32
+// accumulation, no dequantized matrix in memory.
+//
+// Arithmetic (v_mfma_f32_16x16x32_bf16; lane l holds A[l%16][8(l/16) + j],
+// B[8(l/16) + j][l%16], D[4(l/16) + r][l%16]):
+//   - a lane's eight B values are one device word of weight row l%16, decoded
+//     with one shift and one and-or per pair to exact bf16 integers 128 + c;
+//   - per K-group the products accumulate from zero; the group adds
+//     s * (acc - acc136) to the total, acc136 being the same MFMA against the
+//     bf16 constant 136, so a column of code-8 weights cancels exactly;
+//   - within a 64-wide K stage, lane group l/16 takes device words
+//     2(l/16), 2(l/16)+1 of its row, word t in MFMA step t, and the activation
+//     fragment is read with the same K permutation (a dot product allows it).
+//
+// Work split: a 256-thread workgroup is four waves side by side along N.  All
+// four share one 16*MF-row activation tile; each wave owns 16*NF weight rows
+// and computes a (16 MF) x (16 NF) block of Y, so a decoded word feeds MF
+// MFMAs.  Workgroups are numbered so that every M block of an N block runs on
+// one XCD (workgroups go round-robin to the 8 XCDs): the weights are read from
+// HBM once per XCD and the activations stay in that XCD's L2.
+//
+// Memory pipeline: SLOTS ring slots of one 64-wide K stage each.  Every wave
+// issues its share of a stage as DMA loads straight into LDS (16-byte loads
+// for activations, 4-byte loads for codes), SLOTS - 1 stages ahead of the one
+// it multiplies; one explicit vmcnt wait plus one barrier per stage make a
+// stage visible, and the barrier also proves the slot being refilled was
+// released by every wave.  The compiler does not track these loads, so every
+// wait on them is written out here; no other global load runs in the loop.
+// The scales of the workgroup's rows are copied to LDS once, up front.
+//
+// LDS layouts (XOR swizzles keep every LDS read free of bank conflicts, for
+// 32- and 64-bank LDS alike; the DMA writes each instruction's 64 lanes to
+// consecutive addresses, so the swizzle is applied to the global side):
+//   activation row r: 128 bytes, 8 chunks of 8 bf16; position p holds chunk
+//     p ^ g(r), g(r) = (r & 7) ^ ((r >> 3) & 1);
+//   code row i: 32 bytes, 4 units of 2 words; position P holds unit
+//     P ^ h(i), h(i) = ((i & 15) >> 2) & 3.
+#include <cstdio>
+#include <cstdlib>
+#include <type_traits>
+#include <utility>
+
+#include "w4_dispatch.h"
+
+// the DMA asm below clobbers M0, which the compiler reserves; no other M0 use
+// lives across it in this file
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace w4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int kStage = 64;     // K per ring slot
+constexpr int kARow = 128;     // bytes of an activation row in a slot
+constexpr int kBRow = 32;      // bytes of a code row in a slot
+constexpr int kMaxG = 8;       // scale groups per row kept in LDS
+
+struct PfArgs {
+    const uint32_t* codes;   // N x K/8 device words
+    const uint16_t* scales;  // N x G bf16
+    const uint16_t* X;       // M x K bf16, row stride ldx
+    void* Y;                 // M x N, row stride ldy
+    int M, N, K, G, group, ldx, ldy, ydt;
+    int m_blocks, n_blocks;
+    int vec_out;             // Y and its row stride allow 16-byte stores
+};
+
+template <int MF, int NF, int SLOTS>
+struct PfShape {
+    static constexpr int BM = 16 * MF;                 // activation rows per workgroup
+    static constexpr int WN = 16 * NF;                 // weight rows per wave
+    static constexpr int BN = 4 * WN;                  // weight rows per workgroup
+    static constexpr int A_BYTES = BM * kARow;
+    static constexpr int B_BYTES = BN * kBRow;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int A_DMA = A_BYTES / 1024 / 4;   // 16-byte DMA per wave per stage
+    static constexpr int B_DMA = WN * kBRow / 256;     // 4-byte DMA per wave per stage
+    static constexpr int LOADS = A_DMA + B_DMA;        // vector-memory ops per wave per stage
+    static_assert(A_DMA * 4 * 1024 == A_BYTES, "activation tile: whole DMA rounds per wave");
+    static_assert(B_DMA * 256 == WN * kBRow, "code tile: whole DMA rounds per wave");
+    static_assert(LOADS * (SLOTS - 2) < 64, "vmcnt range");
+    static constexpr int OUT_ROW = BN * 4 + 16;        // padded fp32 staging row (bytes)
+    static_assert(BM * OUT_ROW <= SLOTS * SLOT, "output staging fits in the ring");
+    static_assert(MF == 4, "one offset chain per wave: four M fragments for four waves");
+};
+
+// s_waitcnt with vmcnt = N and the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most LOADS * min(pending, P) of this wave's DMA ops are in
+// flight (pending is wave-uniform; the branches are scalar).
+template <int LOADS, int P>
+__device__ __forceinline__ void wait_stage(int pending) {
+    if constexpr (P == 0) {
+        wait_vm<0>();
+    } else {
+        if (pending >= P)
+            wait_vm<LOADS * P>();
+        else
+            wait_stage<LOADS, P - 1>(pending);
+    }
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations;
+// it does not wait for outstanding loads (the explicit waits do that).
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One DMA load: each lane's 16 (or 4) bytes at base + off land in LDS at
+// lds + 16 * lane (or 4 * lane); lds is wave-uniform.  Written as inline asm so
+// that the compiler, which would otherwise wait for every such load before any
+// LDS read that may alias it, leaves all waits on them to the explicit ones.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(uint32_t off, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t off, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
+
+template <int MF, int NF, int SLOTS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(PfArgs a) {
+    using S = PfShape<MF, NF, SLOTS>;
+    __shared__ __align__(16) uint8_t ring[SLOTS * S::SLOT];
+    __shared__ __align__(16) uint16_t sc[S::BN * kMaxG];
+    __shared__ __align__(16) f32x4 xch[4][64];   // offset chains, one per wave
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lk = lane >> 4;
+
+    // XCD x = blockIdx % 8 runs every M block of N blocks x, x + 8, ...
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int mb = j % a.m_blocks;
+    const int nb = (j / a.m_blocks) * 8 + xcd;
+    if (nb >= a.n_blocks) return;
+    const int m0 = mb * S::BM, n0 = nb * S::BN;
+    const int nw0 = n0 + wave * S::WN;
+    const int KW = a.K / 8;
+    const int stages = a.K / kStage;
+
+    // DMA sources: a wave-uniform base that advances one stage per slot plus a
+    // fixed 32-bit per-lane byte offset (the host keeps every offset below
+    // 2^32); destinations: fixed per wave, plus the slot
+    uint32_t aoffs[S::A_DMA];
+#pragma unroll
+    for (int d = 0; d < S::A_DMA; ++d) {
+        const int r = 8 * (wave * S::A_DMA + d) + (lane >> 3);
+        const int q = (lane & 7) ^ swz_a(r);
+        const int m = min(m0 + r, a.M - 1);
+        aoffs[d] = (uint32_t)(((size_t)m * a.ldx + 8 * q) * 2);
+    }
+    uint32_t boffs[S::B_DMA];
+#pragma unroll
+    for (int d = 0; d < S::B_DMA; ++d) {
+        const int iw = 8 * d + (lane >> 3);          // row within the wave's rows
+        const int p = lane & 7;                       // word position within the row
+        const int word = 2 * ((p >> 1) ^ swz_b(iw)) + (p & 1);
+        const int n = min(nw0 + iw, a.N - 1);
+        boffs[d] = (uint32_t)(((size_t)n * KW + word) * 4);
+    }
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t adst = ring0 + 1024 * (wave * S::A_DMA);
+    const uint32_t bdst = ring0 + S::A_BYTES + wave * S::WN * kBRow;
+    auto issue = [&](int st, int slot) {
+        const uint8_t* ab = reinterpret_cast<const uint8_t*>(a.X) + (size_t)st * (kStage * 2);
+        const uint8_t* bb = reinterpret_cast<const uint8_t*>(a.codes) + (size_t)st * (kStage / 2);
+#pragma unroll
+        for (int d = 0; d < S::A_DMA; ++d) dma16(aoffs[d], ab, adst + slot * S::SLOT + 1024 * d);
+#pragma unroll
+        for (int d = 0; d < S::B_DMA; ++d) dma4(boffs[d], bb, bdst + slot * S::SLOT + 256 * d);
+    };
+
+    // per-lane LDS read offsets within a slot
+    const int gl = swz_a(li);
+    const int aoff0 = li * kARow + 16 * ((2 * lk) ^ gl);
+    const int aoff1 = li * kARow + 16 * ((2 * lk + 1) ^ gl);
+    const int boff = S::A_BYTES + wave * S::WN * kBRow + li * kBRow + 8 * (lk ^ swz_b(li));
+    const uint16_t* scrow = sc + (wave * S::WN + li) * a.G;
+
+    const DecodeConsts k = decode_consts();
+    const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 tot[MF][NF], acc[MF][NF], own;   // own: offset chain of M fragment `wave`
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) tot[mf][nf] = zero;
+
+    // One stage's products out of ring slot SL.  The first stage of a group
+    // starts its MFMA chains from a zero accumulator operand.
+    auto compute = [&](auto slc, auto firstc) {
+        constexpr int SL = decltype(slc)::value;
+        constexpr bool FIRST = decltype(firstc)::value;
+        const uint8_t* slot = ring + SL * S::SLOT;
+        u32x2 bw[NF];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+            bw[nf] = *reinterpret_cast<const u32x2*>(slot + boff + nf * 16 * kBRow);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            u32x4 xa[MF];
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+                xa[mf] = *reinterpret_cast<const u32x4*>(slot + (t ? aoff1 : aoff0) +
+                                                         mf * 16 * kARow);
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+                const uint32_t w = bw[nf][t];
+                const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k),
+                                  decode_pair(w, 2, k), decode_pair(w, 3, k)};
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf)
+                    acc[mf][nf] = mfma(xa[mf], bv, (FIRST && t == 0) ? zero : acc[mf][nf]);
+            }
+            // every wave multiplies the same activation rows: wave w runs the
+            // offset chain of M fragment w only, and the chains are swapped
+            // through LDS when the group closes (identical operands and order,
+            // so each chain is bitwise the one every wave would compute)
+            const u32x4 xo = *reinterpret_cast<const u32x4*>(slot + (t ? aoff1 : aoff0) +
+                                                             wave * 16 * kARow);
+            own = mfma(xo, b136, (FIRST && t == 0) ? zero : own);
+        }
+    };
+    // fold the finished group g into the totals; call after a barrier that
+    // follows every wave's publish()
+    auto publish = [&]() {
+        xch[wave][lane] = own;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // visible at the next barrier
+    };
+    auto close_group = [&](int g) {
+        f32x4 a136[MF];
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf) a136[mf] = xch[mf][lane];
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+            const float sv = bf16_to_f32(scrow[nf * 16 * a.G + g]);
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tot[mf][nf][r] = fmaf(sv, acc[mf][nf][r] - a136[mf][r], tot[mf][nf][r]);
+        }
+    };
+    auto stage = [&](int st, auto slc) {
+        constexpr int SL = decltype(slc)::value;
+        // stages issued after st by this wave: min(SLOTS - 2, stages - 1 - st)
+        wait_stage<S::LOADS, SLOTS - 2>(stages - 1 - st);
+        // every wave's DMA of stage st has landed, and every wave has finished
+        // stage st - 1, whose slot the next issue refills
+        ring_barrier();
+        const bool first = (st * kStage) % a.group == 0;
+        if (first && st > 0) close_group((st * kStage) / a.group - 1);
+        if (st + SLOTS - 1 < stages) issue(st + SLOTS - 1, (SL + SLOTS - 1) % SLOTS);
+        if (first)
+            compute(slc, std::true_type{});
+        else
+            compute(slc, std::false_type{});
+        if (((st + 1) * kStage) % a.group == 0) publish();
+    };
+
+    // Scales of the workgroup's rows: rows n0 .. n0 + BN - 1 are one
+    // contiguous run of dwords (n0 * G is even), copied by 4-byte DMA ahead of
+    // stage 0, so stage 0's wait covers them.  Lanes past the run re-read its
+    // last dword into unused LDS; entries past row N only feed outputs that
+    // are never stored.
+    {
+        const int ndw = (min(S::BN, a.N - n0) * a.G + 1) / 2;
+        const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.scales + (size_t)n0 * a.G);
+        const uint32_t sl = lds_addr(sc);
+        for (int i = wave; i < (ndw + 63) / 64; i += 4)
+            dma4((uint32_t)(4 * min(64 * i + lane, ndw - 1)), sb, sl + 256 * i);
+    }
+    const int pro = stages < SLOTS - 1 ? stages : SLOTS - 1;
+    for (int st = 0; st < pro; ++st) issue(st, st);
+
+    // stage st lives in slot st % SLOTS: unrolled by SLOTS so that every slot
+    // offset is a constant
+    for (int st0 = 0; st0 < stages; st0 += SLOTS)
+        static_for<SLOTS>([&](auto slc) {
+            const int st = st0 + decltype(slc)::value;
+            if (st < stages) stage(st, slc);
+        });
+
+    // the last group closes after one more barrier
+    ring_barrier();
+    close_group(a.G - 1);
+
+    // Output: every DMA was waited for in the last iteration, so once all
+    // waves are past the barrier above the ring is free.  The fragments go to
+    // LDS in the output dtype, then each thread writes whole 16-byte pieces of
+    // output rows (fragment-order stores would fill a quarter of each line).
+    const bool f32 = a.ydt == W4_F32;
+    const int esz = f32 ? 4 : 2;
+    uint8_t* ostage = ring;
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint8_t* p = ostage + (16 * mf + 4 * lk + r) * S::OUT_ROW +
+                             (wave * S::WN + 16 * nf + li) * esz;
+                if (f32)
+                    *reinterpret_cast<float*>(p) = tot[mf][nf][r];
+                else
+                    *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(tot[mf][nf][r]);
+            }
+    __syncthreads();
+    const int per = 16 / esz;                 // elements per 16-byte piece
+    const int cpr = S::BN / per;              // pieces per row
+    for (int e = tid; e < S::BM * cpr; e += 256) {
+        const int row = e / cpr, c = e - row * cpr;
+        const int m = m0 + row;
+        if (m >= a.M) break;                  // rows only grow with e
+        const int n = n0 + c * per;
+        if (n >= a.N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + row * S::OUT_ROW + 16 * c);
+        uint8_t* dst = static_cast<uint8_t*>(a.Y) + ((size_t)m * a.ldy + n) * esz;
+        if (a.vec_out && n + per <= a.N) {
+            gstore(reinterpret_cast<u32x4*>(dst), v);
+        } else {
+            for (int i = 0; i < per && n + i < a.N; ++i) {
+                if (f32)
+                    gstore(reinterpret_cast<uint32_t*>(dst) + i, v[i]);
+                else
+                    gstore(reinterpret_cast<uint16_t*>(dst) + i,
+                           (uint16_t)(v[i >> 1] >> (16 * (i & 1))));
+            }
+        }
+    }
+}
+
+struct PfCfg {
+    int MF, NF;
+};
+// 0: 64 x 192 blocks (large M); 1: 64 x 64 blocks (more workgroups at small M)
+constexpr PfCfg kPfCfgs[] = {{4, 3}, {4, 1}};
+constexpr int kPfSlots = 5;
+
+struct PfPlan {
+    int cfg, BM, BN, m_blocks, n_blocks, grid;
+};
+
+PfPlan plan_prefill(int M, int N) {
+    PfPlan p;
+    p.cfg = M <= 128 ? 1 : 0;
+    const char* e = getenv("W4_PREFILL_CFG");  // tuning override: 0..1
+    if (e && (*e == '0' || *e == '1') && e[1] == 0) p.cfg = *e - '0';
+    p.BM = 16 * kPfCfgs[p.cfg].MF;
+    p.BN = 64 * kPfCfgs[p.cfg].NF;
+    p.m_blocks = (M + p.BM - 1) / p.BM;
+    p.n_blocks = (N + p.BN - 1) / p.BN;
+    p.grid = 8 * p.m_blocks * ((p.n_blocks + 7) / 8);
+    return p;
+}
+
+}  // namespace
+
+bool prefill_supported(int M, int N, int K, int group, int ldx) {
+    // per-lane DMA offsets are 32-bit: activation rows and code rows must be
+    // addressable from their buffer's start within 4 GiB
+    const size_t x_span = ((size_t)(M - 1) * (size_t)ldx + (size_t)K) * 2;
+    const size_t c_span = (size_t)N * (size_t)K / 2;
+    return group % kStage == 0 && K % kStage == 0 && K / group <= kMaxG &&
+           x_span < (1ull << 32) && c_span < (1ull << 32);
+}
+
+int launch_prefill(const void* packed, int N, int K, int group, int M, const uint16_t* X,
+                   int ldx, void* Y, int ldy, int ydt, hipStream_t s) {
+    const PfPlan p = plan_prefill(M, N);
+    PfArgs a;
+    a.codes = static_cast<const uint32_t*>(packed);
+    a.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) +
+                                                 scale_offset(N, K));
+    a.X = X;
+    a.Y = Y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.group = group;
+    a.G = K / group;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.ydt = ydt;
+    a.m_blocks = p.m_blocks;
+    a.n_blocks = p.n_blocks;
+    const size_t esz = ydt == W4_F32 ? 4 : 2;
+    a.vec_out = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((size_t)ldy * esz) % 16 == 0;
+    if (p.cfg == 0)
+        prefill_kernel<4, 3, kPfSlots><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    else
+        prefill_kernel<4, 1, kPfSlots><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    return hip_fail(hipGetLastError(), "prefill launch");
+}
+
+void describe_prefill(int M, int N, int K, int group, char* buf, size_t len) {
+    const PfPlan p = plan_prefill(M, N);
+    snprintf(buf, len,
+             "mfma 16x16x32 dma-ring block %dx%d waves 1x4 slots %d stage %d grid=%d (K=%d g=%d)",
+             p.BM, p.BN, kPfSlots, kStage, p.grid, K, group);
+}
+
+}  // namespace w4
