@@ -164,10 +164,12 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
 
-template <int MF, int NF, int SLOTS>
+template <int MF, int NF, int SLOTS, int P>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PfArgs a) {
     using S = PfShape<MF, NF, SLOTS>;
+    static_assert(P == 1 || P == 2, "stages per barrier");
+    static_assert(SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps, double-buffered at least");
     __shared__ __align__(16) uint8_t ring[SLOTS * S::SLOT];
     __shared__ __align__(16) uint16_t sc[S::BN * kMaxG];
     __shared__ __align__(16) f32x4 xch[4][64];   // offset chains, one per wave
@@ -290,21 +292,31 @@ void prefill_kernel(PfArgs a) {
                     tot[mf][nf][r] = fmaf(sv, acc[mf][nf][r] - a136[mf][r], tot[mf][nf][r]);
         }
     };
-    auto stage = [&](int st, auto slc) {
-        constexpr int SL = decltype(slc)::value;
-        // stages issued after st by this wave: min(SLOTS - 2, stages - 1 - st)
-        wait_stage<S::LOADS, SLOTS - 2>(stages - 1 - st);
-        // every wave's DMA of stage st has landed, and every wave has finished
-        // stage st - 1, whose slot the next issue refills
+    // P stages s0 .. s0 + P - 1 (slots SL0 ..) per barrier; a group spans
+    // whole P-stage steps (group >= 128 = 2 stages; P <= 2)
+    auto step = [&](int s0, auto slc) {
+        constexpr int SL0 = decltype(slc)::value * P;
+        // stages issued after s0 + P - 1 by this wave
+        wait_stage<S::LOADS, SLOTS - 2 * P>(stages - P - s0);
+        // every wave's DMA of these stages has landed, and every wave has
+        // finished the previous P stages, whose slots the next issue refills
         ring_barrier();
-        const bool first = (st * kStage) % a.group == 0;
-        if (first && st > 0) close_group((st * kStage) / a.group - 1);
-        if (st + SLOTS - 1 < stages) issue(st + SLOTS - 1, (SL + SLOTS - 1) % SLOTS);
+        const bool first = (s0 * kStage) % a.group == 0;
+        if (first && s0 > 0) close_group((s0 * kStage) / a.group - 1);
+        static_for<P>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            if (s0 + SLOTS - P + I < stages)
+                issue(s0 + SLOTS - P + I, (SL0 + SLOTS - P + I) % SLOTS);
+        });
         if (first)
-            compute(slc, std::true_type{});
+            compute(std::integral_constant<int, SL0>{}, std::true_type{});
         else
-            compute(slc, std::false_type{});
-        if (((st + 1) * kStage) % a.group == 0) publish();
+            compute(std::integral_constant<int, SL0>{}, std::false_type{});
+        static_for<P - 1>([&](auto ic) {
+            compute(std::integral_constant<int, SL0 + 1 + decltype(ic)::value>{},
+                    std::false_type{});
+        });
+        if (((s0 + P) * kStage) % a.group == 0) publish();
     };
 
     // Scales of the workgroup's rows: rows n0 .. n0 + BN - 1 are one
@@ -319,15 +331,15 @@ void prefill_kernel(PfArgs a) {
         for (int i = wave; i < (ndw + 63) / 64; i += 4)
             dma4((uint32_t)(4 * min(64 * i + lane, ndw - 1)), sb, sl + 256 * i);
     }
-    const int pro = stages < SLOTS - 1 ? stages : SLOTS - 1;
+    const int pro = stages < SLOTS - P ? stages : SLOTS - P;
     for (int st = 0; st < pro; ++st) issue(st, st);
 
     // stage st lives in slot st % SLOTS: unrolled by SLOTS so that every slot
-    // offset is a constant
+    // offset is a constant (stages is a multiple of 4, so of P)
     for (int st0 = 0; st0 < stages; st0 += SLOTS)
-        static_for<SLOTS>([&](auto slc) {
-            const int st = st0 + decltype(slc)::value;
-            if (st < stages) stage(st, slc);
+        static_for<SLOTS / P>([&](auto slc) {
+            const int s0 = st0 + P * decltype(slc)::value;
+            if (s0 < stages) step(s0, slc);
         });
 
     // the last group closes after one more barrier
@@ -380,11 +392,15 @@ void prefill_kernel(PfArgs a) {
 }
 
 struct PfCfg {
-    int MF, NF;
+    int MF, NF, slots, per_barrier;
 };
-// 0: 64 x 192 blocks (large M); 1: 64 x 64 blocks (more workgroups at small M)
-constexpr PfCfg kPfCfgs[] = {{4, 3}, {4, 1}};
-constexpr int kPfSlots = 5;
+// 64 x 192 or 64 x 64 blocks; ring slots; stages per barrier.  Measured at
+// N = 12288, K = 1536, g256: two stages per barrier beat one (the per-barrier
+// latency chain, not the DMA depth, bounds the loop), 64 x 192 blocks win from
+// M = 256 up, 64 x 64 blocks (three times the workgroups) below.  Entries 2
+// and 3 are the one-stage variants, kept for comparison runs.
+constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2}, {4, 1, 6, 2}, {4, 3, 5, 1}, {4, 1, 5, 1}};
+constexpr int kPfNumCfgs = sizeof(kPfCfgs) / sizeof(kPfCfgs[0]);
 
 struct PfPlan {
     int cfg, BM, BN, m_blocks, n_blocks, grid;
@@ -393,8 +409,8 @@ struct PfPlan {
 PfPlan plan_prefill(int M, int N) {
     PfPlan p;
     p.cfg = M <= 128 ? 1 : 0;
-    const char* e = getenv("W4_PREFILL_CFG");  // tuning override: 0..1
-    if (e && (*e == '0' || *e == '1') && e[1] == 0) p.cfg = *e - '0';
+    const char* e = getenv("W4_PREFILL_CFG");  // tuning override: a kPfCfgs index
+    if (e && *e >= '0' && *e < '0' + kPfNumCfgs && e[1] == 0) p.cfg = *e - '0';
     p.BM = 16 * kPfCfgs[p.cfg].MF;
     p.BN = 64 * kPfCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -435,18 +451,22 @@ int launch_prefill(const void* packed, int N, int K, int group, int M, const uin
     a.n_blocks = p.n_blocks;
     const size_t esz = ydt == W4_F32 ? 4 : 2;
     a.vec_out = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((size_t)ldy * esz) % 16 == 0;
-    if (p.cfg == 0)
-        prefill_kernel<4, 3, kPfSlots><<<dim3(p.grid), dim3(256), 0, s>>>(a);
-    else
-        prefill_kernel<4, 1, kPfSlots><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    const dim3 g(p.grid), b(256);
+    switch (p.cfg) {
+        case 0: prefill_kernel<4, 3, 4, 2><<<g, b, 0, s>>>(a); break;
+        case 1: prefill_kernel<4, 1, 6, 2><<<g, b, 0, s>>>(a); break;
+        case 2: prefill_kernel<4, 3, 5, 1><<<g, b, 0, s>>>(a); break;
+        default: prefill_kernel<4, 1, 5, 1><<<g, b, 0, s>>>(a); break;
+    }
     return hip_fail(hipGetLastError(), "prefill launch");
 }
 
 void describe_prefill(int M, int N, int K, int group, char* buf, size_t len) {
     const PfPlan p = plan_prefill(M, N);
     snprintf(buf, len,
-             "mfma 16x16x32 dma-ring block %dx%d waves 1x4 slots %d stage %d grid=%d (K=%d g=%d)",
-             p.BM, p.BN, kPfSlots, kStage, p.grid, K, group);
+             "mfma 16x16x32 dma-ring block %dx%d waves 1x4 slots %d stage %d x%d grid=%d (K=%d g=%d)",
+             p.BM, p.BN, kPfCfgs[p.cfg].slots, kStage, kPfCfgs[p.cfg].per_barrier, p.grid, K,
+             group);
 }
 
 }  // namespace w4
