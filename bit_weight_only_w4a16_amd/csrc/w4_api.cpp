@@ -203,6 +203,9 @@ int w4_fwht(const uint16_t* X, int ldx, uint16_t* Xo, int ldo, int M, int K,
     return launch_fwht(X, ldx, Xo, ldo, M, K, block, static_cast<hipStream_t>(stream));
 }
 
+// w4a16_gemm: largest row count that runs on the vector-ALU small-M kernel
+constexpr int kGemmSmallMRows = 8;
+
 size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block) {
     if (had_block == 0 || M < 1 || K < 1) return 0;
     return align_up((size_t)M * (size_t)K * 2, kAlign);
@@ -240,13 +243,17 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
         Xin = Xr;
         ld_in = K;
     }
-    // decode-shaped row counts stay on the vector-ALU kernels; M > 16 goes to
-    // the matrix cores ([P2] "fastgemma": below 16 rows a GEMM is decode-shaped)
+    // decode-shaped row counts stay on the vector-ALU kernels ([P2]
+    // "fastgemma": a GEMM of few rows is decode-shaped); on MI355X the
+    // matrix-core kernel, whose time is flat below 64 rows, wins from 9 rows
+    // on (measured at N = 12288, K = 1536: 8 rows 10.1 us on the small-M
+    // kernel, 9..16 rows 18..25 us there, 11.3 us on the matrix cores)
     if (M == 1) {
         const GemvTile t = pick_gemv_tile(N, K, group);
         return launch_gemv(t, packed, N, K, group, Xin, Y, ydt, s);
     }
-    if (M <= 16) return launch_smallm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
+    if (M <= kGemmSmallMRows)
+        return launch_smallm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
     return launch_mfma_gemm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
 }
 
@@ -435,7 +442,7 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) 
         const GemvTile t = pick_gemv_tile(N, K, group);
         snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d", t.generic ? "_generic" : "",
                  t.L, t.U, t.waves, t.grid);
-    } else if (M <= 16) {
+    } else if (M <= kGemmSmallMRows) {
         describe_smallm(M, N, K, group, buf, len);
     } else {
         if (K % 256 != 0) return fail(W4_ERR_SHAPE, "describe: gemm needs K % 256 == 0");

@@ -164,10 +164,11 @@ size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block);
  * FWHT of X (block had_block, computed into `workspace`, M*K bf16) and W' is
  * stored pre-rotated.  Codes enter the matrix cores as exact bf16 integers;
  * each K-group's partial product is multiplied by its fp32 scale.
- *  group must be 256 (the rotated prefill format of [P2]) or 32.
- *  M >= 1, K % 256 == 0.  Row counts of 16 or fewer are decode-shaped and run
- *  on the vector-ALU kernels (M = 1: the GEMV, 2..16: the small-M product)
- *  after the same transform; M > 16 runs on the matrix cores.
+ *  group must be 256 or 512 (the rotated prefill format of [P2]) or 32.
+ *  M >= 1, K % 256 == 0.  Decode-shaped row counts run on the vector-ALU
+ *  kernels after the same transform (M = 1: the GEMV, 2..8: the small-M
+ *  product); M >= 9 runs on the matrix cores, which are faster from 9 rows on
+ *  for the N = 12288, K = 1536 prefill shape.
  *  X: device, stride ldx (% 8 == 0).  Y: device, stride ldy.
  *  workspace: device, >= w4a16_gemm_workspace_bytes(M, K, had_block) bytes,
  *  16-byte aligned (may be NULL when that size is 0).

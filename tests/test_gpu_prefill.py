@@ -136,10 +136,12 @@ def test_prefill_g256_hadamard(oracle_mod, M):
 @pytest.mark.parametrize("M,N,K,g,had", [(17, 100, 256, 32, 0), (64, 12288, 1536, 32, 0),
                                          (100, 513, 1536, 256, 512), (512, 300, 512, 256, 0),
                                          (65, 1000, 2048, 256, 256), (33, 64, 256, 256, 0),
-                                         (64, 12288, 1536, 512, 512), (40, 300, 1024, 512, 0)])
+                                         (64, 12288, 1536, 512, 512), (40, 300, 1024, 512, 0),
+                                         (9, 200, 512, 256, 0), (16, 1000, 1536, 32, 0),
+                                         (13, 12288, 1536, 256, 512)])
 def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
-    """M > 16 runs on the matrix cores: ragged M and N, both group sizes,
-    with and without the run-time transform."""
+    """M >= 9 runs on the matrix cores: ragged M and N, all group sizes, with
+    and without the run-time transform."""
     note("mfma gemm M=%d N=%d K=%d g=%d had=%d" % (M, N, K, g, had))
     case = synth.make_case("mfma", N, K, g, M, M * 31 + N + K, "bf16", outlier_frac=0.01)
     packed = upload_packed(case.P, case.S, N, K, g)
@@ -151,6 +153,23 @@ def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
     for out_dtype in ("bf16", "f32"):
         Y = from_dev(w4.gemm(packed, N, K, g, X, had_block=had, out_dtype=out_dtype))
         assert_within(Y[rows], Yr, A, out_dtype, "mfma %s" % out_dtype)
+
+
+@pytest.mark.parametrize("env", [{"W4_PREFILL_CFG": str(c)} for c in range(4)] +
+                         [{"W4_PREFILL": "0"}])
+def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env):
+    """Every compiled matrix-core tiling (the tuning overrides select them,
+    one per call) against the oracle on one ragged g256 case."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    M, N, K, g = 70, 1000, 1536, 256
+    note("mfma tiling %s M=%d N=%d K=%d g=%d" % (env, M, N, K, g))
+    case = synth.make_case("tile", N, K, g, M, 77, "bf16", outlier_frac=0.01)
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, oracle_mod.bf16_to_f64(case.X), threads=16)
+    Y = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
+    assert_within(Y, Yr, A, "f32", "tiling %s" % env)
 
 
 def test_matrix_core_code8_columns_exact_zero():
