@@ -259,9 +259,10 @@ def time_prefill(torch, w4, synth, dev):
     return out
 
 
-def cpu_baseline(cases, max_threads=16, min_seconds=2.0, max_passes=4):
+def cpu_baseline(cases, max_threads=16, min_seconds=10.0, max_passes=40):
     """The fp64 oracle over whole decode-step sweeps (all 141 GEMVs), OpenMP
-    over rows, repeated until min_seconds of wall time (at most max_passes)."""
+    over rows, repeated until min_seconds of wall time (at most max_passes):
+    a bounded sample of about 10 s on the host's cores."""
     import oracle
     oracle.build()
     threads = max(1, min(max_threads, os.cpu_count() or 1))
