@@ -57,15 +57,20 @@ __device__ __forceinline__ int part_stride(int D) { return 32 + kAttnHeads * D; 
 
 // Slot c is attended iff c < T and, with positions, the slot's position p is
 // in (cur - window, cur] (window 0: no lower bound).
+template <bool POS>
 __device__ __forceinline__ bool slot_valid(const AttnArgs& a, int c, int p) {
     if (c >= a.T) return false;
-    if (!a.pos) return true;
+    if (!POS) return true;
     return p >= 0 && p <= a.cur && (a.window <= 0 || p > a.cur - a.window);
 }
 
 }  // namespace
 
-template <int D>
+// POS: the cache records a position per slot (ring caches).  Every load of a
+// tile is unconditional (indices clamped into the cache; slots past T are
+// rejected by slot_valid), so the compiler can count the loads in flight
+// exactly and keeps the next tile's loads outstanding across the loop.
+template <int D, bool POS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_split_kernel(AttnArgs a) {
     constexpr int DQ = D / 4;   // dims per wave
@@ -96,14 +101,19 @@ void attn_split_kernel(AttnArgs a) {
     for (int t = 0; t < DT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff(), l_run = 0.f;
 
-    struct TileRegs {
-        u32x4 ka[KS], kb[KS], vf[DT];
-        int pos[8];  // positions of this lane's slots (ring caches)
-    };
-    // Loads of tile tau: score tile a row r is slot p0 + 8 (r / 4) + r % 4, tile b
-    // that + 4, so result row 4 g + j holds slot p0 + 8 g + j (tile a, j < 4) or
-    // + 4 (tile b); V^T rows are dims d0 + 16 t + i, slots 8 g .. 8 g + 7.
-    auto load_tile = [&](int tau, TileRegs& r) {
+    // One register set per tile part, reloaded for the next tile as soon as
+    // the part has been consumed: keys (and positions) right after the score
+    // products, values right after the PV product.  Each load then has about
+    // half a tile of work to hide behind, with half the registers of a
+    // two-set ping-pong (whose register reuse made the compiler drain every
+    // load at each tile).  The last tile reloads itself, so every load is
+    // unconditional and every wait counts exactly.
+    // Score tile a row r is slot p0 + 8 (r / 4) + r % 4, tile b that + 4, so
+    // result row 4 g + j holds slot p0 + 8 g + j (tile a, j < 4) or + 4 (tile
+    // b); V^T rows are dims d0 + 16 t + i, slots 8 g .. 8 g + 7.
+    u32x4 ka[KS], kb[KS], vf[DT];
+    int pos[8];
+    auto load_k = [&](int tau) {
         const int p0 = tau * kAttnTile;
         const int ra = p0 + 8 * (i >> 2) + (i & 3);
         const int rb = ra + 4;
@@ -111,35 +121,41 @@ void attn_split_kernel(AttnArgs a) {
         const uint16_t* krb = a.K + (size_t)(rb < a.T ? rb : a.T - 1) * a.ldk + d0 + 8 * g;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            r.ka[s] = gload(reinterpret_cast<const u32x4*>(kra + 32 * s));
-            r.kb[s] = gload(reinterpret_cast<const u32x4*>(krb + 32 * s));
+            ka[s] = gload(reinterpret_cast<const u32x4*>(kra + 32 * s));
+            kb[s] = gload(reinterpret_cast<const u32x4*>(krb + 32 * s));
         }
+        if (POS) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = p0 + 8 * g + j;
+                pos[j] = gload(a.pos + (c < a.T ? c : a.T - 1));
+            }
+        }
+    };
+    auto load_v = [&](int tau) {
         const uint16_t* vb =
             a.Vt + (size_t)tau * D * kAttnTile + (size_t)(d0 + i) * kAttnTile + 8 * g;
 #pragma unroll
         for (int t = 0; t < DT; ++t)
-            r.vf[t] = gload(reinterpret_cast<const u32x4*>(vb + (size_t)16 * t * kAttnTile));
-        if (a.pos) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = p0 + 8 * g + j;
-                r.pos[j] = c < a.T ? gload(a.pos + c) : -1;
-            }
-        }
+            vf[t] = gload(reinterpret_cast<const u32x4*>(vb + (size_t)16 * t * kAttnTile));
     };
 
-    auto process = [&](int tau, const TileRegs& r) {
+    load_k(tb);
+    load_v(tb);
+    for (int tau = tb; tau < te; ++tau) {
+        const int nxt = tau + 1 < te ? tau + 1 : tau;
         const int p0 = tau * kAttnTile;
         bool valid[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) valid[j] = slot_valid(a, p0 + 8 * g + j, a.pos ? r.pos[j] : 0);
+        for (int j = 0; j < 8; ++j) valid[j] = slot_valid<POS>(a, p0 + 8 * g + j, POS ? pos[j] : 0);
 
         f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            sa = mma(r.ka[s], qf[s], sa);
-            sb = mma(r.kb[s], qf[s], sb);
+            sa = mma(ka[s], qf[s], sa);
+            sb = mma(kb[s], qf[s], sb);
         }
+        load_k(nxt);
         // partial scores of the four dim quarters: summed in wave order 0..3
         float* buf = &sx[tau & 1][0][0][0];
 #pragma unroll
@@ -151,10 +167,10 @@ void attn_split_kernel(AttnArgs a) {
         float t8[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float s = ((buf[(0 * 8 + j) * 64 + lane] + buf[(1 * 8 + j) * 64 + lane]) +
-                             buf[(2 * 8 + j) * 64 + lane]) +
-                            buf[(3 * 8 + j) * 64 + lane];
-            t8[j] = valid[j] ? s * a.scale2 : -__builtin_inff();
+            const float sv = ((buf[(0 * 8 + j) * 64 + lane] + buf[(1 * 8 + j) * 64 + lane]) +
+                              buf[(2 * 8 + j) * 64 + lane]) +
+                             buf[(3 * 8 + j) * 64 + lane];
+            t8[j] = valid[j] ? sv * a.scale2 : -__builtin_inff();
         }
         // online softmax of head i over the tile's 32 slots (4 lanes x 8)
         float mt = t8[0];
@@ -189,23 +205,9 @@ void attn_split_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             acc[t] = acc[t] * alpha;
-            acc[t] = mma(r.vf[t] & vmask, pf, acc[t]);
+            acc[t] = mma(vf[t] & vmask, pf, acc[t]);
         }
-    };
-
-    // two register sets: the next tile's loads are in flight while this one
-    // is computed (the last step re-loads the current tile instead of
-    // branching, so every wait counts exactly)
-    TileRegs ta, tb2;
-    int tau = tb;
-    load_tile(tau, ta);
-    while (true) {
-        load_tile(tau + 1 < te ? tau + 1 : tau, tb2);
-        process(tau, ta);
-        if (++tau >= te) break;
-        load_tile(tau + 1 < te ? tau + 1 : tau, ta);
-        process(tau, tb2);
-        if (++tau >= te) break;
+        load_v(nxt);
     }
 
     // partial of this workgroup: m and l of each head (base 2), unnormalised O
@@ -354,12 +356,19 @@ int launch_attn_decode(const uint16_t* q, const uint16_t* K, int ldk, const uint
     a.tiles = (T + kAttnTile - 1) / kAttnTile;
     a.nwg = a.tiles < kAttnMaxWG ? a.tiles : kAttnMaxWG;
     a.scale2 = scale * kLog2e;
+    const dim3 g(a.nwg), b(256);
     if (D == 512) {
-        attn_split_kernel<512><<<dim3(a.nwg), dim3(256), 0, s>>>(a);
+        if (pos)
+            attn_split_kernel<512, true><<<g, b, 0, s>>>(a);
+        else
+            attn_split_kernel<512, false><<<g, b, 0, s>>>(a);
         attn_merge_kernel<512><<<dim3(kAttnHeads, 512 / 64), dim3(kMergeThreads), 0, s>>>(
             a.part, a.nwg, out, odt);
     } else {
-        attn_split_kernel<256><<<dim3(a.nwg), dim3(256), 0, s>>>(a);
+        if (pos)
+            attn_split_kernel<256, true><<<g, b, 0, s>>>(a);
+        else
+            attn_split_kernel<256, false><<<g, b, 0, s>>>(a);
         attn_merge_kernel<256><<<dim3(kAttnHeads, 256 / 64), dim3(kMergeThreads), 0, s>>>(
             a.part, a.nwg, out, odt);
     }
