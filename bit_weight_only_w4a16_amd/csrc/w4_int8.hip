@@ -15,6 +15,7 @@
 #include <cstdlib>
 
 #include "w4_dispatch.h"
+#include "w4_ring.h"
 
 namespace w4 {
 
@@ -181,6 +182,7 @@ struct I8Args {
     const float* ws;
     void* Y;
     int M, N, K, ldx, ldw, ldy, ydt, m_blocks, n_blocks;
+    int vec_out;  // Y and its row stride allow 16-byte stores
 };
 
 template <int MF, int NF>
@@ -294,25 +296,220 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(I8Args a) {
     }
 }
 
+// DMA-ring int8 GEMM (the layout and pipeline of the int4 prefill ring in
+// w4_prefill.hip, without decode or offset chains).  Four waves side by side
+// along N share one 64-row activation tile; each wave owns 16*NF weight rows
+// and computes 64 x 16*NF outputs.  64-wide K stages (one MFMA step) are
+// DMA'd into an LDS ring of SLOTS slots, P stages per wait and barrier.  Rows
+// are 64 bytes per slot; position p of row r holds 16-byte chunk
+// p ^ swz_i8(r), which keeps every fragment read free of bank
+// conflicts on 32- and 64-bank LDS.  Scales are applied once, at the end,
+// in the order of the register-staged kernel: (acc * xs[m]) * ws[n].
+constexpr int kI8RingStage = 64;
+constexpr int kI8RingRow = 64;   // bytes of a row in a slot
+
+// r is any row index; only its place within its 16-row fragment counts,
+// which is what the fragment reads see
+__device__ __forceinline__ int swz_i8(int r) { return (((r & 15) >> 1) ^ ((r & 15) >> 3)) & 3; }
+
+template <int NF, int SLOTS, int P>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_i8_ring_kernel(I8Args a) {
+    using namespace ring;
+    constexpr int MF = 4, BM = 64, WN = 16 * NF, BN = 4 * WN;
+    constexpr int A_BYTES = BM * kI8RingRow;          // one 16-byte DMA per wave
+    constexpr int SLOT = A_BYTES + BN * kI8RingRow;   // + NF per wave
+    constexpr int LOADS = 1 + NF;
+    constexpr int OUT_ROW = BN * 4 + 16;
+    static_assert(A_BYTES == 4 * 1024, "activation tile: one DMA per wave");
+    static_assert(BM * OUT_ROW <= SLOTS * SLOT, "output staging fits in the ring");
+    static_assert((P == 1 || P == 2) && SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps");
+    static_assert(LOADS * (SLOTS - 2 * P) < 64, "vmcnt range");
+    __shared__ __align__(16) uint8_t ring[SLOTS * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lk = lane >> 4;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int mb = j % a.m_blocks;
+    const int nb = (j / a.m_blocks) * 8 + xcd;
+    if (nb >= a.n_blocks) return;
+    const int m0 = mb * BM, n0 = nb * BN;
+    const int nw0 = n0 + wave * WN;
+    const int stages = a.K / kI8RingStage;
+
+    // scales of this lane's outputs, loaded now, used at the end
+    float xsr[MF][4], wsr[NF];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            xsr[mf][r] = gload(a.xs + min(m0 + 16 * mf + 4 * lk + r, a.M - 1));
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) wsr[nf] = gload(a.ws + min(nw0 + 16 * nf + li, a.N - 1));
+
+    // DMA: lane l of an instruction fills row (l / 4), position (l & 3) of the
+    // instruction's 16 rows; rows past M / N clamp to valid memory
+    uint32_t aoff, boffs[NF];
+    {
+        const int r = 16 * wave + (lane >> 2);
+        const int q = (lane & 3) ^ swz_i8(r);
+        aoff = (uint32_t)((size_t)min(m0 + r, a.M - 1) * a.ldx + 16 * q);
+    }
+#pragma unroll
+    for (int d = 0; d < NF; ++d) {
+        const int iw = 16 * d + (lane >> 2);
+        const int q = (lane & 3) ^ swz_i8(iw);
+        boffs[d] = (uint32_t)((size_t)min(nw0 + iw, a.N - 1) * a.ldw + 16 * q);
+    }
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t adst = ring0 + 1024 * wave;
+    const uint32_t bdst = ring0 + A_BYTES + wave * WN * kI8RingRow;
+    auto issue = [&](int st, int slot) {
+        const int8_t* ab = a.X + (size_t)st * kI8RingStage;
+        const int8_t* bb = a.W + (size_t)st * kI8RingStage;
+        dma16(aoff, ab, adst + slot * SLOT);
+#pragma unroll
+        for (int d = 0; d < NF; ++d) dma16(boffs[d], bb, bdst + slot * SLOT + 1024 * d);
+    };
+
+    const int sl = swz_i8(li);
+    const int aread = li * kI8RingRow + 16 * (lk ^ sl);
+    const int bread = A_BYTES + (wave * WN + li) * kI8RingRow + 16 * (lk ^ sl);
+    i32x4 acc[MF][NF];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) acc[mf][nf] = i32x4{0, 0, 0, 0};
+
+    auto compute = [&](auto slc) {
+        constexpr int SL = decltype(slc)::value;
+        const uint8_t* slot = ring + SL * SLOT;
+        u32x4 xa[MF], wb[NF];
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+            xa[mf] = *reinterpret_cast<const u32x4*>(slot + aread + mf * 16 * kI8RingRow);
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+            wb[nf] = *reinterpret_cast<const u32x4*>(slot + bread + nf * 16 * kI8RingRow);
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf) acc[mf][nf] = mma_i8(xa[mf], wb[nf], acc[mf][nf]);
+    };
+    auto step = [&](int s0, auto slc) {
+        constexpr int SL0 = decltype(slc)::value * P;
+        // stages issued after s0 + P - 1 by this wave
+        wait_stage<LOADS, SLOTS - 2 * P>(stages - P - s0);
+        // every wave's DMA of these stages has landed, and every wave has
+        // finished the previous P stages, whose slots the next issue refills
+        ring_barrier();
+        static_for<P>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            if (s0 + SLOTS - P + I < stages)
+                issue(s0 + SLOTS - P + I, (SL0 + SLOTS - P + I) % SLOTS);
+        });
+        static_for<P>([&](auto ic) { compute(std::integral_constant<int, SL0 + decltype(ic)::value>{}); });
+    };
+
+    const int pro = stages < SLOTS - P ? stages : SLOTS - P;
+    for (int st = 0; st < pro; ++st) issue(st, st);
+    // stage st lives in slot st % SLOTS (stages is a multiple of 2, so of P)
+    for (int st0 = 0; st0 < stages; st0 += SLOTS)
+        static_for<SLOTS / P>([&](auto slc) {
+            const int s0 = st0 + P * decltype(slc)::value;
+            if (s0 < stages) step(s0, slc);
+        });
+
+    // every DMA was waited for in the last step: after this barrier the ring
+    // holds the output tile, which then leaves as whole 16-byte row pieces
+    ring_barrier();
+    const bool f32 = a.ydt == W4_F32;
+    const int esz = f32 ? 4 : 2;
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float y = ((float)acc[mf][nf][r] * xsr[mf][r]) * wsr[nf];
+                uint8_t* p = ring + (16 * mf + 4 * lk + r) * OUT_ROW + (wave * WN + 16 * nf + li) * esz;
+                if (f32)
+                    *reinterpret_cast<float*>(p) = y;
+                else
+                    *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(y);
+            }
+    __syncthreads();
+    const int per = 16 / esz;
+    const int cpr = BN / per;
+    for (int e = tid; e < BM * cpr; e += 256) {
+        const int row = e / cpr, c = e - row * cpr;
+        const int m = m0 + row;
+        if (m >= a.M) break;
+        const int n = n0 + c * per;
+        if (n >= a.N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ring + row * OUT_ROW + 16 * c);
+        uint8_t* dst = static_cast<uint8_t*>(a.Y) + ((size_t)m * a.ldy + n) * esz;
+        if (a.vec_out && n + per <= a.N) {
+            gstore(reinterpret_cast<u32x4*>(dst), v);
+        } else {
+            for (int i = 0; i < per && n + i < a.N; ++i) {
+                if (f32)
+                    gstore(reinterpret_cast<uint32_t*>(dst) + i, v[i]);
+                else
+                    gstore(reinterpret_cast<uint16_t*>(dst) + i, (uint16_t)(v[i >> 1] >> (16 * (i & 1))));
+            }
+        }
+    }
+}
+
 struct I8Plan {
+    bool ring;                  // DMA-ring kernel (else register-staged)
+    int cfg;                    // ring: index into kI8RingCfgs
     int MF, NF, BM, BN, m_blocks, n_blocks, grid;
 };
 
-static I8Plan plan_i8(int M, int N) {
+struct I8RingCfg {
+    int NF, slots, per_barrier;
+};
+// 64 x 192 blocks for M > 256, 64 x 64 blocks (three times the workgroups)
+// up to 256 rows, both with two 64-K stages per barrier (measured at N = 12288,
+// K = 1536: 64 x 64 wins through M = 256, 64 x 192 from 512 on)
+constexpr I8RingCfg kI8RingCfgs[] = {{3, 4, 2}, {1, 6, 2}};
+
+static I8Plan plan_i8(int M, int N, int K, int ldx, int ldw) {
     I8Plan p;
-    // measured on MI355X at N = 12288, K = 1536, M = 64..512: 64 x 64 blocks
-    // (four workgroups per CU) beat 64 x 128, 128 x 64 and 128 x 128 at every M
-    (void)M;
-    p.MF = 2;
-    p.NF = 2;
-    const char* e = getenv("W4_I8_TILE");  // tuning override "MF,NF" (2 or 4 each)
-    int mf = 0, nf = 0;
-    if (e && sscanf(e, "%d,%d", &mf, &nf) == 2 && (mf == 2 || mf == 4) && (nf == 2 || nf == 4)) {
-        p.MF = mf;
-        p.NF = nf;
+    // W4_I8_RING=0 selects the register-staged kernel (comparison runs);
+    // W4_I8_RING=<cfg + 1> forces a ring configuration
+    const char* r = getenv("W4_I8_RING");
+    // per-lane DMA offsets are 32-bit
+    const bool fits = (size_t)(M - 1) * (size_t)ldx + (size_t)K < (1ull << 32) &&
+                      (size_t)(N - 1) * (size_t)ldw + (size_t)K < (1ull << 32);
+    p.ring = fits && !(r && r[0] == '0' && r[1] == 0);
+    if (p.ring) {
+        p.cfg = M <= 256 ? 1 : 0;
+        if (r && (r[0] == '1' || r[0] == '2') && r[1] == 0) p.cfg = r[0] - '1';
+        p.MF = 4;
+        p.NF = kI8RingCfgs[p.cfg].NF;
+        p.BM = 64;
+        p.BN = 64 * p.NF;
+    } else {
+        // register-staged: measured on MI355X at N = 12288, K = 1536, M = 64..512,
+        // 64 x 64 blocks (four workgroups per CU) beat 64 x 128, 128 x 64 and 128 x 128
+        p.cfg = 0;
+        p.MF = 2;
+        p.NF = 2;
+        const char* e = getenv("W4_I8_TILE");  // tuning override "MF,NF" (2 or 4 each)
+        int mf = 0, nf = 0;
+        if (e && sscanf(e, "%d,%d", &mf, &nf) == 2 && (mf == 2 || mf == 4) &&
+            (nf == 2 || nf == 4)) {
+            p.MF = mf;
+            p.NF = nf;
+        }
+        p.BM = 2 * p.MF * 16;
+        p.BN = 2 * p.NF * 16;
     }
-    p.BM = 2 * p.MF * 16;
-    p.BN = 2 * p.NF * 16;
     p.m_blocks = (M + p.BM - 1) / p.BM;
     p.n_blocks = (N + p.BN - 1) / p.BN;
     p.grid = 8 * p.m_blocks * ((p.n_blocks + 7) / 8);
@@ -322,7 +519,7 @@ static I8Plan plan_i8(int M, int N) {
 int launch_gemm_i8(const int8_t* X, int ldx, const float* xs, const int8_t* W, int ldw,
                    const float* ws, int M, int N, int K, void* Y, int ldy, int ydt,
                    hipStream_t s) {
-    const I8Plan p = plan_i8(M, N);
+    const I8Plan p = plan_i8(M, N, K, ldx, ldw);
     I8Args a;
     a.X = X;
     a.xs = xs;
@@ -338,21 +535,37 @@ int launch_gemm_i8(const int8_t* X, int ldx, const float* xs, const int8_t* W, i
     a.ydt = ydt;
     a.m_blocks = p.m_blocks;
     a.n_blocks = p.n_blocks;
-    if (p.MF == 2 && p.NF == 2)
-        gemm_i8_kernel<2, 2><<<dim3(p.grid), dim3(256), 0, s>>>(a);
-    else if (p.MF == 2)
-        gemm_i8_kernel<2, 4><<<dim3(p.grid), dim3(256), 0, s>>>(a);
-    else if (p.NF == 2)
-        gemm_i8_kernel<4, 2><<<dim3(p.grid), dim3(256), 0, s>>>(a);
-    else
-        gemm_i8_kernel<4, 4><<<dim3(p.grid), dim3(256), 0, s>>>(a);
+    const size_t esz = ydt == W4_F32 ? 4 : 2;
+    a.vec_out = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((size_t)ldy * esz) % 16 == 0;
+    const dim3 g(p.grid), b(256);
+    if (p.ring) {
+        if (p.cfg == 0)
+            gemm_i8_ring_kernel<3, 4, 2><<<g, b, 0, s>>>(a);
+        else
+            gemm_i8_ring_kernel<1, 6, 2><<<g, b, 0, s>>>(a);
+    } else if (p.MF == 2 && p.NF == 2) {
+        gemm_i8_kernel<2, 2><<<g, b, 0, s>>>(a);
+    } else if (p.MF == 2) {
+        gemm_i8_kernel<2, 4><<<g, b, 0, s>>>(a);
+    } else if (p.NF == 2) {
+        gemm_i8_kernel<4, 2><<<g, b, 0, s>>>(a);
+    } else {
+        gemm_i8_kernel<4, 4><<<g, b, 0, s>>>(a);
+    }
     return hip_fail(hipGetLastError(), "int8 gemm launch");
 }
 
 void describe_i8(int M, int N, int K, char* buf, size_t len) {
-    const I8Plan p = plan_i8(M, N);
-    snprintf(buf, len, "int8 mfma 16x16x64 block %dx%d waves 2x2 stage 128 grid=%d (K=%d)", p.BM,
-             p.BN, p.grid, K);
+    const I8Plan p = plan_i8(M, N, K, K, K);
+    if (p.ring)
+        snprintf(buf, len,
+                 "int8 mfma 16x16x64 dma-ring block %dx%d waves 1x4 slots %d stage 64 x%d "
+                 "grid=%d (K=%d)",
+                 p.BM, p.BN, kI8RingCfgs[p.cfg].slots, kI8RingCfgs[p.cfg].per_barrier, p.grid,
+                 K);
+    else
+        snprintf(buf, len, "int8 mfma 16x16x64 block %dx%d waves 2x2 stage 128 grid=%d (K=%d)",
+                 p.BM, p.BN, p.grid, K);
 }
 
 }  // namespace w4

@@ -72,6 +72,31 @@ def test_gemm_i8_vs_exact(oracle_mod, M, N, K, out_dtype):
     assert np.all(np.abs(got - ref) <= bound + 1e-30)
 
 
+@pytest.mark.parametrize("ring", ["0", "1", "2"])
+def test_gemm_i8_every_tiling(oracle_mod, monkeypatch, ring):
+    """Every compiled int8 tiling (W4_I8_RING: 0 register-staged, 1 and 2 the
+    DMA-ring configurations) on one ragged case, bitwise equal to the default
+    dispatch and within the exact product's bound."""
+    import torch
+    device()
+    M, N, K = 150, 700, 1536
+    rng = np.random.default_rng(11)
+    Xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    Wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    xs = (rng.random(M) * 0.02 + 1e-3).astype(np.float32)
+    ws = (rng.random(N) * 0.02 + 1e-3).astype(np.float32)
+    note("int8 gemm tiling W4_I8_RING=%s M=%d N=%d K=%d" % (ring, M, N, K))
+    Yd = w4.gemm_i8(_t(Xq), _t(xs), _t(Wq), _t(ws), "f32")
+    monkeypatch.setenv("W4_I8_RING", ring)
+    Y = w4.gemm_i8(_t(Xq), _t(xs), _t(Wq), _t(ws), "f32")
+    torch.cuda.synchronize()
+    got = Y.cpu().numpy().astype(np.float64)
+    ref = oracle_mod.gemm_i8(Xq, xs, Wq, ws)
+    assert np.all(np.abs(got - ref) <= REL * np.abs(ref) + 1e-30)
+    # the int32 sums are exact and the scales apply in one order: bitwise equal
+    assert np.array_equal(Y.cpu().numpy(), Yd.cpu().numpy())
+
+
 @pytest.mark.parametrize("M", [8, 15, 16, 64, 512])
 def test_twin_switch(oracle_mod, M):
     """auto:16 -- below 16 rows the int4 product, at or above the int8 twin:
