@@ -203,7 +203,7 @@ int w4_fwht(const uint16_t* X, int ldx, uint16_t* Xo, int ldo, int M, int K,
     return launch_fwht(X, ldx, Xo, ldo, M, K, block, static_cast<hipStream_t>(stream));
 }
 
-// w4a16_gemm: largest row count that runs on the vector-ALU small-M kernel
+// w4a16_gemm: largest row count that always takes the small-M product
 constexpr int kGemmSmallMRows = 8;
 
 size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block) {
@@ -243,16 +243,18 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
         Xin = Xr;
         ld_in = K;
     }
-    // decode-shaped row counts stay on the vector-ALU kernels ([P2]
-    // "fastgemma": a GEMM of few rows is decode-shaped); on MI355X the
-    // matrix-core kernel, whose time is flat below 64 rows, wins from 9 rows
-    // on (measured at N = 12288, K = 1536: 8 rows 10.1 us on the small-M
-    // kernel, 9..16 rows 18..25 us there, 11.3 us on the matrix cores)
+    // Few rows are decode-shaped ([P2] "fastgemma"): the small-M product,
+    // which for the rotated formats (groups 256 and 512) multiplies one
+    // 16-row tile on the matrix cores and is then the fastest through 16 rows
+    // (measured at N = 12288, K = 1536: 5.6 us at 8 rows, 6.3 us at 16,
+    // against 11.3 us on the tiled matrix-core kernel); otherwise the
+    // vector-ALU small-M kernel up to 8 rows (10.1 us at 8, 18..25 us at
+    // 9..16) and the tiled kernel from 9 rows.
     if (M == 1) {
         const GemvTile t = pick_gemv_tile(N, K, group);
         return launch_gemv(t, packed, N, K, group, Xin, Y, ydt, s);
     }
-    if (M <= kGemmSmallMRows)
+    if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group)))
         return launch_smallm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
     return launch_mfma_gemm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
 }
@@ -442,7 +444,7 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) 
         const GemvTile t = pick_gemv_tile(N, K, group);
         snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d", t.generic ? "_generic" : "",
                  t.L, t.U, t.waves, t.grid);
-    } else if (M <= kGemmSmallMRows) {
+    } else if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group))) {
         describe_smallm(M, N, K, group, buf, len);
     } else {
         if (K % 256 != 0) return fail(W4_ERR_SHAPE, "describe: gemm needs K % 256 == 0");

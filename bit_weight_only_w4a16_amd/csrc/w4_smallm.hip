@@ -13,6 +13,7 @@
 // formed on the fly.  At this size the kernel is bound by vector ALU work
 // (one dot2 per two codes per row).
 #include <cstdio>
+#include <cstdlib>
 
 #include "w4_dispatch.h"
 
@@ -259,6 +260,189 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
     }
 }
 
+
+// ------------------------------------------------ matrix-core small M ---
+//
+// Rotated formats (groups 256 and 512), M <= 16: one 16-row MFMA tile holds
+// every activation row (rows past M repeat row M - 1 and are never stored),
+// so the matrix cores do the per-row work the vector-ALU kernel spends its
+// time on.  v_mfma_f32_16x16x32_bf16 (lane l holds A[l%16][8(l/16) + j],
+// B[8(l/16) + j][l%16], D[4(l/16) + r][l%16]); codes decoded to exact bf16
+// 128 + c, the offset chain (same MFMA against 136) subtracted per group, as
+// in the prefill kernels.
+//
+// A workgroup owns 16 * RG weight rows and splits K into KS slices: wave
+// (row group rg, slice ks) multiplies 16 rows by its 128 * NB slice of K.
+// Each wave loads all of its codes (16 bytes per lane per 128-K block; lane
+// group l/16 takes words 4(l/16) .. 4(l/16) + 3 of its row's block and uses
+// word t in MFMA step t, the activations read with the same K permutation)
+// before anything else, so a workgroup's whole weight stream is in flight at
+// once.  The activation rows are staged once per workgroup in LDS, 16-byte
+// chunk q of row m at position q ^ (m & 15) (fragment reads conflict-free).
+// The slices' results are added through LDS in slice order 0, 1, ..., so
+// the output is deterministic.
+struct SmqArgs {
+    const uint8_t* codes;    // N x K/2 bytes (device words)
+    const uint16_t* scales;  // N x G bf16
+    const uint16_t* X;       // M x K bf16, row stride ldx
+    void* Y;
+    int N, K, G, group, M, ldx, ldy, ydt;
+    int RG, KS;              // row groups and K slices per workgroup
+};
+constexpr int kSmqXPer = 8;                      // activation chunks staged per thread, at most
+constexpr size_t kSmqLds = 64 * 1024;            // activation rows + slice sums, at most
+
+template <int NB>
+__global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int nthr = blockDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 15, lk = lane >> 4;
+    const int rg = wave % a.RG, ks = wave / a.RG;
+    const int n0 = blockIdx.x * 16 * a.RG;
+    const int n = min(n0 + 16 * rg + li, a.N - 1);
+    constexpr int KR = 128 * NB;                 // K per wave
+    const int k0 = ks * KR;
+    const int CPR = a.K / 8;                     // 16-byte chunks per activation row
+    const int GW = KR / a.group;                 // groups per wave (1 or 2)
+
+    // codes and scales of this lane's row and slice: issued first
+    u32x4 q[NB];
+    const uint8_t* crow = a.codes + (size_t)n * (a.K / 2) + k0 / 2 + 16 * lk;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) q[u] = nt_load(reinterpret_cast<const u32x4*>(crow + 64 * u));
+    uint32_t sc[2];
+    sc[0] = gload(a.scales + (size_t)n * a.G + k0 / a.group);
+    sc[1] = gload(a.scales + (size_t)n * a.G + (k0 + KR - 1) / a.group);
+
+    // activation rows -> LDS (all loads before any store)
+    {
+        const int total = a.M * CPR;
+        u32x4 xv[kSmqXPer];
+#pragma unroll
+        for (int i = 0; i < kSmqXPer; ++i) {
+            const int e = tid + i * nthr;
+            if (e < total) {
+                const int m = e / CPR, c = e - m * CPR;
+                xv[i] = gload(reinterpret_cast<const u32x4*>(a.X + (size_t)m * a.ldx) + c);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kSmqXPer; ++i) {
+            const int e = tid + i * nthr;
+            if (e < total) {
+                const int m = e / CPR, c = e - m * CPR;
+                reinterpret_cast<u32x4*>(smem)[m * CPR + (c ^ (m & 15))] = xv[i];
+            }
+        }
+    }
+    __syncthreads();
+
+    const int xm = min(li, a.M - 1);             // A-operand row of this lane
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(smem) + (size_t)xm * CPR;
+    const int xsw = xm & 15;
+    const DecodeConsts k = decode_consts();
+    const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 tot = zero, acc = zero, a136 = zero;
+    const int bpg = a.group / 128;               // blocks per group
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const bool first = (u % bpg) == 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int cq = (k0 + 128 * u + 32 * lk + 8 * t) / 8;
+            const u32x4 xa = xrow[cq ^ xsw];
+            const uint32_t w = q[u][t];
+            const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k), decode_pair(w, 2, k),
+                              decode_pair(w, 3, k)};
+            const bool z = first && t == 0;
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                          __builtin_bit_cast(bf16x8, bv),
+                                                          z ? zero : acc, 0, 0, 0);
+            a136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                           __builtin_bit_cast(bf16x8, b136),
+                                                           z ? zero : a136, 0, 0, 0);
+        }
+        if ((u + 1) % bpg == 0) {
+            const float s = bf16_to_f32(sc[GW > 1 && u >= bpg ? 1 : 0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[r] = fmaf(s, acc[r] - a136[r], tot[r]);
+        }
+    }
+
+    // slices summed in order 0 .. KS - 1
+    f32x4* red = reinterpret_cast<f32x4*>(smem + (size_t)a.M * a.K * 2);
+    if (a.KS > 1) {
+        red[(ks * a.RG + rg) * 64 + lane] = tot;
+        __syncthreads();
+        if (ks != 0) return;
+        tot = red[rg * 64 + lane];
+        for (int j = 1; j < a.KS; ++j) {
+            const f32x4 o = red[(j * a.RG + rg) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[r] += o[r];
+        }
+    }
+    const int nn = n0 + 16 * rg + li;
+    if (nn < a.N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * lk + r;
+            if (m < a.M) store_out(a.Y, (size_t)m * a.ldy + nn, tot[r], a.ydt);
+        }
+    }
+}
+
+struct SmqPlan {
+    bool ok;
+    int NB, RG, KS, grid;
+    size_t lds;
+};
+
+// The matrix-core small-M plan, when the shape allows it: groups of 256 or
+// 512, each wave's K slice (<= 512) a whole number of groups, the activation
+// rows within the LDS budget.
+static SmqPlan plan_smq(int M, int N, int K, int group) {
+    SmqPlan p{};
+    p.ok = false;
+    if (M > 16 || (group != 256 && group != 512) || K % 128 != 0) return p;
+    const int G = K / group;
+    int KS = 0;
+    for (int ks = 1; ks <= 16 && ks <= G; ++ks)
+        if (G % ks == 0 && K / ks <= 512) {
+            KS = ks;
+            break;
+        }
+    if (KS == 0) return p;
+    int RG = 1;
+    for (int r = 4; r >= 1; --r)
+        if (r * KS <= 16 && (N + 16 * r - 1) / (16 * r) >= kNumCUs) {
+            RG = r;
+            break;
+        }
+    const size_t xl = (size_t)M * K * 2;
+    if (xl + (size_t)KS * RG * 64 * 16 > kSmqLds ||
+        (size_t)M * (K / 8) > (size_t)kSmqXPer * 64 * RG * KS)
+        return p;
+    p.ok = true;
+    p.KS = KS;
+    p.RG = RG;
+    p.NB = K / KS / 128;
+    p.grid = (N + 16 * RG - 1) / (16 * RG);
+    p.lds = xl + (size_t)KS * RG * 64 * 16;
+    return p;
+}
+
+bool smallm_mfma_applies(int M, int N, int K, int group) {
+    const char* e = getenv("W4_SMALLM_MFMA");
+    return plan_smq(M, N, K, group).ok && !(e && e[0] == '0' && e[1] == 0);
+}
+
 static size_t smallm_lds(int M, int K) {
     return (size_t)M * K * 2 + (size_t)M * (K / 32) * 4;
 }
@@ -328,6 +512,32 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
     a.ldy = ldy;
     a.ydt = ydt;
     a.K = K;
+    const SmqPlan mp = plan_smq(M, N, K, group);
+    if (smallm_mfma_applies(M, N, K, group)) {   // W4_SMALLM_MFMA=0: vector ALU only
+        SmqArgs b;
+        b.codes = static_cast<const uint8_t*>(packed);
+        b.scales = a.scales;
+        b.X = X;
+        b.Y = Y;
+        b.N = N;
+        b.K = K;
+        b.G = K / group;
+        b.group = group;
+        b.M = M;
+        b.ldx = ldx;
+        b.ldy = ldy;
+        b.ydt = ydt;
+        b.RG = mp.RG;
+        b.KS = mp.KS;
+        const dim3 g(mp.grid), bl(64 * mp.RG * mp.KS);
+        switch (mp.NB) {
+            case 1: smallm_mfma_kernel<1><<<g, bl, mp.lds, s>>>(b); break;
+            case 2: smallm_mfma_kernel<2><<<g, bl, mp.lds, s>>>(b); break;
+            case 3: smallm_mfma_kernel<3><<<g, bl, mp.lds, s>>>(b); break;
+            default: smallm_mfma_kernel<4><<<g, bl, mp.lds, s>>>(b); break;
+        }
+        return hip_fail(hipGetLastError(), "smallM launch");
+    }
     const size_t shm = smallm_lds(M, K);
     const bool lds = shm <= kSmLdsMax;
     int L = 16;
@@ -353,7 +563,12 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
 }
 
 void describe_smallm(int M, int N, int K, int group, char* buf, size_t len) {
-    (void)group;
+    const SmqPlan mp = plan_smq(M, N, K, group);
+    if (smallm_mfma_applies(M, N, K, group)) {
+        snprintf(buf, len, "smallm mfma 16x16x32 rows %d x slices %d (K %d each) grid=%d",
+                 16 * mp.RG, mp.KS, 128 * mp.NB, mp.grid);
+        return;
+    }
     const size_t shm = smallm_lds(M, K);
     int L = 16;
     const int U = smallm_fast_shape(K / 32, &L);

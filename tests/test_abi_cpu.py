@@ -236,8 +236,11 @@ def test_describe_dispatch_tile_table(L):
     assert w4.describe_dispatch(1, 100, 768, 256).startswith("gemv_generic")
     assert w4.describe_dispatch(1, 100, 20000, 32).startswith("gemv_generic")
     assert w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm")
-    assert w4.describe_dispatch(9, 12288, 1536, 256).startswith("mfma")
+    assert w4.describe_dispatch(9, 12288, 1536, 256).startswith("smallm mfma")
+    assert w4.describe_dispatch(16, 12288, 1536, 256).startswith("smallm mfma")
+    assert w4.describe_dispatch(8, 12288, 1536, 32).startswith("smallm MT=8")
     assert w4.describe_dispatch(16, 12288, 1536, 32).startswith("mfma")
+    assert w4.describe_dispatch(17, 12288, 1536, 256).startswith("mfma")
     assert w4.describe_dispatch(64, 12288, 1536, 256).startswith("mfma")
     with pytest.raises(w4.W4Error):
         w4.describe_dispatch(1, 12288, 1500, 32)

@@ -87,6 +87,38 @@ def test_smallm_vs_oracle(oracle_mod, M, N, K, g):
         assert_within(Y, Yr, A, out_dtype, "smallM M=%d" % M)
 
 
+@pytest.mark.parametrize("M", [2, 8, 16])
+@pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (129, 1536, 512)])
+def test_smallm_vector_alu_path(oracle_mod, monkeypatch, M, N, K, g):
+    """The vector-ALU small-M kernels on the rotated formats, which the
+    matrix-core small-M kernel otherwise takes (W4_SMALLM_MFMA=0 keeps them)."""
+    monkeypatch.setenv("W4_SMALLM_MFMA", "0")
+    note("smallM vector ALU M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    assert not w4.describe_dispatch(M, N, K, g).startswith("smallm mfma") or M > 8
+    case = synth.make_case("smallv", N, K, g, M, 7 * M + N + K, "bf16")
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    Y = from_dev(w4.gemm_smallM(packed, N, K, g, X, "f32"))
+    Yr, A = oracle_mod.gemm_bf16(case.P, case.S, N, K, g, case.X, threads=16)
+    assert_within(Y, Yr, A, "f32", "smallM VALU M=%d" % M)
+
+
+def test_smallm_mfma_code8_columns_exact_zero():
+    """Columns whose codes are all 8 are exactly zero through the matrix-core
+    small-M kernel (the offset chain goes through the same arithmetic)."""
+    M, N, K, g = 8, 200, 1536, 256
+    assert w4.describe_dispatch(M, N, K, g).startswith("smallm mfma")
+    rng = np.random.default_rng(6)
+    P, S = synth.draw_weights(rng, N, K, g)
+    P[3, :] = 0x88888888
+    P[150, :] = 0x88888888
+    packed = upload_packed(P, S, N, K, g)
+    X = to_dev_bf16(synth.draw_activations(rng, M, K, outlier_frac=0.01))
+    Y = from_dev(w4.gemm_smallM(packed, N, K, g, X, "f32"))
+    assert np.all(Y[:, 3] == 0.0) and np.all(Y[:, 150] == 0.0)
+    assert np.all(Y[:, 4] != 0.0)
+
+
 def test_smallm_rows_equal_gemv_bitwise():
     """Each row of the small-M product equals the batch-1 GEMV of that row
     within fp32 rounding of a different summation order; row m only depends
