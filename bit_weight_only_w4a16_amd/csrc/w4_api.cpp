@@ -205,6 +205,8 @@ int w4_fwht(const uint16_t* X, int ldx, uint16_t* Xo, int ldo, int M, int K,
 
 // w4a16_gemm: largest row count that always takes the small-M product
 constexpr int kGemmSmallMRows = 8;
+// w4a16_gemm: largest row count whose transform runs inside the small-M kernel
+constexpr int kGemmFusedTransformRows = 4;
 
 size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block) {
     if (had_block == 0 || M < 1 || K < 1) return 0;
@@ -235,6 +237,15 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
         W4_TRY(check_in16(workspace, "workspace"));
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // The 512-block transform of up to 4 rows runs inside the matrix-core
+    // small-M kernel, on the rows it stages anyway (bitwise the same rows the
+    // transform kernel writes; the workspace goes unused).  Every workgroup
+    // transforms all rows itself, so from 8 rows on the separate transform
+    // kernel is faster (measured at N = 12288, K = 1536: fused 6.7 / 7.9 /
+    // 9.8 us at 2 / 4 / 8 rows, separate 8.1 / 8.3 / 8.7 us).
+    if (had_block == 512 && M >= 2 && M <= kGemmFusedTransformRows &&
+        smallm_mfma_applies(M, N, K, group))
+        return launch_smallm(packed, N, K, group, M, X, ldx, Y, ldy, ydt, s, 512);
     const uint16_t* Xin = X;
     int ld_in = ldx;
     if (had_block) {

@@ -26,9 +26,11 @@ int launch_gemv(const GemvTile& t, const void* packed, int N, int K, int group,
 int launch_pack(const uint32_t* P, const uint16_t* S, int N, int K, int group,
                 void* out, hipStream_t s);
 
+// had_block: 0, or 512 to apply the blockwise transform to X inside the
+// matrix-core small-M kernel (only where smallm_mfma_applies)
 int launch_smallm(const void* packed, int N, int K, int group, int M,
                   const uint16_t* X, int ldx, void* Y, int ldy, int ydt,
-                  hipStream_t s);
+                  hipStream_t s, int had_block = 0);
 void describe_smallm(int M, int N, int K, int group, char* buf, size_t len);
 // the matrix-core small-M kernel takes this shape (rotated groups, M <= 16)
 bool smallm_mfma_applies(int M, int N, int K, int group);

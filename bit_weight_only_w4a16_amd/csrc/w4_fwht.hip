@@ -11,6 +11,7 @@
 // stay inside a lane, spans h >= E pair lane l with lane l ^ (h / E).  fp32
 // arithmetic, one scaling at the end, bf16 result rounded to nearest even.
 #include "w4_dispatch.h"
+#include "w4_fwht.h"
 
 namespace w4 {
 
@@ -44,27 +45,7 @@ __global__ __launch_bounds__(256) void fwht_kernel(const uint16_t* X, int ldx,
 #pragma unroll
         for (int e = 0; e < E; ++e) v[e] = active ? bf16_to_f32(src[e]) : 0.f;
     }
-    // spans inside a lane
-#pragma unroll
-    for (int h = 1; h < E; h *= 2) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if ((e & h) == 0) {
-                const float a = v[e], c = v[e + h];
-                v[e] = a + c;
-                v[e + h] = a - c;
-            }
-        }
-    }
-    // spans across lanes: partner lane ^ d, d = h / E
-    for (int d = 1; d < lanes; d *= 2) {
-        const bool upper = (lane & d) != 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float o = __shfl_xor(v[e], d, 64);
-            v[e] = upper ? (o - v[e]) : (v[e] + o);
-        }
-    }
+    fwht_block<E>(v, lane, lanes);
     if (active) {
         uint16_t* dst = Xo + (size_t)m * ldo + (size_t)b * block + (size_t)lane * E;
         if (E >= 8) {

@@ -16,6 +16,7 @@
 #include <cstdlib>
 
 #include "w4_dispatch.h"
+#include "w4_fwht.h"
 
 namespace w4 {
 
@@ -288,11 +289,13 @@ struct SmqArgs {
     void* Y;
     int N, K, G, group, M, ldx, ldy, ydt;
     int RG, KS;              // row groups and K slices per workgroup
+    int had;                 // 512: transform the staged rows (blockwise FWHT) first (HAD)
+    float hscale;            // 512^-1/2
 };
-constexpr int kSmqXPer = 8;                      // activation chunks staged per thread, at most
+constexpr int kSmqXPer = 8;                      // activation chunks per thread and round
 constexpr size_t kSmqLds = 64 * 1024;            // activation rows + slice sums, at most
 
-template <int NB>
+template <int NB, bool HAD>
 __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -319,13 +322,14 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
     sc[0] = gload(a.scales + (size_t)n * a.G + k0 / a.group);
     sc[1] = gload(a.scales + (size_t)n * a.G + (k0 + KR - 1) / a.group);
 
-    // activation rows -> LDS (all loads before any store)
-    {
-        const int total = a.M * CPR;
+    // activation rows -> LDS, in rounds of kSmqXPer chunks per thread (all of
+    // a round's loads before its stores)
+    const int total = a.M * CPR;
+    auto stage_round = [&](int e0) {
         u32x4 xv[kSmqXPer];
 #pragma unroll
         for (int i = 0; i < kSmqXPer; ++i) {
-            const int e = tid + i * nthr;
+            const int e = e0 + tid + i * nthr;
             if (e < total) {
                 const int m = e / CPR, c = e - m * CPR;
                 xv[i] = gload(reinterpret_cast<const u32x4*>(a.X + (size_t)m * a.ldx) + c);
@@ -333,14 +337,46 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < kSmqXPer; ++i) {
-            const int e = tid + i * nthr;
+            const int e = e0 + tid + i * nthr;
             if (e < total) {
                 const int m = e / CPR, c = e - m * CPR;
                 reinterpret_cast<u32x4*>(smem)[m * CPR + (c ^ (m & 15))] = xv[i];
             }
         }
-    }
+    };
+    if (total <= kSmqXPer * nthr)
+        stage_round(0);
+    else
+        for (int e0 = 0; e0 < total; e0 += kSmqXPer * nthr) stage_round(e0);
     __syncthreads();
+
+    // The run-time Hadamard transform of the staged rows, in place: one wave
+    // per (row, 512-block), lane l holding the block's 16-byte chunk l, with
+    // the transform kernel's butterflies, scale and rounding, so the rows
+    // are bitwise those that kernel writes.
+    if (HAD) {
+        const int nbk = a.K / 512;
+        const int nwv = nthr >> 6;
+        for (int job = wave; job < a.M * nbk; job += nwv) {
+            const int m = job / nbk, b = job - m * nbk;
+            u32x4* p = reinterpret_cast<u32x4*>(smem) + m * CPR + ((b * 64 + lane) ^ (m & 15));
+            const u32x4 w = *p;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(w[i] << 16);
+                v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+            fwht_block<8>(v, lane, 64);
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = f32_to_bf16_rne(v[2 * i] * a.hscale) |
+                       (f32_to_bf16_rne(v[2 * i + 1] * a.hscale) << 16);
+            *p = o;
+        }
+        __syncthreads();
+    }
 
     const int xm = min(li, a.M - 1);             // A-operand row of this lane
     const u32x4* xrow = reinterpret_cast<const u32x4*>(smem) + (size_t)xm * CPR;
@@ -426,9 +462,7 @@ static SmqPlan plan_smq(int M, int N, int K, int group) {
             break;
         }
     const size_t xl = (size_t)M * K * 2;
-    if (xl + (size_t)KS * RG * 64 * 16 > kSmqLds ||
-        (size_t)M * (K / 8) > (size_t)kSmqXPer * 64 * RG * KS)
-        return p;
+    if (xl + (size_t)KS * RG * 64 * 16 > kSmqLds) return p;
     p.ok = true;
     p.KS = KS;
     p.RG = RG;
@@ -496,7 +530,9 @@ static void launch_mt(bool lds, dim3 g, dim3 b, size_t shm, hipStream_t s,
 
 int launch_smallm(const void* packed, int N, int K, int group, int M,
                   const uint16_t* X, int ldx, void* Y, int ldy, int ydt,
-                  hipStream_t s) {
+                  hipStream_t s, int had_block) {
+    if (had_block && (had_block != 512 || K % 512 != 0 || !smallm_mfma_applies(M, N, K, group)))
+        return hip_fail(hipErrorInvalidValue, "smallM: fused transform needs the matrix-core path");
     SmallMArgs a;
     a.codes = static_cast<const u32x4*>(packed);
     a.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) +
@@ -529,12 +565,23 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
         b.ydt = ydt;
         b.RG = mp.RG;
         b.KS = mp.KS;
+        b.had = had_block;
+        b.hscale = (float)(1.0 / __builtin_sqrt(512.0));   // as the transform kernel
         const dim3 g(mp.grid), bl(64 * mp.RG * mp.KS);
-        switch (mp.NB) {
-            case 1: smallm_mfma_kernel<1><<<g, bl, mp.lds, s>>>(b); break;
-            case 2: smallm_mfma_kernel<2><<<g, bl, mp.lds, s>>>(b); break;
-            case 3: smallm_mfma_kernel<3><<<g, bl, mp.lds, s>>>(b); break;
-            default: smallm_mfma_kernel<4><<<g, bl, mp.lds, s>>>(b); break;
+        if (had_block) {
+            switch (mp.NB) {
+                case 1: smallm_mfma_kernel<1, true><<<g, bl, mp.lds, s>>>(b); break;
+                case 2: smallm_mfma_kernel<2, true><<<g, bl, mp.lds, s>>>(b); break;
+                case 3: smallm_mfma_kernel<3, true><<<g, bl, mp.lds, s>>>(b); break;
+                default: smallm_mfma_kernel<4, true><<<g, bl, mp.lds, s>>>(b); break;
+            }
+        } else {
+            switch (mp.NB) {
+                case 1: smallm_mfma_kernel<1, false><<<g, bl, mp.lds, s>>>(b); break;
+                case 2: smallm_mfma_kernel<2, false><<<g, bl, mp.lds, s>>>(b); break;
+                case 3: smallm_mfma_kernel<3, false><<<g, bl, mp.lds, s>>>(b); break;
+                default: smallm_mfma_kernel<4, false><<<g, bl, mp.lds, s>>>(b); break;
+            }
         }
         return hip_fail(hipGetLastError(), "smallM launch");
     }

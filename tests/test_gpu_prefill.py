@@ -103,6 +103,24 @@ def test_smallm_vector_alu_path(oracle_mod, monkeypatch, M, N, K, g):
     assert_within(Y, Yr, A, "f32", "smallM VALU M=%d" % M)
 
 
+@pytest.mark.parametrize("M", [2, 3, 4, 8, 16])
+def test_smallm_fused_transform_bitwise(M):
+    """With had_block = 512 the transform runs inside the matrix-core small-M
+    kernel (up to 4 rows) or in the transform kernel before it (more rows):
+    both bitwise equal to the transform kernel followed by the small-M
+    product."""
+    N, K, g = 1000, 1536, 256
+    assert w4.describe_dispatch(M, N, K, g).startswith("smallm mfma")
+    rng = np.random.default_rng(40 + M)
+    P, S = synth.draw_weights(rng, N, K, g)
+    packed = upload_packed(P, S, N, K, g)
+    X = to_dev_bf16(synth.draw_activations(rng, M, K, outlier_frac=0.01))
+    note("fused transform small-M M=%d" % M)
+    Yf = from_dev(w4.gemm(packed, N, K, g, X, had_block=512, out_dtype="f32"))
+    Ys = from_dev(w4.gemm_smallM(packed, N, K, g, w4.fwht(X, 512), "f32"))
+    assert np.array_equal(Yf, Ys)
+
+
 def test_smallm_mfma_code8_columns_exact_zero():
     """Columns whose codes are all 8 are exactly zero through the matrix-core
     small-M kernel (the offset chain goes through the same arithmetic)."""
