@@ -72,7 +72,7 @@ enum w4_status {
     W4_ERR_SHAPE = -2,        /* N, K, M, group, block or size out of range  */
     W4_ERR_ALIGN = -3,        /* pointer or leading dimension misaligned     */
     W4_ERR_DTYPE = -4,        /* output dtype not W4_F32 / W4_BF16           */
-    W4_ERR_UNSUPPORTED = -5,  /* valid request this build does not serve     */
+    W4_ERR_UNSUPPORTED = -5,  /* valid request the library does not serve   */
     W4_ERR_HIP = -6,          /* a HIP runtime call failed                   */
     W4_ERR_NOMEM = -7,        /* allocation failed (sweep creation only)     */
     W4_ERR_ARCH = -8,         /* current device is not gfx950                */
