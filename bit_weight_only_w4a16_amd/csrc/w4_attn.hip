@@ -227,8 +227,9 @@ void attn_split_kernel(AttnArgs a) {
 
 // Workgroup-wide reductions over the merge kernel's threads in a fixed tree
 // order (the same on every run).
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDims = 16;                           // dims per merge workgroup
+constexpr int kMergeRows = kMergeThreads / kMergeDims;   // partial strides per dim
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
     red[threadIdx.x] = v;
@@ -247,9 +248,11 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 
 // out[h][d] = sum_w O_w[h][d] e_w / sum_w l_w e_w, e_w = 2^(m_w - M), M = max_w m_w
 // (e_w = 0 for a partial that attended nothing); NaN when no slot was attended.
-// Workgroup (h, 64-dim block) of 16 waves: the weights e_w are computed once
-// into LDS; wave k sums the partials w = k, k + 16, ... for its 64 dims, eight
-// loads in flight and no branches, and the 16 wave sums are added in order.
+// Workgroup (h, 16-dim block), 256 threads: the weights e_w are computed once
+// into LDS; thread (r, j) sums the partials w = r, r + 16, ... for dim j,
+// eight loads in flight and no branches, and the 16 sums of a dim are added
+// in order r = 0..15.  (A 16-dim block gives 256 workgroups at D = 512, so
+// the partials are read by as many CUs.)
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* __restrict__ part,
                                                                   int nwg,
@@ -257,10 +260,11 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* 
                                                                   int odt) {
     __shared__ float ew[kAttnMaxWG];
     __shared__ float red[kMergeThreads];
-    __shared__ float wsum[kMergeWaves][64];
+    __shared__ float psum[kMergeRows][kMergeDims];
     const int h = blockIdx.x;
-    const int d = blockIdx.y * 64 + (threadIdx.x & 63);
-    const int wave = threadIdx.x >> 6;
+    const int dl = threadIdx.x % kMergeDims;
+    const int pr = threadIdx.x / kMergeDims;
+    const int d = blockIdx.y * kMergeDims + dl;
     const int ps = part_stride(D);
 
     float mloc = -__builtin_inff();
@@ -276,10 +280,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* 
     }
     const float L = block_reduce(lloc, red, false);  // ends with a barrier: ew[] complete
 
-    constexpr int S = kMergeWaves;
+    constexpr int S = kMergeRows;
     float o = 0.f;
     const float* col = part + 32 + (size_t)h * D + d;
-    int w = wave;
+    int w = pr;
     for (; w + 7 * S < nwg; w += 8 * S) {
         float v[8];
 #pragma unroll
@@ -288,13 +292,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* 
         for (int u = 0; u < 8; ++u) o += v[u] * ew[w + u * S];
     }
     for (; w < nwg; w += S) o += gload(col + (size_t)w * ps) * ew[w];
-    wsum[wave][threadIdx.x & 63] = o;
+    psum[pr][dl] = o;
     __syncthreads();
-    if (wave == 0) {
+    if (threadIdx.x < kMergeDims) {
         const int t = threadIdx.x;
-        float tot = wsum[0][t];
+        float tot = psum[0][t];
 #pragma unroll
-        for (int k = 1; k < kMergeWaves; ++k) tot += wsum[k][t];
+        for (int k = 1; k < kMergeRows; ++k) tot += psum[k][t];
         const float v = M == -__builtin_inff() ? __builtin_nanf("") : tot / L;
         store_out(out, (size_t)h * D + d, v, odt);
     }
@@ -362,14 +366,14 @@ int launch_attn_decode(const uint16_t* q, const uint16_t* K, int ldk, const uint
             attn_split_kernel<512, true><<<g, b, 0, s>>>(a);
         else
             attn_split_kernel<512, false><<<g, b, 0, s>>>(a);
-        attn_merge_kernel<512><<<dim3(kAttnHeads, 512 / 64), dim3(kMergeThreads), 0, s>>>(
+        attn_merge_kernel<512><<<dim3(kAttnHeads, 512 / kMergeDims), dim3(kMergeThreads), 0, s>>>(
             a.part, a.nwg, out, odt);
     } else {
         if (pos)
             attn_split_kernel<256, true><<<g, b, 0, s>>>(a);
         else
             attn_split_kernel<256, false><<<g, b, 0, s>>>(a);
-        attn_merge_kernel<256><<<dim3(kAttnHeads, 256 / 64), dim3(kMergeThreads), 0, s>>>(
+        attn_merge_kernel<256><<<dim3(kAttnHeads, 256 / kMergeDims), dim3(kMergeThreads), 0, s>>>(
             a.part, a.nwg, out, odt);
     }
     return hip_fail(hipGetLastError(), "attention launch");
