@@ -248,16 +248,21 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 
 // out[h][d] = sum_w O_w[h][d] e_w / sum_w l_w e_w, e_w = 2^(m_w - M), M = max_w m_w
 // (e_w = 0 for a partial that attended nothing); NaN when no slot was attended.
-// Workgroup (h, 16-dim block), 256 threads: the weights e_w are computed once
-// into LDS; thread (r, j) sums the partials w = r, r + 16, ... for dim j,
-// eight loads in flight and no branches, and the 16 sums of a dim are added
-// in order r = 0..15.  (A 16-dim block gives 256 workgroups at D = 512, so
-// the partials are read by as many CUs.)
-template <int D>
+// Workgroup (h, 16-dim block), 256 threads.  Every load goes out first: thread
+// (r, j) takes O of the partials w = r, r + 16, ... (at most 16 * NV partials;
+// NV is sized to the launch's partial count) for dim j into registers, and m_w, l_w of its share of partials, so the
+// merge costs one memory round trip.  Then M and the weights e_w (once, into
+// LDS), the thread's sum in the order w = r, r + 16, ..., and the 16 sums of a
+// dim added in order r = 0..15.  (A 16-dim block gives 256 workgroups at
+// D = 512, so the partials are read by as many CUs.)
+template <int D, int NV>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* __restrict__ part,
                                                                   int nwg,
                                                                   void* __restrict__ out,
                                                                   int odt) {
+    constexpr int S = kMergeRows;
+    constexpr int NM = kAttnMaxWG / kMergeThreads;       // (m, l) pairs per thread, at most
+    static_assert(NV * S <= kAttnMaxWG && NM * kMergeThreads == kAttnMaxWG, "merge split");
     __shared__ float ew[kAttnMaxWG];
     __shared__ float red[kMergeThreads];
     __shared__ float psum[kMergeRows][kMergeDims];
@@ -267,31 +272,40 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* 
     const int d = blockIdx.y * kMergeDims + dl;
     const int ps = part_stride(D);
 
+    const float* col = part + 32 + (size_t)h * D + d;
+    float v[NV], mv[NM], lv[NM];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int w = pr + u * S;
+        v[u] = w < nwg ? gload(col + (size_t)w * ps) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {
+        const int w = threadIdx.x + u * kMergeThreads;
+        mv[u] = w < nwg ? gload(part + (size_t)w * ps + h) : -__builtin_inff();
+        lv[u] = w < nwg ? gload(part + (size_t)w * ps + 16 + h) : 0.f;
+    }
+
     float mloc = -__builtin_inff();
-    for (int w = threadIdx.x; w < nwg; w += kMergeThreads)
-        mloc = fmaxf(mloc, gload(part + (size_t)w * ps + h));
+#pragma unroll
+    for (int u = 0; u < NM; ++u) mloc = fmaxf(mloc, mv[u]);
     const float M = block_reduce(mloc, red, true);
     float lloc = 0.f;
-    for (int w = threadIdx.x; w < nwg; w += kMergeThreads) {
-        const float mw = gload(part + (size_t)w * ps + h);
-        const float e = mw == -__builtin_inff() ? 0.f : exp2f(mw - M);
-        ew[w] = e;
-        lloc += gload(part + (size_t)w * ps + 16 + h) * e;
+#pragma unroll
+    for (int u = 0; u < NM; ++u) {
+        const int w = threadIdx.x + u * kMergeThreads;
+        const float e = mv[u] == -__builtin_inff() ? 0.f : exp2f(mv[u] - M);
+        if (w < nwg) ew[w] = e;
+        lloc += lv[u] * e;
     }
     const float L = block_reduce(lloc, red, false);  // ends with a barrier: ew[] complete
 
-    constexpr int S = kMergeRows;
     float o = 0.f;
-    const float* col = part + 32 + (size_t)h * D + d;
-    int w = pr;
-    for (; w + 7 * S < nwg; w += 8 * S) {
-        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = gload(col + (size_t)(w + u * S) * ps);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o += v[u] * ew[w + u * S];
+    for (int u = 0; u < NV; ++u) {
+        const int w = pr + u * S;
+        if (w < nwg) o += v[u] * ew[w];
     }
-    for (; w < nwg; w += S) o += gload(col + (size_t)w * ps) * ew[w];
     psum[pr][dl] = o;
     __syncthreads();
     if (threadIdx.x < kMergeDims) {
@@ -299,8 +313,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* 
         float tot = psum[0][t];
 #pragma unroll
         for (int k = 1; k < kMergeRows; ++k) tot += psum[k][t];
-        const float v = M == -__builtin_inff() ? __builtin_nanf("") : tot / L;
-        store_out(out, (size_t)h * D + d, v, odt);
+        const float res = M == -__builtin_inff() ? __builtin_nanf("") : tot / L;
+        store_out(out, (size_t)h * D + d, res, odt);
     }
 }
 
@@ -338,6 +352,18 @@ __global__ __launch_bounds__(256) void attn_store_kv_kernel(const uint16_t* __re
     }
 }
 
+// the merge's per-thread O loads: 16 * NV partials cover nwg
+template <int D>
+static void launch_merge(const float* part, int nwg, void* out, int odt, hipStream_t s) {
+    const dim3 g(kAttnHeads, D / kMergeDims), b(kMergeThreads);
+    if (nwg <= kMergeRows)
+        attn_merge_kernel<D, 1><<<g, b, 0, s>>>(part, nwg, out, odt);
+    else if (nwg <= 8 * kMergeRows)
+        attn_merge_kernel<D, 8><<<g, b, 0, s>>>(part, nwg, out, odt);
+    else
+        attn_merge_kernel<D, kAttnMaxWG / kMergeRows><<<g, b, 0, s>>>(part, nwg, out, odt);
+}
+
 size_t attn_workspace_bytes(int T, int D) {
     const int tiles = (T + kAttnTile - 1) / kAttnTile;
     const int nwg = tiles < kAttnMaxWG ? tiles : kAttnMaxWG;
@@ -366,15 +392,13 @@ int launch_attn_decode(const uint16_t* q, const uint16_t* K, int ldk, const uint
             attn_split_kernel<512, true><<<g, b, 0, s>>>(a);
         else
             attn_split_kernel<512, false><<<g, b, 0, s>>>(a);
-        attn_merge_kernel<512><<<dim3(kAttnHeads, 512 / kMergeDims), dim3(kMergeThreads), 0, s>>>(
-            a.part, a.nwg, out, odt);
+        launch_merge<512>(a.part, a.nwg, out, odt, s);
     } else {
         if (pos)
             attn_split_kernel<256, true><<<g, b, 0, s>>>(a);
         else
             attn_split_kernel<256, false><<<g, b, 0, s>>>(a);
-        attn_merge_kernel<256><<<dim3(kAttnHeads, 256 / kMergeDims), dim3(kMergeThreads), 0, s>>>(
-            a.part, a.nwg, out, odt);
+        launch_merge<256>(a.part, a.nwg, out, odt, s);
     }
     return hip_fail(hipGetLastError(), "attention launch");
 }
