@@ -294,6 +294,10 @@ def main():
                     help="for hardware-counter runs: only --steps replays of the timed "
                          "mode, then three 1 GiB probe copies (the calibration kernel); "
                          "prints nothing")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="M",
+                    help="for hardware-counter runs: only --steps calls of the prefill "
+                         "product (group 256, N=12288, K=1536, no transform) at M rows; "
+                         "prints nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU; this library has no multi-GPU path "
@@ -306,6 +310,18 @@ def main():
 
     dev = torch.device("cuda:0")
     w4.device_check()
+    if args.prefill_only:
+        import numpy as np
+        c = synth.prefill_g256(args.prefill_only)
+        P = torch.from_numpy(c.P.view(np.int32)).to(dev)
+        S = torch.from_numpy(c.S.view(np.int16)).to(dev)
+        packed = w4.pack(P, S, c.N, c.K, c.group)
+        X = torch.from_numpy(c.X.view(np.int16)).to(dev).view(torch.bfloat16)
+        Y = torch.empty((c.M, c.N), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.steps):
+            w4.gemm(packed, c.N, c.K, c.group, X, 0, "bf16", out=Y)
+        torch.cuda.synchronize()
+        return
     log("generating and packing the sweep")
     cases, ops = upload_sweep(torch, w4, synth, dev)
     weight_bytes = sum(c.weight_bytes for c in cases)
