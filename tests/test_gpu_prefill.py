@@ -237,11 +237,15 @@ def test_matrix_core_code8_columns_exact_zero():
     assert np.all(Y[:, 6] != 0.0)
 
 
-def test_matrix_core_deterministic():
-    M, N, K, g = 512, 1024, 1536, 256
-    case = synth.make_case("det", N, K, g, M, 9, "bf16")
+@pytest.mark.parametrize("M,had", [(512, 0), (64, 0), (16, 512), (8, 0), (3, 512)])
+def test_matrix_core_deterministic(M, had):
+    """Run to run bitwise: the tiled matrix-core kernels (512 and 64 rows) and
+    the matrix-core small-M kernel (with and without the fused transform)."""
+    N, K, g = 1024, 1536, 256
+    case = synth.make_case("det", N, K, g, M, 9 + M, "bf16")
     packed = upload_packed(case.P, case.S, N, K, g)
     X = to_dev_bf16(case.X)
-    a = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
-    b = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    a = from_dev(w4.gemm(packed, N, K, g, X, had_block=had, out_dtype="f32"))
+    for _ in range(2):
+        b = from_dev(w4.gemm(packed, N, K, g, X, had_block=had, out_dtype="f32"))
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
