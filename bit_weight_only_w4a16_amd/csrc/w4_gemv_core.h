@@ -79,7 +79,7 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
 
     uint32_t xr[U][16];
     float xb[U];
-    load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
+    if (!BATCH) load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
 
     // chunk offsets, scale dword offsets and scale half selectors per chunk
     int coff[U], soff[U];
@@ -153,6 +153,10 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         }
     };
 
+    // Load order at the start of a range: a stand-alone grid-stride walk loads
+    // the activation slice first, so its offset terms are computed while the
+    // codes arrive; a BATCH walk (one of several ranges a wave runs in a row)
+    // issues the first row group's codes first, which measured faster there.
     // The prefetch is never skipped: on the last row group it re-reads the
     // current one (lines just fetched, so a cache hit) instead of branching.
     // A load issued under a branch that rejoins would leave the wait-count
@@ -164,6 +168,7 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         u32x4 qa[U], qb[U];
         uint32_t sa[U], sb[U];
         load(rg, qa, sa);
+        if (BATCH) load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
         while (true) {
             load(next(rg, step), qb, sb);
             finish(rg, qa, sa);
@@ -181,6 +186,7 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         uint32_t sa[U], sb[U], sc[U];
         load(rg, qa, sa);
         load(next(rg, step), qb, sb);
+        if (BATCH) load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
         while (true) {
             load(next(rg, 2 * step), qc, sc);
             finish(rg, qa, sa);

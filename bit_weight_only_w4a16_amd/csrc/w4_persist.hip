@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kPwThreads) void ordered_kernel(const SweepOp* __re
 }
 
 // STREAM mode: independent ops.  The concatenated tile list of all ops is cut
-// into one contiguous, byte-balanced range per wave (range[w] .. range[w+1]),
+// into one contiguous, byte-balanced range per wave (range[w] .. range[w+1];
+// range[waves + 1 + w] is the op that holds tile range[w]),
 // so each wave streams about total/waves bytes, crossing only the few op
 // boundaries inside its range.  Within one op the wave runs the batch-1 GEMV
 // inner loop over consecutive row groups (activation slice in registers, next
@@ -281,8 +282,7 @@ void stream_kernel(const SweepOp* __restrict__ ops, int n_ops, const int* __rest
     if (tb >= te) return;
     const DecodeConsts k = decode_consts();
 
-    int i = 0;
-    while (i < n_ops && ops[i].base + ops[i].NG <= tb) ++i;
+    int i = range[gridDim.x * kPwWaves + 1 + gw];  // the op that holds tile tb
     for (int t = tb; t < te && i < n_ops; ++i) {
         const SweepOp op = ops[i];
         const int end = te < op.base + op.NG ? te : op.base + op.NG;

@@ -127,8 +127,9 @@ static int setup_persistent(w4_sweep* h) {
 
     // STREAM partition: wave b starts at the first tile whose starting byte
     // offset reaches b * total / waves (tiles of one op are equal-sized)
+    // Then, for each wave, the index of the op that holds its first tile.
     const int parts = GW;
-    std::vector<int> range(parts + 1);
+    std::vector<int> range(2 * (size_t)parts + 1);
     {
         double total_bytes = 0.0;
         for (const w4_gemv_op& o : h->ops)
@@ -146,10 +147,15 @@ static int setup_persistent(w4_sweep* h) {
         while (b <= parts) range[b++] = (int)tiles_before;
         range[0] = 0;
         range[parts] = (int)tiles_before;
+        int i = 0;
+        for (int w = 0; w < parts; ++w) {
+            while (i < n && tab[i].base + tab[i].NG <= range[w]) ++i;
+            range[parts + 1 + w] = i < n ? i : n - 1;
+        }
     }
 
     const size_t tab_bytes = align_up(sizeof(SweepOp) * (size_t)n, kAlign);
-    const size_t range_bytes = align_up(sizeof(int) * (size_t)(parts + 1), kAlign);
+    const size_t range_bytes = align_up(sizeof(int) * range.size(), kAlign);
     const size_t total = tab_bytes + range_bytes + sweep_ctl_bytes(h->grid);
     st = hip_fail(hipMalloc(&h->dev, total), "sweep device buffer");
     if (st != W4_OK) {
@@ -161,7 +167,7 @@ static int setup_persistent(w4_sweep* h) {
     st = hip_fail(hipMemcpy(h->dev, tab.data(), sizeof(SweepOp) * (size_t)n,
                             hipMemcpyHostToDevice), "sweep op table");
     if (st != W4_OK) return st;
-    st = hip_fail(hipMemcpy(h->range, range.data(), sizeof(int) * (size_t)(parts + 1),
+    st = hip_fail(hipMemcpy(h->range, range.data(), sizeof(int) * range.size(),
                             hipMemcpyHostToDevice), "sweep ranges");
     if (st != W4_OK) return st;
     st = hip_fail(hipMemset(h->ctl, 0, sweep_ctl_bytes(h->grid)), "sweep control block");

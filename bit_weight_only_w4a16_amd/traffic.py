@@ -24,7 +24,8 @@ OUT_FILE = os.path.join(ROOT, "profiles", "traffic_sweep_stream.json")
 KERNEL_SOURCES = ("bit_weight_only_w4a16_amd/csrc/w4_persist.hip",
                   "bit_weight_only_w4a16_amd/csrc/w4_persist.h",
                   "bit_weight_only_w4a16_amd/csrc/w4_gemv_core.h",
-                  "bit_weight_only_w4a16_amd/csrc/w4_common.h")
+                  "bit_weight_only_w4a16_amd/csrc/w4_common.h",
+                  "bit_weight_only_w4a16_amd/csrc/w4_sweep.hip")
 KERNEL = "w4::stream_kernel"
 COPY_KERNEL = "w4::probe_copy_kernel"
 COPY_BYTES = 1 << 30
