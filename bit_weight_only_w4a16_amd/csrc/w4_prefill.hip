@@ -20,10 +20,15 @@
 //     2(l/16), 2(l/16)+1 of its row, word t in MFMA step t, and the activation
 //     fragment is read with the same K permutation (a dot product allows it).
 //
-// Work split: a 256-thread workgroup is four waves side by side along N.  All
-// four share one 16*MF-row activation tile; each wave owns 16*NF weight rows
-// and computes a (16 MF) x (16 NF) block of Y, so a decoded word feeds MF
-// MFMAs.  Workgroups are numbered so that every M block of an N block runs on
+// Work split: a workgroup holds KS groups of four waves.  The four waves of a
+// group sit side by side along N and share one 16*MF-row activation tile;
+// each wave owns 16*NF weight rows and computes a (16 MF) x (16 NF) block of
+// Y, so a decoded word feeds MF MFMAs.  With KS > 1 each group takes a
+// contiguous 1/KS of K (whole scale groups) through a ring of its own, and
+// the groups' partial blocks are added in LDS in group order at the end: the
+// same weight and activation bytes per workgroup, KS times the waves to hide
+// each stage's latency, and 1/KS of the stages per wave (few-row products,
+// whose workgroups do not fill the chip).  Workgroups are numbered so that every M block of an N block runs on
 // one XCD (workgroups go round-robin to the 8 XCDs): the weights are read from
 // HBM once per XCD and the activations stay in that XCD's L2.
 //
@@ -76,7 +81,7 @@ struct PfArgs {
     int vec_out;             // Y and its row stride allow 16-byte stores
 };
 
-template <int MF, int NF, int SLOTS>
+template <int MF, int NF, int SLOTS, int KS>
 struct PfShape {
     static constexpr int BM = 16 * MF;                 // activation rows per workgroup
     static constexpr int WN = 16 * NF;                 // weight rows per wave
@@ -92,6 +97,9 @@ struct PfShape {
     static_assert(LOADS * (SLOTS - 2) < 64, "vmcnt range");
     static constexpr int OUT_ROW = BN * 4 + 16;        // padded fp32 staging row (bytes)
     static_assert(BM * OUT_ROW <= SLOTS * SLOT, "output staging fits in the ring");
+    static constexpr int PART = 4 * 64 * MF * NF * 16; // one K group's partial block (bytes)
+    static_assert(KS == 1 || PART <= SLOTS * SLOT, "partial block fits in the group's ring");
+    static constexpr int THREADS = 256 * KS;
     static_assert(MF == 4, "one offset chain per wave: four M fragments for four waves");
 };
 
@@ -103,19 +111,23 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
 
-template <int MF, int NF, int SLOTS, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int MF, int NF, int SLOTS, int P, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : 2)))
 void prefill_kernel(PfArgs a) {
-    using S = PfShape<MF, NF, SLOTS>;
+    using S = PfShape<MF, NF, SLOTS, KS>;
     static_assert(P == 1 || P == 2, "stages per barrier");
     static_assert(SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps, double-buffered at least");
-    __shared__ __align__(16) uint8_t ring[SLOTS * S::SLOT];
+    __shared__ __align__(16) uint8_t rings[KS * SLOTS * S::SLOT];
     __shared__ __align__(16) uint16_t sc[S::BN * kMaxG];
-    __shared__ __align__(16) f32x4 xch[4][64];   // offset chains, one per wave
+    __shared__ __align__(16) f32x4 xchs[KS][4][64];   // offset chains, one per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wave_id & 3;   // position along N within the K group
+    const int kg = wave_id >> 2;    // K group
+    uint8_t* const ring = rings + kg * (SLOTS * S::SLOT);
+    f32x4 (*const xch)[64] = xchs[kg];
     const int li = lane & 15, lk = lane >> 4;
 
     // XCD x = blockIdx % 8 runs every M block of N blocks x, x + 8, ...
@@ -126,7 +138,10 @@ void prefill_kernel(PfArgs a) {
     const int m0 = mb * S::BM, n0 = nb * S::BN;
     const int nw0 = n0 + wave * S::WN;
     const int KW = a.K / 8;
-    const int stages = a.K / kStage;
+    const int stages = a.K / kStage / KS;   // this K group's stages
+    const int kq = kg * stages * kStage;    // this K group's first K
+    const int g0 = kq / a.group;            // and its first scale group
+    const int G = a.G / KS;                 // scale groups per K group
 
     // DMA sources: a wave-uniform base that advances one stage per slot plus a
     // fixed 32-bit per-lane byte offset (the host keeps every offset below
@@ -152,8 +167,10 @@ void prefill_kernel(PfArgs a) {
     const uint32_t adst = ring0 + 1024 * (wave * S::A_DMA);
     const uint32_t bdst = ring0 + S::A_BYTES + wave * S::WN * kBRow;
     auto issue = [&](int st, int slot) {
-        const uint8_t* ab = reinterpret_cast<const uint8_t*>(a.X) + (size_t)st * (kStage * 2);
-        const uint8_t* bb = reinterpret_cast<const uint8_t*>(a.codes) + (size_t)st * (kStage / 2);
+        const uint8_t* ab =
+            reinterpret_cast<const uint8_t*>(a.X) + (size_t)(kq + st * kStage) * 2;
+        const uint8_t* bb =
+            reinterpret_cast<const uint8_t*>(a.codes) + (size_t)(kq + st * kStage) / 2;
 #pragma unroll
         for (int d = 0; d < S::A_DMA; ++d) dma16(aoffs[d], ab, adst + slot * S::SLOT + 1024 * d);
 #pragma unroll
@@ -165,7 +182,7 @@ void prefill_kernel(PfArgs a) {
     const int aoff0 = li * kARow + 16 * ((2 * lk) ^ gl);
     const int aoff1 = li * kARow + 16 * ((2 * lk + 1) ^ gl);
     const int boff = S::A_BYTES + wave * S::WN * kBRow + li * kBRow + 8 * (lk ^ swz_b(li));
-    const uint16_t* scrow = sc + (wave * S::WN + li) * a.G;
+    const uint16_t* scrow = sc + (wave * S::WN + li) * a.G + g0;
 
     const DecodeConsts k = decode_consts();
     const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
@@ -267,7 +284,7 @@ void prefill_kernel(PfArgs a) {
         const int ndw = (min(S::BN, a.N - n0) * a.G + 1) / 2;
         const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.scales + (size_t)n0 * a.G);
         const uint32_t sl = lds_addr(sc);
-        for (int i = wave; i < (ndw + 63) / 64; i += 4)
+        for (int i = wave_id; i < (ndw + 63) / 64; i += 4 * KS)
             dma4((uint32_t)(4 * min(64 * i + lane, ndw - 1)), sb, sl + 256 * i);
     }
     const int pro = stages < SLOTS - P ? stages : SLOTS - P;
@@ -283,7 +300,32 @@ void prefill_kernel(PfArgs a) {
 
     // the last group closes after one more barrier
     ring_barrier();
-    close_group(a.G - 1);
+    close_group(G - 1);
+
+    // K groups 1 .. KS - 1 leave their partial blocks in their own rings (all
+    // their stages are consumed: every wave is past the barrier above), and
+    // K group 0 adds them in group order
+    if (KS > 1) {
+        if (kg > 0) {
+            f32x4* part = reinterpret_cast<f32x4*>(ring) + (wave * MF * NF) * 64 + lane;
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) part[(mf * NF + nf) * 64] = tot[mf][nf];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int q = 1; q < KS; ++q) {
+                const f32x4* part = reinterpret_cast<const f32x4*>(rings + q * (SLOTS * S::SLOT)) +
+                                    (wave * MF * NF) * 64 + lane;
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                    for (int nf = 0; nf < NF; ++nf) tot[mf][nf] += part[(mf * NF + nf) * 64];
+            }
+        }
+    }
 
     // Output: every DMA was waited for in the last iteration, so once all
     // waves are past the barrier above the ring is free.  The fragments go to
@@ -291,24 +333,27 @@ void prefill_kernel(PfArgs a) {
     // output rows (fragment-order stores would fill a quarter of each line).
     const bool f32 = a.ydt == W4_F32;
     const int esz = f32 ? 4 : 2;
-    uint8_t* ostage = ring;
+    uint8_t* ostage = rings;   // K group 0's ring
+    if (kg == 0) {
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+        for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
+            for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint8_t* p = ostage + (16 * mf + 4 * lk + r) * S::OUT_ROW +
-                             (wave * S::WN + 16 * nf + li) * esz;
-                if (f32)
-                    *reinterpret_cast<float*>(p) = tot[mf][nf][r];
-                else
-                    *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(tot[mf][nf][r]);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    uint8_t* p = ostage + (16 * mf + 4 * lk + r) * S::OUT_ROW +
+                                 (wave * S::WN + 16 * nf + li) * esz;
+                    if (f32)
+                        *reinterpret_cast<float*>(p) = tot[mf][nf][r];
+                    else
+                        *reinterpret_cast<uint16_t*>(p) =
+                            (uint16_t)f32_to_bf16_rne(tot[mf][nf][r]);
+                }
+    }
     __syncthreads();
     const int per = 16 / esz;                 // elements per 16-byte piece
     const int cpr = S::BN / per;              // pieces per row
-    for (int e = tid; e < S::BM * cpr; e += 256) {
+    for (int e = tid; e < S::BM * cpr; e += S::THREADS) {
         const int row = e / cpr, c = e - row * cpr;
         const int m = m0 + row;
         if (m >= a.M) break;                  // rows only grow with e
@@ -331,25 +376,37 @@ void prefill_kernel(PfArgs a) {
 }
 
 struct PfCfg {
-    int MF, NF, slots, per_barrier;
+    int MF, NF, slots, per_barrier, ks;
 };
-// 64 x 192 or 64 x 64 blocks; ring slots; stages per barrier.  Measured at
-// N = 12288, K = 1536, g256: two stages per barrier beat one (the per-barrier
-// latency chain, not the DMA depth, bounds the loop), 64 x 192 blocks win from
-// M = 256 up, 64 x 64 blocks (three times the workgroups) below.  Entries 2
-// and 3 are the one-stage variants, kept for comparison runs.
-constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2}, {4, 1, 6, 2}, {4, 3, 5, 1}, {4, 1, 5, 1}};
+// 64 x 192 or 64 x 64 blocks; ring slots; stages per barrier; K groups.
+// Measured at N = 12288, K = 1536, g256: two stages per barrier beat one (the
+// per-barrier latency chain, not the DMA depth, bounds the loop), 64 x 192
+// blocks win from M = 256 up, 64 x 64 blocks (three times the workgroups)
+// below.  Entries 2 and 3 are the one-stage variants, kept for comparison
+// runs; entries 4 and 5 split K over three or two wave groups.
+constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2, 1}, {4, 1, 6, 2, 1}, {4, 3, 5, 1, 1},
+                             {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2}};
 constexpr int kPfNumCfgs = sizeof(kPfCfgs) / sizeof(kPfCfgs[0]);
 
 struct PfPlan {
     int cfg, BM, BN, m_blocks, n_blocks, grid;
 };
 
-PfPlan plan_prefill(int M, int N) {
+PfPlan plan_prefill(int M, int N, int K, int group) {
     PfPlan p;
     p.cfg = M <= 128 ? 1 : 0;
+    // 64 x 64 blocks that leave CUs idle (one 64-row block: N / 64 workgroups
+    // of at most one per CU) split K over three or two wave groups.  Measured
+    // at N = 12288, K = 1536, g256: 64 rows 11.8 -> 9.0 us, 32 rows 11.6 ->
+    // 8.7 us; at 128 rows (768 workgroup slots wanted, one per CU fits) the
+    // split is slower (14.4 -> 16.6 us).
+    const int G = K / group;
+    if (p.cfg == 1 && (M + 63) / 64 * ((N + 63) / 64) <= kNumCUs)
+        p.cfg = G % 3 == 0 ? 4 : (G % 2 == 0 ? 5 : 1);
     const char* e = getenv("W4_PREFILL_CFG");  // tuning override: a kPfCfgs index
     if (e && *e >= '0' && *e < '0' + kPfNumCfgs && e[1] == 0) p.cfg = *e - '0';
+    // a K split needs whole scale groups per wave group
+    if (G % kPfCfgs[p.cfg].ks != 0) p.cfg = M <= 128 ? 1 : 0;
     p.BM = 16 * kPfCfgs[p.cfg].MF;
     p.BN = 64 * kPfCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -371,7 +428,7 @@ bool prefill_supported(int M, int N, int K, int group, int ldx) {
 
 int launch_prefill(const void* packed, int N, int K, int group, int M, const uint16_t* X,
                    int ldx, void* Y, int ldy, int ydt, hipStream_t s) {
-    const PfPlan p = plan_prefill(M, N);
+    const PfPlan p = plan_prefill(M, N, K, group);
     PfArgs a;
     a.codes = static_cast<const uint32_t*>(packed);
     a.scales = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(packed) +
@@ -390,22 +447,24 @@ int launch_prefill(const void* packed, int N, int K, int group, int M, const uin
     a.n_blocks = p.n_blocks;
     const size_t esz = ydt == W4_F32 ? 4 : 2;
     a.vec_out = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((size_t)ldy * esz) % 16 == 0;
-    const dim3 g(p.grid), b(256);
+    const dim3 g(p.grid), b(256 * kPfCfgs[p.cfg].ks);
     switch (p.cfg) {
-        case 0: prefill_kernel<4, 3, 4, 2><<<g, b, 0, s>>>(a); break;
-        case 1: prefill_kernel<4, 1, 6, 2><<<g, b, 0, s>>>(a); break;
-        case 2: prefill_kernel<4, 3, 5, 1><<<g, b, 0, s>>>(a); break;
-        default: prefill_kernel<4, 1, 5, 1><<<g, b, 0, s>>>(a); break;
+        case 0: prefill_kernel<4, 3, 4, 2, 1><<<g, b, 0, s>>>(a); break;
+        case 1: prefill_kernel<4, 1, 6, 2, 1><<<g, b, 0, s>>>(a); break;
+        case 2: prefill_kernel<4, 3, 5, 1, 1><<<g, b, 0, s>>>(a); break;
+        case 3: prefill_kernel<4, 1, 5, 1, 1><<<g, b, 0, s>>>(a); break;
+        case 4: prefill_kernel<4, 1, 4, 2, 3><<<g, b, 0, s>>>(a); break;
+        default: prefill_kernel<4, 1, 6, 2, 2><<<g, b, 0, s>>>(a); break;
     }
     return hip_fail(hipGetLastError(), "prefill launch");
 }
 
 void describe_prefill(int M, int N, int K, int group, char* buf, size_t len) {
-    const PfPlan p = plan_prefill(M, N);
+    const PfPlan p = plan_prefill(M, N, K, group);
     snprintf(buf, len,
-             "mfma 16x16x32 dma-ring block %dx%d waves 1x4 slots %d stage %d x%d grid=%d (K=%d g=%d)",
-             p.BM, p.BN, kPfCfgs[p.cfg].slots, kStage, kPfCfgs[p.cfg].per_barrier, p.grid, K,
-             group);
+             "mfma 16x16x32 dma-ring block %dx%d waves %dx4 slots %d stage %d x%d grid=%d (K=%d g=%d)",
+             p.BM, p.BN, kPfCfgs[p.cfg].ks, kPfCfgs[p.cfg].slots, kStage,
+             kPfCfgs[p.cfg].per_barrier, p.grid, K, group);
 }
 
 }  // namespace w4

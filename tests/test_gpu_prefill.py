@@ -205,14 +205,16 @@ def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
         assert_within(Y[rows], Yr, A, out_dtype, "mfma %s" % out_dtype)
 
 
-@pytest.mark.parametrize("env", [{"W4_PREFILL_CFG": str(c)} for c in range(4)] +
-                         [{"W4_PREFILL": "0"}])
-def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env):
+@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(6)] +
+                         [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
+                          ({"W4_PREFILL": "0"}, 256)])
+def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
     """Every compiled matrix-core tiling (the tuning overrides select them,
-    one per call) against the oracle on one ragged g256 case."""
+    one per call) against the oracle on one ragged case; at group 512 the
+    two-way K split falls back to an unsplit tiling (3 groups)."""
     for k, v in env.items():
         monkeypatch.setenv(k, v)
-    M, N, K, g = 70, 1000, 1536, 256
+    M, N, K = 70, 1000, 1536
     note("mfma tiling %s M=%d N=%d K=%d g=%d" % (env, M, N, K, g))
     case = synth.make_case("tile", N, K, g, M, 77, "bf16", outlier_frac=0.01)
     packed = upload_packed(case.P, case.S, N, K, g)
