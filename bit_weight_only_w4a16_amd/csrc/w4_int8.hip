@@ -312,8 +312,8 @@ constexpr int kI8RingRow = 64;   // bytes of a row in a slot
 // which is what the fragment reads see
 __device__ __forceinline__ int swz_i8(int r) { return (((r & 15) >> 1) ^ ((r & 15) >> 3)) & 3; }
 
-template <int NF, int SLOTS, int P>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int NF, int SLOTS, int P, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : 2)))
 void gemm_i8_ring_kernel(I8Args a) {
     using namespace ring;
     constexpr int MF = 4, BM = 64, WN = 16 * NF, BN = 4 * WN;
@@ -321,15 +321,20 @@ void gemm_i8_ring_kernel(I8Args a) {
     constexpr int SLOT = A_BYTES + BN * kI8RingRow;   // + NF per wave
     constexpr int LOADS = 1 + NF;
     constexpr int OUT_ROW = BN * 4 + 16;
+    constexpr int PART = 4 * 64 * MF * NF * 16;       // one K group's partial block
     static_assert(A_BYTES == 4 * 1024, "activation tile: one DMA per wave");
     static_assert(BM * OUT_ROW <= SLOTS * SLOT, "output staging fits in the ring");
+    static_assert(KS == 1 || PART <= SLOTS * SLOT, "partial block fits in the group's ring");
     static_assert((P == 1 || P == 2) && SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps");
     static_assert(LOADS * (SLOTS - 2 * P) < 64, "vmcnt range");
-    __shared__ __align__(16) uint8_t ring[SLOTS * SLOT];
+    __shared__ __align__(16) uint8_t rings[KS * SLOTS * SLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wave_id & 3;   // position along N within the K group
+    const int kg = wave_id >> 2;    // K group: a contiguous 1/KS of K
+    uint8_t* const ring = rings + kg * (SLOTS * SLOT);
     const int li = lane & 15, lk = lane >> 4;
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int mb = j % a.m_blocks;
@@ -337,7 +342,8 @@ void gemm_i8_ring_kernel(I8Args a) {
     if (nb >= a.n_blocks) return;
     const int m0 = mb * BM, n0 = nb * BN;
     const int nw0 = n0 + wave * WN;
-    const int stages = a.K / kI8RingStage;
+    const int stages = a.K / kI8RingStage / KS;   // this K group's stages
+    const int kq = kg * stages * kI8RingStage;     // and its first K
 
     // scales of this lane's outputs, loaded now, used at the end
     float xsr[MF][4], wsr[NF];
@@ -367,8 +373,8 @@ void gemm_i8_ring_kernel(I8Args a) {
     const uint32_t adst = ring0 + 1024 * wave;
     const uint32_t bdst = ring0 + A_BYTES + wave * WN * kI8RingRow;
     auto issue = [&](int st, int slot) {
-        const int8_t* ab = a.X + (size_t)st * kI8RingStage;
-        const int8_t* bb = a.W + (size_t)st * kI8RingStage;
+        const int8_t* ab = a.X + (size_t)(kq + st * kI8RingStage);
+        const int8_t* bb = a.W + (size_t)(kq + st * kI8RingStage);
         dma16(aoff, ab, adst + slot * SLOT);
 #pragma unroll
         for (int d = 0; d < NF; ++d) dma16(boffs[d], bb, bdst + slot * SLOT + 1024 * d);
@@ -425,31 +431,59 @@ void gemm_i8_ring_kernel(I8Args a) {
     // every DMA was waited for in the last step: after this barrier the ring
     // holds the output tile, which then leaves as whole 16-byte row pieces
     ring_barrier();
+    // K groups 1 .. KS - 1 leave their integer partials in their own rings and
+    // K group 0 adds them: integer sums, so the result is bitwise that of one
+    // group walking all of K
+    if (KS > 1) {
+        if (kg > 0) {
+            i32x4* part = reinterpret_cast<i32x4*>(ring) + (wave * MF * NF) * 64 + lane;
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) part[(mf * NF + nf) * 64] = acc[mf][nf];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int q = 1; q < KS; ++q) {
+                const i32x4* part = reinterpret_cast<const i32x4*>(rings + q * (SLOTS * SLOT)) +
+                                    (wave * MF * NF) * 64 + lane;
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                    for (int nf = 0; nf < NF; ++nf) acc[mf][nf] += part[(mf * NF + nf) * 64];
+            }
+        }
+    }
     const bool f32 = a.ydt == W4_F32;
     const int esz = f32 ? 4 : 2;
+    uint8_t* const ostage = rings;   // K group 0's ring
+    if (kg == 0) {
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
+        for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
+            for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float y = ((float)acc[mf][nf][r] * xsr[mf][r]) * wsr[nf];
-                uint8_t* p = ring + (16 * mf + 4 * lk + r) * OUT_ROW + (wave * WN + 16 * nf + li) * esz;
-                if (f32)
-                    *reinterpret_cast<float*>(p) = y;
-                else
-                    *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(y);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const float y = ((float)acc[mf][nf][r] * xsr[mf][r]) * wsr[nf];
+                    uint8_t* p = ostage + (16 * mf + 4 * lk + r) * OUT_ROW +
+                                 (wave * WN + 16 * nf + li) * esz;
+                    if (f32)
+                        *reinterpret_cast<float*>(p) = y;
+                    else
+                        *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(y);
+                }
+    }
     __syncthreads();
     const int per = 16 / esz;
     const int cpr = BN / per;
-    for (int e = tid; e < BM * cpr; e += 256) {
+    for (int e = tid; e < BM * cpr; e += 256 * KS) {
         const int row = e / cpr, c = e - row * cpr;
         const int m = m0 + row;
         if (m >= a.M) break;
         const int n = n0 + c * per;
         if (n >= a.N) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ring + row * OUT_ROW + 16 * c);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + row * OUT_ROW + 16 * c);
         uint8_t* dst = static_cast<uint8_t*>(a.Y) + ((size_t)m * a.ldy + n) * esz;
         if (a.vec_out && n + per <= a.N) {
             gstore(reinterpret_cast<u32x4*>(dst), v);
@@ -471,12 +505,15 @@ struct I8Plan {
 };
 
 struct I8RingCfg {
-    int NF, slots, per_barrier;
+    int NF, slots, per_barrier, ks;
 };
 // 64 x 192 blocks for M > 256, 64 x 64 blocks (three times the workgroups)
 // up to 256 rows, both with two 64-K stages per barrier (measured at N = 12288,
-// K = 1536: 64 x 64 wins through M = 256, 64 x 192 from 512 on)
-constexpr I8RingCfg kI8RingCfgs[] = {{3, 4, 2}, {1, 6, 2}};
+// K = 1536: 64 x 64 wins through M = 256, 64 x 192 from 512 on); entries 2
+// and 3 split K over three or two wave groups, for 64 x 64 blocks that leave
+// CUs idle
+constexpr I8RingCfg kI8RingCfgs[] = {{3, 4, 2, 1}, {1, 6, 2, 1}, {1, 4, 2, 3}, {1, 6, 2, 2}};
+constexpr int kI8NumRingCfgs = sizeof(kI8RingCfgs) / sizeof(kI8RingCfgs[0]);
 
 static I8Plan plan_i8(int M, int N, int K, int ldx, int ldw) {
     I8Plan p;
@@ -489,7 +526,13 @@ static I8Plan plan_i8(int M, int N, int K, int ldx, int ldw) {
     p.ring = fits && !(r && r[0] == '0' && r[1] == 0);
     if (p.ring) {
         p.cfg = M <= 256 ? 1 : 0;
-        if (r && (r[0] == '1' || r[0] == '2') && r[1] == 0) p.cfg = r[0] - '1';
+        // one 64-row block (N / 64 workgroups, at most one per CU): split K
+        const int st = K / kI8RingStage;
+        if (p.cfg == 1 && (N + 63) / 64 * ((M + 63) / 64) <= kNumCUs)
+            p.cfg = st % 6 == 0 ? 2 : (st % 4 == 0 ? 3 : 1);
+        if (r && r[0] >= '1' && r[0] < '1' + kI8NumRingCfgs && r[1] == 0) p.cfg = r[0] - '1';
+        // each K group needs a whole number of two-stage steps
+        if (st % (2 * kI8RingCfgs[p.cfg].ks) != 0) p.cfg = M <= 256 ? 1 : 0;
         p.MF = 4;
         p.NF = kI8RingCfgs[p.cfg].NF;
         p.BM = 64;
@@ -537,12 +580,14 @@ int launch_gemm_i8(const int8_t* X, int ldx, const float* xs, const int8_t* W, i
     a.n_blocks = p.n_blocks;
     const size_t esz = ydt == W4_F32 ? 4 : 2;
     a.vec_out = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((size_t)ldy * esz) % 16 == 0;
-    const dim3 g(p.grid), b(256);
+    const dim3 g(p.grid), b(p.ring ? 256 * kI8RingCfgs[p.cfg].ks : 256);
     if (p.ring) {
-        if (p.cfg == 0)
-            gemm_i8_ring_kernel<3, 4, 2><<<g, b, 0, s>>>(a);
-        else
-            gemm_i8_ring_kernel<1, 6, 2><<<g, b, 0, s>>>(a);
+        switch (p.cfg) {
+            case 0: gemm_i8_ring_kernel<3, 4, 2, 1><<<g, b, 0, s>>>(a); break;
+            case 1: gemm_i8_ring_kernel<1, 6, 2, 1><<<g, b, 0, s>>>(a); break;
+            case 2: gemm_i8_ring_kernel<1, 4, 2, 3><<<g, b, 0, s>>>(a); break;
+            default: gemm_i8_ring_kernel<1, 6, 2, 2><<<g, b, 0, s>>>(a); break;
+        }
     } else if (p.MF == 2 && p.NF == 2) {
         gemm_i8_kernel<2, 2><<<g, b, 0, s>>>(a);
     } else if (p.MF == 2) {
@@ -559,10 +604,10 @@ void describe_i8(int M, int N, int K, char* buf, size_t len) {
     const I8Plan p = plan_i8(M, N, K, K, K);
     if (p.ring)
         snprintf(buf, len,
-                 "int8 mfma 16x16x64 dma-ring block %dx%d waves 1x4 slots %d stage 64 x%d "
+                 "int8 mfma 16x16x64 dma-ring block %dx%d waves %dx4 slots %d stage 64 x%d "
                  "grid=%d (K=%d)",
-                 p.BM, p.BN, kI8RingCfgs[p.cfg].slots, kI8RingCfgs[p.cfg].per_barrier, p.grid,
-                 K);
+                 p.BM, p.BN, kI8RingCfgs[p.cfg].ks, kI8RingCfgs[p.cfg].slots,
+                 kI8RingCfgs[p.cfg].per_barrier, p.grid, K);
     else
         snprintf(buf, len, "int8 mfma 16x16x64 block %dx%d waves 2x2 stage 128 grid=%d (K=%d)",
                  p.BM, p.BN, p.grid, K);

@@ -72,14 +72,16 @@ def test_gemm_i8_vs_exact(oracle_mod, M, N, K, out_dtype):
     assert np.all(np.abs(got - ref) <= bound + 1e-30)
 
 
-@pytest.mark.parametrize("ring", ["0", "1", "2"])
-def test_gemm_i8_every_tiling(oracle_mod, monkeypatch, ring):
-    """Every compiled int8 tiling (W4_I8_RING: 0 register-staged, 1 and 2 the
-    DMA-ring configurations) on one ragged case, bitwise equal to the default
-    dispatch and within the exact product's bound."""
+@pytest.mark.parametrize("ring,K", [(r, 1536) for r in "01234"] + [("3", 1024), ("4", 1024)])
+def test_gemm_i8_every_tiling(oracle_mod, monkeypatch, ring, K):
+    """Every compiled int8 tiling (W4_I8_RING: 0 register-staged, 1 to 4 the
+    DMA-ring configurations, 3 and 4 splitting K over three or two wave
+    groups; at K = 1024 the three-way split falls back) on one ragged case,
+    bitwise equal to the default dispatch and within the exact product's
+    bound."""
     import torch
     device()
-    M, N, K = 150, 700, 1536
+    M, N = 150, 700
     rng = np.random.default_rng(11)
     Xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
     Wq = rng.integers(-127, 128, (N, K)).astype(np.int8)
