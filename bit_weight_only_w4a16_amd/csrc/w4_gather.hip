@@ -14,48 +14,44 @@
 
 namespace w4 {
 
-// One thread per 32-element chunk of an output row: one 16-byte code load
-// and one scale; consecutive threads take consecutive chunks of a row, so a
-// wave's code loads are 1 KB contiguous.  An id outside [0, N) reads nothing
-// and writes a row of quiet NaNs.
+// One thread per device word (8 elements) of an output row: one 4-byte code
+// load and one scale; consecutive threads take consecutive words of a row,
+// so a wave's code loads are 256 contiguous bytes and its stores 1 KB (bf16)
+// or 2 KB (fp32) contiguous.  An id outside [0, N) reads nothing and writes
+// quiet NaNs.
 template <int YDT>
-__global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ codes,
+__global__ __launch_bounds__(256) void gather_kernel(const uint32_t* __restrict__ words,
                                                      const uint16_t* __restrict__ scales,
-                                                     int N, int C, int G, int gshift,
+                                                     int N, int W, int G, int gshift,
                                                      const int32_t* __restrict__ ids,
                                                      int B, void* __restrict__ Y, int ldy) {
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (long long)B * C) return;
-    const int b = (int)(t / C);
-    const int c = (int)(t - (long long)b * C);
+    if (t >= (long long)B * W) return;
+    const int b = (int)(t / W);
+    const int d = (int)(t - (long long)b * W);   // word of the row: elements 8d .. 8d + 7
     const int id = gload(ids + b);
     const bool valid = id >= 0 && id < N;
 
-    uint32_t out[16];  // bf16 pairs (elements 2j, 2j+1) or, for fp32, unused
-    float v[32];
+    // element 8d + 2i at bits [4i, 4i + 4), element 8d + 2i + 1 at bits
+    // [16 + 4i, 20 + 4i)
+    float v[8];
     if (valid) {
-        const u32x4 q = gload(codes + (size_t)id * C + c);
-        const float s = bf16_to_f32(gload(scales + (size_t)id * G + (c >> gshift)));
-        // device word d holds elements 8d..8d+7: element 8d+2i at bits
-        // [4i, 4i+4), element 8d+2i+1 at bits [16+4i, 20+4i)
+        const uint32_t w = gload(words + (size_t)id * W + d);
+        const float s = bf16_to_f32(gload(scales + (size_t)id * G + ((d >> 2) >> gshift)));
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t w = q[d];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[8 * d + 2 * i] = (float)((int)((w >> (4 * i)) & 15u) - 8) * s;
-                v[8 * d + 2 * i + 1] = (float)((int)((w >> (16 + 4 * i)) & 15u) - 8) * s;
-            }
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = (float)((int)((w >> (4 * i)) & 15u) - 8) * s;
+            v[2 * i + 1] = (float)((int)((w >> (16 + 4 * i)) & 15u) - 8) * s;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) v[e] = __builtin_nanf("");
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_nanf("");
     }
 
     if (YDT == W4_F32) {
-        u32x4* y = reinterpret_cast<u32x4*>(static_cast<float*>(Y) + (size_t)b * ldy + 32 * c);
+        u32x4* y = reinterpret_cast<u32x4*>(static_cast<float*>(Y) + (size_t)b * ldy + 8 * d);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 2; ++j) {
             u32x4 o;
             o[0] = __float_as_uint(v[4 * j + 0]);
             o[1] = __float_as_uint(v[4 * j + 1]);
@@ -64,38 +60,29 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ c
             gstore(y + j, o);
         }
     } else {
+        u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            out[j] = valid ? (f32_to_bf16_rne(v[2 * j]) | (f32_to_bf16_rne(v[2 * j + 1]) << 16))
-                           : 0x7FC07FC0u;
-        u32x4* y =
-            reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Y) + (size_t)b * ldy + 32 * c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32x4 o;
-            o[0] = out[4 * j + 0];
-            o[1] = out[4 * j + 1];
-            o[2] = out[4 * j + 2];
-            o[3] = out[4 * j + 3];
-            gstore(y + j, o);
-        }
+        for (int j = 0; j < 4; ++j)
+            o[j] = valid ? (f32_to_bf16_rne(v[2 * j]) | (f32_to_bf16_rne(v[2 * j + 1]) << 16))
+                         : 0x7FC07FC0u;
+        gstore(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(Y) + (size_t)b * ldy + 8 * d), o);
     }
 }
 
 int launch_gather(const void* packed, int N, int K, int group, const int32_t* ids, int B,
                   void* Y, int ldy, int ydt, hipStream_t s) {
     if (B == 0) return W4_OK;
-    const int C = K / 32;
-    const u32x4* codes = static_cast<const u32x4*>(packed);
+    const int W = K / 8;   // device words per row
+    const uint32_t* words = static_cast<const uint32_t*>(packed);
     const uint16_t* scales = reinterpret_cast<const uint16_t*>(
         static_cast<const uint8_t*>(packed) + scale_offset(N, K));
-    const long long work = (long long)B * C;
+    const long long work = (long long)B * W;
     const dim3 grid((unsigned)((work + 255) / 256)), block(256);
     if (ydt == W4_F32)
-        gather_kernel<W4_F32><<<grid, block, 0, s>>>(codes, scales, N, C, K / group,
+        gather_kernel<W4_F32><<<grid, block, 0, s>>>(words, scales, N, W, K / group,
                                                       ilog2(group / 32), ids, B, Y, ldy);
     else
-        gather_kernel<W4_BF16><<<grid, block, 0, s>>>(codes, scales, N, C, K / group,
+        gather_kernel<W4_BF16><<<grid, block, 0, s>>>(words, scales, N, W, K / group,
                                                        ilog2(group / 32), ids, B, Y, ldy);
     return hip_fail(hipGetLastError(), "gather launch");
 }
