@@ -378,14 +378,16 @@ void prefill_kernel(PfArgs a) {
 struct PfCfg {
     int MF, NF, slots, per_barrier, ks;
 };
-// 64 x 192 or 64 x 64 blocks; ring slots; stages per barrier; K groups.
-// Measured at N = 12288, K = 1536, g256: two stages per barrier beat one (the
-// per-barrier latency chain, not the DMA depth, bounds the loop), 64 x 192
-// blocks win from M = 256 up, 64 x 64 blocks (three times the workgroups)
-// below.  Entries 2 and 3 are the one-stage variants, kept for comparison
-// runs; entries 4 and 5 split K over three or two wave groups.
+// 64 x 192, 64 x 128 or 64 x 64 blocks; ring slots; stages per barrier; K
+// groups.  Measured at N = 12288, K = 1536, g256: two stages per barrier beat
+// one (the per-barrier latency chain, not the DMA depth, bounds the loop);
+// 64 x 192 blocks win above 256 rows, 64 x 128 blocks from 129 to 256 rows
+// (19.4 against 21.2 us at 256), 64 x 64 blocks (three times the
+// workgroups) up to 128.  Entries 2 and 3 are the one-stage variants, kept
+// for comparison runs; entries 4 and 5 split K over three or two wave groups.
 constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2, 1}, {4, 1, 6, 2, 1}, {4, 3, 5, 1, 1},
-                             {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2}};
+                             {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2},
+                             {4, 2, 4, 2, 1}};
 constexpr int kPfNumCfgs = sizeof(kPfCfgs) / sizeof(kPfCfgs[0]);
 
 struct PfPlan {
@@ -394,7 +396,7 @@ struct PfPlan {
 
 PfPlan plan_prefill(int M, int N, int K, int group) {
     PfPlan p;
-    p.cfg = M <= 128 ? 1 : 0;
+    p.cfg = M <= 128 ? 1 : (M <= 256 ? 6 : 0);
     // 64 x 64 blocks that leave CUs idle (one 64-row block: N / 64 workgroups
     // of at most one per CU) split K over three or two wave groups.  Measured
     // at N = 12288, K = 1536, g256: 64 rows 11.8 -> 9.0 us, 32 rows 11.6 ->
@@ -406,7 +408,7 @@ PfPlan plan_prefill(int M, int N, int K, int group) {
     const char* e = getenv("W4_PREFILL_CFG");  // tuning override: a kPfCfgs index
     if (e && *e >= '0' && *e < '0' + kPfNumCfgs && e[1] == 0) p.cfg = *e - '0';
     // a K split needs whole scale groups per wave group
-    if (G % kPfCfgs[p.cfg].ks != 0) p.cfg = M <= 128 ? 1 : 0;
+    if (G % kPfCfgs[p.cfg].ks != 0) p.cfg = 1;   // the split entries are 64 x 64 blocks
     p.BM = 16 * kPfCfgs[p.cfg].MF;
     p.BN = 64 * kPfCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -454,7 +456,8 @@ int launch_prefill(const void* packed, int N, int K, int group, int M, const uin
         case 2: prefill_kernel<4, 3, 5, 1, 1><<<g, b, 0, s>>>(a); break;
         case 3: prefill_kernel<4, 1, 5, 1, 1><<<g, b, 0, s>>>(a); break;
         case 4: prefill_kernel<4, 1, 4, 2, 3><<<g, b, 0, s>>>(a); break;
-        default: prefill_kernel<4, 1, 6, 2, 2><<<g, b, 0, s>>>(a); break;
+        case 5: prefill_kernel<4, 1, 6, 2, 2><<<g, b, 0, s>>>(a); break;
+        default: prefill_kernel<4, 2, 4, 2, 1><<<g, b, 0, s>>>(a); break;
     }
     return hip_fail(hipGetLastError(), "prefill launch");
 }

@@ -205,7 +205,7 @@ def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
         assert_within(Y[rows], Yr, A, out_dtype, "mfma %s" % out_dtype)
 
 
-@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(6)] +
+@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(7)] +
                          [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
                           ({"W4_PREFILL": "0"}, 256)])
 def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
@@ -239,9 +239,9 @@ def test_matrix_core_code8_columns_exact_zero():
     assert np.all(Y[:, 6] != 0.0)
 
 
-@pytest.mark.parametrize("M,had", [(512, 0), (64, 0), (16, 512), (8, 0), (3, 512)])
+@pytest.mark.parametrize("M,had", [(512, 0), (200, 0), (64, 0), (16, 512), (8, 0), (3, 512)])
 def test_matrix_core_deterministic(M, had):
-    """Run to run bitwise: the tiled matrix-core kernels (512 and 64 rows) and
+    """Run to run bitwise: the tiled matrix-core kernels (512, 200 and 64 rows) and
     the matrix-core small-M kernel (with and without the fused transform)."""
     N, K, g = 1024, 1536, 256
     case = synth.make_case("det", N, K, g, M, 9 + M, "bf16")
