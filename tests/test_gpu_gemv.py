@@ -101,7 +101,9 @@ RAGGED = [(1, 32, 32), (3, 64, 32), (33, 96, 32), (65, 288, 32), (97, 1056, 32),
           (31, 256, 256), (65, 1536, 256), (17, 512, 256), (4097, 1536, 32),
           (2, 160, 32), (63, 4096, 256),
           # group 512 (the int4 g512 build): odd and even group counts per row
-          (100, 1536, 512), (33, 1024, 512), (12288, 1536, 512), (65, 6144, 512)]
+          (100, 1536, 512), (33, 1024, 512), (12288, 1536, 512), (65, 6144, 512),
+          # the largest K the calls accept (2^20)
+          (3, 1 << 20, 32), (2, 1 << 20, 512)]
 
 
 @pytest.mark.parametrize("N,K,g", RAGGED)

@@ -87,6 +87,20 @@ def test_smallm_vs_oracle(oracle_mod, M, N, K, g):
         assert_within(Y, Yr, A, out_dtype, "smallM M=%d" % M)
 
 
+@pytest.mark.parametrize("M,N,g", [(5, 3, 256), (3, 5, 32)])
+def test_smallm_largest_k(oracle_mod, M, N, g):
+    """Small M at the largest K the call accepts (2^20)."""
+    K = 1 << 20
+    note("smallM M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    case = synth.make_case("smk", N, K, g, M, 91 + M, "bf16")
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, oracle_mod.bf16_to_f64(case.X), threads=16)
+    for out_dtype in ("bf16", "f32"):
+        Y = from_dev(w4.gemm_smallM(packed, N, K, g, X, out_dtype=out_dtype))
+        assert_within(Y, Yr, A, out_dtype, "smallM largest K %s" % out_dtype)
+
+
 @pytest.mark.parametrize("M", [2, 8, 16])
 @pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (129, 1536, 512)])
 def test_smallm_vector_alu_path(oracle_mod, monkeypatch, M, N, K, g):
@@ -188,10 +202,12 @@ def test_prefill_g256_hadamard(oracle_mod, M):
                                          (65, 1000, 2048, 256, 256), (33, 64, 256, 256, 0),
                                          (64, 12288, 1536, 512, 512), (40, 300, 1024, 512, 0),
                                          (9, 200, 512, 256, 0), (16, 1000, 1536, 32, 0),
-                                         (13, 12288, 1536, 256, 512)])
+                                         (13, 12288, 1536, 256, 512),
+                                         # the largest K the call accepts (2^20)
+                                         (20, 40, 1 << 20, 256, 0), (70, 24, 1 << 20, 32, 0)])
 def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
     """M >= 9 runs on the matrix cores: ragged M and N, all group sizes, with
-    and without the run-time transform."""
+    and without the run-time transform, up to the largest K."""
     note("mfma gemm M=%d N=%d K=%d g=%d had=%d" % (M, N, K, g, had))
     case = synth.make_case("mfma", N, K, g, M, M * 31 + N + K, "bf16", outlier_frac=0.01)
     packed = upload_packed(case.P, case.S, N, K, g)
@@ -203,6 +219,22 @@ def test_matrix_core_gemm_shapes(oracle_mod, M, N, K, g, had):
     for out_dtype in ("bf16", "f32"):
         Y = from_dev(w4.gemm(packed, N, K, g, X, had_block=had, out_dtype=out_dtype))
         assert_within(Y[rows], Yr, A, out_dtype, "mfma %s" % out_dtype)
+
+
+def test_matrix_core_largest_m(oracle_mod):
+    """The largest M the call accepts (2^20 rows, 16384 row blocks), checked
+    on sampled rows."""
+    M, N, K, g = 1 << 20, 40, 256, 256
+    note("mfma gemm largest M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    rng = np.random.default_rng(2024)
+    P, S = synth.draw_weights(rng, N, K, g)
+    X = synth.draw_activations(rng, M, K)
+    packed = upload_packed(P, S, N, K, g)
+    Xd = to_dev_bf16(X)
+    rows = np.concatenate([[0, M - 1], rng.choice(M, 62, replace=False)])
+    Yr, A = oracle_mod.gemm(P, S, N, K, g, oracle_mod.bf16_to_f64(X[rows]), threads=16)
+    Y = from_dev(w4.gemm(packed, N, K, g, Xd, out_dtype="bf16"))
+    assert_within(Y[rows], Yr, A, "bf16", "largest M")
 
 
 @pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(7)] +
