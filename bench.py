@@ -259,6 +259,27 @@ def time_prefill(torch, w4, synth, dev):
     return out
 
 
+def time_smallm_g32(torch, w4, synth, dev):
+    """A few rows through the decode-format (group 32) gate+up weight,
+    12288 x 1536: the small-M product at 2, 8 and 16 rows, bf16 out."""
+    import numpy as np
+    c = synth.make_case("smallm_g32", 12288, 1536, 32, 16, 16, "bf16")
+    P = torch.from_numpy(c.P.view(np.int32)).to(dev)
+    S = torch.from_numpy(c.S.view(np.int16)).to(dev)
+    packed = w4.pack(P, S, c.N, c.K, c.group)
+    X16 = torch.from_numpy(c.X.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = {}
+    for M in (2, 8, 16):
+        X = X16[:M]
+        Y = torch.empty((M, c.N), dtype=torch.bfloat16, device=dev)
+        us = time_calls(torch, lambda: w4.gemm_smallM(packed, c.N, c.K, c.group, X, "bf16",
+                                                        out=Y))
+        out["M%d" % M] = {"kernel": w4.describe_dispatch(M, c.N, c.K, c.group), "us": us,
+                          "weight_GBps": c.weight_bytes / us / 1e3}
+    del P, S, packed, X16
+    return out
+
+
 def cpu_baseline(cases, max_threads=16, min_seconds=10.0, max_passes=40):
     """The fp64 oracle over whole decode-step sweeps (all 141 GEMVs), OpenMP
     over rows, repeated until min_seconds of wall time (at most max_passes):
@@ -376,6 +397,7 @@ def main():
             "modes": results,
             "trials_us": trials,
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
+            "smallm_g32_N12288_K1536": time_smallm_g32(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
             "quantize_rotate": time_quantize(torch, w4, synth, dev),
             "int8_twin_auto16": time_twin(torch, w4, synth, dev),

@@ -72,6 +72,7 @@ inline int ilog2(int v) {
 
 // ------------------------------------------------------------------ device --
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kPairMask = 0x000F000Fu;

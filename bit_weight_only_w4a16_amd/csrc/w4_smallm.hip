@@ -264,21 +264,25 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
 
 // ------------------------------------------------ matrix-core small M ---
 //
-// Rotated formats (groups 256 and 512), M <= 16: one 16-row MFMA tile holds
-// every activation row (rows past M repeat row M - 1 and are never stored),
-// so the matrix cores do the per-row work the vector-ALU kernel spends its
-// time on.  v_mfma_f32_16x16x32_bf16 (lane l holds A[l%16][8(l/16) + j],
+// Groups 32, 256 and 512, M <= 16: one 16-row MFMA tile holds every
+// activation row (rows past M repeat row M - 1 and are never stored), so the
+// matrix cores do the per-row work the vector-ALU kernel spends its time on.
+// v_mfma_f32_16x16x32_bf16 (lane l holds A[l%16][8(l/16) + j],
 // B[8(l/16) + j][l%16], D[4(l/16) + r][l%16]); codes decoded to exact bf16
 // 128 + c, the offset chain (same MFMA against 136) subtracted per group, as
 // in the prefill kernels.
 //
 // A workgroup owns 16 * RG weight rows and splits K into KS slices: wave
 // (row group rg, slice ks) multiplies 16 rows by its 128 * NB slice of K.
-// Each wave loads all of its codes (16 bytes per lane per 128-K block; lane
-// group l/16 takes words 4(l/16) .. 4(l/16) + 3 of its row's block and uses
-// word t in MFMA step t, the activations read with the same K permutation)
-// before anything else, so a workgroup's whole weight stream is in flight at
-// once.  The activation rows are staged once per workgroup in LDS, 16-byte
+// Each wave loads all of its codes before anything else, so a workgroup's
+// whole weight stream is in flight at once.  Groups of 256 and 512: 16 bytes
+// per lane per 128-K block, lane group l/16 taking words 4(l/16) .. 4(l/16) +
+// 3 of its row's block and using word t in MFMA step t (the activations read
+// with the same K permutation).  Group 32 (G32): MFMA step t of a block must
+// cover exactly group t, so lane group l/16 needs word 4t + l/16: the same
+// 16-byte loads, then a 4 x 4 transpose of the words across the four lane
+// groups (two exchange steps, lanes 16 and 32 apart); every step closes its
+// group.  The activation rows are staged once per workgroup in LDS, 16-byte
 // chunk q of row m at position q ^ (m & 15) (fragment reads conflict-free).
 // The slices' results are added through LDS in slice order 0, 1, ..., so
 // the output is deterministic.
@@ -293,9 +297,9 @@ struct SmqArgs {
     float hscale;            // 512^-1/2
 };
 constexpr int kSmqXPer = 8;                      // activation chunks per thread and round
-constexpr size_t kSmqLds = 64 * 1024;            // activation rows + slice sums, at most
+constexpr size_t kSmqLds = 160 * 1024;           // activation rows + slice sums, at most
 
-template <int NB, bool HAD>
+template <int NB, bool HAD, bool G32>
 __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -315,12 +319,29 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
 
     // codes and scales of this lane's row and slice: issued first
     u32x4 q[NB];
-    const uint8_t* crow = a.codes + (size_t)n * (a.K / 2) + k0 / 2 + 16 * lk;
+    uint32_t sc[G32 ? 2 * NB : 2];
+    if (G32) {
+        // words 4lk .. 4lk + 3 of each block (transposed below), and the
+        // scales of groups 4u .. 4u + 3 as one 8-byte load per block (row
+        // and slice offsets are multiples of 4 groups: K % 128 == 0)
+        const uint8_t* crow = a.codes + (size_t)n * (a.K / 2) + k0 / 2 + 16 * lk;
 #pragma unroll
-    for (int u = 0; u < NB; ++u) q[u] = nt_load(reinterpret_cast<const u32x4*>(crow + 64 * u));
-    uint32_t sc[2];
-    sc[0] = gload(a.scales + (size_t)n * a.G + k0 / a.group);
-    sc[1] = gload(a.scales + (size_t)n * a.G + (k0 + KR - 1) / a.group);
+        for (int u = 0; u < NB; ++u) q[u] = nt_load(reinterpret_cast<const u32x4*>(crow + 64 * u));
+        const u32x2* srow =
+            reinterpret_cast<const u32x2*>(a.scales + (size_t)n * a.G + k0 / 32);
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const u32x2 v = gload(srow + u);
+            sc[2 * u] = v[0];
+            sc[2 * u + 1] = v[1];
+        }
+    } else {
+        const uint8_t* crow = a.codes + (size_t)n * (a.K / 2) + k0 / 2 + 16 * lk;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) q[u] = nt_load(reinterpret_cast<const u32x4*>(crow + 64 * u));
+        sc[0] = gload(a.scales + (size_t)n * a.G + k0 / a.group);
+        sc[1] = gload(a.scales + (size_t)n * a.G + (k0 + KR - 1) / a.group);
+    }
 
     // activation rows -> LDS, in rounds of kSmqXPer chunks per thread (all of
     // a round's loads before its stores)
@@ -385,9 +406,61 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
     const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 tot = zero, acc = zero, a136 = zero;
+    if (G32) {
+        // Lane group r holds row r of the block's 4 x 4 word matrix
+        // M[r][c] = word 4r + c; two exchange steps leave it column r,
+        // q[u][t] = M[t][r] = word 4t + r.  Step 1 pairs lane groups r, r ^ 1
+        // (lanes 16 apart) and swaps M[even r][odd c] with M[odd r][even c];
+        // step 2 pairs r, r ^ 2 (lanes 32 apart) and swaps positions 2, 3 of
+        // the lower pair with positions 0, 1 of the upper pair.
+        const bool b0 = (lk & 1) != 0, b1 = (lk & 2) != 0;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            u32x4 v = q[u];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t snd = b0 ? v[2 * h] : v[2 * h + 1];
+                const uint32_t rcv = (uint32_t)__shfl_xor((int)snd, 16, 64);
+                if (b0)
+                    v[2 * h] = rcv;
+                else
+                    v[2 * h + 1] = rcv;
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t snd = b1 ? v[h] : v[2 + h];
+                const uint32_t rcv = (uint32_t)__shfl_xor((int)snd, 32, 64);
+                if (b1)
+                    v[h] = rcv;
+                else
+                    v[2 + h] = rcv;
+            }
+            q[u] = v;
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int cq = (k0 + 128 * u + 32 * t + 8 * lk) / 8;
+                const u32x4 xa = xrow[cq ^ xsw];
+                const uint32_t w = q[u][t];
+                const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k),
+                                  decode_pair(w, 2, k), decode_pair(w, 3, k)};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                              __builtin_bit_cast(bf16x8, bv),
+                                                              zero, 0, 0, 0);
+                a136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
+                                                               __builtin_bit_cast(bf16x8, b136),
+                                                               zero, 0, 0, 0);
+                const uint32_t sw = sc[2 * u + (t >> 1)];
+                const float s = __uint_as_float((t & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tot[r] = fmaf(s, acc[r] - a136[r], tot[r]);
+            }
+    }
     const int bpg = a.group / 128;               // blocks per group
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
+    for (int u = 0; u < NB && !G32; ++u) {
         const bool first = (u % bpg) == 0;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -440,17 +513,20 @@ struct SmqPlan {
     size_t lds;
 };
 
-// The matrix-core small-M plan, when the shape allows it: groups of 256 or
-// 512, each wave's K slice (<= 512) a whole number of groups, the activation
-// rows within the LDS budget.
+// The matrix-core small-M plan, when the shape allows it: groups of 32, 256
+// or 512, each wave's K slice (<= 512) a whole number of 128-K blocks and of
+// groups, the activation rows within the LDS budget (a CU's 160 KB).  Group
+// 32 from 5 rows: below that the vector-ALU kernel measured faster (N = 12288,
+// K = 1536: 5.0 against 6.2 us at 2 rows, 10.1 against 6.7 us at 8).
 static SmqPlan plan_smq(int M, int N, int K, int group) {
     SmqPlan p{};
     p.ok = false;
-    if (M > 16 || (group != 256 && group != 512) || K % 128 != 0) return p;
-    const int G = K / group;
+    if (M > 16 || (group != 32 && group != 256 && group != 512) || K % 128 != 0) return p;
+    if (group == 32 && M < 5) return p;
+    const int units = group == 32 ? K / 128 : K / group;   // slices hold whole units
     int KS = 0;
-    for (int ks = 1; ks <= 16 && ks <= G; ++ks)
-        if (G % ks == 0 && K / ks <= 512) {
+    for (int ks = 1; ks <= 16 && ks <= units; ++ks)
+        if (units % ks == 0 && K / ks <= 512) {
             KS = ks;
             break;
         }
@@ -528,6 +604,28 @@ static void launch_mt(bool lds, dim3 g, dim3 b, size_t shm, hipStream_t s,
         smallm_kernel<MT, false><<<g, b, 0, s>>>(a);
 }
 
+// More than 64 KB of dynamic LDS needs the kernel's limit raised once.
+template <int NB, bool HAD, bool G32>
+static void launch_smq_nb(dim3 g, dim3 b, size_t shm, hipStream_t s, const SmqArgs& a) {
+    static bool raised = false;
+    if (shm > 64 * 1024 && !raised) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&smallm_mfma_kernel<NB, HAD, G32>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmqLds);
+        raised = true;
+    }
+    smallm_mfma_kernel<NB, HAD, G32><<<g, b, shm, s>>>(a);
+}
+
+template <bool HAD, bool G32>
+static void launch_smq(int NB, dim3 g, dim3 b, size_t shm, hipStream_t s, const SmqArgs& a) {
+    switch (NB) {
+        case 1: launch_smq_nb<1, HAD, G32>(g, b, shm, s, a); break;
+        case 2: launch_smq_nb<2, HAD, G32>(g, b, shm, s, a); break;
+        case 3: launch_smq_nb<3, HAD, G32>(g, b, shm, s, a); break;
+        default: launch_smq_nb<4, HAD, G32>(g, b, shm, s, a); break;
+    }
+}
+
 int launch_smallm(const void* packed, int N, int K, int group, int M,
                   const uint16_t* X, int ldx, void* Y, int ldy, int ydt,
                   hipStream_t s, int had_block) {
@@ -568,20 +666,16 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
         b.had = had_block;
         b.hscale = (float)(1.0 / __builtin_sqrt(512.0));   // as the transform kernel
         const dim3 g(mp.grid), bl(64 * mp.RG * mp.KS);
-        if (had_block) {
-            switch (mp.NB) {
-                case 1: smallm_mfma_kernel<1, true><<<g, bl, mp.lds, s>>>(b); break;
-                case 2: smallm_mfma_kernel<2, true><<<g, bl, mp.lds, s>>>(b); break;
-                case 3: smallm_mfma_kernel<3, true><<<g, bl, mp.lds, s>>>(b); break;
-                default: smallm_mfma_kernel<4, true><<<g, bl, mp.lds, s>>>(b); break;
-            }
+        if (group == 32) {
+            if (had_block)
+                launch_smq<true, true>(mp.NB, g, bl, mp.lds, s, b);
+            else
+                launch_smq<false, true>(mp.NB, g, bl, mp.lds, s, b);
         } else {
-            switch (mp.NB) {
-                case 1: smallm_mfma_kernel<1, false><<<g, bl, mp.lds, s>>>(b); break;
-                case 2: smallm_mfma_kernel<2, false><<<g, bl, mp.lds, s>>>(b); break;
-                case 3: smallm_mfma_kernel<3, false><<<g, bl, mp.lds, s>>>(b); break;
-                default: smallm_mfma_kernel<4, false><<<g, bl, mp.lds, s>>>(b); break;
-            }
+            if (had_block)
+                launch_smq<true, false>(mp.NB, g, bl, mp.lds, s, b);
+            else
+                launch_smq<false, false>(mp.NB, g, bl, mp.lds, s, b);
         }
         return hip_fail(hipGetLastError(), "smallM launch");
     }

@@ -238,8 +238,16 @@ def test_describe_dispatch_tile_table(L):
     assert w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm")
     assert w4.describe_dispatch(9, 12288, 1536, 256).startswith("smallm mfma")
     assert w4.describe_dispatch(16, 12288, 1536, 256).startswith("smallm mfma")
-    assert w4.describe_dispatch(8, 12288, 1536, 32).startswith("smallm MT=8")
-    assert w4.describe_dispatch(16, 12288, 1536, 32).startswith("mfma")
+    assert w4.describe_dispatch(8, 12288, 1536, 32).startswith("smallm mfma")
+    assert w4.describe_dispatch(16, 12288, 1536, 32).startswith("smallm mfma")
+    # group 32 below 5 rows, and K not a multiple of 128: vector ALU
+    assert w4.describe_dispatch(4, 12288, 1536, 32).startswith("smallm MT=4")
+    assert w4.describe_dispatch(8, 97, 288, 32).startswith("smallm MT=8")
+    # activation rows within a CU's LDS: matrix cores; past it (16 x 6144
+    # bf16 = 192 KB) the tiled kernel
+    assert w4.describe_dispatch(8, 1536, 6144, 32).startswith("smallm mfma")
+    assert w4.describe_dispatch(16, 1536, 2048, 32).startswith("smallm mfma")
+    assert w4.describe_dispatch(16, 1536, 6144, 32).startswith("mfma")
     assert w4.describe_dispatch(17, 12288, 1536, 256).startswith("mfma")
     assert w4.describe_dispatch(64, 12288, 1536, 256).startswith("mfma")
     with pytest.raises(w4.W4Error):

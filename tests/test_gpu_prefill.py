@@ -75,7 +75,8 @@ def test_fwht_twice_is_identity_within_rounding():
 
 @pytest.mark.parametrize("M", [2, 3, 4, 5, 8, 11, 16])
 @pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (97, 288, 32), (1536, 6144, 32),
-                                   (33, 16384, 32), (65, 1024, 256), (129, 1536, 512)])
+                                   (33, 16384, 32), (65, 1024, 256), (129, 1536, 512),
+                                   (12288, 1536, 32), (1000, 2048, 32), (2560, 1536, 32)])
 def test_smallm_vs_oracle(oracle_mod, M, N, K, g):
     note("smallM M=%d N=%d K=%d g=%d" % (M, N, K, g))
     case = synth.make_case("smallm", N, K, g, M, 10 * M + N + K, "bf16")
@@ -102,10 +103,10 @@ def test_smallm_largest_k(oracle_mod, M, N, g):
 
 
 @pytest.mark.parametrize("M", [2, 8, 16])
-@pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (129, 1536, 512)])
+@pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (129, 1536, 512), (12288, 1536, 32)])
 def test_smallm_vector_alu_path(oracle_mod, monkeypatch, M, N, K, g):
-    """The vector-ALU small-M kernels on the rotated formats, which the
-    matrix-core small-M kernel otherwise takes (W4_SMALLM_MFMA=0 keeps them)."""
+    """The vector-ALU small-M kernels on shapes the matrix-core small-M
+    kernel otherwise takes (W4_SMALLM_MFMA=0 keeps them)."""
     monkeypatch.setenv("W4_SMALLM_MFMA", "0")
     note("smallM vector ALU M=%d N=%d K=%d g=%d" % (M, N, K, g))
     assert not w4.describe_dispatch(M, N, K, g).startswith("smallm mfma") or M > 8
@@ -135,10 +136,11 @@ def test_smallm_fused_transform_bitwise(M):
     assert np.array_equal(Yf, Ys)
 
 
-def test_smallm_mfma_code8_columns_exact_zero():
+@pytest.mark.parametrize("g", [256, 32])
+def test_smallm_mfma_code8_columns_exact_zero(g):
     """Columns whose codes are all 8 are exactly zero through the matrix-core
     small-M kernel (the offset chain goes through the same arithmetic)."""
-    M, N, K, g = 8, 200, 1536, 256
+    M, N, K = 8, 200, 1536
     assert w4.describe_dispatch(M, N, K, g).startswith("smallm mfma")
     rng = np.random.default_rng(6)
     P, S = synth.draw_weights(rng, N, K, g)
@@ -151,12 +153,12 @@ def test_smallm_mfma_code8_columns_exact_zero():
     assert np.all(Y[:, 4] != 0.0)
 
 
-def test_smallm_rows_equal_gemv_bitwise():
-    """Each row of the small-M product equals the batch-1 GEMV of that row
-    within fp32 rounding of a different summation order; row m only depends
-    on X[m]."""
+@pytest.mark.parametrize("K", [1536, 288])
+def test_smallm_rows_equal_gemv_bitwise(K):
+    """Row m of the small-M product depends on X[m] only, bit for bit (the
+    matrix-core kernel at K = 1536, the vector-ALU kernel at K = 288)."""
     import torch
-    N, K, g, M = 2560, 1536, 32, 5
+    N, g, M = 2560, 32, 5
     case = synth.make_case("rows", N, K, g, M, 77, "f32")
     packed = upload_packed(case.P, case.S, N, K, g)
     X = to_dev_bf16(case.X)
