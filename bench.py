@@ -259,6 +259,45 @@ def time_prefill(torch, w4, synth, dev):
     return out
 
 
+def time_single_gemv(torch, w4, synth, dev, cases, ops):
+    """The single-GEMV workloads, batch 1: the 256 x 512 case, the four
+    decoder-layer shapes (layer 0 of the sweep) and the 262144 x 1536
+    lm_head.  Warm: 20 calls on one copy, graph-replayed.  Cold: one call on
+    each of at least 1 GiB of distinct device copies of the same packed
+    matrix (the copies count is reported), so the 256 MB last-level cache
+    holds none of them when its turn comes.  The 256 x 512 case (73 KB) is
+    latency-bound and reported warm only."""
+    import numpy as np
+    out = {}
+    c1 = synth.make_case("single", 256, 512, 32, 1, 0, "f32")
+    P = torch.from_numpy(c1.P.view(np.int32)).to(dev)
+    S = torch.from_numpy(c1.S.view(np.int16)).to(dev)
+    p1 = w4.pack(P, S, 256, 512, 32)
+    x1 = torch.from_numpy(c1.X[0].view(np.int16)).to(dev).view(torch.bfloat16)
+    y1 = torch.empty(256, dtype=torch.float32, device=dev)
+    out["256x512_g32"] = {"warm_us": time_calls(torch, lambda: w4.gemv(p1, 256, 512, 32, x1,
+                                                                        "f32", out=y1))}
+    del P, S, p1
+    for idx in (0, 1, 2, 3, len(ops) - 1):
+        packed, N, K, g, x, y = ops[idx]
+        odt = "f32" if y.dtype == torch.float32 else "bf16"
+        name = "%s_%dx%d" % (cases[idx].name.split("_seed")[0], N, K)
+        res = {"warm_us": time_calls(torch, lambda: w4.gemv(packed, N, K, g, x, odt, out=y))}
+        nbytes = cases[idx].weight_bytes
+        n = int(max(2, -(-(1 << 30) // packed.numel())))
+        copies = [packed.clone() for _ in range(n)]
+        it = iter(range(1 << 30))
+        res["cold_us"] = time_calls(torch, lambda: w4.gemv(copies[next(it) % n], N, K, g, x, odt,
+                                                              out=y), calls=n, reps=3)
+        res["cold_copies"] = n
+        res["cold_GBps"] = nbytes / res["cold_us"] / 1e3
+        res["warm_GBps"] = nbytes / res["warm_us"] / 1e3
+        out[name] = res
+        del copies
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_smallm_g32(torch, w4, synth, dev):
     """A few rows through the decode-format (group 32) gate+up weight,
     12288 x 1536: the small-M product at 2, 8 and 16 rows, bf16 out."""
@@ -396,6 +435,7 @@ def main():
             "ms_per_1222.8MiB_at_this_rate": 1282203648 / (value * 1e9) * 1e3,
             "modes": results,
             "trials_us": trials,
+            "single_gemv": time_single_gemv(torch, w4, synth, dev, cases, ops),
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
             "smallm_g32_N12288_K1536": time_smallm_g32(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
