@@ -453,8 +453,8 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) 
     if (M < 1) return fail(W4_ERR_SHAPE, "describe: M must be >= 1");
     if (M == 1) {
         const GemvTile t = pick_gemv_tile(N, K, group);
-        snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d", t.generic ? "_generic" : "",
-                 t.L, t.U, t.waves, t.grid);
+        snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d%s", t.generic ? "_generic" : "",
+                 t.L, t.U, t.waves, t.grid, t.contig ? " contiguous" : "");
     } else if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group))) {
         describe_smallm(M, N, K, group, buf, len);
     } else {

@@ -17,6 +17,7 @@ struct GemvTile {
     int waves = 4;
     int grid = 1;
     bool generic = false;
+    bool contig = false;   // contiguous row-group ranges per wave (large N)
 };
 
 GemvTile pick_gemv_tile(int N, int K, int group);

@@ -27,6 +27,23 @@ __global__ __launch_bounds__(256) void gemv_xreg_kernel(GemvArgs a) {
     gemv_rows<L, U, FULLC>(a, blockIdx.x * nw + wave, NG, gridDim.x * nw, lane, k);
 }
 
+// Large matrices (e.g. a 262144-row output layer): every wave streams one
+// contiguous range of row groups with the next row group in flight and the
+// outputs written in 64-row blocks, as one op of the decode-step stream
+// kernel does; 16 waves per CU (<= 128 VGPRs).
+template <int L, int U>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void gemv_contig_kernel(GemvArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const DecodeConsts k = decode_consts();
+    const int NG = (a.N + 64 / L - 1) / (64 / L);
+    const long long W = (long long)gridDim.x * nw, w = (long long)blockIdx.x * nw + wave;
+    const int rg0 = (int)(w * NG / W), rg1 = (int)((w + 1) * NG / W);
+    gemv_rows<L, U, true, 2, true>(a, rg0, rg1, 1, lane, k);
+}
+
 template <int L>
 __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
     const int lane = threadIdx.x & 63;
@@ -37,8 +54,23 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
     gemv_rows_generic<L>(a, blockIdx.x * nw + wave, NG, gridDim.x * nw, lane, k);
 }
 
+// Row groups from which a full-width tiling of at most 3 chunks per lane
+// streams contiguous ranges: 16 per wave of 16 waves per CU.
+constexpr int kContigWaves = kNumCUs * 16;
+constexpr int kContigRowGroups = 16 * kContigWaves;
+
 template <int L, int U>
-static void launch_xreg_LU(bool full, dim3 g, dim3 b, hipStream_t s, const GemvArgs& a) {
+static void contig_launch(dim3 g, hipStream_t s, const GemvArgs& a) {
+    if constexpr (U <= 3) gemv_contig_kernel<L, U><<<g, dim3(256), 0, s>>>(a);
+}
+
+template <int L, int U>
+static void launch_xreg_LU(bool full, bool contig, dim3 g, dim3 b, hipStream_t s,
+                           const GemvArgs& a) {
+    if (contig) {
+        contig_launch<L, U>(g, s, a);
+        return;
+    }
     if (full)
         gemv_xreg_kernel<L, U, true><<<g, b, 0, s>>>(a);
     else
@@ -46,17 +78,18 @@ static void launch_xreg_LU(bool full, dim3 g, dim3 b, hipStream_t s, const GemvA
 }
 
 template <int L>
-static void launch_xreg_L(int U, dim3 g, dim3 b, hipStream_t s, const GemvArgs& a) {
+static void launch_xreg_L(int U, bool contig, dim3 g, dim3 b, hipStream_t s,
+                          const GemvArgs& a) {
     const bool full = L * U == a.C;
     switch (U) {
-        case 1: launch_xreg_LU<L, 1>(full, g, b, s, a); break;
-        case 2: launch_xreg_LU<L, 2>(full, g, b, s, a); break;
-        case 3: launch_xreg_LU<L, 3>(full, g, b, s, a); break;
-        case 4: launch_xreg_LU<L, 4>(full, g, b, s, a); break;
-        case 5: launch_xreg_LU<L, 5>(full, g, b, s, a); break;
-        case 6: launch_xreg_LU<L, 6>(full, g, b, s, a); break;
-        case 7: launch_xreg_LU<L, 7>(full, g, b, s, a); break;
-        default: launch_xreg_LU<L, 8>(full, g, b, s, a); break;
+        case 1: launch_xreg_LU<L, 1>(full, contig, g, b, s, a); break;
+        case 2: launch_xreg_LU<L, 2>(full, contig, g, b, s, a); break;
+        case 3: launch_xreg_LU<L, 3>(full, contig, g, b, s, a); break;
+        case 4: launch_xreg_LU<L, 4>(full, contig, g, b, s, a); break;
+        case 5: launch_xreg_LU<L, 5>(full, contig, g, b, s, a); break;
+        case 6: launch_xreg_LU<L, 6>(full, contig, g, b, s, a); break;
+        case 7: launch_xreg_LU<L, 7>(full, contig, g, b, s, a); break;
+        default: launch_xreg_LU<L, 8>(full, contig, g, b, s, a); break;
     }
 }
 
@@ -122,6 +155,12 @@ GemvTile pick_gemv_tile(int N, int K, int group) {
     }
     const int R = 64 / t.L;
     const int NG = (N + R - 1) / R;
+    if (!t.generic && t.L * t.U == C && t.U <= 3 && t.waves == 4 && NG >= kContigRowGroups &&
+        !getenv("W4_GEMV_TILE")) {
+        t.contig = true;
+        t.grid = kContigWaves / 4;
+        return t;
+    }
     const int waves = NG < target ? NG : target;
     t.grid = (waves + t.waves - 1) / t.waves;
     if (t.grid < 1) t.grid = 1;
@@ -141,10 +180,10 @@ int launch_gemv(const GemvTile& t, const void* packed, int N, int K, int group,
         }
     } else {
         switch (t.L) {
-            case 8: launch_xreg_L<8>(t.U, g, b, s, a); break;
-            case 16: launch_xreg_L<16>(t.U, g, b, s, a); break;
-            case 32: launch_xreg_L<32>(t.U, g, b, s, a); break;
-            default: launch_xreg_L<64>(t.U, g, b, s, a); break;
+            case 8: launch_xreg_L<8>(t.U, t.contig, g, b, s, a); break;
+            case 16: launch_xreg_L<16>(t.U, t.contig, g, b, s, a); break;
+            case 32: launch_xreg_L<32>(t.U, t.contig, g, b, s, a); break;
+            default: launch_xreg_L<64>(t.U, t.contig, g, b, s, a); break;
         }
     }
     return hip_fail(hipGetLastError(), "gemv launch");
