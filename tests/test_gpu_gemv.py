@@ -103,7 +103,9 @@ RAGGED = [(1, 32, 32), (3, 64, 32), (33, 96, 32), (65, 288, 32), (97, 1056, 32),
           # group 512 (the int4 g512 build): odd and even group counts per row
           (100, 1536, 512), (33, 1024, 512), (12288, 1536, 512), (65, 6144, 512),
           # the largest K the calls accept (2^20)
-          (3, 1 << 20, 32), (2, 1 << 20, 512)]
+          (3, 1 << 20, 32), (2, 1 << 20, 512),
+          # large N on the contiguous-range kernel, ragged row groups and ranges
+          (262141, 1536, 32), (65539, 6144, 32)]
 
 
 @pytest.mark.parametrize("N,K,g", RAGGED)
