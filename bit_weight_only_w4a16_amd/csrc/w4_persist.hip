@@ -23,8 +23,12 @@
 //    slices from LDS.
 //  - Ordering (PERSISTENT mode).  Before a workgroup reads op i's activations
 //    it waits until every workgroup has published "op i-1 done" (one flag
-//    word per workgroup, release/acquire at agent scope); so nothing of op i
-//    is computed before op i-1's outputs are all written, as in a decode step.
+//    word per workgroup); so nothing of op i is computed before op i-1's
+//    outputs are all written, as in a decode step.  Outputs are stored and
+//    activations loaded with agent-scope (L2-bypassing) accesses, and a
+//    workgroup publishes its flag only after its output stores have
+//    completed, so no whole-L2 write-back or invalidate is needed (those
+//    cost ~11 us per op: 2.5 ms against 0.93 ms per sweep).
 //  - Safety.  Flags carry an epoch (launch count / grid) so replays need no
 //    reset.  Every wait is bounded; a wait that gives up sets an error word,
 //    and every other wait then gives up too, so the grid always drains.
@@ -79,6 +83,16 @@ __device__ __forceinline__ void load_tile(const SweepOp& op, int rg, int lane, T
     }
 }
 
+// Agent-scope stores of an output: visible to every CU once they complete.
+__device__ __forceinline__ void store_out_agent(void* y, size_t i, float v, int ydt) {
+    if (ydt == W4_BF16)
+        __hip_atomic_store(static_cast<uint16_t*>(y) + i, (uint16_t)f32_to_bf16_rne(v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_store(static_cast<uint32_t*>(y) + i, __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ void compute_tile(const SweepOp& op, int rg, int lane,
                                              const TileRegs& t, const uint32_t* xs,
                                              const float* bs, const DecodeConsts& k) {
@@ -111,7 +125,7 @@ __device__ __forceinline__ void compute_tile(const SweepOp& op, int rg, int lane
     else
         acc = group_sum<64>(acc);
     const int n = rg * op.R + lr;
-    if (lk == 0 && n < op.N) store_out(op.y, (size_t)n, acc, op.ydt);
+    if (lk == 0 && n < op.N) store_out_agent(op.y, (size_t)n, acc, op.ydt);
 }
 
 // Thread t < C writes chunk t of the activation (held in v) and its negated
@@ -129,9 +143,13 @@ __device__ __forceinline__ void put_chunk(const u32x4 (&v)[4], int t, uint32_t* 
     bs[t] = -chunk_bias(xr);
 }
 
+// Agent-scope loads of an activation chunk (an activation written by another
+// CU's op is never read from a stale L2 line).
 __device__ __forceinline__ void get_chunk(const SweepOp& op, int t, u32x4 (&v)[4]) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(op.x + 4 * t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = gload(op.x + 4 * t + i);
+    for (int i = 0; i < 16; ++i)
+        v[i >> 2][i & 3] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ unsigned wave_min(unsigned v) {
@@ -176,9 +194,7 @@ __device__ __forceinline__ bool wait_all(SweepCtl* ctl, int nflags, unsigned tar
         }
     }
     __syncthreads();
-    const bool ok = *s_ok != 0;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return ok;
+    return *s_ok != 0;
 }
 
 // PERSISTENT mode: decode order.  Every workgroup takes part in every op
@@ -231,12 +247,16 @@ __global__ __launch_bounds__(kPwThreads) void ordered_kernel(const SweepOp* __re
             prg = nrg;
         }
 
-        // publish "op i done": every wave's outputs are written (barrier),
-        // then one release at agent scope and the flag
+        // publish "op i done": every wave waits until its agent-scope output
+        // stores have completed (all counters 0: the stores may be flat
+        // accesses, which count in vmcnt and lgkmcnt), the barrier joins the
+        // waves, then the flag
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
         __syncthreads();
         if (tid == 0)
             __hip_atomic_store(&ctl->flags[blockIdx.x], ebase + (unsigned)i + 1u,
-                               __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
