@@ -146,8 +146,15 @@ static int setup_persistent(w4_sweep* h) {
         static const double kRoundWeight[4] = {1.2, 1.1, 0.9, 0.8};
         const int per_round = ncu * kPwWaves;   // waves per dispatch round
         std::vector<double> cum((size_t)parts + 1, 0.0);
-        for (int w = 0; w < parts; ++w)
-            cum[w + 1] = cum[w] + (bpc == 4 ? kRoundWeight[w / per_round] : 1.0);
+        for (int w = 0; w < parts; ++w) {
+            // workgroup b runs on XCD b % 8; even-numbered XCDs streamed
+            // ~7% slower in every timestamped run, so their waves take 0.97
+            // of a share and the odd ones 1.03 (138.3 -> 136.7 us; 0.95 :
+            // 1.05 and the inverse were slower)
+            const int b = w / kPwWaves;
+            const double xw = (b & 1) ? 1.03 : 0.97;
+            cum[w + 1] = cum[w] + (bpc == 4 ? kRoundWeight[w / per_round] * xw : 1.0);
+        }
         int b = 0;
         double at = 0.0;  // byte offset of the current tile
         for (int i = 0; i < n && b <= parts; ++i) {
