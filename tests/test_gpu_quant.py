@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 CASES = [  # N, K, group, had_block
     (33, 512, 32, 0), (64, 1536, 256, 512), (100, 1536, 32, 512), (7, 96, 32, 0),
     (5, 768, 256, 256), (65, 2048, 32, 64), (12288, 1536, 256, 512), (1536, 6144, 32, 512),
-    (300, 1536, 512, 512), (17, 1024, 512, 0),
+    (300, 1536, 512, 512), (17, 1024, 512, 0), (40, 640, 32, 128), (9, 1152, 32, 128),
 ]
 
 
