@@ -134,9 +134,10 @@ int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
 /*
  * Y = X W^T for 2 <= M <= 16 activation rows, reading each weight byte once
  * for all M rows ([P2] "Why AMX for GEMM but not for attention": a weight GEMM
- * reuses each byte across all M rows).  Groups 256 and 512 (when the rows fit
- * the kernel's 64 KB of LDS) multiply one 16-row tile on the matrix cores;
- * group 32 and larger shapes run on the vector ALU.
+ * reuses each byte across all M rows).  When the activation rows fit a CU's
+ * 160 KB of LDS and K % 128 == 0, one 16-row tile runs on the matrix cores
+ * for groups 256 and 512, and for group 32 from 5 rows; other shapes run on
+ * the vector ALU.
  *  X: device, M rows of K bf16, row stride ldx >= K elements (ldx % 8 == 0),
  *     16-byte aligned.
  *  Y: device, M rows of N y_dtype elements, row stride ldy >= N elements.
@@ -169,8 +170,8 @@ size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block);
  *  group must be 256 or 512 (the rotated prefill format of [P2]) or 32.
  *  M >= 1, K % 256 == 0.  Decode-shaped row counts take the decode kernels
  *  after the same transform: M = 1 the GEMV; 2..8 the small-M product, and
- *  9..16 too where it runs on the matrix cores (groups 256 and 512).  Larger
- *  row counts run on the tiled matrix-core kernels.
+ *  9..16 too where it runs on the matrix cores (see w4a16_gemm_smallM).
+ *  Larger row counts run on the tiled matrix-core kernels.
  *  X: device, stride ldx (% 8 == 0).  Y: device, stride ldy.
  *  workspace: device, >= w4a16_gemm_workspace_bytes(M, K, had_block) bytes,
  *  16-byte aligned (may be NULL when that size is 0).
