@@ -456,6 +456,14 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one sweep")
         cpu = cpu_baseline(cases)
+        if not args.no_extra:
+            # the same oracle on one host thread, on decoder layer 0's four
+            # GEMVs (19.9 MB), scaled to a whole sweep
+            one = cpu_baseline(cases[:4], max_threads=1, min_seconds=1.0, max_passes=5)
+            extra["cpu_oracle_one_thread"] = {
+                "GBps": one["value"], "sample": one["sample"].replace(
+                    "full decode-step sweep(s) (141 GEMVs", "pass(es) over decoder layer 0 (4 GEMVs"),
+                "ms_per_sweep_scaled": weight_bytes / one["value"] / 1e6}
 
     out = {
         "metric": METRIC,
