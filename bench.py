@@ -226,7 +226,18 @@ def time_twin(torch, w4, synth, dev):
     return out
 
 
-def time_prefill(torch, w4, synth, dev):
+def time_mfma_probe(torch, w4):
+    """Measured matrix-core ceiling: back-to-back independent bf16 MFMAs from
+    registers at two waves per SIMD (w4_probe_mfma)."""
+    iters = 512
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    us = time_calls(torch, lambda: w4.probe_mfma(iters, out), calls=10, reps=5)
+    flops = 2048.0 * iters * 16 * 16384
+    return {"iters": iters, "us": us, "TFLOPs": flops / us / 1e6,
+            "pct_of_2.5PF_bf16": flops / us / 1e6 / 2500 * 100}
+
+
+def time_prefill(torch, w4, synth, dev, mfma_tflops=None):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
     cores); also the transform alone and the product without it."""
@@ -252,6 +263,8 @@ def time_prefill(torch, w4, synth, dev):
         t = res["gemm_us"] * 1e-6
         res["gemm_TFLOPs"] = flops / t / 1e12
         res["gemm_pct_of_2.5PF_bf16"] = flops / t / 2.5e15 * 100
+        if mfma_tflops:
+            res["gemm_pct_of_mfma_probe"] = flops / t / 1e12 / mfma_tflops * 100
         res["gemm_weight_GBps"] = c.weight_bytes / t / 1e9
         out["M%d" % M] = res
         del P, S, packed, X, Y, Xr, ws
@@ -427,6 +440,7 @@ def main():
     value = weight_bytes / (ms * 1e-3) / 1e9
 
     if not args.no_extra:
+        mfma = time_mfma_probe(torch, w4)
         extra = {
             "pct_of_8TBps_spec": value / PEAK_HBM_GBPS * 100,
             "probe_read_4GiB_GBps": probe,
@@ -436,7 +450,8 @@ def main():
             "modes": results,
             "trials_us": trials,
             "single_gemv": time_single_gemv(torch, w4, synth, dev, cases, ops),
-            "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev),
+            "mfma_probe": mfma,
+            "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev, mfma["TFLOPs"]),
             "smallm_g32_N12288_K1536": time_smallm_g32(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
             "quantize_rotate": time_quantize(torch, w4, synth, dev),

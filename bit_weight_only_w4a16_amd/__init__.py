@@ -47,7 +47,7 @@ EXPORTS = (
     "w4_gather", "w4_quantize", "w4_quantize_rows_i8", "w4_gemm_i8",
     "w4a16_gemm_twin_workspace_bytes", "w4a16_gemm_twin", "w4_attn_workspace_bytes",
     "w4_attn_decode",
-    "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy",
+    "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy", "w4_probe_mfma",
 )
 
 
@@ -125,6 +125,7 @@ def lib():
             "w4_attn_store_kv": ([vp, vp, i, vp, i, vp, i, vp], i),
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
+            "w4_probe_mfma": ([i, vp, vp], i),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -454,6 +455,16 @@ def probe_read(buf, nbytes: int = None, out=None, stream=None):
     if out is None:
         out = torch.empty(1, dtype=torch.int32, device=buf.device)
     _check(lib().w4_probe_read(_ptr(buf), nbytes, _ptr(out), _stream(stream)))
+    return out
+
+
+def probe_mfma(iters: int, out=None, stream=None):
+    """Matrix-core throughput probe: 2048 waves x iters x 16 bf16 MFMAs
+    (16384 FLOP each) from registers; returns the (untouched) out buffer."""
+    import torch
+    if out is None:
+        out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    _check(lib().w4_probe_mfma(int(iters), _ptr(out), _stream(stream)))
     return out
 
 

@@ -473,6 +473,14 @@ int w4_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream) {
     return launch_probe_read(buf, bytes, out, static_cast<hipStream_t>(stream));
 }
 
+int w4_probe_mfma(int iters, float* out, void* stream) {
+    if (iters < 1 || iters > (1 << 20))
+        return fail(W4_ERR_SHAPE, "probe: iters must be in 1..2^20 (got %d)", iters);
+    if (!out) return fail(W4_ERR_ARG, "probe: out is NULL");
+    if (!aligned(out, 4)) return fail(W4_ERR_ALIGN, "probe: out must be 4-byte aligned");
+    return launch_probe_mfma(iters, out, static_cast<hipStream_t>(stream));
+}
+
 int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
     W4_TRY(check_in16(src, "src"));
     W4_TRY(check_in16(dst, "dst"));

@@ -95,6 +95,40 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict
         __builtin_nontemporal_store(nt_load(src + i), dst + i);
 }
 
+// Matrix-core throughput: every wave runs `iters` rounds of 16 independent
+// v_mfma_f32_16x16x32_bf16 chains (no memory traffic), two waves per SIMD as
+// the prefill kernels run.  The sum of the accumulators is stored only if it
+// is negative, which it never is (all operands are positive), so the work
+// cannot be dropped and nothing is written.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void probe_mfma_kernel(int iters, float* out) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const uint32_t lane = threadIdx.x & 63;
+    // bf16 pairs of values in [1, 2): 0x3F80 | small mantissa bits
+    const u32x4 a = {0x3F803F80u | (lane & 7u), 0x3F813F80u, 0x3F823F80u, 0x3F833F80u | (lane >> 3)};
+    const u32x4 b = {0x3F843F80u, 0x3F853F80u | (lane & 3u), 0x3F863F80u, 0x3F873F80u};
+    f32x4 acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, b),
+                                                             acc[j], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += (acc[j][0] + acc[j][1]) + (acc[j][2] + acc[j][3]);
+    if (sum < 0.f) gstore(out, sum);
+}
+
+int launch_probe_mfma(int iters, float* out, hipStream_t s) {
+    probe_mfma_kernel<<<dim3(kNumCUs * 2), dim3(256), 0, s>>>(iters, out);
+    return hip_fail(hipGetLastError(), "probe mfma launch");
+}
+
 int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
     const size_t n16 = bytes / 16;
     size_t blocks = (n16 + 255) / 256;

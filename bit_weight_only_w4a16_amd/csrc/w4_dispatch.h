@@ -74,5 +74,6 @@ void describe_i8(int M, int N, int K, char* buf, size_t len);
 int launch_probe_read(const void* buf, size_t bytes, uint32_t* out,
                       hipStream_t s);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+int launch_probe_mfma(int iters, float* out, hipStream_t s);
 
 }  // namespace w4

@@ -391,6 +391,17 @@ int w4_probe_read(const void* buf, size_t bytes, uint32_t* out, void* stream);
  * reference kernel for calibrating hardware byte counters. */
 int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/*
+ * Matrix-core throughput probe (the measured ceiling the prefill products are
+ * compared with): 512 workgroups of four waves, two waves per SIMD, each wave
+ * running `iters` rounds of 16 independent v_mfma_f32_16x16x32_bf16 chains
+ * from registers; 2 * 16 * 16 * 32 = 16384 FLOP per MFMA, so one call does
+ * 2048 waves * iters * 16 * 16384 FLOP.  Nothing is written (out is touched
+ * only if the positive sum turned negative).  iters in 1..2^20.  out: device,
+ * 4-byte aligned, not NULL.
+ */
+int w4_probe_mfma(int iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -219,6 +219,10 @@ def test_probe_validation(L):
     assert L.w4_probe_read(A16, 24, A16, VP(0)) == -2
     assert L.w4_probe_read(A2, 32, A16, VP(0)) == -3
     assert L.w4_probe_copy(A16, A2, 32, VP(0)) == -3
+    assert L.w4_probe_mfma(0, A16, VP(0)) == -2
+    assert L.w4_probe_mfma((1 << 20) + 1, A16, VP(0)) == -2
+    assert L.w4_probe_mfma(8, VP(0), VP(0)) == -1
+    assert L.w4_probe_mfma(8, A2, VP(0)) == -3
 
 
 def test_describe_dispatch_tile_table(L):

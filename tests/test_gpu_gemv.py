@@ -167,3 +167,23 @@ def test_selftest_passes():
     """The library's own start-up check (closed-form one-hot outputs)."""
     device()
     w4.selftest()
+
+
+def test_probes_run():
+    """The bandwidth and matrix-core probes run and report what they state:
+    the read probe's integer sum, the copy, and an MFMA probe that writes
+    nothing."""
+    import torch
+    device()
+    buf = torch.arange(1 << 16, dtype=torch.int32, device=device())
+    s = w4.probe_read(buf)
+    torch.cuda.synchronize()
+    expect = int(np.arange(1 << 16, dtype=np.int64).sum() % (1 << 32))
+    assert (int(s.item()) & 0xFFFFFFFF) == expect
+    dst = torch.empty_like(buf)
+    w4.probe_copy(buf, dst)
+    out = torch.full((1,), 7.0, dtype=torch.float32, device=device())
+    w4.probe_mfma(4, out)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, buf)
+    assert out.item() == 7.0
