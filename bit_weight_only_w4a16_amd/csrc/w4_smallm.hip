@@ -604,14 +604,18 @@ static void launch_mt(bool lds, dim3 g, dim3 b, size_t shm, hipStream_t s,
         smallm_kernel<MT, false><<<g, b, 0, s>>>(a);
 }
 
-// More than 64 KB of dynamic LDS needs the kernel's limit raised once.
+// More than 64 KB of dynamic LDS needs the kernel's limit raised, once per
+// device (setting it again is harmless, so racing threads are benign; a
+// failure shows as the launch's error).
 template <int NB, bool HAD, bool G32>
 static void launch_smq_nb(dim3 g, dim3 b, size_t shm, hipStream_t s, const SmqArgs& a) {
-    static bool raised = false;
-    if (shm > 64 * 1024 && !raised) {
+    static bool raised[64] = {};
+    int dev = 0;
+    if (shm > 64 * 1024 && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 &&
+        !raised[dev]) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&smallm_mfma_kernel<NB, HAD, G32>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSmqLds);
-        raised = true;
+        raised[dev] = true;
     }
     smallm_mfma_kernel<NB, HAD, G32><<<g, b, shm, s>>>(a);
 }
