@@ -40,7 +40,10 @@ __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
 
 constexpr int kAttnHeads = 8;
 constexpr int kAttnTile = 32;
-constexpr int kAttnMaxWG = 512;
+// split workgroups, at most: one per CU (measured at D = 512: 131072 slots
+// 48.0 -> 45.5 us, 32768 slots 21.3 -> 17.8 us against two per CU; three per
+// CU were slower still): fewer partials for the merge to read
+constexpr int kAttnMaxWG = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
