@@ -122,3 +122,27 @@ def test_sweep_ragged_shapes(oracle_mod, name, mode):
         for gbuf in guards:
             assert np.isnan(from_dev(gbuf[-1:]))[0], "write past N"
     sw.close()
+
+
+@pytest.mark.parametrize("bpc", ["1", "3"])
+def test_sweep_stream_other_grids(oracle_mod, monkeypatch, bpc):
+    """The stream partition at other workgroup counts per CU (equal shares
+    instead of the four-round weighting): every output still computed once
+    and correct, on the ragged op list."""
+    import torch
+    device()
+    monkeypatch.setenv("W4_SWEEP_BLOCKS_PER_CU", bpc)
+    cases, ops = [], []
+    for j, (N, K, g, odt) in enumerate(RAGGED_OPS):
+        c = synth.make_case("grid%d" % j, N, K, g, 1, 700 + j, odt)
+        dt = torch.float32 if odt == "f32" else torch.bfloat16
+        y = torch.full((N,), float("nan"), dtype=dt, device=device())
+        ops.append((upload_packed(c.P, c.S, N, K, g), N, K, g, to_dev_bf16(c.X[0]), y))
+        cases.append(c)
+    note("stream sweep blocks per CU %s ops=%d" % (bpc, len(ops)))
+    sw = w4.DecodeSweep(ops, w4.W4_SWEEP_STREAM)
+    sw.launch()
+    sw.check()
+    torch.cuda.synchronize()
+    _check_all(oracle_mod, cases, ops, "stream bpc %s" % bpc)
+    sw.close()
