@@ -68,7 +68,7 @@ using namespace ring;
 constexpr int kStage = 64;     // K per ring slot
 constexpr int kARow = 128;     // bytes of an activation row in a slot
 constexpr int kBRow = 32;      // bytes of a code row in a slot
-constexpr int kMaxG = 8;       // scale groups per row kept in LDS
+constexpr int kMaxG = 32;      // scale groups per row kept in LDS (K = 8192 at g256)
 
 struct PfArgs {
     const uint32_t* codes;   // N x K/8 device words
@@ -379,11 +379,10 @@ struct PfCfg {
 };
 // 64 x 192, 64 x 128 or 64 x 64 blocks; ring slots; stages per barrier; K
 // groups.  Measured at N = 12288, K = 1536, g256: two stages per barrier beat
-// one (the per-barrier latency chain, not the DMA depth, bounds the loop);
-// 64 x 192 blocks win above 256 rows, 64 x 128 blocks from 129 to 256 rows
-// (19.4 against 21.2 us at 256), 64 x 64 blocks (three times the
-// workgroups) up to 128.  Entries 2 and 3 are the one-stage variants, kept
-// for comparison runs; entries 4 and 5 split K over three or two wave groups.
+// one (the per-barrier latency chain, not the DMA depth, bounds the loop).
+// Entries 0, 6 and 1 are the unsplit block shapes chosen below; entries 2
+// and 3 are the one-stage variants, kept for comparison runs; entries 4 and
+// 5 split K over three or two wave groups.
 constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2, 1}, {4, 1, 6, 2, 1}, {4, 3, 5, 1, 1},
                              {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2},
                              {4, 2, 4, 2, 1}};
@@ -393,11 +392,36 @@ struct PfPlan {
     int cfg, BM, BN, m_blocks, n_blocks, grid;
 };
 
+// Unsplit block shape: all three keep two workgroups per CU, so a launch runs
+// in rounds of 2 * CUs workgroups.  Choose the fewest rounds times the
+// measured time of one full round (N = 12288, K = 1536, g256: 64 x 64 blocks
+// 14.1 us, 64 x 128 20.9 us, 64 x 192 27.6 us), wider blocks on ties.  This
+// picks, at N = 12288, 64 x 64 for 65..128 rows, 64 x 128 for 129..320 and
+// 513..640, 64 x 192 for 321..512 and from 641: the measured best at every
+// row count tried from 80 to 1024.
+static int pick_block_cfg(int M, int N) {
+    static const struct { int cfg, BN; double t_round; } kCand[3] = {
+        {0, 192, 27.6}, {6, 128, 20.9}, {1, 64, 14.1}};
+    const long long slots = 2LL * kNumCUs;
+    const long long mb = (M + 63) / 64;
+    int best = 0;
+    double best_t = 1e300;
+    for (const auto& c : kCand) {
+        const long long wgs = mb * ((N + c.BN - 1) / c.BN);
+        const double t = (double)((wgs + slots - 1) / slots) * c.t_round;
+        if (t < best_t - 1e-9) {   // candidates in decreasing width: ties keep the wider
+            best_t = t;
+            best = c.cfg;
+        }
+    }
+    return best;
+}
+
 PfPlan plan_prefill(int M, int N, int K, int group) {
     PfPlan p;
-    p.cfg = M <= 128 ? 1 : (M <= 256 ? 6 : 0);
-    // 64 x 64 blocks that leave CUs idle (one 64-row block: N / 64 workgroups
-    // of at most one per CU) split K over three or two wave groups.  Measured
+    p.cfg = pick_block_cfg(M, N);
+    // 64 x 64 blocks that leave CUs idle (at most one workgroup per CU)
+    // split K over three or two wave groups.  Measured
     // at N = 12288, K = 1536, g256: 64 rows 11.8 -> 9.0 us, 32 rows 11.6 ->
     // 8.7 us; at 128 rows (768 workgroup slots wanted, one per CU fits) the
     // split is slower (14.4 -> 16.6 us).

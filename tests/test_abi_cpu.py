@@ -254,6 +254,18 @@ def test_describe_dispatch_tile_table(L):
     assert w4.describe_dispatch(16, 1536, 6144, 32).startswith("mfma")
     assert w4.describe_dispatch(17, 12288, 1536, 256).startswith("mfma")
     assert w4.describe_dispatch(64, 12288, 1536, 256).startswith("mfma")
+    # DMA ring: block shape by workgroup rounds, K split for one-block grids,
+    # up to 32 scale groups per row
+    ring = lambda M, N, K, g: w4.describe_dispatch(M, N, K, g).split("block ")[1]
+    assert ring(128, 12288, 1536, 256).startswith("64x64 waves 1x4")
+    assert ring(320, 12288, 1536, 256).startswith("64x128 waves 1x4")
+    assert ring(384, 12288, 1536, 256).startswith("64x192 waves 1x4")
+    assert ring(640, 12288, 1536, 256).startswith("64x128 waves 1x4")
+    assert ring(1024, 12288, 1536, 256).startswith("64x192 waves 1x4")
+    assert ring(64, 1536, 6144, 256).startswith("64x64 waves 3x4")
+    assert ring(256, 4096, 1536, 256).startswith("64x64 waves 3x4")
+    assert ring(64, 1536, 8192, 256).startswith("64x64 waves 2x4")
+    assert "dma-ring" not in w4.describe_dispatch(64, 1536, 1 << 14, 256)  # 64 groups
     with pytest.raises(w4.W4Error):
         w4.describe_dispatch(1, 12288, 1500, 32)
 

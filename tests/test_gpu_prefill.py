@@ -258,6 +258,25 @@ def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
     assert_within(Y, Yr, A, "f32", "tiling %s" % env)
 
 
+@pytest.mark.parametrize("cfg,K,g", [(c, 6144, 256) for c in (0, 1, 4, 5, 6)] +
+                         [(0, 8192, 256), (5, 8192, 256), (4, 8192, 256), (6, 6144, 512)])
+def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
+    """The DMA-ring tilings with 12 to 32 scale groups per row (the
+    down-projection K = 6144 at groups 256 and 512; K = 8192, the most the
+    ring takes), ragged M and N; a split that does not divide the groups
+    falls back unsplit."""
+    monkeypatch.setenv("W4_PREFILL_CFG", str(cfg))
+    M, N = 70, 1000
+    assert "dma-ring" in w4.describe_dispatch(M, N, K, g)
+    note("mfma many groups cfg=%d M=%d N=%d K=%d g=%d" % (cfg, M, N, K, g))
+    case = synth.make_case("groups", N, K, g, M, 91 + cfg, "bf16", outlier_frac=0.01)
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, oracle_mod.bf16_to_f64(case.X), threads=16)
+    Y = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
+    assert_within(Y, Yr, A, "f32", "cfg %d K %d g %d" % (cfg, K, g))
+
+
 def test_matrix_core_code8_columns_exact_zero():
     """Columns whose codes are all 8 are exactly zero through the matrix-core
     path (the offset MFMA goes through the same arithmetic)."""
