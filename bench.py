@@ -272,6 +272,30 @@ def time_prefill(torch, w4, synth, dev, mfma_tflops=None):
     return out
 
 
+def time_gemm_shapes(torch, w4, synth, dev, N, K, group, Ms):
+    """The W4A16 product alone (no transform), bf16 out, at one weight shape
+    and several row counts: the down projection (N = 1536, K = 6144) and the
+    group-32 form of the gate+up shape."""
+    import numpy as np
+    out = {}
+    for M in Ms:
+        c = synth.make_case("gemm_%dx%d_g%d_M%d" % (N, K, group, M), N, K, group, M,
+                            2000 + M, "bf16", outlier_frac=0.01)
+        P = torch.from_numpy(c.P.view(np.int32)).to(dev)
+        S = torch.from_numpy(c.S.view(np.int16)).to(dev)
+        packed = w4.pack(P, S, N, K, group)
+        X = torch.from_numpy(c.X.view(np.int16)).to(dev).view(torch.bfloat16)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        us = time_calls(torch, lambda: w4.gemm(packed, N, K, group, X, 0, "bf16", out=Y))
+        flops = 2.0 * M * N * K
+        out["M%d" % M] = {"kernel": w4.describe_dispatch(M, N, K, group), "gemm_us": us,
+                          "gemm_TFLOPs": flops / us / 1e6,
+                          "gemm_pct_of_2.5PF_bf16": flops / us / 1e6 / 2500 * 100}
+        del P, S, packed, X, Y
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_single_gemv(torch, w4, synth, dev, cases, ops):
     """The single-GEMV workloads, batch 1: the 256 x 512 case, the four
     decoder-layer shapes (layer 0 of the sweep) and the 262144 x 1536
@@ -452,6 +476,10 @@ def main():
             "single_gemv": time_single_gemv(torch, w4, synth, dev, cases, ops),
             "mfma_probe": mfma,
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev, mfma["TFLOPs"]),
+            "prefill_down_g256_N1536_K6144": time_gemm_shapes(torch, w4, synth, dev, 1536,
+                                                              6144, 256, (64, 512)),
+            "prefill_g32_N12288_K1536": time_gemm_shapes(torch, w4, synth, dev, 12288, 1536,
+                                                         32, (64, 512)),
             "smallm_g32_N12288_K1536": time_smallm_g32(torch, w4, synth, dev),
             "gather_bf16": time_gather(torch, w4, synth, dev, ops[-1][0]),
             "quantize_rotate": time_quantize(torch, w4, synth, dev),
