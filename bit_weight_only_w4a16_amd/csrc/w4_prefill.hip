@@ -5,7 +5,9 @@
 // section "Why AMX for GEMM but not for attention" -- a weight GEMM reuses each
 // weight byte across all M activation rows, so at prefill row counts the
 // multiply units bound it; section "What is in the file" -- int4 weights in
-// groups of 256 (or 512), rotated along K.  Same product as w4_mfma.hip:
+// groups of 256 (or 512), rotated along K; group 32 too (the format of the
+// decode-step weights), where every 32-wide MFMA step is one scale group and
+// is scaled on its own.  Same product as w4_mfma.hip:
 // Y[m][n] = sum_g s[n][g] * sum_{k in g} (c[n][k] - 8) * x[m][k], fp32
 // accumulation, no dequantized matrix in memory.
 //
@@ -69,6 +71,7 @@ constexpr int kStage = 64;     // K per ring slot
 constexpr int kARow = 128;     // bytes of an activation row in a slot
 constexpr int kBRow = 32;      // bytes of a code row in a slot
 constexpr int kMaxG = 32;      // scale groups per row kept in LDS (K = 8192 at g256)
+constexpr int kMaxG32 = 48;    // the same for group 32 (K = 1536)
 
 struct PfArgs {
     const uint32_t* codes;   // N x K/8 device words
@@ -110,14 +113,14 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
 
-template <int MF, int NF, int SLOTS, int P, int KS>
+template <int MF, int NF, int SLOTS, int P, int KS, bool G32>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : 2)))
 void prefill_kernel(PfArgs a) {
     using S = PfShape<MF, NF, SLOTS, KS>;
     static_assert(P == 1 || P == 2, "stages per barrier");
     static_assert(SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps, double-buffered at least");
     __shared__ __align__(16) uint8_t rings[KS * SLOTS * S::SLOT];
-    __shared__ __align__(16) uint16_t sc[S::BN * kMaxG];
+    __shared__ __align__(16) uint16_t sc[S::BN * (G32 ? kMaxG32 : kMaxG)];
     __shared__ __align__(16) f32x4 xchs[KS][4][64];   // offset chains, one per wave
 
     const int tid = threadIdx.x;
@@ -177,10 +180,17 @@ void prefill_kernel(PfArgs a) {
     };
 
     // per-lane LDS read offsets within a slot
+    // Groups of 64 or more: MFMA step t takes words 2j + t of the stage (lane
+    // group j = lk), one 8-byte code read per stage.  Group 32: step t takes
+    // words 4t + j, so that each step is exactly one scale group (two 4-byte
+    // code reads; both layouts stay free of bank conflicts).
     const int gl = swz_a(li);
-    const int aoff0 = li * kARow + 16 * ((2 * lk) ^ gl);
-    const int aoff1 = li * kARow + 16 * ((2 * lk + 1) ^ gl);
-    const int boff = S::A_BYTES + wave * S::WN * kBRow + li * kBRow + 8 * (lk ^ swz_b(li));
+    const int aoff0 = li * kARow + 16 * ((G32 ? lk : 2 * lk) ^ gl);
+    const int aoff1 = li * kARow + 16 * ((G32 ? 4 + lk : 2 * lk + 1) ^ gl);
+    const int brow = S::A_BYTES + wave * S::WN * kBRow + li * kBRow;
+    const int boff = brow + 8 * (lk ^ swz_b(li));
+    const int boff0 = brow + 8 * ((lk >> 1) ^ swz_b(li)) + 4 * (lk & 1);        // word lk
+    const int boff1 = brow + 8 * ((2 + (lk >> 1)) ^ swz_b(li)) + 4 * (lk & 1);  // word 4 + lk
     const uint16_t* scrow = sc + (wave * S::WN + li) * a.G + g0;
 
     const DecodeConsts k = decode_consts();
@@ -194,10 +204,51 @@ void prefill_kernel(PfArgs a) {
 
     // One stage's products out of ring slot SL.  The first stage of a group
     // starts its MFMA chains from a zero accumulator operand.
-    auto compute = [&](auto slc, auto firstc) {
+    auto compute = [&](auto slc, auto firstc, int st) {
         constexpr int SL = decltype(slc)::value;
         constexpr bool FIRST = decltype(firstc)::value;
         const uint8_t* slot = ring + SL * S::SLOT;
+        if constexpr (G32) {
+            // every MFMA step is one whole scale group: products and the four
+            // offset chains start from zero, and each group is scaled into
+            // the totals at once (step t of stage st is group 2 st + t)
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t bw[2][NF], sw[NF];
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+                bw[0][nf] = *reinterpret_cast<const uint32_t*>(slot + boff0 + nf * 16 * kBRow);
+                bw[1][nf] = *reinterpret_cast<const uint32_t*>(slot + boff1 + nf * 16 * kBRow);
+                sw[nf] = *reinterpret_cast<const uint32_t*>(scrow + nf * 16 * a.G + 2 * st);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                u32x4 xa[MF];
+                f32x4 c136[MF];
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf) {
+                    xa[mf] = *reinterpret_cast<const u32x4*>(slot + (t ? aoff1 : aoff0) +
+                                                             mf * 16 * kARow);
+                    c136[mf] = mfma(xa[mf], b136, zero);
+                }
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) {
+                    const uint32_t w = bw[t][nf];
+                    const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k),
+                                      decode_pair(w, 2, k), decode_pair(w, 3, k)};
+                    const float sv = __uint_as_float(t ? (sw[nf] & 0xFFFF0000u) : (sw[nf] << 16));
+#pragma unroll
+                    for (int mf = 0; mf < MF; ++mf) {
+                        const f32x4 p = mfma(xa[mf], bv, zero);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            tot[mf][nf][r] = fmaf(sv, p[r] - c136[mf][r], tot[mf][nf][r]);
+                    }
+                    // keep one N fragment's products live at a time
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            return;   // (a stage's code and scale reads are not hoisted into the one before)
+        }
         u32x2 bw[NF];
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf)
@@ -256,7 +307,7 @@ void prefill_kernel(PfArgs a) {
         // every wave's DMA of these stages has landed, and every wave has
         // finished the previous P stages, whose slots the next issue refills
         ring_barrier();
-        const bool first = (s0 * kStage) % a.group == 0;
+        const bool first = !G32 && (s0 * kStage) % a.group == 0;
         if (first && s0 > 0) close_group((s0 * kStage) / a.group - 1);
         static_for<P>([&](auto ic) {
             constexpr int I = decltype(ic)::value;
@@ -264,14 +315,14 @@ void prefill_kernel(PfArgs a) {
                 issue(s0 + SLOTS - P + I, (SL0 + SLOTS - P + I) % SLOTS);
         });
         if (first)
-            compute(std::integral_constant<int, SL0>{}, std::true_type{});
+            compute(std::integral_constant<int, SL0>{}, std::true_type{}, s0);
         else
-            compute(std::integral_constant<int, SL0>{}, std::false_type{});
+            compute(std::integral_constant<int, SL0>{}, std::false_type{}, s0);
         static_for<P - 1>([&](auto ic) {
-            compute(std::integral_constant<int, SL0 + 1 + decltype(ic)::value>{},
-                    std::false_type{});
+            constexpr int I = 1 + decltype(ic)::value;
+            compute(std::integral_constant<int, SL0 + I>{}, std::false_type{}, s0 + I);
         });
-        if (((s0 + P) * kStage) % a.group == 0) publish();
+        if (!G32 && ((s0 + P) * kStage) % a.group == 0) publish();
     };
 
     // Scales of the workgroup's rows: rows n0 .. n0 + BN - 1 are one
@@ -299,7 +350,7 @@ void prefill_kernel(PfArgs a) {
 
     // the last group closes after one more barrier
     ring_barrier();
-    close_group(G - 1);
+    if (!G32) close_group(G - 1);
 
     // K groups 1 .. KS - 1 leave their partial blocks in their own rings (all
     // their stages are consumed: every wave is past the barrier above), and
@@ -398,15 +449,26 @@ struct PfPlan {
 // 14.1 us, 64 x 128 20.9 us, 64 x 192 27.6 us), wider blocks on ties.  This
 // picks, at N = 12288, 64 x 64 for 65..128 rows, 64 x 128 for 129..320 and
 // 513..640, 64 x 192 for 321..512 and from 641: the measured best at every
-// row count tried from 80 to 1024.
-static int pick_block_cfg(int M, int N) {
-    static const struct { int cfg, BN; double t_round; } kCand[3] = {
-        {0, 192, 27.6}, {6, 128, 20.9}, {1, 64, 14.1}};
+// row count tried from 80 to 1024.  Group 32 (a scale per MFMA step: more
+// registers and ALU work per block) has no 64 x 192 entry, which spills, and
+// its own round times (64 x 128 26 us, 64 x 64 17.5 us): 64 x 64 up to 128
+// rows, 64 x 128 above (28.1 against 32.0 us at 256 rows, 51.3 against 55.4
+// at 512, 86.8 against 105.4 at 1024).
+struct PfCand {
+    int cfg, BN;
+    double t_round;
+};
+static int pick_block_cfg(int M, int N, int group) {
+    static const PfCand kCand[3] = {{0, 192, 27.6}, {6, 128, 20.9}, {1, 64, 14.1}};
+    static const PfCand kCand32[2] = {{6, 128, 26.0}, {1, 64, 17.5}};
+    const PfCand* cand = group == 32 ? kCand32 : kCand;
+    const int ncand = group == 32 ? 2 : 3;
     const long long slots = 2LL * kNumCUs;
     const long long mb = (M + 63) / 64;
     int best = 0;
     double best_t = 1e300;
-    for (const auto& c : kCand) {
+    for (int i = 0; i < ncand; ++i) {
+        const PfCand& c = cand[i];
         const long long wgs = mb * ((N + c.BN - 1) / c.BN);
         const double t = (double)((wgs + slots - 1) / slots) * c.t_round;
         if (t < best_t - 1e-9) {   // candidates in decreasing width: ties keep the wider
@@ -419,15 +481,17 @@ static int pick_block_cfg(int M, int N) {
 
 PfPlan plan_prefill(int M, int N, int K, int group) {
     PfPlan p;
-    p.cfg = pick_block_cfg(M, N);
+    p.cfg = pick_block_cfg(M, N, group);
     // 64 x 64 blocks that leave CUs idle (at most one workgroup per CU)
     // split K over three or two wave groups.  Measured
     // at N = 12288, K = 1536, g256: 64 rows 11.8 -> 9.0 us, 32 rows 11.6 ->
     // 8.7 us; at 128 rows (768 workgroup slots wanted, one per CU fits) the
     // split is slower (14.4 -> 16.6 us).
     const int G = K / group;
+    // Group 32 splits two ways: its three-way split spills registers
+    // (M = 64: 11.7 us against 12.3 us, unsplit 15.7 us).
     if (p.cfg == 1 && (M + 63) / 64 * ((N + 63) / 64) <= kNumCUs)
-        p.cfg = G % 3 == 0 ? 4 : (G % 2 == 0 ? 5 : 1);
+        p.cfg = G % 3 == 0 && group != 32 ? 4 : (G % 2 == 0 ? 5 : 1);
     const char* e = getenv("W4_PREFILL_CFG");  // tuning override: a kPfCfgs index
     if (e && *e >= '0' && *e < '0' + kPfNumCfgs && e[1] == 0) p.cfg = *e - '0';
     // a K split needs whole scale groups per wave group
@@ -447,8 +511,25 @@ bool prefill_supported(int M, int N, int K, int group, int ldx) {
     // addressable from their buffer's start within 4 GiB
     const size_t x_span = ((size_t)(M - 1) * (size_t)ldx + (size_t)K) * 2;
     const size_t c_span = (size_t)N * (size_t)K / 2;
-    return group % kStage == 0 && K % kStage == 0 && K / group <= kMaxG &&
+    // group 32: K a multiple of 256 as for group 256, so that every K group
+    // of every split holds an even number of stages (whole two-stage steps)
+    const bool groups_fit = group == 32 ? K % 256 == 0 && K / group <= kMaxG32
+                                        : group % kStage == 0 && K / group <= kMaxG;
+    return groups_fit && K % kStage == 0 &&
            x_span < (1ull << 32) && c_span < (1ull << 32);
+}
+
+template <bool G32>
+static void launch_cfg(int cfg, dim3 g, dim3 b, hipStream_t s, const PfArgs& a) {
+    switch (cfg) {
+        case 0: prefill_kernel<4, 3, 4, 2, 1, G32><<<g, b, 0, s>>>(a); break;
+        case 1: prefill_kernel<4, 1, 6, 2, 1, G32><<<g, b, 0, s>>>(a); break;
+        case 2: prefill_kernel<4, 3, 5, 1, 1, G32><<<g, b, 0, s>>>(a); break;
+        case 3: prefill_kernel<4, 1, 5, 1, 1, G32><<<g, b, 0, s>>>(a); break;
+        case 4: prefill_kernel<4, 1, 4, 2, 3, G32><<<g, b, 0, s>>>(a); break;
+        case 5: prefill_kernel<4, 1, 6, 2, 2, G32><<<g, b, 0, s>>>(a); break;
+        default: prefill_kernel<4, 2, 4, 2, 1, G32><<<g, b, 0, s>>>(a); break;
+    }
 }
 
 int launch_prefill(const void* packed, int N, int K, int group, int M, const uint16_t* X,
@@ -473,15 +554,10 @@ int launch_prefill(const void* packed, int N, int K, int group, int M, const uin
     const size_t esz = ydt == W4_F32 ? 4 : 2;
     a.vec_out = (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && ((size_t)ldy * esz) % 16 == 0;
     const dim3 g(p.grid), b(256 * kPfCfgs[p.cfg].ks);
-    switch (p.cfg) {
-        case 0: prefill_kernel<4, 3, 4, 2, 1><<<g, b, 0, s>>>(a); break;
-        case 1: prefill_kernel<4, 1, 6, 2, 1><<<g, b, 0, s>>>(a); break;
-        case 2: prefill_kernel<4, 3, 5, 1, 1><<<g, b, 0, s>>>(a); break;
-        case 3: prefill_kernel<4, 1, 5, 1, 1><<<g, b, 0, s>>>(a); break;
-        case 4: prefill_kernel<4, 1, 4, 2, 3><<<g, b, 0, s>>>(a); break;
-        case 5: prefill_kernel<4, 1, 6, 2, 2><<<g, b, 0, s>>>(a); break;
-        default: prefill_kernel<4, 2, 4, 2, 1><<<g, b, 0, s>>>(a); break;
-    }
+    if (group == 32)
+        launch_cfg<true>(p.cfg, g, b, s, a);
+    else
+        launch_cfg<false>(p.cfg, g, b, s, a);
     return hip_fail(hipGetLastError(), "prefill launch");
 }
 

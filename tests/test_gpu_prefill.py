@@ -240,6 +240,8 @@ def test_matrix_core_largest_m(oracle_mod):
 
 
 @pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(7)] +
+                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(7)] +
+                         [({"W4_PREFILL": "0"}, 32)] +
                          [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
                           ({"W4_PREFILL": "0"}, 256)])
 def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
@@ -277,10 +279,11 @@ def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     assert_within(Y, Yr, A, "f32", "cfg %d K %d g %d" % (cfg, K, g))
 
 
-def test_matrix_core_code8_columns_exact_zero():
+@pytest.mark.parametrize("g", [256, 32])
+def test_matrix_core_code8_columns_exact_zero(g):
     """Columns whose codes are all 8 are exactly zero through the matrix-core
     path (the offset MFMA goes through the same arithmetic)."""
-    M, N, K, g = 64, 128, 1536, 256
+    M, N, K = 64, 128, 1536
     rng = np.random.default_rng(4)
     P, S = synth.draw_weights(rng, N, K, g)
     P[5, :] = 0x88888888
