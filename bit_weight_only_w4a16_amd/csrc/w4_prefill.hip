@@ -72,6 +72,8 @@ constexpr int kARow = 128;     // bytes of an activation row in a slot
 constexpr int kBRow = 32;      // bytes of a code row in a slot
 constexpr int kMaxG = 32;      // scale groups per row kept in LDS (K = 8192 at g256)
 constexpr int kMaxG32 = 48;    // the same for group 32 (K = 1536)
+constexpr int kMaxG32Split = 192;   // group 32 in K-split workgroups (K = 6144),
+                                    // which hold one workgroup per CU anyway
 
 struct PfArgs {
     const uint32_t* codes;   // N x K/8 device words
@@ -120,7 +122,7 @@ void prefill_kernel(PfArgs a) {
     static_assert(P == 1 || P == 2, "stages per barrier");
     static_assert(SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps, double-buffered at least");
     __shared__ __align__(16) uint8_t rings[KS * SLOTS * S::SLOT];
-    __shared__ __align__(16) uint16_t sc[S::BN * (G32 ? kMaxG32 : kMaxG)];
+    __shared__ __align__(16) uint16_t sc[S::BN * (G32 ? (KS > 1 ? kMaxG32Split : kMaxG32) : kMaxG)];
     __shared__ __align__(16) f32x4 xchs[KS][4][64];   // offset chains, one per wave
 
     const int tid = threadIdx.x;
@@ -488,14 +490,19 @@ PfPlan plan_prefill(int M, int N, int K, int group) {
     // 8.7 us; at 128 rows (768 workgroup slots wanted, one per CU fits) the
     // split is slower (14.4 -> 16.6 us).
     const int G = K / group;
-    // Group 32 splits two ways: its three-way split spills registers
-    // (M = 64: 11.7 us against 12.3 us, unsplit 15.7 us).
+    // Group 32 splits two ways at K = 1536: its three-way split spills
+    // registers (M = 64: 11.7 us against 12.3 us, unsplit 15.7 us); at
+    // K = 6144 (96 stages) three ways still wins for few rows (M = 64: 32.5
+    // against 35.7 us; equal at 256 and 512).
     if (p.cfg == 1 && (M + 63) / 64 * ((N + 63) / 64) <= kNumCUs)
-        p.cfg = G % 3 == 0 && group != 32 ? 4 : (G % 2 == 0 ? 5 : 1);
+        p.cfg = G % 3 == 0 && (group != 32 || G > kMaxG32) ? 4 : (G % 2 == 0 ? 5 : 1);
     const char* e = getenv("W4_PREFILL_CFG");  // tuning override: a kPfCfgs index
     if (e && *e >= '0' && *e < '0' + kPfNumCfgs && e[1] == 0) p.cfg = *e - '0';
     // a K split needs whole scale groups per wave group
     if (G % kPfCfgs[p.cfg].ks != 0) p.cfg = 1;   // the split entries are 64 x 64 blocks
+    // group 32 beyond 48 groups: only the split workgroups hold the scale table
+    // (G is a multiple of 8 here, so the two-way split divides it)
+    if (group == 32 && G > kMaxG32 && kPfCfgs[p.cfg].ks == 1) p.cfg = 5;
     p.BM = 16 * kPfCfgs[p.cfg].MF;
     p.BN = 64 * kPfCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -513,7 +520,7 @@ bool prefill_supported(int M, int N, int K, int group, int ldx) {
     const size_t c_span = (size_t)N * (size_t)K / 2;
     // group 32: K a multiple of 256 as for group 256, so that every K group
     // of every split holds an even number of stages (whole two-stage steps)
-    const bool groups_fit = group == 32 ? K % 256 == 0 && K / group <= kMaxG32
+    const bool groups_fit = group == 32 ? K % 256 == 0 && K / group <= kMaxG32Split
                                         : group % kStage == 0 && K / group <= kMaxG;
     return groups_fit && K % kStage == 0 &&
            x_span < (1ull << 32) && c_span < (1ull << 32);

@@ -269,7 +269,9 @@ def test_describe_dispatch_tile_table(L):
     assert ring(64, 12288, 1536, 32).startswith("64x64 waves 2x4")
     assert ring(128, 12288, 1536, 32).startswith("64x64 waves 1x4")
     assert ring(512, 12288, 1536, 32).startswith("64x128 waves 1x4")
-    assert "dma-ring" not in w4.describe_dispatch(64, 1536, 6144, 32)  # 192 groups
+    assert ring(64, 1536, 6144, 32).startswith("64x64 waves 3x4")      # 192 groups
+    assert ring(1024, 1536, 6144, 32).startswith("64x64 waves 2x4")
+    assert "dma-ring" not in w4.describe_dispatch(64, 1536, 6400, 32)  # 200 groups
     with pytest.raises(w4.W4Error):
         w4.describe_dispatch(1, 12288, 1500, 32)
 

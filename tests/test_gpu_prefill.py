@@ -261,12 +261,14 @@ def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
 
 
 @pytest.mark.parametrize("cfg,K,g", [(c, 6144, 256) for c in (0, 1, 4, 5, 6)] +
-                         [(0, 8192, 256), (5, 8192, 256), (4, 8192, 256), (6, 6144, 512)])
+                         [(0, 8192, 256), (5, 8192, 256), (4, 8192, 256), (6, 6144, 512),
+                          (5, 6144, 32), (1, 6144, 32), (4, 6144, 32), (0, 2048, 32)])
 def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
-    """The DMA-ring tilings with 12 to 32 scale groups per row (the
-    down-projection K = 6144 at groups 256 and 512; K = 8192, the most the
-    ring takes), ragged M and N; a split that does not divide the groups
-    falls back unsplit."""
+    """The DMA-ring tilings with 12 to 32 scale groups per row at groups 256
+    and 512 (the down-projection K = 6144; K = 8192, the most the ring takes)
+    and 64 to 192 at group 32 (only the split tilings hold more than 48; the
+    others are replaced by the two-way split), ragged M and N; a split that
+    does not divide the groups falls back unsplit."""
     monkeypatch.setenv("W4_PREFILL_CFG", str(cfg))
     M, N = 70, 1000
     assert "dma-ring" in w4.describe_dispatch(M, N, K, g)
