@@ -297,11 +297,16 @@ def test_matrix_core_code8_columns_exact_zero(g):
     assert np.all(Y[:, 6] != 0.0)
 
 
-@pytest.mark.parametrize("M,had", [(512, 0), (200, 0), (64, 0), (16, 512), (8, 0), (3, 512)])
-def test_matrix_core_deterministic(M, had):
-    """Run to run bitwise: the tiled matrix-core kernels (512, 200 and 64 rows) and
-    the matrix-core small-M kernel (with and without the fused transform)."""
-    N, K, g = 1024, 1536, 256
+@pytest.mark.parametrize("M,had,g,K", [(512, 0, 256, 1536), (200, 0, 256, 1536),
+                                       (64, 0, 256, 1536), (16, 512, 256, 1536),
+                                       (8, 0, 256, 1536), (3, 512, 256, 1536),
+                                       (512, 0, 32, 1536), (64, 0, 32, 1536),
+                                       (64, 0, 32, 6144)])
+def test_matrix_core_deterministic(M, had, g, K):
+    """Run to run bitwise: the tiled matrix-core kernels (512, 200 and 64 rows,
+    K-split workgroups included, groups 256 and 32) and the matrix-core
+    small-M kernel (with and without the fused transform)."""
+    N = 1024
     case = synth.make_case("det", N, K, g, M, 9 + M, "bf16")
     packed = upload_packed(case.P, case.S, N, K, g)
     X = to_dev_bf16(case.X)
