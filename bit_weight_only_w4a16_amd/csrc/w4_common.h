@@ -1,19 +1,29 @@
 // w4_common.h -- internal helpers shared by the library's translation units.
 //
-// Decode scheme (gfx950).  A code c in 0..15 placed in the low mantissa bits
-// of the bf16 pattern 0x4300 (= 128.0) is the bf16 number 128 + c, exactly:
-// bf16 has 7 stored mantissa bits and the spacing of bf16 numbers in
-// [128, 256) is 1.  The device layout puts the codes of elements 2j and 2j+1
-// of an 8-element word at bits [4j, 4j+4) and [16+4j, 20+4j), so one shift and
-// one and-or turn a word into a bf16 pair (128 + c_2j, 128 + c_2j+1) that
-// v_dot2_f32_bf16 multiplies by the activation pair (x_2j, x_2j+1) with fp32
-// accumulation.  Products of two bf16 numbers are exact in fp32.  The offset
-// is removed once per 32-element chunk: sum (128 + c) x - 136 sum x
-// = sum (c - 8) x, the offset-binary value of the pages' decode
-// ([P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than
-// llama.cpp", paragraph on the w4gemv.py kernel: each 4-bit value becomes the
-// exact float (value - 8)).  For a one-hot activation the result is exactly
-// (c - 8) * scale.
+// Exact decode ([P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster
+// than llama.cpp", paragraph on the w4gemv.py kernel: each 4-bit value becomes
+// the exact float (value - 8) before it is multiplied).  Every product the
+// kernels form is exactly (c - 8) * x (times a power of two), so a code of 8
+// contributes an exact zero and the fp32 accumulators only ever see terms of
+// the size of (c - 8) * x.  Two decodes, both exact:
+//
+//  - fp16 (batch-1 GEMV, HBM-bound, where ALU work per code must stay small):
+//    the device layout puts the codes of elements 2j and 2j+1 of an
+//    8-element word at bits [4j, 4j+4) and [16+4j, 20+4j).  Masking nibble 0
+//    (or 1) of both halves into the mantissa of the fp16 pair (1024, 1024)
+//    gives the exact fp16 pair (1024 + c, ...) (or (1024 + 16c, ...)), and one
+//    packed fp16 add (or multiply-add by 1/16) turns it into (c - 8, ...),
+//    exactly: every intermediate is an integer (or a sixteenth) inside fp16's
+//    exact range.  The activations are scaled per 32-element chunk by a power
+//    of two 2^s and rounded to fp16, which is exact whenever every nonzero
+//    element of the chunk is a normal bf16 within 2^29 of the chunk's largest
+//    magnitude; v_dot2_f32_f16 then forms exact products.  A chunk outside
+//    that range (or holding inf / NaN) sends its wave to the bf16 decode.
+//  - bf16 (matrix cores, small M, and the fallback): the nibble is moved to
+//    the top of a byte and its offset bit flipped, so the byte read as a
+//    signed integer is 16 (c - 8); one byte-select convert per code and one
+//    pack per pair give the exact bf16 pair (16 (c_2j - 8), 16 (c_2j+1 - 8)),
+//    the activations stay bf16, and the scale carries the factor 1/16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,10 +84,9 @@ inline int ilog2(int v) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr uint32_t kPairMask = 0x000F000Fu;
-constexpr uint32_t kMagic = 0x43004300u;      // bf16 pair (128, 128)
-constexpr uint32_t kOffsetPair = 0x43084308u; // bf16 pair (136, 136)
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
@@ -90,59 +99,134 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// bf16 pair dot product into fp32: a.lo * b.lo + a.hi * b.hi + c.
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c,
                                            false);
 }
 
-// The decode constants as opaque VGPR values: with the mask and the magic in
-// registers the compiler selects one v_and_or_b32 per operand pair (gfx9 VOP3
-// encodings take no literal constants).
+// fp16 pair dot product into fp32.
+__device__ __forceinline__ float dot2h(f16x2 a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2, b), c, false);
+}
+
+// ------------------------------------------------------ fp16 exact decode --
+// The decode constants as opaque VGPR values: with the masks and the magic
+// in registers the compiler selects one v_and_or_b32 per operand pair (gfx9
+// VOP3 encodings take no literal constants).
 struct DecodeConsts {
-    uint32_t mask, magic, offset;
+    uint32_t m0, m1, magic;   // masks of nibbles 0 and 1 of both halves; fp16 (1024, 1024)
+    f16x2 add0;               // (-1032, -1032)
+    f16x2 mul1, add1;         // (1/16, 1/16), (-72, -72)
 };
 __device__ __forceinline__ DecodeConsts decode_consts() {
     DecodeConsts k;
-    asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(k.mask));
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(k.magic));
-    asm volatile("v_mov_b32 %0, 0x43084308" : "=v"(k.offset));
+    asm volatile("v_mov_b32 %0, 0xf000f" : "=v"(k.m0));
+    asm volatile("v_mov_b32 %0, 0xf000f0" : "=v"(k.m1));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
+    k.add0 = f16x2{(_Float16)-1032.0f, (_Float16)-1032.0f};
+    k.mul1 = f16x2{(_Float16)0.0625f, (_Float16)0.0625f};
+    k.add1 = f16x2{(_Float16)-72.0f, (_Float16)-72.0f};
     return k;
 }
 
-// Operand pair j of device word w: bf16 (128 + c_2j, 128 + c_2j+1).
-__device__ __forceinline__ uint32_t decode_pair(uint32_t w, int j, const DecodeConsts& k) {
-    return ((w >> (4 * j)) & k.mask) | k.magic;
+// Pair (c_2j - 8, c_2j+1 - 8) of device word w for j = 0 (nibble 0 of each
+// half) and j = 1 (nibble 1); pairs 2 and 3 are pairs 0 and 1 of w >> 8.
+__device__ __forceinline__ f16x2 dec16_n0(uint32_t w, const DecodeConsts& k) {
+    return __builtin_bit_cast(f16x2, (w & k.m0) | k.magic) + k.add0;      // (1024 + c) - 1032
+}
+__device__ __forceinline__ f16x2 dec16_n1(uint32_t w, const DecodeConsts& k) {
+    return __builtin_bit_cast(f16x2, (w & k.m1) | k.magic) * k.mul1 + k.add1;  // (64 + c) - 72
 }
 
-// One 32-element chunk: sum over the chunk of (128 + c_k) * x_k, with q the
-// chunk's 4 device words and xr its 16 bf16 activation pairs (pair i holds
-// elements 2i, 2i+1).  Two accumulation chains (even / odd pairs), each
-// started at zero, in the same order as chunk_bias: for a chunk whose codes
-// are all 8 the decoded pairs equal the offset pair (136, 136), both
-// computations round identically, and the chunk contributes exactly zero.
-__device__ __forceinline__ float chunk_dot(u32x4 q, const uint32_t* xr,
-                                           const DecodeConsts& k) {
+// One 32-element chunk: sum of (c_k - 8) * xh_k, with q the chunk's 4 device
+// words and xh its 16 fp16 activation pairs (pair i = elements 2i, 2i+1, in
+// the chunk's scaled units).  Products are exact; two fp32 chains.
+__device__ __forceinline__ float chunk_dot16(u32x4 q, const uint32_t* xh, const DecodeConsts& k) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t w = q[d];
-        a0 = dot2(decode_pair(w, 0, k), xr[4 * d + 0], a0);
-        a1 = dot2(decode_pair(w, 1, k), xr[4 * d + 1], a1);
-        a0 = dot2(decode_pair(w, 2, k), xr[4 * d + 2], a0);
-        a1 = dot2(decode_pair(w, 3, k), xr[4 * d + 3], a1);
+        const uint32_t v = w >> 8;
+        a0 = dot2h(dec16_n0(w, k), xh[4 * d + 0], a0);
+        a1 = dot2h(dec16_n1(w, k), xh[4 * d + 1], a1);
+        a0 = dot2h(dec16_n0(v, k), xh[4 * d + 2], a0);
+        a1 = dot2h(dec16_n1(v, k), xh[4 * d + 3], a1);
     }
     return a0 + a1;
 }
 
-// 136 * sum of the chunk's 32 activations (the bias of chunk_dot plus the
-// code offset 8), fp32, accumulated exactly like chunk_dot.
-__device__ __forceinline__ float chunk_bias(const uint32_t* xr) {
+// Converts NC chunks of bf16 activation pairs (16 pairs each) in place to
+// fp16 pairs of x * 2^s with one shared scale and returns 2^-s.
+// s = min(142 - e_max, 126), e_max the largest biased bf16 exponent present,
+// puts the largest magnitude below 2^16 (fp16's largest finite value is
+// 65504 >= 255 * 2^8) and keeps 2^-s a normal fp32.  `ok` is cleared unless
+// the conversion is exact: every nonzero element normal (biased exponent
+// >= 1) and within 2^29 of the largest (so it lands on a normal fp16), and
+// no inf or NaN.
+template <int NC>
+__device__ __forceinline__ float chunks_to_f16(uint32_t (&xr)[NC][16], bool& ok) {
+    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+    const u16x2 one = {1, 1};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const u16x2 mag = __builtin_bit_cast(u16x2, xr[c][i] & 0x7FFF7FFFu);
+            mx = __builtin_elementwise_max(mx, mag);
+            mn = __builtin_elementwise_min(mn, (u16x2)(mag - one));   // zero wraps to 0xFFFF
+        }
+    const uint32_t big = mx[0] > mx[1] ? mx[0] : mx[1];
+    const uint32_t low = (mn[0] < mn[1] ? mn[0] : mn[1]) + 1u;   // 0x10000: all zero
+    const int emax = (int)(big >> 7);
+    const int emin = (int)(low >> 7);
+    const int s = 142 - emax < 126 ? 142 - emax : 126;
+    if (emax >= 255 || (low < 0x10000u && (emin < 1 || emin < emax - 29))) ok = false;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const f32x2 f = {ldexpf(__uint_as_float(xr[c][i] << 16), s),
+                             ldexpf(__uint_as_float(xr[c][i] & 0xFFFF0000u), s)};
+            xr[c][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+        }
+    return ldexpf(1.0f, -s);
+}
+
+__device__ __forceinline__ float chunk_to_f16(uint32_t (&xr)[16], bool& ok) {
+    return chunks_to_f16<1>(reinterpret_cast<uint32_t (&)[1][16]>(xr), ok);
+}
+
+// ------------------------------------------------------ bf16 exact decode --
+// Device word w -> the bf16 pairs (16 (c_2j - 8), 16 (c_2j+1 - 8)),
+// j = 0..3, in element order.  Byte b of w holds nibble positions 2b and
+// 2b + 1, i.e. elements (0, 2), (4, 6), (1, 3), (5, 7) for b = 0..3.
+__device__ __forceinline__ float sbyte16(uint32_t v, int b) {
+    return (float)(int)(int8_t)(v >> (8 * b));
+}
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const f32x2 f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ u32x4 decode_x16(uint32_t w) {
+    const uint32_t hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;          // elements 2, 6, 3, 7
+    const uint32_t lo = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u;   // elements 0, 4, 1, 5
+    return u32x4{pack_bf16(sbyte16(lo, 0), sbyte16(lo, 2)), pack_bf16(sbyte16(hi, 0), sbyte16(hi, 2)),
+                 pack_bf16(sbyte16(lo, 1), sbyte16(lo, 3)), pack_bf16(sbyte16(hi, 1), sbyte16(hi, 3))};
+}
+
+// One 32-element chunk: sum of 16 (c_k - 8) * x_k with bf16 activation pairs
+// xr (exact products; two fp32 chains).  The caller scales by s / 16.
+__device__ __forceinline__ float chunk_dot_x16(u32x4 q, const uint32_t* xr) {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-        a0 = dot2(kOffsetPair, xr[i], a0);
-        a1 = dot2(kOffsetPair, xr[i + 1], a1);
+    for (int d = 0; d < 4; ++d) {
+        const u32x4 b = decode_x16(q[d]);
+        a0 = dot2(b[0], xr[4 * d + 0], a0);
+        a1 = dot2(b[1], xr[4 * d + 1], a1);
+        a0 = dot2(b[2], xr[4 * d + 2], a0);
+        a1 = dot2(b[3], xr[4 * d + 3], a1);
     }
     return a0 + a1;
 }
@@ -223,6 +307,16 @@ constexpr uint32_t kScaleSelHi = 0x03020C0Cu;  // bytes 3,2 -> 3,2; zeros below
 
 __device__ __forceinline__ float scale_from_word(uint32_t w, uint32_t sel) {
     return __uint_as_float(__builtin_amdgcn_perm(0u, w, sel));
+}
+
+// Agent-scope store of an output: visible to every CU once it completes.
+__device__ __forceinline__ void store_out_agent(void* y, size_t i, float v, int ydt) {
+    if (ydt == W4_BF16)
+        __hip_atomic_store(static_cast<uint16_t*>(y) + i, (uint16_t)f32_to_bf16_rne(v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_store(static_cast<uint32_t*>(y) + i, __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void store_out(void* y, size_t i, float v, int ydt) {

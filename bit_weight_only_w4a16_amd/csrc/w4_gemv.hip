@@ -49,9 +49,8 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(GemvArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nw = blockDim.x >> 6;
-    const DecodeConsts k = decode_consts();
     const int NG = (a.N + 64 / L - 1) / (64 / L);
-    gemv_rows_generic<L>(a, blockIdx.x * nw + wave, NG, gridDim.x * nw, lane, k);
+    gemv_rows_generic<L>(a, blockIdx.x * nw + wave, NG, gridDim.x * nw, lane);
 }
 
 // Row groups from which a full-width tiling of at most 3 chunks per lane

@@ -9,8 +9,11 @@
 // load, one K-group of 32).  L lanes share a row; lane l of a row owns chunks
 // l, l + L, ..., l + (U-1)L, so for each u the L lanes read L consecutive
 // chunks and a wave reads R = 64/L rows at once (a "row group").  A lane's
-// chunks are the same for every row, so its activation slice (16 bf16 pairs
-// per chunk) and the chunks' offset terms stay in registers.
+// chunks are the same for every row, so its activation slice stays in
+// registers, converted once to fp16 with one power-of-two scale per lane
+// (w4_common.h); the codes are decoded to the exact fp16 values c - 8.  A
+// wave with a lane whose slice fp16 cannot represent exactly (a dynamic
+// range beyond 2^29, inf or NaN) runs the exact bf16 loop instead.
 #pragma once
 
 #include "w4_dispatch.h"
@@ -25,11 +28,13 @@ struct GemvArgs {
     int N, C, G, gshift, ydt;
 };
 
-// Loads this lane's activation slice and the negated offset terms
-// -136 * sum(x) (zero slices for chunks past the row end).
+// Loads this lane's activation slice, converts it to fp16 pairs in place and
+// sets xv to its inverse scale (zero slices for chunks past the row end).
+// Returns whether the conversion was exact.
 template <int L, int U>
-__device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
-                                             uint32_t (&xr)[U][16], float (&xb)[U]) {
+__device__ __forceinline__ bool load_x_slice(const uint32_t* x, int C, int lk,
+                                             uint32_t (&xr)[U][16], float& xv) {
+    bool ok = true;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = lk + L * u;
@@ -43,14 +48,23 @@ __device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
                 xr[u][4 * i + 2] = v[2];
                 xr[u][4 * i + 3] = v[3];
             }
-            xb[u] = -chunk_bias(xr[u]);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) xr[u][i] = 0u;
-            xb[u] = 0.f;
         }
     }
+    xv = chunks_to_f16<U>(xr, ok);
+    return ok;
 }
+
+// True when some lane of the wave saw a chunk fp16 cannot hold exactly.
+__device__ __forceinline__ bool wave_any_inexact(bool ok) {
+    return __builtin_amdgcn_ballot_w64(!ok) != 0;
+}
+
+template <int L>
+__device__ __forceinline__ void gemv_rows_generic(const struct GemvArgs& a, int rg0, int rg1,
+                                                  int step, int lane);
 
 // Row groups rg0, rg0 + step, ... (< rg1) of one matrix for one wave.
 // Needs an even number of groups per row (G).  FULLC: L * U == C.  Otherwise lanes past the row end read a clamped, valid
@@ -73,13 +87,19 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
                                           int lane, const DecodeConsts& k) {
     static_assert(STAGES == 2 || STAGES == 3, "register stages");
     constexpr int R = 64 / L;
+    if (rg0 >= rg1) return;
+    // lane-derived offsets are formed per call, not hoisted to the kernel's
+    // entry (a kernel with several tile shapes would hold all of them live)
+    asm volatile("" : "+v"(lane));
     const int lk = lane % L;
     const int lr = lane / L;
-    if (rg0 >= rg1) return;
 
     uint32_t xr[U][16];
-    float xb[U];
-    if (!BATCH) load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
+    float xv;
+    if (!BATCH && wave_any_inexact(load_x_slice<L, U>(a.x, a.C, lk, xr, xv))) {
+        gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+        return;
+    }
 
     // chunk offsets, scale dword offsets and scale half selectors per chunk
     int coff[U], soff[U];
@@ -120,7 +140,8 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         float acc = 0.f;
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            acc = fmaf(scale_from_word(sc[u], ssel[u]), chunk_dot(q[u], xr[u], k) + xb[u], acc);
+            acc = fmaf(scale_from_word(sc[u], ssel[u]), chunk_dot16(q[u], xr[u], k), acc);
+        acc *= xv;
         if (BATCH) {
             acc = row16_sum(acc);
             const int row0 = g * R;
@@ -168,7 +189,10 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         u32x4 qa[U], qb[U];
         uint32_t sa[U], sb[U];
         load(rg, qa, sa);
-        if (BATCH) load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
+        if (BATCH && wave_any_inexact(load_x_slice<L, U>(a.x, a.C, lk, xr, xv))) {
+            gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+            return;
+        }
         while (true) {
             load(next(rg, step), qb, sb);
             finish(rg, qa, sa);
@@ -186,7 +210,10 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         uint32_t sa[U], sb[U], sc[U];
         load(rg, qa, sa);
         load(next(rg, step), qb, sb);
-        if (BATCH) load_x_slice<L, U>(a.x, a.C, lk, xr, xb);
+        if (BATCH && wave_any_inexact(load_x_slice<L, U>(a.x, a.C, lk, xr, xv))) {
+            gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+            return;
+        }
         while (true) {
             load(next(rg, 2 * step), qc, sc);
             finish(rg, qa, sa);
@@ -205,20 +232,29 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
     }
 }
 
-// Any K: the activation chunk is re-read (from cache) for every row.
+// Any K, and the exact fallback of gemv_rows: codes decoded to bf16
+// 16 (c - 8), activations used as bf16 and re-read (from cache) for every
+// row, scale / 16 per chunk.  Exact products for every input, inf and NaN
+// included.
 template <int L>
 __device__ __forceinline__ void gemv_rows_generic(const GemvArgs& a, int rg0, int rg1, int step,
-                                                  int lane, const DecodeConsts& k) {
+                                                  int lane) {
     constexpr int R = 64 / L;
-    const int lk = lane % L;
-    const int lr = lane / L;
+    // lane-derived offsets are formed here, not hoisted to the kernel's
+    // entry, where they would stay live across the fast loops that share a
+    // kernel with this one (and spill there)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lk = ln % L;
+    const int lr = ln / L;
     for (int rg = rg0; rg < rg1; rg += step) {
         const int n = rg * R + lr;
         float acc = 0.f;
         if (n < a.N) {
             for (int c = lk; c < a.C; c += L) {
                 const u32x4 q = nt_load(a.codes + (size_t)n * a.C + c);
-                const float s = bf16_to_f32(gload(a.scales + (size_t)n * a.G + (c >> a.gshift)));
+                const float s =
+                    bf16_to_f32(gload(a.scales + (size_t)n * a.G + (c >> a.gshift))) * 0.0625f;
                 uint32_t xr[16];
                 const u32x4* p = reinterpret_cast<const u32x4*>(a.x + 16 * c);
 #pragma unroll
@@ -229,7 +265,7 @@ __device__ __forceinline__ void gemv_rows_generic(const GemvArgs& a, int rg0, in
                     xr[4 * i + 2] = v[2];
                     xr[4 * i + 3] = v[3];
                 }
-                acc = fmaf(s, chunk_dot(q, xr, k) - chunk_bias(xr), acc);
+                acc = fmaf(s, chunk_dot_x16(q, xr), acc);
             }
         }
         acc = group_sum<L>(acc);

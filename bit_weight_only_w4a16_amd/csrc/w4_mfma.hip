@@ -14,11 +14,8 @@
 // A[l%16][8(l/16) + j], B[8(l/16) + j][l%16] for j = 0..7, and
 // D[4(l/16) + r][l%16] for r = 0..3).  B is W^T: lane l's eight B values are
 // eight consecutive codes of weight row n = l%16, which is one device word,
-// decoded with one shift and one and-or per pair to exact bf16 integers
-// 128 + c.  Per K-group the products accumulate from zero; the group's result
-// is scale * (acc - acc136), where acc136 is the same MFMA against a B made of
-// the bf16 value 136 (the decode bias plus the code offset 8): a column whose
-// codes are all 8 goes through the identical arithmetic and cancels exactly.
+// decoded to the exact bf16 values 16 (c - 8) (w4_common.h).  Per K-group the
+// products accumulate from zero; the group's result is (scale / 16) * acc.
 //
 // Block tiling: a 256-thread workgroup (2 x 2 waves) computes a BM x BN block
 // of Y; each wave a (16 MF) x (16 NF) part of it.  K advances in 128-wide
@@ -61,10 +58,6 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x4 decode_word(uint32_t w, const DecodeConsts& k) {
-    return u32x4{decode_pair(w, 0, k), decode_pair(w, 1, k), decode_pair(w, 2, k),
-                 decode_pair(w, 3, k)};
-}
 
 template <int WM, int WN, int MF, int NF, bool SUPER>
 __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
@@ -89,8 +82,6 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
     const int nb = (j / a.m_blocks) * 8 + xcd;
     if (nb >= a.n_blocks) return;
     const int m0 = mb * BM, n0 = nb * BN;
-    const DecodeConsts k = decode_consts();
-    const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
     const int KW = a.K / 8;
     const int stages = a.K / kStageK;
 
@@ -144,10 +135,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
             *reinterpret_cast<u32x4*>(&Bs[buf][boff[c]]) = rb[c];
     };
 
-    f32x4 tot[MF][NF], acc[MF][NF], a136[MF];
+    f32x4 tot[MF][NF], acc[MF][NF];
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
-        a136[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
             tot[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -158,17 +148,15 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
     auto close_group = [&](int g) {
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
-            const float sc = bf16_to_f32(srow[nf][g]);
+            const float sc = bf16_to_f32(srow[nf][g]) * 0.0625f;
 #pragma unroll
             for (int mf = 0; mf < MF; ++mf) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    tot[mf][nf][r] = fmaf(sc, acc[mf][nf][r] - a136[mf][r], tot[mf][nf][r]);
+                    tot[mf][nf][r] = fmaf(sc, acc[mf][nf][r], tot[mf][nf][r]);
                 acc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) a136[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
 
     const int arow0 = (wm * MF * 16 + li) * kArow;
@@ -196,12 +184,10 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
                                                              2 * (32 * lk + 8 * t));
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
-                    const u32x4 bv = decode_word(wv[nf][t], k);
+                    const u32x4 bv = decode_x16(wv[nf][t]);
 #pragma unroll
                     for (int mf = 0; mf < MF; ++mf) acc[mf][nf] = mfma(xa[mf], bv, acc[mf][nf]);
                 }
-#pragma unroll
-                for (int mf = 0; mf < MF; ++mf) a136[mf] = mfma(xa[mf], b136, a136[mf]);
             }
             if (((st + 1) * kStageK) % a.group == 0) close_group((st * kStageK) / a.group);
         } else {
@@ -216,12 +202,10 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs a) {
                 for (int nf = 0; nf < NF; ++nf) {
                     const uint32_t w = *reinterpret_cast<const uint32_t*>(
                         B + brow0 + nf * 16 * kBrow + 4 * (4 * t + lk));
-                    const u32x4 bv = decode_word(w, k);
+                    const u32x4 bv = decode_x16(w);
 #pragma unroll
                     for (int mf = 0; mf < MF; ++mf) acc[mf][nf] = mfma(xa[mf], bv, acc[mf][nf]);
                 }
-#pragma unroll
-                for (int mf = 0; mf < MF; ++mf) a136[mf] = mfma(xa[mf], b136, a136[mf]);
                 close_group(st * 4 + t);
             }
         }

@@ -11,6 +11,16 @@ constexpr int kPwThreads = 64 * kPwWaves;
 constexpr int kPwMaxU = 4;                  // chunks per lane per row
 constexpr int kPwMaxC = 256;                // chunks per row (K <= 8192)
 
+// Decode-ordered kernel (w4_ordered.hip): 8 waves per workgroup, wave 0 the
+// control wave, waves 1..7 DMA the next resident op's share; two LDS slots.
+constexpr int kOrdWaves = 8;
+constexpr int kOrdThreads = 64 * kOrdWaves;
+constexpr int kOrdDmaWaves = kOrdWaves - 1;
+constexpr int kOrdCodeBytes = 7 * kOrdDmaWaves * 1024;   // 49 KB of codes per slot
+constexpr int kOrdScaleBytes = kOrdDmaWaves * 1024;      // 7 KB of scales per slot
+constexpr int kOrdMaxK = 32 * kPwMaxC;                   // 8192
+constexpr int kOrdMaxRows = 512;                         // rows of a resident share
+
 // One GEMV of the step, as the kernel reads it.
 struct SweepOp {
     const u32x4* codes;      // N x C chunks
@@ -23,6 +33,10 @@ struct SweepOp {
     int rot;                 // first wave of this op's tile rotation (decode order)
     int base;                // index of this op's first tile in the step's tile list
     int cfg;                 // STREAM: compiled tile shape (kCfg*), or kCfgGeneric
+    // decode-ordered mode
+    int res;                 // 1: every workgroup's share fits an LDS slot (DMA'd ahead)
+    int slot;                // its slot (0 or 1)
+    int next;                // resident op DMA'd into this op's slot after it (-1: none)
 };
 
 // Tile shapes (L lanes per row, U chunks per lane, L * U == C) compiled into
@@ -50,20 +64,24 @@ inline int stream_cfg(int C, int* L) {
     return kCfgGeneric;
 }
 
-// Control block: launch counter (epochs), error word, one flag per workgroup.
+// Control block: error word; the decode-ordered kernel's completion
+// counters (one per XCD, each in its own 128-byte line) and the count of
+// workgroups that finished a replay.
 struct SweepCtl {
-    unsigned launch_count;
     unsigned error;
-    unsigned pad[62];
-    unsigned flags[1];
+    unsigned pad0[31];
+    unsigned cnt[8 * 32];
+    unsigned fin;
+    unsigned pad1[31];
 };
 
-inline size_t sweep_ctl_bytes(int grid) {
-    return sizeof(SweepCtl) + sizeof(unsigned) * (size_t)grid;
-}
+inline size_t sweep_ctl_bytes(int) { return sizeof(SweepCtl); }
 
 int persist_occupancy(bool dep, int* blocks_per_cu);
 int launch_persist(bool dep, const SweepOp* ops_dev, int n_ops, SweepCtl* ctl,
-                   const int* range, int grid, hipStream_t s);
+                   const int* range, int grid, int first0, int first1, hipStream_t s);
+int ordered_lds_bytes();
+__global__ void ordered_kernel(const SweepOp* __restrict__ ops, int n_ops, SweepCtl* ctl,
+                               int first0, int first1);
 
 }  // namespace w4

@@ -14,10 +14,10 @@
 // Arithmetic (v_mfma_f32_16x16x32_bf16; lane l holds A[l%16][8(l/16) + j],
 // B[8(l/16) + j][l%16], D[4(l/16) + r][l%16]):
 //   - a lane's eight B values are one device word of weight row l%16, decoded
-//     with one shift and one and-or per pair to exact bf16 integers 128 + c;
+//     to the exact bf16 values 16 (c - 8) (w4_common.h), so every product is
+//     exact and a code of 8 contributes an exact zero;
 //   - per K-group the products accumulate from zero; the group adds
-//     s * (acc - acc136) to the total, acc136 being the same MFMA against the
-//     bf16 constant 136, so a column of code-8 weights cancels exactly;
+//     (s / 16) * acc to the total;
 //   - within a 64-wide K stage, lane group l/16 takes device words
 //     2(l/16), 2(l/16)+1 of its row, word t in MFMA step t, and the activation
 //     fragment is read with the same K permutation (a dot product allows it).
@@ -104,7 +104,6 @@ struct PfShape {
     static constexpr int PART = 4 * 64 * MF * NF * 16; // one K group's partial block (bytes)
     static_assert(KS == 1 || PART <= SLOTS * SLOT, "partial block fits in the group's ring");
     static constexpr int THREADS = 256 * KS;
-    static_assert(MF == 4, "one offset chain per wave: four M fragments for four waves");
 };
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -123,7 +122,6 @@ void prefill_kernel(PfArgs a) {
     static_assert(SLOTS % P == 0 && SLOTS >= 2 * P, "ring of whole steps, double-buffered at least");
     __shared__ __align__(16) uint8_t rings[KS * SLOTS * S::SLOT];
     __shared__ __align__(16) uint16_t sc[S::BN * (G32 ? (KS > 1 ? kMaxG32Split : kMaxG32) : kMaxG)];
-    __shared__ __align__(16) f32x4 xchs[KS][4][64];   // offset chains, one per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -131,7 +129,6 @@ void prefill_kernel(PfArgs a) {
     const int wave = wave_id & 3;   // position along N within the K group
     const int kg = wave_id >> 2;    // K group
     uint8_t* const ring = rings + kg * (SLOTS * S::SLOT);
-    f32x4 (*const xch)[64] = xchs[kg];
     const int li = lane & 15, lk = lane >> 4;
 
     // XCD x = blockIdx % 8 runs every M block of N blocks x, x + 8, ...
@@ -195,10 +192,8 @@ void prefill_kernel(PfArgs a) {
     const int boff1 = brow + 8 * ((2 + (lk >> 1)) ^ swz_b(li)) + 4 * (lk & 1);  // word 4 + lk
     const uint16_t* scrow = sc + (wave * S::WN + li) * a.G + g0;
 
-    const DecodeConsts k = decode_consts();
-    const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 tot[MF][NF], acc[MF][NF], own;   // own: offset chain of M fragment `wave`
+    f32x4 tot[MF][NF], acc[MF][NF];
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
@@ -211,9 +206,9 @@ void prefill_kernel(PfArgs a) {
         constexpr bool FIRST = decltype(firstc)::value;
         const uint8_t* slot = ring + SL * S::SLOT;
         if constexpr (G32) {
-            // every MFMA step is one whole scale group: products and the four
-            // offset chains start from zero, and each group is scaled into
-            // the totals at once (step t of stage st is group 2 st + t)
+            // every MFMA step is one whole scale group: products start from
+            // zero, and each group is scaled into the totals at once (step t
+            // of stage st is group 2 st + t)
             __builtin_amdgcn_sched_barrier(0);
             uint32_t bw[2][NF], sw[NF];
 #pragma unroll
@@ -225,25 +220,21 @@ void prefill_kernel(PfArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 u32x4 xa[MF];
-                f32x4 c136[MF];
 #pragma unroll
-                for (int mf = 0; mf < MF; ++mf) {
+                for (int mf = 0; mf < MF; ++mf)
                     xa[mf] = *reinterpret_cast<const u32x4*>(slot + (t ? aoff1 : aoff0) +
                                                              mf * 16 * kARow);
-                    c136[mf] = mfma(xa[mf], b136, zero);
-                }
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
-                    const uint32_t w = bw[t][nf];
-                    const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k),
-                                      decode_pair(w, 2, k), decode_pair(w, 3, k)};
-                    const float sv = __uint_as_float(t ? (sw[nf] & 0xFFFF0000u) : (sw[nf] << 16));
+                    const u32x4 bv = decode_x16(bw[t][nf]);
+                    const float sv =
+                        __uint_as_float(t ? (sw[nf] & 0xFFFF0000u) : (sw[nf] << 16)) * 0.0625f;
 #pragma unroll
                     for (int mf = 0; mf < MF; ++mf) {
                         const f32x4 p = mfma(xa[mf], bv, zero);
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            tot[mf][nf][r] = fmaf(sv, p[r] - c136[mf][r], tot[mf][nf][r]);
+                            tot[mf][nf][r] = fmaf(sv, p[r], tot[mf][nf][r]);
                     }
                     // keep one N fragment's products live at a time
                     __builtin_amdgcn_sched_barrier(0);
@@ -264,40 +255,23 @@ void prefill_kernel(PfArgs a) {
                                                          mf * 16 * kARow);
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf) {
-                const uint32_t w = bw[nf][t];
-                const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k),
-                                  decode_pair(w, 2, k), decode_pair(w, 3, k)};
+                const u32x4 bv = decode_x16(bw[nf][t]);
 #pragma unroll
                 for (int mf = 0; mf < MF; ++mf)
                     acc[mf][nf] = mfma(xa[mf], bv, (FIRST && t == 0) ? zero : acc[mf][nf]);
             }
-            // every wave multiplies the same activation rows: wave w runs the
-            // offset chain of M fragment w only, and the chains are swapped
-            // through LDS when the group closes (identical operands and order,
-            // so each chain is bitwise the one every wave would compute)
-            const u32x4 xo = *reinterpret_cast<const u32x4*>(slot + (t ? aoff1 : aoff0) +
-                                                             wave * 16 * kARow);
-            own = mfma(xo, b136, (FIRST && t == 0) ? zero : own);
         }
     };
-    // fold the finished group g into the totals; call after a barrier that
-    // follows every wave's publish()
-    auto publish = [&]() {
-        xch[wave][lane] = own;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // visible at the next barrier
-    };
+    // fold the finished group g into the totals
     auto close_group = [&](int g) {
-        f32x4 a136[MF];
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) a136[mf] = xch[mf][lane];
 #pragma unroll
         for (int nf = 0; nf < NF; ++nf) {
-            const float sv = bf16_to_f32(scrow[nf * 16 * a.G + g]);
+            const float sv = bf16_to_f32(scrow[nf * 16 * a.G + g]) * 0.0625f;
 #pragma unroll
             for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    tot[mf][nf][r] = fmaf(sv, acc[mf][nf][r] - a136[mf][r], tot[mf][nf][r]);
+                    tot[mf][nf][r] = fmaf(sv, acc[mf][nf][r], tot[mf][nf][r]);
         }
     };
     // P stages s0 .. s0 + P - 1 (slots SL0 ..) per barrier; a group spans
@@ -324,7 +298,6 @@ void prefill_kernel(PfArgs a) {
             constexpr int I = 1 + decltype(ic)::value;
             compute(std::integral_constant<int, SL0 + I>{}, std::false_type{}, s0 + I);
         });
-        if (!G32 && ((s0 + P) * kStage) % a.group == 0) publish();
     };
 
     // Scales of the workgroup's rows: rows n0 .. n0 + BN - 1 are one

@@ -2,16 +2,15 @@
 //
 // [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 / AVX-512 VNNI", section
 // "Why AMX for GEMM but not for attention": a weight GEMM reuses each weight
-// byte across all M rows.  Each packed chunk is loaded and decoded to bf16
-// operand pairs once, then multiplied by every activation row.
+// byte across all M rows.  Each packed chunk is loaded and decoded once to
+// the exact bf16 operand pairs 16 (c - 8) (w4_common.h), then multiplied by
+// every activation row; each chunk's sum is scaled by s / 16.
 //
 // Work split as in the batch-1 GEMV: L lanes share a weight row (lane l owns
 // chunks l, l + L, ...), a wave covers 64/L rows per step.  The activation
-// rows and their per-chunk offset terms (136 * sum of the chunk's
-// activations) are staged once per workgroup in LDS when they fit; otherwise
-// (generic kernel) they are read through the cache and the offset term is
-// formed on the fly.  At this size the kernel is bound by vector ALU work
-// (one dot2 per two codes per row).
+// rows are staged once per workgroup in LDS when they fit; otherwise
+// (generic kernel) they are read through the cache.  At this size the kernel
+// is bound by vector ALU work (one dot2 per two codes per row).
 #include <cstdio>
 #include <cstdlib>
 
@@ -42,21 +41,12 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmallMArgs a) {
     const int lr = lane / L;
 
     uint32_t* xs = reinterpret_cast<uint32_t*>(smem);                   // [M][K/2]
-    float* xbs = reinterpret_cast<float*>(smem + (size_t)a.M * a.K * 2);  // [M][C]
     if (XLDS) {
         const int vec_per_row = a.K / 8;  // u32x4 per row
         for (int i = threadIdx.x; i < a.M * vec_per_row; i += blockDim.x) {
             const int m = i / vec_per_row, v = i % vec_per_row;
             const u32x4 val = reinterpret_cast<const u32x4*>(a.X + (size_t)m * a.ldx)[v];
             reinterpret_cast<u32x4*>(xs)[i] = val;
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < a.M * a.C; i += blockDim.x) {
-            const int m = i / a.C, c = i % a.C;
-            uint32_t xr[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) xr[j] = xs[(size_t)m * (a.K / 2) + c * 16 + j];
-            xbs[i] = chunk_bias(xr);
         }
         __syncthreads();
     }
@@ -70,19 +60,19 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmallMArgs a) {
         if (n < a.N) {
             for (int c = lk; c < a.C; c += L) {
                 const u32x4 q = nt_load(a.codes + (size_t)n * a.C + c);
-                const float s = bf16_to_f32(a.scales[(size_t)n * a.G + (c >> a.gshift)]);
+                const float s =
+                    bf16_to_f32(a.scales[(size_t)n * a.G + (c >> a.gshift)]) * 0.0625f;
                 uint32_t d[16];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
+                    const u32x4 b = decode_x16(q[w]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        d[4 * w + j] = ((q[w] >> (4 * j)) & kPairMask) | kMagic;
+                    for (int j = 0; j < 4; ++j) d[4 * w + j] = b[j];
                 }
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     if (m < a.M) {
                         uint32_t xr[16];
-                        float xb;
                         if (XLDS) {
                             const u32x4* p = reinterpret_cast<const u32x4*>(
                                 xs + (size_t)m * (a.K / 2) + c * 16);
@@ -94,7 +84,6 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmallMArgs a) {
                                 xr[4 * i + 2] = v[2];
                                 xr[4 * i + 3] = v[3];
                             }
-                            xb = xbs[m * a.C + c];
                         } else {
                             const u32x4* p = reinterpret_cast<const u32x4*>(
                                 a.X + (size_t)m * a.ldx + (size_t)c * 32);
@@ -106,16 +95,14 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmallMArgs a) {
                                 xr[4 * i + 2] = v[2];
                                 xr[4 * i + 3] = v[3];
                             }
-                            xb = chunk_bias(xr);
                         }
-                        // same chain order as chunk_bias (exact zero for code 8)
                         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
                         for (int i = 0; i < 16; i += 2) {
                             d0 = dot2(d[i], xr[i], d0);
                             d1 = dot2(d[i + 1], xr[i + 1], d1);
                         }
-                        acc[m] = fmaf(s, (d0 + d1) - xb, acc[m]);
+                        acc[m] = fmaf(s, d0 + d1, acc[m]);
                     }
                 }
             }
@@ -149,13 +136,11 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
     const int nw = blockDim.x >> 6;
     const int lk = lane % L;
     const int lr = lane / L;
-    const DecodeConsts k = decode_consts();
 
     // X in LDS, one 64-byte chunk per (row m, chunk c); quarter i of chunk c
     // is stored at quarter (i + c/2) mod 4, so the 16-byte reads of eight
     // consecutive chunks (one per lane of an 8-lane group) hit all 32 banks.
     uint32_t* xs = reinterpret_cast<uint32_t*>(smem);                   // [M][C][16]
-    float* xbs = reinterpret_cast<float*>(smem + (size_t)a.M * a.K * 2);  // [M][C]
     {
         const int vec_per_row = a.K / 8;
         for (int i = threadIdx.x; i < a.M * vec_per_row; i += blockDim.x) {
@@ -163,21 +148,6 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
             const int c = v >> 2, q = v & 3;
             reinterpret_cast<u32x4*>(xs)[((size_t)m * a.C + c) * 4 + ((q + (c >> 1)) & 3)] =
                 reinterpret_cast<const u32x4*>(a.X + (size_t)m * a.ldx)[v];
-        }
-        __syncthreads();
-        for (int i = threadIdx.x; i < a.M * a.C; i += blockDim.x) {
-            const int c = i % a.C;
-            const u32x4* p = reinterpret_cast<const u32x4*>(xs) + (size_t)i * 4;
-            uint32_t xr[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 v = p[(q + (c >> 1)) & 3];
-                xr[4 * q + 0] = v[0];
-                xr[4 * q + 1] = v[1];
-                xr[4 * q + 2] = v[2];
-                xr[4 * q + 3] = v[3];
-            }
-            xbs[i] = chunk_bias(xr);
         }
         __syncthreads();
     }
@@ -207,10 +177,12 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
             const int c = lk + L * u;
             uint32_t d[16];
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
+            for (int w = 0; w < 4; ++w) {
+                const u32x4 b = decode_x16(q[u][w]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) d[4 * w + j] = decode_pair(q[u][w], j, k);
-            const float s = bf16_to_f32(sc[u]);
+                for (int j = 0; j < 4; ++j) d[4 * w + j] = b[j];
+            }
+            const float s = bf16_to_f32(sc[u]) * 0.0625f;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 if (m < a.M) {
@@ -225,14 +197,13 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
                         xr[4 * i + 2] = v[2];
                         xr[4 * i + 3] = v[3];
                     }
-                    // same chain order as chunk_bias (exact zero for code 8)
                     float d0 = 0.f, d1 = 0.f;
 #pragma unroll
                     for (int i = 0; i < 16; i += 2) {
                         d0 = dot2(d[i], xr[i], d0);
                         d1 = dot2(d[i + 1], xr[i + 1], d1);
                     }
-                    acc[m] = fmaf(s, (d0 + d1) - xbs[m * a.C + c], acc[m]);
+                    acc[m] = fmaf(s, d0 + d1, acc[m]);
                 }
             }
         }
@@ -268,9 +239,9 @@ __global__ __launch_bounds__(256) void smallm_fast_kernel(SmallMArgs a) {
 // activation row (rows past M repeat row M - 1 and are never stored), so the
 // matrix cores do the per-row work the vector-ALU kernel spends its time on.
 // v_mfma_f32_16x16x32_bf16 (lane l holds A[l%16][8(l/16) + j],
-// B[8(l/16) + j][l%16], D[4(l/16) + r][l%16]); codes decoded to exact bf16
-// 128 + c, the offset chain (same MFMA against 136) subtracted per group, as
-// in the prefill kernels.
+// B[8(l/16) + j][l%16], D[4(l/16) + r][l%16]); codes decoded to the exact
+// bf16 values 16 (c - 8), each group's product scaled by s / 16, as in the
+// prefill kernels.
 //
 // A workgroup owns 16 * RG weight rows and splits K into KS slices: wave
 // (row group rg, slice ks) multiplies 16 rows by its 128 * NB slice of K.
@@ -402,10 +373,8 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
     const int xm = min(li, a.M - 1);             // A-operand row of this lane
     const u32x4* xrow = reinterpret_cast<const u32x4*>(smem) + (size_t)xm * CPR;
     const int xsw = xm & 15;
-    const DecodeConsts k = decode_consts();
-    const u32x4 b136 = {kOffsetPair, kOffsetPair, kOffsetPair, kOffsetPair};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 tot = zero, acc = zero, a136 = zero;
+    f32x4 tot = zero, acc = zero;
     if (G32) {
         // Lane group r holds row r of the block's 4 x 4 word matrix
         // M[r][c] = word 4r + c; two exchange steps leave it column r,
@@ -443,19 +412,15 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
             for (int t = 0; t < 4; ++t) {
                 const int cq = (k0 + 128 * u + 32 * t + 8 * lk) / 8;
                 const u32x4 xa = xrow[cq ^ xsw];
-                const uint32_t w = q[u][t];
-                const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k),
-                                  decode_pair(w, 2, k), decode_pair(w, 3, k)};
+                const u32x4 bv = decode_x16(q[u][t]);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
                                                               __builtin_bit_cast(bf16x8, bv),
                                                               zero, 0, 0, 0);
-                a136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                               __builtin_bit_cast(bf16x8, b136),
-                                                               zero, 0, 0, 0);
                 const uint32_t sw = sc[2 * u + (t >> 1)];
-                const float s = __uint_as_float((t & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+                const float s =
+                    __uint_as_float((t & 1) ? (sw & 0xFFFF0000u) : (sw << 16)) * 0.0625f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) tot[r] = fmaf(s, acc[r] - a136[r], tot[r]);
+                for (int r = 0; r < 4; ++r) tot[r] = fmaf(s, acc[r], tot[r]);
             }
     }
     const int bpg = a.group / 128;               // blocks per group
@@ -466,21 +431,16 @@ __global__ __launch_bounds__(1024) void smallm_mfma_kernel(SmqArgs a) {
         for (int t = 0; t < 4; ++t) {
             const int cq = (k0 + 128 * u + 32 * lk + 8 * t) / 8;
             const u32x4 xa = xrow[cq ^ xsw];
-            const uint32_t w = q[u][t];
-            const u32x4 bv = {decode_pair(w, 0, k), decode_pair(w, 1, k), decode_pair(w, 2, k),
-                              decode_pair(w, 3, k)};
+            const u32x4 bv = decode_x16(q[u][t]);
             const bool z = first && t == 0;
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
                                                           __builtin_bit_cast(bf16x8, bv),
                                                           z ? zero : acc, 0, 0, 0);
-            a136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa),
-                                                           __builtin_bit_cast(bf16x8, b136),
-                                                           z ? zero : a136, 0, 0, 0);
         }
         if ((u + 1) % bpg == 0) {
-            const float s = bf16_to_f32(sc[GW > 1 && u >= bpg ? 1 : 0]);
+            const float s = bf16_to_f32(sc[GW > 1 && u >= bpg ? 1 : 0]) * 0.0625f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tot[r] = fmaf(s, acc[r] - a136[r], tot[r]);
+            for (int r = 0; r < 4; ++r) tot[r] = fmaf(s, acc[r], tot[r]);
         }
     }
 
@@ -554,7 +514,7 @@ bool smallm_mfma_applies(int M, int N, int K, int group) {
 }
 
 static size_t smallm_lds(int M, int K) {
-    return (size_t)M * K * 2 + (size_t)M * (K / 32) * 4;
+    return (size_t)M * K * 2;
 }
 
 static int smallm_grid(int N, int R = 4) {

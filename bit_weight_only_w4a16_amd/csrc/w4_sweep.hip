@@ -23,6 +23,7 @@ struct w4_sweep {
     void* dev = nullptr;              // persistent modes: op table, ranges, control block
     w4::SweepCtl* ctl = nullptr;
     int* range = nullptr;             // STREAM: first tile of each wave (waves + 1)
+    int first0 = -1, first1 = -1;     // PERSISTENT: first two resident ops
 };
 
 namespace w4 {
@@ -76,8 +77,8 @@ static int setup_persistent(w4_sweep* h) {
     int st = persist_occupancy(dep, &occ);
     if (st != W4_OK) return st;
     if (occ < 1) return fail(W4_ERR_UNSUPPORTED, "sweep: persistent kernel does not fit a CU");
-    int bpc = blocks_per_cu_override();
-    if (bpc == 0) bpc = dep ? 1 : 5;
+    int bpc = dep ? 1 : blocks_per_cu_override();   // decode order: one per CU
+    if (bpc == 0) bpc = 5;
     if (bpc > occ) bpc = occ;  // every workgroup must be resident at once
     int ncu = kNumCUs;
     int dev = 0;
@@ -105,9 +106,21 @@ static int setup_persistent(w4_sweep* h) {
         t.G = o.K / o.group;
         t.gshift = ilog2(o.group / 32);
         t.ydt = o.y_dtype;
+        t.res = 0;
+        t.slot = 0;
+        t.next = -1;
         if (dep) {
             t.L = persist_lanes(t.C);
             t.cfg = kCfgGeneric;
+            // resident: every workgroup's share of codes and scales fits an
+            // LDS slot, both byte ranges are whole 16-byte units (a row of
+            // codes is K / 2 bytes, a row of scales 2 K / group: K % 256 == 0
+            // and K / group % 8 == 0), and the DMA offsets fit 32 bits
+            const long long rows = (o.N + h->grid - 1) / h->grid;
+            t.res = o.K % 256 == 0 && (o.K / o.group) % 8 == 0 &&
+                    rows * (o.K / 2) <= kOrdCodeBytes &&
+                    rows * (o.K / o.group) * 2 <= kOrdScaleBytes && rows <= kOrdMaxRows &&
+                    (long long)o.N * (o.K / 2) < (1LL << 32);
         } else {
             t.cfg = stream_cfg(t.C, &t.L);
             if (t.G & 1) {  // the tiled loop reads scales in dword pairs
@@ -124,6 +137,19 @@ static int setup_persistent(w4_sweep* h) {
         tiles_before += t.NG;
     }
     if (tiles_before >= (1LL << 31)) return fail(W4_ERR_SHAPE, "sweep: too many tiles");
+    if (dep) {
+        // resident ops alternate between the two slots; resident op r_k is
+        // DMA'd after r_{k-2} is computed (the first two at the start)
+        std::vector<int> res;
+        for (int i = 0; i < n; ++i)
+            if (tab[i].res) res.push_back(i);
+        for (size_t k = 0; k < res.size(); ++k) {
+            tab[res[k]].slot = (int)(k & 1);
+            tab[res[k]].next = k + 2 < res.size() ? res[k + 2] : -1;
+        }
+        h->first0 = res.size() > 0 ? res[0] : -1;
+        h->first1 = res.size() > 1 ? res[1] : -1;
+    }
 
     // STREAM partition: contiguous tile ranges, wave b's share of the bytes
     // set by its dispatch round (tiles of one op are equal-sized); then, for
@@ -275,7 +301,7 @@ int w4_decode_sweep_launch(w4_sweep* h, void* stream) {
     if (h->mode != W4_SWEEP_GRAPH)
         return launch_persist(h->mode == W4_SWEEP_PERSISTENT,
                               static_cast<const SweepOp*>(h->dev), (int)h->ops.size(), h->ctl,
-                              h->range, h->grid, s);
+                              h->range, h->grid, h->first0, h->first1, s);
     if (!h->exec) return fail(W4_ERR_ARG, "sweep: bad handle");
     return hip_fail(hipGraphLaunch(h->exec, s), "graph launch");
 }
@@ -289,8 +315,9 @@ int w4_decode_sweep_check(w4_sweep* h, void* stream) {
                   "sweep error word");
     if (st != W4_OK) return st;
     if (err != 0) {
-        const unsigned zero = 0;
-        (void)hipMemcpy(&h->ctl->error, &zero, sizeof zero, hipMemcpyHostToDevice);
+        // a replay that gave up leaves its counters part-way: start over
+        (void)hipMemset(h->ctl, 0, sweep_ctl_bytes(h->grid));
+        (void)hipDeviceSynchronize();
         return fail(W4_ERR_TIMEOUT, "sweep: a bounded in-kernel wait gave up");
     }
     return W4_OK;

@@ -107,6 +107,62 @@ def make_case(name, N, K, group, M, seed, out_dtype, outlier_frac=0.0,
                     hadamard_block)
 
 
+def codes_to_words(codes: np.ndarray) -> np.ndarray:
+    """Canonical packed words of a code matrix [N][K] (values 0..15): element
+    k of a row in word k/8, bits [4*(k%8), +4)."""
+    N, K = codes.shape
+    out = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        out |= codes[:, j::8].astype(np.uint32) << np.uint32(4 * j)
+    return out
+
+
+def sparse_case(name, N, K, group, M, seed, out_dtype, small=(1e-3, 1e-2), big=3.0,
+                per_chunk=3, wide=False) -> GemvCase:
+    """Near-zero rows: every code is 8 (value 0) except at most `per_chunk`
+    positions per 32-element chunk (0..per_chunk, uniform per row and chunk;
+    every 7th row has exactly one non-8 code in the whole row).  The
+    activations are big * N(0,1) everywhere except at four positions per
+    chunk, the only places where non-8 codes sit, whose magnitudes are
+    uniform in `small` with a random sign.  `wide`: one chunk position per
+    row of X instead holds 1e30 and another 1e-10 (a dynamic range far beyond
+    fp16's), both at small-activation positions' neighbours."""
+    rng = np.random.default_rng(seed)
+    C = K // 32
+    pos = np.stack([rng.choice(32, size=4, replace=False) for _ in range(C)])   # [C, 4]
+    sel = pos + 32 * np.arange(C)[:, None]
+    x = (rng.standard_normal(size=(M, K), dtype=np.float32) * np.float32(big))
+    mag = rng.uniform(small[0], small[1], size=(M, C, 4)).astype(np.float32)
+    sign = np.where(rng.integers(0, 2, size=(M, C, 4)) == 1, 1.0, -1.0).astype(np.float32)
+    x[:, sel.reshape(-1)] = (mag * sign).reshape(M, -1)
+    if wide:
+        for m in range(M):
+            c = int(rng.integers(0, C))
+            free = [j for j in range(32) if j not in set(pos[c].tolist())]
+            a, b = rng.choice(free, size=2, replace=False)
+            x[m, 32 * c + a] = np.float32(1e30)
+            x[m, 32 * c + b] = np.float32(1e-10)
+    # per (row, chunk): 0..per_chunk of the chunk's four small positions
+    # (a random subset), each with a code drawn from the 15 non-8 values
+    cnt = rng.integers(0, per_chunk + 1, size=(N, C))
+    single = (np.arange(N) % 7) == 3
+    cnt[single] = 0
+    cnt[single, rng.integers(0, C, size=int(single.sum()))] = 1
+    perms = np.array(list(__import__("itertools").permutations(range(4))))   # 24 x 4
+    rank = perms[rng.integers(0, 24, size=(N, C))]
+    take = rank < cnt[:, :, None]
+    vals = rng.integers(0, 15, size=(N, C, 4))
+    vals = vals + (vals >= 8)
+    codes = np.full((N, K), 8, dtype=np.uint8)
+    rows = np.broadcast_to(np.arange(N)[:, None, None], take.shape)
+    cols = np.broadcast_to(sel[None, :, :], take.shape)
+    codes[rows[take], cols[take]] = vals[take]
+    P = codes_to_words(codes)
+    z = rng.standard_normal(size=(N, K // group), dtype=np.float32)
+    S = f32_to_bf16_bits(np.abs(z) * np.float32(0.02) + np.float32(1e-3))
+    return GemvCase(name, N, K, group, M, P, S, f32_to_bf16_bits(x), out_dtype, seed)
+
+
 def layer_seed(layer: int, j: int) -> int:
     return 1 + 4 * layer + j
 

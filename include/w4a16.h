@@ -53,6 +53,16 @@
  * next 256-byte boundary, the scales unchanged.  Callers treat it as opaque.
  * Activations X[M][K] are bf16, row stride ldx elements.  Outputs are fp32 or
  * bf16 (round to nearest even from the fp32 accumulator).
+ *
+ * Arithmetic of every product: each weight enters as the exact value
+ * (code - 8), before it is multiplied ([P1], paragraph on the w4gemv.py
+ * kernel), so a code of 8 contributes an exact zero; every product
+ * (code - 8) * x is exact and only the fp32 sums round.  The batch-1 GEMV
+ * scales each 32-element activation chunk by a power of two into fp16
+ * (exact for chunks whose nonzero magnitudes lie within 2^29 of the largest,
+ * and without inf / NaN; any other chunk sends its wave to an exact bf16
+ * path); the matrix-core and small-M kernels keep the activations in bf16
+ * and enter each code as the bf16 value 16 (code - 8).
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -165,8 +175,14 @@ size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block);
  * Y = X' W'^T, the prefill-shaped product on the matrix cores (bf16 MFMA,
  * fp32 accumulation): X' = X when had_block == 0, else X' is the blockwise
  * FWHT of X (block had_block, computed into `workspace`, M*K bf16) and W' is
- * stored pre-rotated.  Codes enter the matrix cores as exact bf16 integers;
- * each K-group's partial product is multiplied by its fp32 scale.
+ * stored pre-rotated.  [P2] "fastgemma -- Gemma 4 E2B, CPU-only, AMX INT8 /
+ * AVX-512 VNNI": section "What is in the file" (int4 groups of 256, Hadamard
+ * rotation W' = W H^T with a run-time FWHT of the activation) and section
+ * "Why AMX for GEMM but not for attention" (a weight GEMM reuses every weight
+ * byte across all M rows, so at prefill row counts the multiply units, not
+ * memory, bound it).  Codes enter the matrix cores as the exact bf16 values
+ * 16 (code - 8); each K-group's partial product is multiplied by its fp32
+ * scale / 16.
  *  group must be 256 or 512 (the rotated prefill format of [P2]) or 32.
  *  M >= 1, K % 256 == 0.  Decode-shaped row counts take the decode kernels
  *  after the same transform: M = 1 the GEMV; 2..8 the small-M product, and
@@ -180,6 +196,7 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
                const uint16_t* X, int ldx, int had_block, void* workspace,
                size_t ws_bytes, void* Y, int ldy, int y_dtype, void* stream);
 
+
 /*
  * A decode step's worth of GEMVs replayed as one unit ([P1] paragraph on the
  * decode step captured once as a graph and replayed per token).
@@ -190,13 +207,20 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
  * Modes:
  *  W4_SWEEP_GRAPH      one GEMV kernel per op captured into a hipGraph;
  *                      op i+1 starts after op i has finished (stream order).
- *  W4_SWEEP_PERSISTENT one persistent kernel walks all ops in order; weight
- *                      tiles are prefetched ahead across op boundaries, but no
- *                      output of op i+1 is computed (and no activation of op
- *                      i+1 is read) before every output of op i is written:
- *                      the same ordering as a decode step.  Bounded waits:
- *                      a wait that exceeds its limit ends the kernel and is
- *                      reported by w4_decode_sweep_check as W4_ERR_TIMEOUT.
+ *  W4_SWEEP_PERSISTENT one persistent kernel (one workgroup per CU) walks all
+ *                      ops in order; each workgroup's share of the next op's
+ *                      weights is loaded into LDS ahead of time (weights never
+ *                      depend on activations), but no output of op i+1 is
+ *                      computed, and no activation of op i+1 is read, before
+ *                      every output of op i is written: the ordering of a
+ *                      decode step, so op i+1 may read op i's output.
+ *                      Replays of one handle must not overlap (the handle's
+ *                      counters serve one replay at a time), and the kernel
+ *                      needs every workgroup resident at once (nothing else
+ *                      occupying the CUs).  Bounded waits: a wait that exceeds
+ *                      its limit ends the kernel and is reported by
+ *                      w4_decode_sweep_check as W4_ERR_TIMEOUT (the check then
+ *                      resets the handle's counters).
  *  W4_SWEEP_STREAM     the persistent kernel without the op-to-op ordering
  *                      (ops treated as independent); an upper bound.
  * The persistent modes are one kernel launch per replay.

@@ -187,3 +187,21 @@ def test_probes_run():
     torch.cuda.synchronize()
     assert torch.equal(dst, buf)
     assert out.item() == 7.0
+
+
+def test_one_hot_through_the_contiguous_kernel(oracle_mod):
+    """x = e_k through the 262144 x 1536 lm_head (the contiguous-range
+    kernel): every output is exactly (code - 8) * scale of column k."""
+    import torch
+    case = synth.lm_head()
+    N, K = case.N, case.K
+    assert "contiguous" in w4.describe_dispatch(1, N, K, 32)
+    packed = upload_packed(case.P, case.S, N, K, 32)
+    for k in (0, 1, 31, 32, 777, K - 1):
+        x = torch.zeros(K, dtype=torch.bfloat16, device=device())
+        x[k] = 1.0
+        y = from_dev(w4.gemv(packed, N, K, 32, x, "f32"))
+        q = k // 32
+        col = oracle_mod.dequant(np.ascontiguousarray(case.P[:, 4 * q:4 * q + 4]),
+                                 np.ascontiguousarray(case.S[:, q:q + 1]), N, 32, 32)[:, k % 32]
+        assert np.array_equal(y.view(np.uint32), col.astype(np.float32).view(np.uint32)), k

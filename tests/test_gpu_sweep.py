@@ -146,3 +146,80 @@ def test_sweep_stream_other_grids(oracle_mod, monkeypatch, bpc):
     torch.cuda.synchronize()
     _check_all(oracle_mod, cases, ops, "stream bpc %s" % bpc)
     sw.close()
+
+
+def _column(oracle_mod, c, k):
+    """Column k of a group-32 case's dequantized weights, from the oracle's
+    dequantization of the 32-element chunk that holds k."""
+    q = k // 32
+    Pq = np.ascontiguousarray(c.P[:, 4 * q:4 * q + 4])
+    Sq = np.ascontiguousarray(c.S[:, q:q + 1])
+    return oracle_mod.dequant(Pq, Sq, c.N, 32, 32)[:, k % 32].astype(np.float32)
+
+
+@pytest.mark.parametrize("name,mode", MODES)
+def test_sweep_one_hot_is_bit_exact(oracle_mod, sweep_data, name, mode):
+    """Every one of the 141 ops with a one-hot activation and fp32 output:
+    each output is exactly (code - 8) * scale of the hot column, through
+    the stream kernel (the headline), the decode-ordered kernel and the
+    graph of GEMV kernels."""
+    import torch
+    cases, ops = sweep_data
+    rng = np.random.default_rng(17)
+    ks, probe = [], []
+    for j, (c, op) in enumerate(zip(cases, ops)):
+        k = [0, c.K - 1, int(rng.integers(0, c.K))][j % 3]
+        x = torch.zeros(c.K, dtype=torch.bfloat16, device=device())
+        x[k] = 1.0
+        y = torch.full((c.N,), float("nan"), dtype=torch.float32, device=device())
+        probe.append((op[0], c.N, c.K, c.group, x, y))
+        ks.append(k)
+    note("one-hot sweep mode=%s" % name)
+    sw = w4.DecodeSweep(probe, mode)
+    sw.launch()
+    sw.check()
+    torch.cuda.synchronize()
+    for c, k, op in zip(cases, ks, probe):
+        got = from_dev(op[5])
+        assert np.array_equal(got.view(np.uint32), _column(oracle_mod, c, k).view(np.uint32)), \
+            (name, c.name, c.seed, k)
+    sw.close()
+
+
+@pytest.mark.parametrize("name,mode", MODES[:2])
+def test_chained_ops_read_the_previous_output(oracle_mod, name, mode):
+    """Decode order: op i + 1 multiplies op i's bf16 output (square 1536 x
+    1536 weights, x_{i+1} = y_i), outputs NaN-filled before every replay, so
+    an op that read its input before the previous op finished writing it
+    would see NaN.  Each y_i is checked against the oracle applied to the
+    GPU's own y_{i-1}."""
+    import torch
+    device()
+    n_ops, N = 12, 1536
+    cases, ys = [], []
+    x0b = synth.draw_activations(np.random.default_rng(4), 1, N)[0]
+    x0 = to_dev_bf16(x0b)
+    ops = []
+    for i in range(n_ops):
+        c = synth.make_case("chain%d" % i, N, N, 32, 1, 300 + i, "bf16")
+        y = torch.full((N,), float("nan"), dtype=torch.bfloat16, device=device())
+        ops.append((upload_packed(c.P, c.S, N, N, 32), N, N, 32, x0 if i == 0 else ys[-1], y))
+        cases.append(c)
+        ys.append(y)
+    note("chained sweep mode=%s ops=%d" % (name, n_ops))
+    sw = w4.DecodeSweep(ops, mode)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        sw.launch()
+        sw.check()
+        torch.cuda.synchronize()
+        xin = x0b
+        for i, c in enumerate(cases):
+            got = ys[i].view(torch.int16).cpu().numpy().view(np.uint16)
+            Y, A = oracle_mod.gemm_bf16(c.P, c.S, N, N, 32, xin, threads=16)
+            assert_within(synth.bf16_bits_to_f32(got), Y, A, "bf16",
+                          "%s rep %d op %d" % (name, rep, i))
+            xin = got
+    sw.close()
