@@ -48,6 +48,7 @@ EXPORTS = (
     "w4a16_gemm_twin_workspace_bytes", "w4a16_gemm_twin", "w4_attn_workspace_bytes",
     "w4_attn_decode",
     "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy", "w4_probe_mfma",
+    "w4a16_gemm_noalloc", "w4a16_gemm_noalloc_max_bytes",
 )
 
 
@@ -126,6 +127,8 @@ def lib():
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
             "w4_probe_mfma": ([i, vp, vp], i),
+            "w4a16_gemm_noalloc": ([vp, i, i, i, i, vp, i, i, vp, i, i, vp], i),
+            "w4a16_gemm_noalloc_max_bytes": ([], sz),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -401,6 +404,23 @@ def gemm(packed, N: int, K: int, group: int, X, had_block: int = 0,
                             had_block, _ptr(workspace), ws, _ptr(out), out.stride(0),
                             _dt(out_dtype), _stream(stream)))
     return out
+
+
+def gemm_noalloc(packed, N: int, K: int, group: int, X, had_block: int = 0,
+                 out_dtype: str = "bf16", out=None, stream=None):
+    """w4a16_gemm with the transform output in the library's static device
+    array (no workspace, no allocation inside the call)."""
+    M = X.shape[0]
+    if out is None:
+        out = _empty_out((M, N), out_dtype, X.device)
+    _check(lib().w4a16_gemm_noalloc(_ptr(packed), N, K, group, M, _ptr(X), X.stride(0),
+                                    had_block, _ptr(out), out.stride(0), _dt(out_dtype),
+                                    _stream(stream)))
+    return out
+
+
+def gemm_noalloc_max_bytes() -> int:
+    return int(lib().w4a16_gemm_noalloc_max_bytes())
 
 
 class DecodeSweep:

@@ -213,9 +213,12 @@ size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block) {
     return align_up((size_t)M * (size_t)K * 2, kAlign);
 }
 
-int w4a16_gemm(const void* packed, int N, int K, int group, int M,
-               const uint16_t* X, int ldx, int had_block, void* workspace,
-               size_t ws_bytes, void* Y, int ldy, int ydt, void* stream) {
+}  // extern "C"
+
+namespace w4 {
+
+int check_gemm_args(const void* packed, int N, int K, int group, int M, const uint16_t* X,
+                    int ldx, int had_block, const void* Y, int ldy, int ydt) {
     W4_TRY(check_weight_shape(N, K, group));
     W4_TRY(check_dtype(ydt));
     if (M < 1 || M > (1 << 20)) return fail(W4_ERR_SHAPE, "gemm: M out of range (got %d)", M);
@@ -229,6 +232,17 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
     W4_TRY(check_in16(packed, "packed"));
     W4_TRY(check_in16(X, "X"));
     W4_TRY(check_out_ptr(Y, ydt, "Y"));
+    return W4_OK;
+}
+
+}  // namespace w4
+
+extern "C" {
+
+int w4a16_gemm(const void* packed, int N, int K, int group, int M,
+               const uint16_t* X, int ldx, int had_block, void* workspace,
+               size_t ws_bytes, void* Y, int ldy, int ydt, void* stream) {
+    W4_TRY(check_gemm_args(packed, N, K, group, M, X, ldx, had_block, Y, ldy, ydt));
     const size_t need = w4a16_gemm_workspace_bytes(M, K, had_block);
     if (need) {
         if (ws_bytes < need)

@@ -21,6 +21,10 @@ struct GemvTile {
 };
 
 GemvTile pick_gemv_tile(int N, int K, int group);
+
+// Argument validation of w4a16_gemm (no HIP call); W4_OK or a status.
+int check_gemm_args(const void* packed, int N, int K, int group, int M, const uint16_t* X,
+                    int ldx, int had_block, const void* Y, int ldy, int ydt);
 int launch_gemv(const GemvTile& t, const void* packed, int N, int K, int group,
                 const uint16_t* x, void* y, int ydt, hipStream_t s);
 

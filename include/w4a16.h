@@ -196,6 +196,26 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
                const uint16_t* X, int ldx, int had_block, void* workspace,
                size_t ws_bytes, void* Y, int ldy, int y_dtype, void* stream);
 
+/*
+ * w4a16_gemm for callers that cannot allocate memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product and kernels, but the transform's output (when had_block != 0) is
+ * written to a fixed 8 MiB device array of this library instead of a caller
+ * workspace, so the call allocates nothing.  Each GPU holds its own copy of
+ * that array until the process ends; its device address is looked up once
+ * per device on the first call made with that device current.
+ *  Size limit: M * K * 2 bytes (rounded up to 256) must not exceed
+ *  w4a16_gemm_noalloc_max_bytes() when had_block != 0; larger calls return
+ *  W4_ERR_SHAPE before any HIP call.  Every other argument as w4a16_gemm.
+ *  Calls that overlap on one GPU (on different streams, or from several
+ *  threads) share the array and race; serialize them.  The array keeps the
+ *  last call's transform output; nothing in it needs to start at zero.
+ */
+int w4a16_gemm_noalloc(const void* packed, int N, int K, int group, int M,
+                       const uint16_t* X, int ldx, int had_block, void* Y, int ldy,
+                       int y_dtype, void* stream);
+/* Bytes of the static transform array (8 MiB). */
+size_t w4a16_gemm_noalloc_max_bytes(void);
 
 /*
  * A decode step's worth of GEMVs replayed as one unit ([P1] paragraph on the

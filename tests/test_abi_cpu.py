@@ -199,6 +199,19 @@ def test_gemm_validation(L):
     assert w4.gemm_workspace_bytes(512, 1536, 0) == 0
 
 
+def test_gemm_noalloc_validation(L):
+    """Bad arguments and a transform larger than the static array are
+    rejected before any HIP call (this machine has no GPU)."""
+    f = L.w4a16_gemm_noalloc
+    assert L.w4a16_gemm_noalloc_max_bytes() == 8 << 20
+    assert f(VP(0), 64, 1536, 256, 64, A16, 1536, 512, A16, 64, 1, VP(0)) == -1    # NULL
+    assert f(A16, 64, 1536, 256, 64, A16, 1536, 384, A16, 64, 1, VP(0)) == -2      # had_block
+    assert f(A16, 64, 1536, 256, 64, A2, 1536, 512, A16, 64, 1, VP(0)) == -3       # X align
+    M = (8 << 20) // (1536 * 2) + 1
+    assert f(A16, 64, 1536, 256, M, A16, 1536, 512, A16, 64, 1, VP(0)) == -2       # too big
+    assert "static scratch" in w4.last_error()
+
+
 def test_sweep_validation(L):
     ops = (w4.GemvOp * 2)()
     ops[0] = w4.GemvOp(0x10000, 64, 512, 32, 0x10000, 0x10000, 0)
