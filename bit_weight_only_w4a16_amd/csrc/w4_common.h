@@ -157,40 +157,56 @@ __device__ __forceinline__ float chunk_dot16(u32x4 q, const uint32_t* xh, const 
     return a0 + a1;
 }
 
-// Converts NC chunks of bf16 activation pairs (16 pairs each) in place to
-// fp16 pairs of x * 2^s with one shared scale and returns 2^-s.
-// s = min(142 - e_max, 126), e_max the largest biased bf16 exponent present,
-// puts the largest magnitude below 2^16 (fp16's largest finite value is
-// 65504 >= 255 * 2^8) and keeps 2^-s a normal fp32.  `ok` is cleared unless
-// the conversion is exact: every nonzero element normal (biased exponent
-// >= 1) and within 2^29 of the largest (so it lands on a normal fp16), and
-// no inf or NaN.
-template <int NC>
-__device__ __forceinline__ float chunks_to_f16(uint32_t (&xr)[NC][16], bool& ok) {
-    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+// Magnitude range of n bf16 activation pairs: the largest magnitude bits
+// (mx) and the smallest nonzero magnitude bits minus one (mn; 0xFFFF when
+// every element is zero), per half.
+__device__ __forceinline__ void pairs_range(const uint32_t* xr, int n, u16x2& mx, u16x2& mn) {
     const u16x2 one = {1, 1};
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const u16x2 mag = __builtin_bit_cast(u16x2, xr[c][i] & 0x7FFF7FFFu);
-            mx = __builtin_elementwise_max(mx, mag);
-            mn = __builtin_elementwise_min(mn, (u16x2)(mag - one));   // zero wraps to 0xFFFF
-        }
+    for (int i = 0; i < n; ++i) {
+        const u16x2 mag = __builtin_bit_cast(u16x2, xr[i] & 0x7FFF7FFFu);
+        mx = __builtin_elementwise_max(mx, mag);
+        mn = __builtin_elementwise_min(mn, (u16x2)(mag - one));   // zero wraps to 0xFFFF
+    }
+}
+
+// The power-of-two scale exponent s for a range (pairs_range over every
+// element that shares it): s = min(142 - e_max, 126), e_max the largest
+// biased bf16 exponent present, puts the largest magnitude below 2^16
+// (fp16's largest finite value is 65504 >= 255 * 2^8) and keeps 2^-s a
+// normal fp32.  `ok` is cleared unless the conversion is exact: every
+// nonzero element normal (biased exponent >= 1) and within 2^29 of the
+// largest (so it lands on a normal fp16), and no inf or NaN.
+__device__ __forceinline__ int f16_scale_exp(u16x2 mx, u16x2 mn, bool& ok) {
     const uint32_t big = mx[0] > mx[1] ? mx[0] : mx[1];
     const uint32_t low = (mn[0] < mn[1] ? mn[0] : mn[1]) + 1u;   // 0x10000: all zero
     const int emax = (int)(big >> 7);
     const int emin = (int)(low >> 7);
-    const int s = 142 - emax < 126 ? 142 - emax : 126;
     if (emax >= 255 || (low < 0x10000u && (emin < 1 || emin < emax - 29))) ok = false;
+    return 142 - emax < 126 ? 142 - emax : 126;
+}
+
+// n bf16 activation pairs -> fp16 pairs of x * 2^s, in place.
+__device__ __forceinline__ void pairs_to_f16(uint32_t* xr, int n, int s) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int i = 0; i < n; ++i) {
+        const f32x2 f = {ldexpf(__uint_as_float(xr[i] << 16), s),
+                         ldexpf(__uint_as_float(xr[i] & 0xFFFF0000u), s)};
+        xr[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+    }
+}
+
+// Converts NC chunks of bf16 activation pairs (16 pairs each) in place to
+// fp16 pairs of x * 2^s with one shared scale (f16_scale_exp) and returns
+// 2^-s.
+template <int NC>
+__device__ __forceinline__ float chunks_to_f16(uint32_t (&xr)[NC][16], bool& ok) {
+    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const f32x2 f = {ldexpf(__uint_as_float(xr[c][i] << 16), s),
-                             ldexpf(__uint_as_float(xr[c][i] & 0xFFFF0000u), s)};
-            xr[c][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-        }
+    for (int c = 0; c < NC; ++c) pairs_range(xr[c], 16, mx, mn);
+    const int s = f16_scale_exp(mx, mn, ok);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) pairs_to_f16(xr[c], 16, s);
     return ldexpf(1.0f, -s);
 }
 

@@ -66,10 +66,28 @@ template <int L>
 __device__ __forceinline__ void gemv_rows_generic(const struct GemvArgs& a, int rg0, int rg1,
                                                   int step, int lane);
 
+// Where gemv_rows takes a lane's activation slice from, and what it runs when
+// the slice is not exact in fp16.  GlobalX: the slice from a.x in global
+// memory (written before the launch), the exact bf16 loop as fallback.
+struct GlobalX {
+    template <int L, int U>
+    __device__ __forceinline__ bool load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16],
+                                         float& xv) const {
+        return load_x_slice<L, U>(a.x, a.C, lk, xr, xv);
+    }
+    template <int L>
+    __device__ __forceinline__ void fallback(const GemvArgs& a, int rg0, int rg1, int step,
+                                             int lane) const {
+        gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+    }
+};
+
 // Row groups rg0, rg0 + step, ... (< rg1) of one matrix for one wave.
 // Needs an even number of groups per row (G).  FULLC: L * U == C.  Otherwise lanes past the row end read a clamped, valid
 // chunk and multiply it by a zero activation slice.  Rows past N are clamped
 // to row N - 1 and not stored, so the loop has no divergent branches.
+// XS supplies the activation slice and the exact fallback (GlobalX); AGENT
+// stores the outputs at agent scope (read by other CUs in the same launch).
 // STAGES register sets rotate: STAGES - 1 row groups are in flight while the
 // current one is decoded.  Lane partials are summed in a fixed order, so the
 // result is bitwise deterministic.
@@ -82,9 +100,10 @@ __device__ __forceinline__ void gemv_rows_generic(const struct GemvArgs& a, int 
 // sums every lane of a 16-lane row already holds its row's total, so a row
 // group's outputs are taken with one compare and no cross-lane move (32- and
 // 64-lane rows finish with DPP row broadcasts and one readlane per row).
-template <int L, int U, bool FULLC, int STAGES = 2, bool BATCH = false>
+template <int L, int U, bool FULLC, int STAGES = 2, bool BATCH = false, bool AGENT = false,
+          class XS = GlobalX>
 __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, int step,
-                                          int lane, const DecodeConsts& k) {
+                                          int lane, const DecodeConsts& k, const XS& xs = XS()) {
     static_assert(STAGES == 2 || STAGES == 3, "register stages");
     constexpr int R = 64 / L;
     if (rg0 >= rg1) return;
@@ -96,8 +115,8 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
 
     uint32_t xr[U][16];
     float xv;
-    if (!BATCH && wave_any_inexact(load_x_slice<L, U>(a.x, a.C, lk, xr, xv))) {
-        gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+    if (!BATCH && wave_any_inexact(xs.template load<L, U>(a, lk, xr, xv))) {
+        xs.template fallback<L>(a, rg0, rg1, step, lane);
         return;
     }
 
@@ -122,7 +141,12 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
     auto flush = [&]() {
         const int t = lane % L;
         const int n = ob + R * t + lane / L;
-        if (ob >= 0 && t >= olo && t < ohi && n < a.N) store_out(a.y, (size_t)n, outv, a.ydt);
+        if (ob >= 0 && t >= olo && t < ohi && n < a.N) {
+            if (AGENT)
+                store_out_agent(a.y, (size_t)n, outv, a.ydt);
+            else
+                store_out(a.y, (size_t)n, outv, a.ydt);
+        }
     };
 
     auto load = [&](int g, u32x4 (&q)[U], uint32_t (&sc)[U]) {
@@ -170,7 +194,12 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         } else {
             acc = group_sum<L>(acc);
             const int n = g * R + lr;
-            if (lk == 0 && n < a.N) store_out(a.y, (size_t)n, acc, a.ydt);
+            if (lk == 0 && n < a.N) {
+                if (AGENT)
+                    store_out_agent(a.y, (size_t)n, acc, a.ydt);
+                else
+                    store_out(a.y, (size_t)n, acc, a.ydt);
+            }
         }
     };
 
@@ -189,8 +218,8 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         u32x4 qa[U], qb[U];
         uint32_t sa[U], sb[U];
         load(rg, qa, sa);
-        if (BATCH && wave_any_inexact(load_x_slice<L, U>(a.x, a.C, lk, xr, xv))) {
-            gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+        if (BATCH && wave_any_inexact(xs.template load<L, U>(a, lk, xr, xv))) {
+            xs.template fallback<L>(a, rg0, rg1, step, lane);
             return;
         }
         while (true) {
@@ -210,8 +239,8 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         uint32_t sa[U], sb[U], sc[U];
         load(rg, qa, sa);
         load(next(rg, step), qb, sb);
-        if (BATCH && wave_any_inexact(load_x_slice<L, U>(a.x, a.C, lk, xr, xv))) {
-            gemv_rows_generic<L>(a, rg0, rg1, step, lane);
+        if (BATCH && wave_any_inexact(xs.template load<L, U>(a, lk, xr, xv))) {
+            xs.template fallback<L>(a, rg0, rg1, step, lane);
             return;
         }
         while (true) {

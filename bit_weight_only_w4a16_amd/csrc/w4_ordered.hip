@@ -17,16 +17,19 @@
 //    compute reads its weights from LDS;
 //  - wave 0 is the control wave: it issues no DMA (so its waits cover only
 //    its own accesses), polls the completion counters, loads the activation
-//    (agent scope, 16-byte loads), converts it to fp16 once for the whole
-//    workgroup, stores the workgroup's outputs (agent scope), waits for them
-//    to complete and signals;
+//    (agent scope, 16-byte loads) into LDS for the whole workgroup, stores
+//    the workgroup's outputs (agent scope), waits for them to complete and
+//    signals;
+//  - the activation is multiplied as it is, bf16, against the exact bf16
+//    decode of the codes (w4_common.h): no conversion pass and no range
+//    fallback, so one barrier per op separates the handoff from the compute;
 //  - completion is counted in eight counters, one per XCD's workgroups
 //    (workgroup b runs on XCD b mod 8), each in its own 128-byte line: eight
 //    adders per address instead of one counter for all (measured 1.9 us
 //    against 3.7 us per bare handoff; per-workgroup flags polled as a whole
 //    3.6 us).
 // Shares too large for a slot (the 262144-row output layer: 885 KB per
-// workgroup) are streamed from HBM by waves 1..7 after the handoff, with the
+// workgroup) are streamed from HBM by all 8 waves after the handoff, with the
 // next row group in flight.
 //
 // Safety: every wait is bounded; a wait that gives up sets the error word
@@ -48,11 +51,14 @@ constexpr unsigned kOrdSpin = 1u << 20;
 
 // Dynamic LDS layout of a workgroup.
 constexpr int kSlotBytes = kOrdCodeBytes + kOrdScaleBytes;
-constexpr int kXhOff = 2 * kSlotBytes;                  // fp16 activation pairs
-constexpr int kXbOff = kXhOff + kOrdMaxK * 2;           // bf16 activation pairs
-constexpr int kXvOff = kXbOff + kOrdMaxK * 2;           // per-chunk inverse scales
-constexpr int kOutOff = kXvOff + (kOrdMaxK / 32) * 4;   // the share's outputs (fp32)
-constexpr int kFlagOff = kOutOff + kOrdMaxRows * 4;     // s_ok, s_inexact
+// The activation copy is quarter-major: 16-byte quarter q of chunk c (32
+// elements, 64 bytes) sits at q * kQStride + 16 c, so lanes that touch
+// consecutive chunks touch consecutive 16-byte words (a chunk-major copy puts
+// them 64 bytes apart, on the same LDS banks).
+constexpr int kQStride = (kOrdMaxK / 32) * 16;
+constexpr int kXbOff = 2 * kSlotBytes;                  // bf16 activation pairs
+constexpr int kOutOff = kXbOff + kOrdMaxK * 2;          // the share's outputs (fp32)
+constexpr int kFlagOff = kOutOff + kOrdMaxRows * 4;     // s_ok
 constexpr int kOrdLds = kFlagOff + 16;
 
 __device__ __forceinline__ void share_rows(int N, int w, int G, int& rb, int& re) {
@@ -152,75 +158,72 @@ __device__ __forceinline__ void load_x4_agent(const uint32_t* x, int c0, int C,
         : "memory");
 }
 
-// One lane's activation slice for tile (L, U): chunks lk + L u, from the
-// workgroup's converted copy in LDS (fp16 pairs and inverse scales, or bf16
-// pairs when EXACT); chunks past the row end read as zero.
-template <int L, bool EXACT>
-__device__ __forceinline__ void slice_from_lds(const uint8_t* smem, int C, int U, int lk,
-                                               uint32_t (&xr)[kPwMaxU][16],
-                                               float (&xv)[kPwMaxU]) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(smem + (EXACT ? kXbOff : kXhOff));
-    const float* inv = reinterpret_cast<const float*>(smem + kXvOff);
+// One lane's activation slice for tile (L, U): chunks chunk_of(lk, rot, u)
+// of the workgroup's bf16 copy in LDS; chunks past the row end read as zero.
+// The lanes of a row take its chunks (lk + rot) mod L + L u: a row's lanes
+// still cover every chunk, and with rot = 4 (row within the wave) the rows a
+// wave reads at once start on different LDS banks.
+template <int L>
+__device__ __forceinline__ int chunk_of(int lk, int rot, int u) {
+    return ((lk + rot) & (L - 1)) + L * u;
+}
+
+// UT > 0: the chunk count U per lane is the compile-time UT (every load can
+// be issued up front); UT == 0: U at run time.
+template <int L, int UT = 0>
+__device__ __forceinline__ void slice_from_lds(const uint8_t* smem, int C, int U, int lk, int rot,
+                                               uint32_t (&xr)[kPwMaxU][16]) {
 #pragma unroll
-    for (int u = 0; u < kPwMaxU; ++u) {
-        const int c = lk + L * u;
-        if (u < U && c < C) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(src + 16 * c);
+    for (int u = 0; u < (UT > 0 ? UT : kPwMaxU); ++u) {
+        const int c = chunk_of<L>(lk, rot, u);
+        if ((UT > 0 || u < U) && c < C) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const u32x4 v = p[i];
+                const u32x4 v =
+                    *reinterpret_cast<const u32x4*>(smem + kXbOff + i * kQStride + 16 * c);
                 xr[u][4 * i + 0] = v[0];
                 xr[u][4 * i + 1] = v[1];
                 xr[u][4 * i + 2] = v[2];
                 xr[u][4 * i + 3] = v[3];
             }
-            xv[u] = EXACT ? 0.0625f : inv[c];
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) xr[u][i] = 0u;
-            xv[u] = 0.f;
         }
     }
 }
 
-// Row sum of one lane's chunks: q the codes, sc the scales (bf16 bits) of
-// chunks lk + L u.
-template <bool EXACT>
+// Row sum of one lane's chunks: q the codes, sc the scales (bf16 bits).
+// Codes enter as the exact bf16 values 16 (c - 8) (w4_common.h), so the
+// activations need no conversion; each chunk's sum is scaled by s / 16.
+template <int UT = 0>
 __device__ __forceinline__ float row_partial(const u32x4 (&q)[kPwMaxU], const uint32_t (&sc)[kPwMaxU],
-                                             const uint32_t (&xr)[kPwMaxU][16],
-                                             const float (&xv)[kPwMaxU], int U,
-                                             const DecodeConsts& k) {
+                                             const uint32_t (&xr)[kPwMaxU][16], int U) {
     float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < kPwMaxU; ++u) {
-        if (u < U) {
-            const float d = EXACT ? chunk_dot_x16(q[u], xr[u]) : chunk_dot16(q[u], xr[u], k);
-            acc = fmaf(bf16_to_f32(sc[u]), d * xv[u], acc);
-        }
+    for (int u = 0; u < (UT > 0 ? UT : kPwMaxU); ++u) {
+        if (UT > 0 || u < U)
+            acc = fmaf(bf16_to_f32(sc[u]) * 0.0625f, chunk_dot_x16(q[u], xr[u]), acc);
     }
     return acc;
 }
 
-template <int L>
-__device__ __forceinline__ float lane_group_sum(float v) {
-    return group_sum<L>(v);
-}
-
 // Resident share: rows 0 .. R-1 of the slot, row groups of 64/L rows taken by
 // the workgroup's 8 waves in turn; row sums go to the LDS output buffer.
-template <int L, bool EXACT>
+template <int L, int UT = 0>
 __device__ __forceinline__ void compute_resident(const SweepOp& op, const uint8_t* smem,
-                                                 const uint8_t* slot, int R, int wave, int lane,
-                                                 const DecodeConsts& k) {
+                                                 const uint8_t* slot, int R, int wave,
+                                                 int lane) {
     constexpr int RG = 64 / L;
     const int lk = lane % L, lr = lane / L;
-    const int C = op.C, U = op.U, K = C * 32;
+    const int C = op.C, U = UT > 0 ? UT : op.U, K = C * 32;
+    const int ngroups = (R + RG - 1) / RG;
+    if (wave >= ngroups) return;
+    const int rot = 4 * lr;
     uint32_t xr[kPwMaxU][16];
-    float xv[kPwMaxU];
-    slice_from_lds<L, EXACT>(smem, C, U, lk, xr, xv);
+    slice_from_lds<L, UT>(smem, C, U, lk, rot, xr);
     float* outv = reinterpret_cast<float*>(const_cast<uint8_t*>(smem) + kOutOff);
     const uint16_t* sslot = reinterpret_cast<const uint16_t*>(slot + kOrdCodeBytes);
-    const int ngroups = (R + RG - 1) / RG;
     for (int g = wave; g < ngroups; g += kOrdWaves) {
         int r = g * RG + lr;
         const bool live = r < R;
@@ -228,35 +231,33 @@ __device__ __forceinline__ void compute_resident(const SweepOp& op, const uint8_
         u32x4 q[kPwMaxU];
         uint32_t sc[kPwMaxU];
 #pragma unroll
-        for (int u = 0; u < kPwMaxU; ++u) {
-            int c = lk + L * u;
+        for (int u = 0; u < (UT > 0 ? UT : kPwMaxU); ++u) {
+            int c = chunk_of<L>(lk, rot, u);
             c = c < C ? c : C - 1;
             q[u] = *reinterpret_cast<const u32x4*>(slot + (size_t)r * (K / 2) + 16 * c);
             sc[u] = sslot[r * op.G + (c >> op.gshift)];
         }
-        const float acc = lane_group_sum<L>(row_partial<EXACT>(q, sc, xr, xv, U, k));
+        const float acc = group_sum<L>(row_partial<UT>(q, sc, xr, U));
         if (lk == 0 && live) outv[r] = acc;
     }
 }
 
-// Streamed share (larger than a slot): waves 1..7 each stream a contiguous
-// part of the rows from HBM, the next row group's codes in flight while the
+// Streamed share (larger than a slot): every wave streams a contiguous part
+// of the rows from HBM, the next row group's codes in flight while the
 // current one is multiplied; outputs stored at agent scope.
-template <int L, bool EXACT>
+template <int L>
 __device__ __forceinline__ void compute_streamed(const SweepOp& op, const uint8_t* smem, int rb,
-                                                 int re, int dw, int lane,
-                                                 const DecodeConsts& k) {
+                                                 int re, int wv, int lane) {
     constexpr int RG = 64 / L;
     const int lk = lane % L, lr = lane / L;
     const int C = op.C, U = op.U;
     const int R = re - rb;
     const int ng = (R + RG - 1) / RG;
-    const int g0 = (int)((long long)dw * ng / kOrdDmaWaves);
-    const int g1 = (int)((long long)(dw + 1) * ng / kOrdDmaWaves);
+    const int g0 = (int)((long long)wv * ng / kOrdWaves);
+    const int g1 = (int)((long long)(wv + 1) * ng / kOrdWaves);
     if (g0 >= g1) return;
     uint32_t xr[kPwMaxU][16];
-    float xv[kPwMaxU];
-    slice_from_lds<L, EXACT>(smem, C, U, lk, xr, xv);
+    slice_from_lds<L>(smem, C, U, lk, 0, xr);
     auto load = [&](int g, u32x4 (&q)[kPwMaxU], uint32_t (&sc)[kPwMaxU]) {
         int n = rb + g * RG + lr;
         n = n < re ? n : re - 1;
@@ -273,7 +274,7 @@ __device__ __forceinline__ void compute_streamed(const SweepOp& op, const uint8_
         }
     };
     auto finish = [&](int g, const u32x4 (&q)[kPwMaxU], const uint32_t (&sc)[kPwMaxU]) {
-        const float acc = lane_group_sum<L>(row_partial<EXACT>(q, sc, xr, xv, U, k));
+        const float acc = group_sum<L>(row_partial(q, sc, xr, U));
         const int n = rb + g * RG + lr;
         if (lk == 0 && n < re) store_out_agent(op.y, (size_t)n, acc, op.ydt);
     };
@@ -289,23 +290,118 @@ __device__ __forceinline__ void compute_streamed(const SweepOp& op, const uint8_
         finish(g, qb, sb);
         if (++g >= g1) break;
     }
+    // The last prefetch is still in flight.  Use its registers here, so the
+    // compiler waits for it on this path; otherwise it stays pending across
+    // the op loop and the compiler waits for it (with vmcnt(0), which also
+    // covers the DMA loads of later ops) before the next resident op's
+    // compute.
+#pragma unroll
+    for (int u = 0; u < kPwMaxU; ++u)
+        asm volatile("" ::"v"(qa[u]), "v"(qb[u]), "v"(sa[u]), "v"(sb[u]));
 }
 
-template <bool EXACT>
+// The activation slice of a streamed share for gemv_rows: from the
+// workgroup's bf16 copy in LDS (the global activation may be stale in this
+// CU's L2), converted to fp16 in registers.  The caller has already checked
+// that every lane's slice converts exactly (fallback is never reached).
+struct LdsX {
+    const uint8_t* smem;
+    template <int L, int U>
+    __device__ __forceinline__ bool load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16],
+                                         float& xv) const {
+        uint32_t t[kPwMaxU][16];
+        slice_from_lds<L, U>(smem, a.C, U, lk, 0, t);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xr[u][i] = t[u][i];
+        bool ok = true;
+        xv = chunks_to_f16<U>(xr, ok);
+        return ok;
+    }
+    template <int L>
+    __device__ __forceinline__ void fallback(const GemvArgs&, int, int, int, int) const {}
+};
+
+// Streamed share with L * U == C and an even number of scale groups per row:
+// the stand-alone GEMV's fp16 loop (three row groups in flight per wave,
+// outputs gathered per 64-row block) over the share's rows, a contiguous part
+// per wave, outputs stored at agent scope.
+template <int L, int U>
+__device__ __forceinline__ void streamed_fast(const SweepOp& op, const uint8_t* smem, int rb,
+                                              int re, int wv, int lane) {
+    constexpr int RG = 64 / L;
+    GemvArgs a;
+    a.codes = op.codes + (size_t)rb * op.C;
+    a.scales = op.scales + (size_t)rb * op.G;
+    a.x = nullptr;
+    a.y = static_cast<uint8_t*>(op.y) + (size_t)rb * (op.ydt == W4_BF16 ? 2 : 4);
+    a.N = re - rb;
+    a.C = op.C;
+    a.G = op.G;
+    a.gshift = op.gshift;
+    a.ydt = op.ydt;
+    const int ng = (a.N + RG - 1) / RG;
+    const int g0 = (int)((long long)wv * ng / kOrdWaves);
+    const int g1 = (int)((long long)(wv + 1) * ng / kOrdWaves);
+    if (g0 >= g1) return;
+    // a wave with a slice fp16 cannot hold exactly runs the bf16 loop
+    {
+        uint32_t t[kPwMaxU][16];
+        slice_from_lds<L, U>(smem, op.C, U, lane % L, 0, t);
+        u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+#pragma unroll
+        for (int u = 0; u < U; ++u) pairs_range(t[u], 16, mx, mn);
+        bool ok = true;
+        (void)f16_scale_exp(mx, mn, ok);
+        if (wave_any_inexact(ok)) {
+            compute_streamed<L>(op, smem, rb, re, wv, lane);
+            return;
+        }
+    }
+    const DecodeConsts k = decode_consts();
+    gemv_rows<L, U, true, 3, true, true>(a, g0, g1, 1, lane, k, LdsX{smem});
+}
+
 __device__ __forceinline__ void compute_op(const SweepOp& op, const uint8_t* smem,
                                            const uint8_t* slot, int rb, int re, int wave,
-                                           int lane, const DecodeConsts& k) {
+                                           int lane) {
     if (op.res) {
-        switch (op.L) {
-            case 16: compute_resident<16, EXACT>(op, smem, slot, re - rb, wave, lane, k); break;
-            case 32: compute_resident<32, EXACT>(op, smem, slot, re - rb, wave, lane, k); break;
-            default: compute_resident<64, EXACT>(op, smem, slot, re - rb, wave, lane, k); break;
+        const int R = re - rb;
+        // the lane tilings of the ordered sweep (L from the row length,
+        // U = ceil(C / L)) with U known at compile time
+        switch (op.L * 8 + op.U) {
+            case 16 * 8 + 1: compute_resident<16, 1>(op, smem, slot, R, wave, lane); return;
+            case 16 * 8 + 2: compute_resident<16, 2>(op, smem, slot, R, wave, lane); return;
+            case 16 * 8 + 3: compute_resident<16, 3>(op, smem, slot, R, wave, lane); return;
+            case 16 * 8 + 4: compute_resident<16, 4>(op, smem, slot, R, wave, lane); return;
+            case 32 * 8 + 3: compute_resident<32, 3>(op, smem, slot, R, wave, lane); return;
+            case 32 * 8 + 4: compute_resident<32, 4>(op, smem, slot, R, wave, lane); return;
+            case 64 * 8 + 3: compute_resident<64, 3>(op, smem, slot, R, wave, lane); return;
+            case 64 * 8 + 4: compute_resident<64, 4>(op, smem, slot, R, wave, lane); return;
+            default: break;
         }
-    } else if (wave > 0) {
         switch (op.L) {
-            case 16: compute_streamed<16, EXACT>(op, smem, rb, re, wave - 1, lane, k); break;
-            case 32: compute_streamed<32, EXACT>(op, smem, rb, re, wave - 1, lane, k); break;
-            default: compute_streamed<64, EXACT>(op, smem, rb, re, wave - 1, lane, k); break;
+            case 16: compute_resident<16>(op, smem, slot, R, wave, lane); break;
+            case 32: compute_resident<32>(op, smem, slot, R, wave, lane); break;
+            default: compute_resident<64>(op, smem, slot, R, wave, lane); break;
+        }
+    } else {
+        if (op.L * op.U == op.C && (op.G & 1) == 0) {
+            switch (op.L * 8 + op.U) {
+                case 16 * 8 + 3: streamed_fast<16, 3>(op, smem, rb, re, wave, lane); return;
+                case 16 * 8 + 4: streamed_fast<16, 4>(op, smem, rb, re, wave, lane); return;
+                case 32 * 8 + 3: streamed_fast<32, 3>(op, smem, rb, re, wave, lane); return;
+                case 32 * 8 + 4: streamed_fast<32, 4>(op, smem, rb, re, wave, lane); return;
+                case 64 * 8 + 3: streamed_fast<64, 3>(op, smem, rb, re, wave, lane); return;
+                case 64 * 8 + 4: streamed_fast<64, 4>(op, smem, rb, re, wave, lane); return;
+                default: break;
+            }
+        }
+        switch (op.L) {
+            case 16: compute_streamed<16>(op, smem, rb, re, wave, lane); break;
+            case 32: compute_streamed<32>(op, smem, rb, re, wave, lane); break;
+            default: compute_streamed<64>(op, smem, rb, re, wave, lane); break;
         }
     }
 }
@@ -321,8 +417,7 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = gridDim.x;
     const int w = blockIdx.x;
-    int* s_flags = reinterpret_cast<int*>(smem + kFlagOff);   // [0] ok, [1] inexact
-    const DecodeConsts k = decode_consts();
+    int* s_flags = reinterpret_cast<int*>(smem + kFlagOff);   // [0] ok
     auto slot_at = [&](int sl) { return smem + sl * kSlotBytes; };
 
     // the first two resident ops' shares go to the slots at once
@@ -345,60 +440,51 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
                 ok = false;
                 const unsigned target = (unsigned)i * (unsigned)G;
                 for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
-                    unsigned c = 0;
+                    // one round trip per poll: lanes 0..7 read the counters,
+                    // lane 8 the error word
+                    unsigned c = 0, e = 0;
                     if (lane < 8)
                         c = __hip_atomic_load(&ctl->cnt[32 * lane], __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    else if (lane == 8)
+                        e = __hip_atomic_load(&ctl->error, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
                     c += __shfl_xor(c, 1, 64);
                     c += __shfl_xor(c, 2, 64);
                     c += __shfl_xor(c, 4, 64);
                     c = __shfl(c, 0, 64);   // lane 0's total on every lane
+                    e = __shfl(e, 8, 64);
                     if ((int)(c - target) >= 0) {
                         ok = true;
                         break;
                     }
-                    if (__hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                        break;
+                    if (e) break;
                 }
             }
-            // op i's activation: agent-scope loads (written by any CU), then
-            // the workgroup's fp16 copy, its inverse scales and the bf16 copy
-            bool exact_ok = true;
+            // op i's activation (written by any CU): agent-scope loads into
+            // the workgroup's bf16 copy
             if (ok && lane < op.C) {
                 u32x4 xg[4][4];
                 load_x4_agent(reinterpret_cast<const uint32_t*>(op.x), lane, op.C, xg);
-                uint32_t* xh = reinterpret_cast<uint32_t*>(smem + kXhOff);
                 uint32_t* xb = reinterpret_cast<uint32_t*>(smem + kXbOff);
-                float* xvs = reinterpret_cast<float*>(smem + kXvOff);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = lane + 64 * j;
                     if (c < op.C) {
-                        uint32_t xr[16];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            reinterpret_cast<u32x4*>(xb + 16 * c)[q] = xg[j][q];
-                            xr[4 * q + 0] = xg[j][q][0];
-                            xr[4 * q + 1] = xg[j][q][1];
-                            xr[4 * q + 2] = xg[j][q][2];
-                            xr[4 * q + 3] = xg[j][q][3];
-                        }
-                        xvs[c] = chunk_to_f16(xr, exact_ok);
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            reinterpret_cast<u32x4*>(xh + 16 * c)[q] =
-                                u32x4{xr[4 * q], xr[4 * q + 1], xr[4 * q + 2], xr[4 * q + 3]};
+                            *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(xb) +
+                                                      q * kQStride + 16 * c) = xg[j][q];
                     }
                 }
             }
-            const bool inexact = __builtin_amdgcn_ballot_w64(!exact_ok) != 0;
             if (lane == 0) {
                 if (!ok)
                     __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 s_flags[0] = ok ? 1 : 0;
-                s_flags[1] = inexact ? 1 : 0;
             }
-        } else if (op.res) {
+        }
+        if (wave > 0 && op.res) {
             // this op's share has landed: only the next resident op's DMA
             // loads may still be in flight
             wait_vm_rt(pend_next);
@@ -409,12 +495,9 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
             return;
         }
         const uint8_t* slot = slot_at(op.slot);
-        if (s_flags[1])
-            compute_op<true>(op, smem, slot, rb, re, wave, lane, k);
-        else
-            compute_op<false>(op, smem, slot, rb, re, wave, lane, k);
+        compute_op(op, smem, slot, rb, re, wave, lane);
         if (!op.res) {
-            // streamed outputs were stored by waves 1..7: complete before B
+            // streamed outputs were stored by every wave: complete before B
             __builtin_amdgcn_s_waitcnt(0);
             asm volatile("" ::: "memory");
         }

@@ -97,9 +97,14 @@ def test_gemv_inf_activation(oracle_mod, N, K):
     assert np.array_equal(y[fin], Y[fin].astype(np.float32))   # +-inf
 
 
+# The last four are larger than a workgroup's LDS slot in the decode-ordered
+# kernel, so they are streamed: ragged shares of 16 x 3, 16 x 4 and 64 x 3
+# tiles (the even-numbered ones with wide-range activations, which take the
+# exact bf16 loop there) and a 16 x 2 tile, which always takes it.
 RAGGED_SPARSE_OPS = [(2560, 1536, "bf16"), (1536, 2048, "bf16"), (12288, 1536, "bf16"),
                      (1536, 6144, "bf16"), (33, 512, "f32"), (100, 1536, "f32"),
-                     (65, 6144, "bf16"), (4097, 1536, "f32")]
+                     (65, 6144, "bf16"), (4097, 1536, "f32"), (65537, 1536, "f32"),
+                     (16385, 2048, "bf16"), (8193, 6144, "bf16"), (30001, 1024, "f32")]
 
 
 @pytest.mark.parametrize("mode", [w4.W4_SWEEP_GRAPH, w4.W4_SWEEP_PERSISTENT, w4.W4_SWEEP_STREAM])
