@@ -11,15 +11,22 @@
 // visible, every workgroup told) costs ~3 us against 0.2-1.3 us of HBM time
 // per layer op, so everything that does not depend on the previous op is
 // taken off that path:
-//  - weights never depend on activations: waves 1..7 DMA the workgroup's
-//    share of the next resident op (codes and scales, up to 56 KB) into one
-//    of two LDS slots while the current op waits and computes, so an op's
-//    compute reads its weights from LDS;
+//  - weights never depend on activations: wave 7, the DMA wave, copies the
+//    workgroup's share of a later resident op (codes and scales, up to 56 KB)
+//    into one of two LDS slots, so an op's compute reads its weights from
+//    LDS.  It issues the copy when the op before that one starts computing:
+//    the copy's HBM traffic then overlaps compute that reads only LDS, not the
+//    handoff's stores, polls and loads (issued at the end of the previous op
+//    it slowed each handoff by ~0.6 us), and the issue, which stalls while
+//    every CU copies at once, delays no compute wave;
+//  - waves 0..6 compute a resident share: each row's chunks are cut into
+//    parts that 16-lane groups take (the host's plan), so that shares of a
+//    few rows still keep every compute wave busy;
 //  - wave 0 is the control wave: it issues no DMA (so its waits cover only
 //    its own accesses), polls the completion counters, loads the activation
-//    (agent scope, 16-byte loads) into LDS for the whole workgroup, stores
-//    the workgroup's outputs (agent scope), waits for them to complete and
-//    signals;
+//    (agent scope, 16-byte loads) into LDS for the whole workgroup, adds the
+//    partial sums, stores the workgroup's outputs (agent scope), waits for
+//    them to complete and signals;
 //  - the activation is multiplied as it is, bf16, against the exact bf16
 //    decode of the codes (w4_common.h): no conversion pass and no range
 //    fallback, so one barrier per op separates the handoff from the compute;
@@ -57,8 +64,8 @@ constexpr int kSlotBytes = kOrdCodeBytes + kOrdScaleBytes;
 // them 64 bytes apart, on the same LDS banks).
 constexpr int kQStride = (kOrdMaxK / 32) * 16;
 constexpr int kXbOff = 2 * kSlotBytes;                  // bf16 activation pairs
-constexpr int kOutOff = kXbOff + kOrdMaxK * 2;          // the share's outputs (fp32)
-constexpr int kFlagOff = kOutOff + kOrdMaxRows * 4;     // s_ok
+constexpr int kOutOff = kXbOff + kOrdMaxK * 2;          // the share's partial sums (fp32)
+constexpr int kFlagOff = kOutOff + kOrdMaxPartials * 4; // flags and the LDS count
 constexpr int kOrdLds = kFlagOff + 16;
 
 __device__ __forceinline__ void share_rows(int N, int w, int G, int& rb, int& re) {
@@ -66,57 +73,57 @@ __device__ __forceinline__ void share_rows(int N, int w, int G, int& rb, int& re
     re = (int)((long long)(w + 1) * N / G);
 }
 
-// wait until at most n of this wave's DMA loads are in flight (0 <= n < 64)
+// wait until at most n of this wave's DMA loads are in flight (0 <= n < 64;
+// larger n waits for all)
 __device__ __forceinline__ void wait_vm_rt(int n) {
     switch (n) {
 #define W4_CASE(N) case N: wait_vm<N>(); break;
-        W4_CASE(0) W4_CASE(1) W4_CASE(2) W4_CASE(3) W4_CASE(4) W4_CASE(5) W4_CASE(6)
-        W4_CASE(7) W4_CASE(8) W4_CASE(9) W4_CASE(10) W4_CASE(11) W4_CASE(12) W4_CASE(13)
-        W4_CASE(14) W4_CASE(15) W4_CASE(16)
+#define W4_CASE8(B) W4_CASE(B) W4_CASE(B + 1) W4_CASE(B + 2) W4_CASE(B + 3) \
+                    W4_CASE(B + 4) W4_CASE(B + 5) W4_CASE(B + 6) W4_CASE(B + 7)
+        W4_CASE8(0) W4_CASE8(8) W4_CASE8(16) W4_CASE8(24)
+        W4_CASE8(32) W4_CASE8(40) W4_CASE8(48) W4_CASE8(56)
+#undef W4_CASE8
 #undef W4_CASE
         default: wait_vm<0>(); break;
     }
 }
 
-// DMA instructions each DMA wave issues for a share of `bytes` bytes (1 KB
-// per wave per instruction, waves 1..7 side by side).
-__device__ __forceinline__ int dma_rounds(int bytes) {
-    return (bytes + kOrdDmaWaves * 1024 - 1) / (kOrdDmaWaves * 1024);
-}
-
-// Issue the DMA of op's share for workgroup w into `slot` (DMA wave dw =
-// 0..6).  Codes [rb K/2, re K/2) and scales [rb G 2, re G 2) are contiguous
-// byte ranges, whole 16-byte units for a resident op (K % 256 == 0 and
-// G % 8 == 0, checked on the host); lanes past a range re-read its last 16
-// bytes into slot space past the share.  An empty share issues nothing.
+// Issue the DMA of op's share for workgroup w into `slot`, 1 KB per
+// instruction (16 bytes per lane).  Codes [rb K/2, re K/2) and scales
+// [rb G 2, re G 2) are contiguous byte ranges, whole 16-byte units for a
+// resident op (K % 256 == 0 and G % 8 == 0, checked on the host); lanes past
+// a range re-read its last 16 bytes into slot space past the share (the
+// slot's code and scale areas are whole kilobytes).  An empty share issues
+// nothing.
 __device__ __forceinline__ void issue_share(const SweepOp& op, int w, int G, uint8_t* slot,
-                                            int dw, int lane) {
+                                            int lane) {
     int rb, re;
     share_rows(op.N, w, G, rb, re);
     const int K = op.C * 32;
     const uint32_t cb = (uint32_t)(re - rb) * (uint32_t)(K / 2);
     const uint32_t c0 = (uint32_t)rb * (uint32_t)(K / 2);
-    const int nc = dma_rounds((int)cb);
+    const int nc = (int)((cb + 1023u) / 1024u);
     const uint32_t lds0 = lds_addr(slot);
     for (int d = 0; d < nc; ++d) {
-        const uint32_t o = (uint32_t)(d * kOrdDmaWaves + dw) * 1024u + 16u * lane;
+        const uint32_t o = (uint32_t)d * 1024u + 16u * lane;
         const uint32_t src = c0 + (o < cb ? o : (cb >= 16u ? cb - 16u : 0u));
-        dma16(src, op.codes, lds0 + (uint32_t)(d * kOrdDmaWaves + dw) * 1024u);
+        dma16(src, op.codes, lds0 + (uint32_t)d * 1024u);
     }
     const uint32_t sb = (uint32_t)(re - rb) * (uint32_t)(op.G * 2);
     const uint32_t s0 = (uint32_t)rb * (uint32_t)(op.G * 2);
-    const int ns = dma_rounds((int)sb);
+    const int ns = (int)((sb + 1023u) / 1024u);
     for (int d = 0; d < ns; ++d) {
-        const uint32_t o = (uint32_t)(d * kOrdDmaWaves + dw) * 1024u + 16u * lane;
+        const uint32_t o = (uint32_t)d * 1024u + 16u * lane;
         const uint32_t src = s0 + (o < sb ? o : (sb >= 16u ? sb - 16u : 0u));
-        dma16(src, op.scales, lds0 + kOrdCodeBytes + (uint32_t)(d * kOrdDmaWaves + dw) * 1024u);
+        dma16(src, op.scales, lds0 + kOrdCodeBytes + (uint32_t)d * 1024u);
     }
 }
 
+// DMA instructions issue_share issues for op's share of workgroup w
 __device__ __forceinline__ int share_dmas(const SweepOp& op, int w, int G) {
     int rb, re;
     share_rows(op.N, w, G, rb, re);
-    return dma_rounds((re - rb) * (op.C * 16)) + dma_rounds((re - rb) * (op.G * 2));
+    return ((re - rb) * (op.C * 16) + 1023) / 1024 + ((re - rb) * (op.G * 2) + 1023) / 1024;
 }
 
 // Chunks c0 + 64 j (j = 0..3) of an activation as agent-scope 16-byte loads
@@ -158,24 +165,15 @@ __device__ __forceinline__ void load_x4_agent(const uint32_t* x, int c0, int C,
         : "memory");
 }
 
-// One lane's activation slice for tile (L, U): chunks chunk_of(lk, rot, u)
-// of the workgroup's bf16 copy in LDS; chunks past the row end read as zero.
-// The lanes of a row take its chunks (lk + rot) mod L + L u: a row's lanes
-// still cover every chunk, and with rot = 4 (row within the wave) the rows a
-// wave reads at once start on different LDS banks.
-template <int L>
-__device__ __forceinline__ int chunk_of(int lk, int rot, int u) {
-    return ((lk + rot) & (L - 1)) + L * u;
-}
-
-// UT > 0: the chunk count U per lane is the compile-time UT (every load can
-// be issued up front); UT == 0: U at run time.
+// One lane's activation slice for tile (L, U) of a streamed share: chunks
+// lk + L u of the workgroup's bf16 copy in LDS; chunks past the row end read
+// as zero.  UT > 0: U is the compile-time UT; UT == 0: U at run time.
 template <int L, int UT = 0>
-__device__ __forceinline__ void slice_from_lds(const uint8_t* smem, int C, int U, int lk, int rot,
+__device__ __forceinline__ void slice_from_lds(const uint8_t* smem, int C, int U, int lk,
                                                uint32_t (&xr)[kPwMaxU][16]) {
 #pragma unroll
     for (int u = 0; u < (UT > 0 ? UT : kPwMaxU); ++u) {
-        const int c = chunk_of<L>(lk, rot, u);
+        const int c = lk + L * u;
         if ((UT > 0 || u < U) && c < C) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -208,37 +206,74 @@ __device__ __forceinline__ float row_partial(const u32x4 (&q)[kPwMaxU], const ui
     return acc;
 }
 
-// Resident share: rows 0 .. R-1 of the slot, row groups of 64/L rows taken by
-// the workgroup's 8 waves in turn; row sums go to the LDS output buffer.
-template <int L, int UT = 0>
+// Resident share (rows 0 .. R-1 of the slot): each row's C chunks are cut
+// into P parts of CP chunks, and the workgroup's 32 groups of 16 lanes take
+// (part p, rows q, q + Q, ...) with P Q <= 32 (the host's plan, which keeps
+// every lane busy even for shares of a few rows).  Lane k of a group holds
+// the activation of chunks c0 + k + 16 u of its part for all its rows; the
+// next row's codes are read from the slot while the current one is
+// multiplied.  A row's partial sums go to the LDS buffer, entry r P + p.
+template <int UP>
 __device__ __forceinline__ void compute_resident(const SweepOp& op, const uint8_t* smem,
                                                  const uint8_t* slot, int R, int wave,
                                                  int lane) {
-    constexpr int RG = 64 / L;
-    const int lk = lane % L, lr = lane / L;
-    const int C = op.C, U = UT > 0 ? UT : op.U, K = C * 32;
-    const int ngroups = (R + RG - 1) / RG;
-    if (wave >= ngroups) return;
-    const int rot = 4 * lr;
-    uint32_t xr[kPwMaxU][16];
-    slice_from_lds<L, UT>(smem, C, U, lk, rot, xr);
-    float* outv = reinterpret_cast<float*>(const_cast<uint8_t*>(smem) + kOutOff);
-    const uint16_t* sslot = reinterpret_cast<const uint16_t*>(slot + kOrdCodeBytes);
-    for (int g = wave; g < ngroups; g += kOrdWaves) {
-        int r = g * RG + lr;
-        const bool live = r < R;
-        r = live ? r : R - 1;
-        u32x4 q[kPwMaxU];
-        uint32_t sc[kPwMaxU];
+    const int j = wave * (64 / 16) + (lane >> 4), lk = lane & 15;
+    const int P = op.P, Q = op.Q;
+    if (j >= P * Q) return;
+    const int p = j % P, q0 = j / P;
+    if (q0 >= R) return;
+    const int C = op.C, G = op.G, gshift = op.gshift, rowb = 16 * C;
+    const int c0 = p * op.CP;
+    const int c1 = c0 + op.CP < C ? c0 + op.CP : C;
+    // chunks past the part's end read chunk c0 of the row (a valid address)
+    // against a zero activation slice
+    uint32_t xr[UP][16];
+    int cu[UP];
 #pragma unroll
-        for (int u = 0; u < (UT > 0 ? UT : kPwMaxU); ++u) {
-            int c = chunk_of<L>(lk, rot, u);
-            c = c < C ? c : C - 1;
-            q[u] = *reinterpret_cast<const u32x4*>(slot + (size_t)r * (K / 2) + 16 * c);
-            sc[u] = sslot[r * op.G + (c >> op.gshift)];
+    for (int u = 0; u < UP; ++u) {
+        const int c = c0 + lk + 16 * u;
+        const bool in = c < c1;
+        cu[u] = in ? c : c0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (in) v = *reinterpret_cast<const u32x4*>(smem + kXbOff + i * kQStride + 16 * c);
+            xr[u][4 * i + 0] = v[0];
+            xr[u][4 * i + 1] = v[1];
+            xr[u][4 * i + 2] = v[2];
+            xr[u][4 * i + 3] = v[3];
         }
-        const float acc = group_sum<L>(row_partial<UT>(q, sc, xr, U));
-        if (lk == 0 && live) outv[r] = acc;
+    }
+    float* part = reinterpret_cast<float*>(const_cast<uint8_t*>(smem) + kOutOff);
+    const uint16_t* sslot = reinterpret_cast<const uint16_t*>(slot + kOrdCodeBytes);
+    auto load = [&](int r, u32x4 (&qq)[UP], uint32_t (&ss)[UP]) {
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+            qq[u] = *reinterpret_cast<const u32x4*>(slot + (size_t)r * rowb + 16 * cu[u]);
+            ss[u] = sslot[r * G + (cu[u] >> gshift)];
+        }
+    };
+    auto finish = [&](int r, const u32x4 (&qq)[UP], const uint32_t (&ss)[UP]) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < UP; ++u)
+            acc = fmaf(bf16_to_f32(ss[u]) * 0.0625f, chunk_dot_x16(qq[u], xr[u]), acc);
+        acc = group_sum<16>(acc);
+        if (lk == 0) part[r * P + p] = acc;
+    };
+    u32x4 qa[UP], qb[UP];
+    uint32_t sa[UP], sb[UP];
+    int r = q0;
+    load(r, qa, sa);
+    while (true) {
+        load(r + Q < R ? r + Q : r, qb, sb);
+        finish(r, qa, sa);
+        r += Q;
+        if (r >= R) break;
+        load(r + Q < R ? r + Q : r, qa, sa);
+        finish(r, qb, sb);
+        r += Q;
+        if (r >= R) break;
     }
 }
 
@@ -257,7 +292,7 @@ __device__ __forceinline__ void compute_streamed(const SweepOp& op, const uint8_
     const int g1 = (int)((long long)(wv + 1) * ng / kOrdWaves);
     if (g0 >= g1) return;
     uint32_t xr[kPwMaxU][16];
-    slice_from_lds<L>(smem, C, U, lk, 0, xr);
+    slice_from_lds<L>(smem, C, U, lk, xr);
     auto load = [&](int g, u32x4 (&q)[kPwMaxU], uint32_t (&sc)[kPwMaxU]) {
         int n = rb + g * RG + lr;
         n = n < re ? n : re - 1;
@@ -310,7 +345,7 @@ struct LdsX {
     __device__ __forceinline__ bool load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16],
                                          float& xv) const {
         uint32_t t[kPwMaxU][16];
-        slice_from_lds<L, U>(smem, a.C, U, lk, 0, t);
+        slice_from_lds<L, U>(smem, a.C, U, lk, t);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -348,7 +383,7 @@ __device__ __forceinline__ void streamed_fast(const SweepOp& op, const uint8_t* 
     // a wave with a slice fp16 cannot hold exactly runs the bf16 loop
     {
         uint32_t t[kPwMaxU][16];
-        slice_from_lds<L, U>(smem, op.C, U, lane % L, 0, t);
+        slice_from_lds<L, U>(smem, op.C, U, lane % L, t);
         u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
         for (int u = 0; u < U; ++u) pairs_range(t[u], 16, mx, mn);
@@ -368,23 +403,11 @@ __device__ __forceinline__ void compute_op(const SweepOp& op, const uint8_t* sme
                                            int lane) {
     if (op.res) {
         const int R = re - rb;
-        // the lane tilings of the ordered sweep (L from the row length,
-        // U = ceil(C / L)) with U known at compile time
-        switch (op.L * 8 + op.U) {
-            case 16 * 8 + 1: compute_resident<16, 1>(op, smem, slot, R, wave, lane); return;
-            case 16 * 8 + 2: compute_resident<16, 2>(op, smem, slot, R, wave, lane); return;
-            case 16 * 8 + 3: compute_resident<16, 3>(op, smem, slot, R, wave, lane); return;
-            case 16 * 8 + 4: compute_resident<16, 4>(op, smem, slot, R, wave, lane); return;
-            case 32 * 8 + 3: compute_resident<32, 3>(op, smem, slot, R, wave, lane); return;
-            case 32 * 8 + 4: compute_resident<32, 4>(op, smem, slot, R, wave, lane); return;
-            case 64 * 8 + 3: compute_resident<64, 3>(op, smem, slot, R, wave, lane); return;
-            case 64 * 8 + 4: compute_resident<64, 4>(op, smem, slot, R, wave, lane); return;
-            default: break;
-        }
-        switch (op.L) {
-            case 16: compute_resident<16>(op, smem, slot, R, wave, lane); break;
-            case 32: compute_resident<32>(op, smem, slot, R, wave, lane); break;
-            default: compute_resident<64>(op, smem, slot, R, wave, lane); break;
+        switch (op.UP) {
+            case 1: compute_resident<1>(op, smem, slot, R, wave, lane); break;
+            case 2: compute_resident<2>(op, smem, slot, R, wave, lane); break;
+            case 3: compute_resident<3>(op, smem, slot, R, wave, lane); break;
+            default: compute_resident<4>(op, smem, slot, R, wave, lane); break;
         }
     } else {
         if (op.L * op.U == op.C && (op.G & 1) == 0) {
@@ -417,16 +440,28 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = gridDim.x;
     const int w = blockIdx.x;
-    int* s_flags = reinterpret_cast<int*>(smem + kFlagOff);   // [0] ok
+    // [i & 1] op i may run (by parity: a wave may still read op i's flag
+    // while wave 0 writes op i + 1's, never op i - 1's); [2] compute waves
+    // that finished an op (running count)
+    int* s_flags = reinterpret_cast<int*>(smem + kFlagOff);
+    if (tid == 0) s_flags[2] = 0;
     auto slot_at = [&](int sl) { return smem + sl * kSlotBytes; };
 
     // the first two resident ops' shares go to the slots at once
-    if (wave > 0) {
-        if (first0 >= 0) issue_share(ops[first0], w, G, slot_at(ops[first0].slot), wave - 1, lane);
-        if (first1 >= 0) issue_share(ops[first1], w, G, slot_at(ops[first1].slot), wave - 1, lane);
+    if (wave == kOrdDmaWave) {
+        if (first0 >= 0) issue_share(ops[first0], w, G, slot_at(ops[first0].slot), lane);
+        if (first1 >= 0) issue_share(ops[first1], w, G, slot_at(ops[first1].slot), lane);
     }
-    // DMA loads this wave has issued and not yet waited for, per pending op
+    // DMA loads issued after those of the next resident op (the second
+    // op's, until the first one has been waited for)
     int pend_next = first1 >= 0 ? share_dmas(ops[first1], w, G) : 0;
+    // resident op whose share is to be DMA'd once the next resident op's
+    // compute starts (nx_slot < 0: none).  Its table entry is read when the
+    // slot is freed, so the scalar load's latency hides behind the handoff.
+    SweepOp nx;
+    int nx_slot = -1;
+    // running count of compute-wave completions wave 0 waits for
+    unsigned arrived = 0;
 
     for (int i = 0; i < n_ops; ++i) {
         const SweepOp op = ops[i];
@@ -481,49 +516,84 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
             if (lane == 0) {
                 if (!ok)
                     __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_flags[0] = ok ? 1 : 0;
+                s_flags[i & 1] = ok ? 1 : 0;
             }
         }
-        if (wave > 0 && op.res) {
-            // this op's share has landed: only the next resident op's DMA
-            // loads may still be in flight
+        if (wave == kOrdDmaWave && op.res) {
+            // this op's share has landed: only DMA loads issued after it
+            // (the second op's, at the start) may still be in flight
             wait_vm_rt(pend_next);
+            pend_next = 0;
         }
         __syncthreads();   // A: activation and weights of op i visible
-        if (s_flags[0] == 0) {
+        if (s_flags[i & 1] == 0) {
             __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the workgroup
             return;
         }
         const uint8_t* slot = slot_at(op.slot);
+        if (wave == kOrdDmaWave && op.res && nx_slot >= 0) {
+            // the previous resident op's slot is free: the resident op after
+            // this one goes in.  Issued here, not when that slot was freed,
+            // so that the DMA traffic overlaps this op's compute (which reads
+            // only LDS) instead of the handoff's stores, polls and loads.
+            issue_share(nx, w, G, slot_at(nx_slot), lane);
+            nx_slot = -1;
+        }
         compute_op(op, smem, slot, rb, re, wave, lane);
+        // B: the compute waves (0..6 for a resident share, all 8 for a
+        // streamed one) count themselves done in LDS, partial sums written
+        // (resident) or outputs stored and complete (streamed); wave 0 waits
+        // for the count.  Not a workgroup barrier, so the DMA wave, whose
+        // copy may still be issuing, holds nobody up.
         if (!op.res) {
-            // streamed outputs were stored by every wave: complete before B
             __builtin_amdgcn_s_waitcnt(0);
             asm volatile("" ::: "memory");
         }
-        __syncthreads();   // B: every output of the share computed (and stored)
+        const bool computes = !op.res || wave != kOrdDmaWave;
+        arrived += op.res ? kOrdWaves - 1 : kOrdWaves;
+        if (computes && lane == 0)
+            __hip_atomic_fetch_add(&s_flags[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 
         if (wave == 0) {
+            bool done = false;
+            for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
+                const unsigned c = (unsigned)__hip_atomic_load(&s_flags[2], __ATOMIC_ACQUIRE,
+                                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+                if ((int)(c - arrived) >= 0) {
+                    done = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (!done) {
+                // cannot happen unless a wave is lost; the next poll sees the
+                // error word and every workgroup leaves
+                if (lane == 0)
+                    __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
             if (op.res) {
-                const float* outv = reinterpret_cast<const float*>(smem + kOutOff);
-                for (int r = lane; r < re - rb; r += 64)
-                    store_out_agent(op.y, (size_t)(rb + r), outv[r], op.ydt);
+                // a row's P partial sums, added in order
+                const float* part = reinterpret_cast<const float*>(smem + kOutOff);
+                for (int r = lane; r < re - rb; r += 64) {
+                    float v = part[r * op.P];
+                    for (int q = 1; q < op.P; ++q) v += part[r * op.P + q];
+                    store_out_agent(op.y, (size_t)(rb + r), v, op.ydt);
+                }
             }
             __builtin_amdgcn_s_waitcnt(0);   // the outputs are visible to every CU
             asm volatile("" ::: "memory");
             if (lane == 0)
                 __hip_atomic_fetch_add(&ctl->cnt[32 * (w & 7)], 1u, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-        } else if (op.res) {
-            // the slot is free: the resident op after the next one goes in
+        } else if (wave == kOrdDmaWave && op.res) {
+            // the slot is free once the compute waves are past this op (they
+            // are when the next op's barrier A opens): the resident op after
+            // the next one goes in once the next resident op starts computing
             if (op.next >= 0) {
-                const SweepOp nx = ops[op.next];
-                issue_share(nx, w, G, slot_at(nx.slot), wave - 1, lane);
-                // pending now: the next resident op's loads, then these
-                const int mine = share_dmas(nx, w, G);
-                pend_next = mine;
-            } else {
-                pend_next = 0;
+                nx = ops[op.next];
+                nx_slot = nx.slot;
             }
         }
     }

@@ -11,15 +11,18 @@ constexpr int kPwThreads = 64 * kPwWaves;
 constexpr int kPwMaxU = 4;                  // chunks per lane per row
 constexpr int kPwMaxC = 256;                // chunks per row (K <= 8192)
 
-// Decode-ordered kernel (w4_ordered.hip): 8 waves per workgroup, wave 0 the
-// control wave, waves 1..7 DMA the next resident op's share; two LDS slots.
+// Decode-ordered kernel (w4_ordered.hip): 8 waves per workgroup; wave 0 the
+// control wave, wave 7 the DMA wave (it fills the two LDS slots with the
+// next resident ops' shares), waves 0..6 compute resident shares.
 constexpr int kOrdWaves = 8;
 constexpr int kOrdThreads = 64 * kOrdWaves;
-constexpr int kOrdDmaWaves = kOrdWaves - 1;
-constexpr int kOrdCodeBytes = 7 * kOrdDmaWaves * 1024;   // 49 KB of codes per slot
-constexpr int kOrdScaleBytes = kOrdDmaWaves * 1024;      // 7 KB of scales per slot
+constexpr int kOrdDmaWave = kOrdWaves - 1;
+constexpr int kOrdCodeBytes = 49 * 1024;                 // codes per slot
+constexpr int kOrdScaleBytes = 7 * 1024;                 // scales per slot
 constexpr int kOrdMaxK = 32 * kPwMaxC;                   // 8192
 constexpr int kOrdMaxRows = 512;                         // rows of a resident share
+constexpr int kOrdGroups = 16 * (kOrdWaves - 1) / 4;     // 16-lane groups of waves 0..6
+constexpr int kOrdMaxPartials = 1024;                    // rows x parts of a resident share
 
 // One GEMV of the step, as the kernel reads it.
 struct SweepOp {
@@ -37,6 +40,8 @@ struct SweepOp {
     int res;                 // 1: every workgroup's share fits an LDS slot (DMA'd ahead)
     int slot;                // its slot (0 or 1)
     int next;                // resident op DMA'd into this op's slot after it (-1: none)
+    int P, Q, CP, UP;        // resident: parts per row, row stride, chunks per part and
+                             // per lane (P Q <= kOrdGroups, UP = ceil(CP / 16))
 };
 
 // Tile shapes (L lanes per row, U chunks per lane, L * U == C) compiled into

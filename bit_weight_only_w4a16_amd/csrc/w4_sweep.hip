@@ -65,6 +65,52 @@ static int persist_lanes(int C) {
     return 64;
 }
 
+// How a resident share is split over the workgroup's 16-lane groups: each
+// row's C chunks in P parts of CP chunks, Q = kOrdGroups / P groups per part;
+// group j takes part j % P of rows j / P, j / P + Q, ... and its lanes hold
+// UP = ceil(CP / 16) chunks each.  The cost of a plan is the issue time of
+// the busiest SIMD: waves w and w + 4 share one, a wave runs as long as its
+// busiest group, and a row costs UP chunk decodes (about 84 vector
+// instructions each) plus about 25 for the row sum and its write (waves
+// 0..6 compute, wave 7 only issues the DMA).  Picks the
+// cheapest plan (the smallest P on ties: fewer partial sums) with no empty
+// part, at most kPwMaxU chunks per lane and R P partials within the LDS
+// buffer.
+static bool resident_split(int R, int C, SweepOp* t) {
+    int best = 0;
+    long long best_cost = 0;
+    for (int P = 1; P <= kOrdGroups; ++P) {
+        const int Q = kOrdGroups / P;
+        const int CP = (C + P - 1) / P;
+        const int UP = (CP + 15) / 16;
+        if ((P - 1) * CP >= C || UP > kPwMaxU || R * P > kOrdMaxPartials) continue;
+        long long cost = 0;
+        for (int simd = 0; simd < 4; ++simd) {
+            long long c = 0;
+            for (int w = simd; w < kOrdGroups / 4; w += 4) {
+                int rows = 0;
+                for (int j = 4 * w; j < 4 * w + 4 && j < P * Q; ++j) {
+                    const int q = j / P;
+                    const int n = q < R ? (R - q + Q - 1) / Q : 0;
+                    rows = n > rows ? n : rows;
+                }
+                c += (long long)rows * (84 * UP + 25);
+            }
+            cost = c > cost ? c : cost;
+        }
+        if (best == 0 || cost < best_cost) {
+            best = P;
+            best_cost = cost;
+        }
+    }
+    if (best == 0) return false;
+    t->P = best;
+    t->Q = kOrdGroups / best;
+    t->CP = (C + best - 1) / best;
+    t->UP = (t->CP + 15) / 16;
+    return true;
+}
+
 static int blocks_per_cu_override() {
     const char* e = getenv("W4_SWEEP_BLOCKS_PER_CU");
     const int v = e ? atoi(e) : 0;
@@ -109,6 +155,7 @@ static int setup_persistent(w4_sweep* h) {
         t.res = 0;
         t.slot = 0;
         t.next = -1;
+        t.P = t.Q = t.CP = t.UP = 0;
         if (dep) {
             t.L = persist_lanes(t.C);
             t.cfg = kCfgGeneric;
@@ -121,6 +168,7 @@ static int setup_persistent(w4_sweep* h) {
                     rows * (o.K / 2) <= kOrdCodeBytes &&
                     rows * (o.K / o.group) * 2 <= kOrdScaleBytes && rows <= kOrdMaxRows &&
                     (long long)o.N * (o.K / 2) < (1LL << 32);
+            if (t.res && !resident_split((int)rows, t.C, &t)) t.res = 0;
         } else {
             t.cfg = stream_cfg(t.C, &t.L);
             if (t.G & 1) {  // the tiled loop reads scales in dword pairs
