@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark: W4A16 GEMV effective HBM GB/s and ms per decode-step sweep.
+"""Benchmark: ms per decode-step weight sweep and its effective HBM GB/s.
 
 One step = one replay of a decode step's weight sweep on one GPU: 35 decoder
 layers x {qkv 2560x1536, o 1536x2048, gate_up 12288x1536, down 1536x6144}
@@ -10,13 +10,20 @@ weight bytes with 1 GB = 1e9 B, the accounting of the pages' own figures
 ([P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp",
 summary line of the w4gemv.py kernel).
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 500] [--mode stream]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--mode persistent]
 
-Prints one JSON line.  The timed mode (default "stream") replays the 141
-independent GEMVs as one persistent kernel captured in a graph; the other
-modes (one kernel per GEMV in a graph; decode-ordered persistent kernel) and a
-plain-sum read of a 4 GiB buffer are measured alongside and reported under
-"extra".  The CPU baseline times the fp64 oracle on one full sweep.
+Prints one JSON line.  The headline respects decode order: op i + 1 starts
+only after every output of op i is written, as in a decode step ([P1],
+paragraph on the step captured once as a graph and replayed per token).
+Each step is one replay of a captured graph: by default the decode-ordered
+persistent kernel captured as a one-node graph ("persistent"); "graph" is the
+141 GEMV kernels captured in order; "auto" times both and reports the faster.
+ms_per_step is the median of five timed regions of --steps replays each.
+Reported under "extra", labelled: the other ordered mode, direct launches
+without a graph, and the 141 GEMVs with no ordering between them
+("stream", an upper bound: no decode step can run its GEMVs unordered), plus
+the other workloads' kernels.  The CPU baseline times the fp64 oracle on the
+host's cores.
 """
 from __future__ import annotations
 
@@ -32,20 +39,22 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 GEMV effective HBM GB/s (% of peak) + ms per 35-layer+lm_head sweep"
 PEAK_HBM_GBPS = 8000.0
 MODES = {"graph": 0, "persistent": 1, "stream": 2}
+ORDERED = ("persistent", "graph")
+KERNEL_OF = {"persistent": "w4::ordered_kernel", "stream": "w4::stream_kernel"}
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def load_traffic(weight_bytes: int):
-    """HBM bytes per launch of the stream kernel from the committed counter
+def load_traffic(kernel: str):
+    """HBM bytes per launch of a sweep kernel from the committed counter
     summary, or None when it is missing or was taken on other kernel source."""
     from bit_weight_only_w4a16_amd import traffic
     try:
-        with open(traffic.OUT_FILE) as f:
+        with open(traffic.out_file(kernel)) as f:
             t = json.load(f)
-    except (OSError, ValueError):
+    except (OSError, ValueError, KeyError):
         return None
-    if t.get("kernel_source_hash") != traffic.kernel_source_hash():
+    if t.get("kernel_source_hash") != traffic.kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -67,20 +76,64 @@ def upload_sweep(torch, w4, synth, dev):
     return cases, ops
 
 
-def time_sweep(torch, sw, steps, warmup):
+def time_steps(torch, step, steps, warmup, trials=5):
+    """ms per step of `step()` (one replay): `warmup` untimed steps, then
+    `trials` timed regions of `steps` steps, each between HIP events on the
+    current stream with a device synchronize on both sides."""
     for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out
+
+
+def captured(torch, sw):
+    """One launch of the sweep captured as a graph (replayed per step)."""
+    for _ in range(3):
         sw.launch()
     sw.check()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
         sw.launch()
-    e1.record()
     torch.cuda.synchronize()
+    return g
+
+
+def trial_stats(ms_list):
+    t = sorted(v * 1e3 for v in ms_list)
+    med = t[len(t) // 2]
+    return {"n": len(t), "median_us": med, "min_us": t[0], "max_us": t[-1],
+            "spread_pct": (t[-1] - t[0]) / med * 100, "trials_us": [v * 1e3 for v in ms_list]}
+
+
+def time_mode(torch, w4, ops, name, steps, warmup, direct=False):
+    """Trials of one sweep mode.  graph: the 141-node graph (its launch is a
+    graph launch); persistent, stream: one kernel launch, captured as a
+    one-node graph unless direct."""
+    sw = w4.DecodeSweep(ops, MODES[name])
+    if name == "graph" or direct:
+        step = sw.launch
+        g = None
+    else:
+        g = captured(torch, sw)
+        step = g.replay
+    ms = time_steps(torch, step, steps, warmup)
     sw.check()
-    return e0.elapsed_time(e1) / steps  # ms per step
+    info = sw.info()
+    del g
+    sw.close()
+    return ms, info
 
 
 def probe_read(torch, w4, dev, nbytes=4 << 30, reps=10):
@@ -356,13 +409,26 @@ def time_smallm_g32(torch, w4, synth, dev):
     return out
 
 
-def cpu_baseline(cases, max_threads=16, min_seconds=10.0, max_passes=40):
+def host_threads():
+    """Threads for the CPU baseline: every core this process may run on,
+    capped by OMP_NUM_THREADS when it is set (a shared host's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(cases, max_threads=None, min_seconds=10.0, max_passes=40):
     """The fp64 oracle over whole decode-step sweeps (all 141 GEMVs), OpenMP
-    over rows, repeated until min_seconds of wall time (at most max_passes):
-    a bounded sample of about 10 s on the host's cores."""
+    over rows on the host's cores, repeated until min_seconds of wall time (at
+    most max_passes): a bounded sample of about 10 s."""
     import oracle
     oracle.build()
-    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    threads = host_threads() if max_threads is None else max(1, max_threads)
     total = 0
     passes = 0
     t0 = time.perf_counter()
@@ -375,16 +441,21 @@ def cpu_baseline(cases, max_threads=16, min_seconds=10.0, max_passes=40):
             break
     dt = time.perf_counter() - t0
     return {"value": total / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": "%d full decode-step sweep(s) (141 GEMVs, %d weight bytes each) in "
-                      "%.1f s with the scalar fp64 oracle" % (passes, total // passes, dt)}
+                      "%.1f s with the scalar fp64 oracle on %d threads (nproc %s)"
+                      % (passes, total // passes, dt, threads, os.cpu_count())}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--mode", choices=sorted(MODES), default="stream")
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--mode", choices=sorted(MODES) + ["auto"], default="persistent",
+                    help="headline mode: persistent (default) or graph, the two "
+                         "decode-ordered modes; auto = the faster of them; stream = the "
+                         "unordered upper bound (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
@@ -425,7 +496,9 @@ def main():
     io_bytes = sum(c.K * 2 + c.N * (4 if c.out_dtype == "f32" else 2) for c in cases)
 
     if args.kernel_only:
-        sw = w4.DecodeSweep(ops, MODES[args.mode])
+        # one kernel per step: the persistent kernels only
+        mode = "persistent" if args.mode in ("auto", "graph") else args.mode
+        sw = w4.DecodeSweep(ops, MODES[mode])
         for _ in range(args.steps):
             sw.launch()
         sw.check()
@@ -438,41 +511,48 @@ def main():
         return
 
     extra = {}
-    results = {}
-    # the other modes and the read probe run first; they also bring the GPU
-    # out of idle before the timed mode's warm-up
+    # the read probe and the other modes run first; they also bring the GPU
+    # out of idle before the headline's warm-up
     probe = probe_read(torch, w4, dev) if not args.no_extra else None
-    order = ([m for m in ("graph", "persistent", "stream") if m != args.mode]
-             if not args.no_extra else []) + [args.mode]
-    trials = None
-    for name in order:
-        sw = w4.DecodeSweep(ops, MODES[name])
-        steps = args.steps if name == args.mode else max(5, min(args.steps, 20))
-        warm = args.warmup if name == args.mode else 3
-        ms = time_sweep(torch, sw, steps, warm)
-        info = sw.info()
-        results[name] = {"ms_per_sweep": ms, "GBps": weight_bytes / (ms * 1e-3) / 1e9,
-                         "kernels_per_sweep": info["kernels"]}
-        log("%-10s %.1f us/sweep  %.1f GB/s" % (name, ms * 1e3, results[name]["GBps"]))
-        if name == args.mode and not args.no_extra:
-            # run-to-run spread: five more timed regions of the same length
-            t = sorted(time_sweep(torch, sw, steps, 0) * 1e3 for _ in range(5))
-            trials = {"n": 5, "steps_each": steps, "median_us": t[2], "min_us": t[0],
-                      "max_us": t[-1], "spread_pct": (t[-1] - t[0]) / t[2] * 100}
-        sw.close()
-    ms = results[args.mode]["ms_per_sweep"]
+    head_modes = list(ORDERED) if args.mode == "auto" else [args.mode]
+    modes = {}
+    side = 20
+    if not args.no_extra:
+        for name in ("graph", "persistent", "stream"):
+            if name in head_modes:
+                continue
+            ms, _ = time_mode(torch, w4, ops, name, side, 5)
+            modes[name] = trial_stats(ms)
+        for name in ("persistent", "stream"):
+            ms, _ = time_mode(torch, w4, ops, name, side, 5, direct=True)
+            modes[name + "_direct_launch"] = trial_stats(ms)
+    head = {}
+    for name in head_modes:
+        ms, info = time_mode(torch, w4, ops, name, args.steps, args.warmup)
+        head[name] = (ms, info)
+        modes[name] = trial_stats(ms)
+        log("%-10s median %.1f us/step" % (name, modes[name]["median_us"]))
+    mode = min(head, key=lambda m: modes[m]["median_us"])
+    ms = modes[mode]["median_us"] / 1e3
+    kernels = head[mode][1]["kernels"]
     value = weight_bytes / (ms * 1e-3) / 1e9
+    for name, t in modes.items():
+        t["GBps"] = weight_bytes / (t["median_us"] * 1e-6) / 1e9
+        t["pct_of_8TBps"] = t["GBps"] / PEAK_HBM_GBPS * 100
+        t["decode_ordered"] = not name.startswith("stream")
+        t["graph_captured"] = not name.endswith("_direct_launch")
 
     if not args.no_extra:
         mfma = time_mfma_probe(torch, w4)
         extra = {
             "pct_of_8TBps_spec": value / PEAK_HBM_GBPS * 100,
             "probe_read_4GiB_GBps": probe,
-            "pct_of_probe_read": value / probe * 100,
             "GBps_incl_x_y": (weight_bytes + io_bytes) / (ms * 1e-3) / 1e9,
             "ms_per_1222.8MiB_at_this_rate": 1282203648 / (value * 1e9) * 1e3,
-            "modes": results,
-            "trials_us": trials,
+            "modes": modes,
+            "stream_upper_bound_note": "stream: the 141 GEMVs with no ordering between them "
+                                       "(one kernel, graph-captured); no decode step can run "
+                                       "unordered, so it bounds what ordering costs",
             "single_gemv": time_single_gemv(torch, w4, synth, dev, cases, ops),
             "mfma_probe": mfma,
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev, mfma["TFLOPs"]),
@@ -486,14 +566,21 @@ def main():
             "int8_twin_auto16": time_twin(torch, w4, synth, dev),
             "attention_decode": time_attention(torch, w4, dev),
         }
+        if "stream" in modes:
+            st = modes["stream"]
+            extra["stream_roofline"] = {
+                "kernel": KERNEL_OF["stream"], "achieved": st["GBps"], "peak": PEAK_HBM_GBPS,
+                "frac": st["GBps"] / PEAK_HBM_GBPS, "traffic": load_traffic("stream")}
 
-    # roofline of the dominant (only) kernel of the timed step
-    kernels = results[args.mode]["kernels_per_sweep"]
-    achieved = weight_bytes / kernels / (ms / kernels * 1e-3) / 1e9 if kernels == 1 else None
+    # Roofline of the step's dominant kernel.  persistent: the step is one
+    # kernel, so bytes per launch / replay time (HIP events on the stream the
+    # graph is replayed on; the replay adds the graph launch to the kernel).
+    # graph: 141 kernels per step, none dominant; the step's rate is given.
+    achieved = weight_bytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": (achieved / PEAK_HBM_GBPS) if achieved else None,
-                "traffic": load_traffic(weight_bytes),
-                "kernel": "w4::stream_kernel" if args.mode == "stream" else args.mode}
+                "frac": achieved / PEAK_HBM_GBPS,
+                "traffic": load_traffic(mode) if mode in KERNEL_OF else None,
+                "kernel": KERNEL_OF.get(mode, "141 GEMV kernels (whole step)")}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -527,7 +614,11 @@ def main():
                         "int4 group-32 bf16 scales, M=1, fresh seed per matrix",
             "weight_bytes": weight_bytes,
             "ops": len(cases),
-            "mode": args.mode,
+            "mode": mode,
+            "decode_ordered": mode != "stream",
+            "graph_captured": True,
+            "kernels_per_step": kernels,
+            "ms_per_step_is": "median of 5 timed regions of --steps replays",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

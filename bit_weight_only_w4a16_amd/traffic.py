@@ -1,15 +1,18 @@
-"""HBM traffic of the decode-step stream kernel from two hardware-counter runs.
+"""HBM traffic of a decode-step sweep kernel from two hardware-counter runs.
 
-    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv \\
-        -d <out>/pmc_fetch -o fetch -- python3 <repo>/bench.py --kernel-only --steps 20
-    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv \\
-        -d <out>/pmc_write -o write -- python3 <repo>/bench.py --kernel-only --steps 20
-    python -m bit_weight_only_w4a16_amd.traffic <out>/pmc_fetch <out>/pmc_write
+    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE --output-format csv \
+        -d <out>/pmc_fetch -o fetch -- python3 <repo>/bench.py --kernel-only \
+        --mode <persistent|stream> --steps 20
+    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE --output-format csv \
+        -d <out>/pmc_write -o write -- python3 <repo>/bench.py --kernel-only \
+        --mode <persistent|stream> --steps 20
+    python -m bit_weight_only_w4a16_amd.traffic <persistent|stream> \
+        <out>/pmc_fetch <out>/pmc_write
 
-`bench.py --kernel-only` runs the timed kernel, then three plain 1 GiB copies
+`bench.py --kernel-only` runs the mode's kernel, then three plain 1 GiB copies
 (`w4_probe_copy`).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by
 what they read for the copy, whose bytes are known, and the result is written
-to profiles/traffic_sweep_stream.json together with a hash of the kernel's
+to profiles/traffic_sweep_<mode>.json together with a hash of the kernel's
 source files: bench.py reports the figure only while that hash still matches.
 """
 import csv
@@ -20,31 +23,40 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OUT_FILE = os.path.join(ROOT, "profiles", "traffic_sweep_stream.json")
-KERNEL_SOURCES = ("bit_weight_only_w4a16_amd/csrc/w4_persist.hip",
-                  "bit_weight_only_w4a16_amd/csrc/w4_persist.h",
-                  "bit_weight_only_w4a16_amd/csrc/w4_gemv_core.h",
-                  "bit_weight_only_w4a16_amd/csrc/w4_common.h",
-                  "bit_weight_only_w4a16_amd/csrc/w4_sweep.hip")
-KERNEL = "w4::stream_kernel"
+_COMMON = ("bit_weight_only_w4a16_amd/csrc/w4_persist.h",
+           "bit_weight_only_w4a16_amd/csrc/w4_gemv_core.h",
+           "bit_weight_only_w4a16_amd/csrc/w4_common.h",
+           "bit_weight_only_w4a16_amd/csrc/w4_sweep.hip")
+SWEEP_KERNELS = {
+    "stream": ("w4::stream_kernel",
+               ("bit_weight_only_w4a16_amd/csrc/w4_persist.hip",) + _COMMON),
+    "persistent": ("w4::ordered_kernel",
+                   ("bit_weight_only_w4a16_amd/csrc/w4_ordered.hip",
+                    "bit_weight_only_w4a16_amd/csrc/w4_ring.h") + _COMMON),
+}
 COPY_KERNEL = "w4::probe_copy_kernel"
 COPY_BYTES = 1 << 30
 
 
-def kernel_source_hash() -> str:
+def out_file(mode: str) -> str:
+    SWEEP_KERNELS[mode]
+    return os.path.join(ROOT, "profiles", "traffic_sweep_%s.json" % mode)
+
+
+def kernel_source_hash(mode: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in SWEEP_KERNELS[mode][1]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def _counter_means(path: str, counter: str):
+def _counter_means(path: str, counter: str, kernel: str):
     """Mean counter value (KiB) per dispatch of the kernel and of the copy."""
     files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit("no *counter_collection.csv under %s" % path)
-    vals = {KERNEL: [], COPY_KERNEL: []}
+    vals = {kernel: [], COPY_KERNEL: []}
     for fn in files:
         with open(fn, newline="") as f:
             for row in csv.DictReader(f):
@@ -61,10 +73,12 @@ def _counter_means(path: str, counter: str):
 
 
 def main(argv):
-    if len(argv) != 3:
+    if len(argv) != 4 or argv[1] not in SWEEP_KERNELS:
         raise SystemExit(__doc__)
-    fetch, n_fetch = _counter_means(argv[1], "FETCH_SIZE")
-    write, _ = _counter_means(argv[2], "WRITE_SIZE")
+    mode = argv[1]
+    KERNEL = SWEEP_KERNELS[mode][0]
+    fetch, n_fetch = _counter_means(argv[2], "FETCH_SIZE", KERNEL)
+    write, _ = _counter_means(argv[3], "WRITE_SIZE", KERNEL)
     fetch_scale = COPY_BYTES / 1024.0 / fetch[COPY_KERNEL]
     write_scale = COPY_BYTES / 1024.0 / write[COPY_KERNEL]
     sys.path.insert(0, ROOT)
@@ -75,7 +89,7 @@ def main(argv):
     hbm = fetch[KERNEL] * 1024.0 * fetch_scale + write[KERNEL] * 1024.0 * write_scale
     out = {
         "kernel": KERNEL,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(mode),
         "hbm_bytes_per_launch": int(round(hbm)),
         "algorithmic_weight_bytes_per_launch": weight_bytes,
         "fetch_kib_per_dispatch": fetch[KERNEL],
@@ -89,19 +103,20 @@ def main(argv):
         "commands": [
             "cd /tmp && TMPDIR=/tmp timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE "
             "--output-format csv -d <out>/pmc_fetch -o fetch -- python3 <repo>/bench.py "
-            "--kernel-only --steps 20",
+            "--kernel-only --mode %s --steps 20" % mode,
             "cd /tmp && TMPDIR=/tmp timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE "
             "--output-format csv -d <out>/pmc_write -o write -- python3 <repo>/bench.py "
-            "--kernel-only --steps 20",
-            "python -m bit_weight_only_w4a16_amd.traffic <out>/pmc_fetch <out>/pmc_write",
+            "--kernel-only --mode %s --steps 20" % mode,
+            "python -m bit_weight_only_w4a16_amd.traffic %s <out>/pmc_fetch <out>/pmc_write"
+            % mode,
         ],
         "dispatches": n_fetch,
     }
-    with open(OUT_FILE, "w") as f:
+    with open(out_file(mode), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print("%s: %.1f MB per launch (%.4f x the weight bytes)"
-          % (OUT_FILE, hbm / 1e6, hbm / weight_bytes))
+          % (out_file(mode), hbm / 1e6, hbm / weight_bytes))
 
 
 if __name__ == "__main__":
