@@ -206,74 +206,110 @@ __device__ __forceinline__ float row_partial(const u32x4 (&q)[kPwMaxU], const ui
     return acc;
 }
 
-// Resident share (rows 0 .. R-1 of the slot): each row's C chunks are cut
-// into P parts of CP chunks, and the workgroup's 32 groups of 16 lanes take
-// (part p, rows q, q + Q, ...) with P Q <= 32 (the host's plan, which keeps
-// every lane busy even for shares of a few rows).  Lane k of a group holds
-// the activation of chunks c0 + k + 16 u of its part for all its rows; the
-// next row's codes are read from the slot while the current one is
-// multiplied.  A row's partial sums go to the LDS buffer, entry r P + p.
+// Resident share (rows 0 .. R-1 of the slot): tasks (part p, row r), a
+// row's sum over part p's CP chunks, numbered t = p Rm + r (Rm the largest
+// share's rows; rows r >= R are skipped).  The host's plan gives each 16-lane
+// group of waves 0..6 a contiguous run of tasks (entry = first << 16 |
+// count), balanced over the SIMDs.  Lane k of a group holds the activation of
+// chunks c0 + k + 16 u of the current part (reloaded when the part changes);
+// the next task's codes are read from the slot while the current one is
+// multiplied.  A task's sum goes to the LDS buffer, entry r P + p.
 template <int UP>
 __device__ __forceinline__ void compute_resident(const SweepOp& op, const uint8_t* smem,
-                                                 const uint8_t* slot, int R, int wave,
-                                                 int lane) {
-    const int j = wave * (64 / 16) + (lane >> 4), lk = lane & 15;
-    const int P = op.P, Q = op.Q;
-    if (j >= P * Q) return;
-    const int p = j % P, q0 = j / P;
-    if (q0 >= R) return;
+                                                 const uint8_t* slot, int R, int lane,
+                                                 uint32_t entry) {
+    const int n = (int)(entry & 0xFFFFu);
+    if (n == 0 || R <= 0) return;
+    const int lk = lane & 15;
+    const int P = op.P, CP = op.CP, Rm = op.Rm;
     const int C = op.C, G = op.G, gshift = op.gshift, rowb = 16 * C;
-    const int c0 = p * op.CP;
-    const int c1 = c0 + op.CP < C ? c0 + op.CP : C;
-    // chunks past the part's end read chunk c0 of the row (a valid address)
-    // against a zero activation slice
-    uint32_t xr[UP][16];
-    int cu[UP];
-#pragma unroll
-    for (int u = 0; u < UP; ++u) {
-        const int c = c0 + lk + 16 * u;
-        const bool in = c < c1;
-        cu[u] = in ? c : c0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (in) v = *reinterpret_cast<const u32x4*>(smem + kXbOff + i * kQStride + 16 * c);
-            xr[u][4 * i + 0] = v[0];
-            xr[u][4 * i + 1] = v[1];
-            xr[u][4 * i + 2] = v[2];
-            xr[u][4 * i + 3] = v[3];
-        }
-    }
+    const int t0 = (int)(entry >> 16);
     float* part = reinterpret_cast<float*>(const_cast<uint8_t*>(smem) + kOutOff);
     const uint16_t* sslot = reinterpret_cast<const uint16_t*>(slot + kOrdCodeBytes);
-    auto load = [&](int r, u32x4 (&qq)[UP], uint32_t (&ss)[UP]) {
+
+    // chunk of lane lk for step u of part p; chunks past the part's end read
+    // the part's first chunk (a valid address) against a zero activation
+    auto chunk = [&](int p, int u) {
+        const int c0 = p * CP;
+        const int c = c0 + lk + 16 * u;
+        return c < c0 + CP && c < C ? c : c0;
+    };
+    uint32_t xr[UP][16];
+    auto load_x = [&](int p) {
 #pragma unroll
         for (int u = 0; u < UP; ++u) {
-            qq[u] = *reinterpret_cast<const u32x4*>(slot + (size_t)r * rowb + 16 * cu[u]);
-            ss[u] = sslot[r * G + (cu[u] >> gshift)];
+            const int c0 = p * CP;
+            const int c = c0 + lk + 16 * u;
+            const bool in = c < c0 + CP && c < C;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (in) v = *reinterpret_cast<const u32x4*>(smem + kXbOff + i * kQStride + 16 * c);
+                xr[u][4 * i + 0] = v[0];
+                xr[u][4 * i + 1] = v[1];
+                xr[u][4 * i + 2] = v[2];
+                xr[u][4 * i + 3] = v[3];
+            }
         }
     };
-    auto finish = [&](int r, const u32x4 (&qq)[UP], const uint32_t (&ss)[UP]) {
+    auto load = [&](int p, int r, u32x4 (&qq)[UP], uint32_t (&ss)[UP]) {
+        r = r < R ? r : R - 1;
+#pragma unroll
+        for (int u = 0; u < UP; ++u) {
+            const int c = chunk(p, u);
+            qq[u] = *reinterpret_cast<const u32x4*>(slot + (size_t)r * rowb + 16 * c);
+            ss[u] = sslot[r * G + (c >> gshift)];
+        }
+    };
+    auto finish = [&](int p, int r, const u32x4 (&qq)[UP], const uint32_t (&ss)[UP]) {
         float acc = 0.f;
 #pragma unroll
         for (int u = 0; u < UP; ++u)
             acc = fmaf(bf16_to_f32(ss[u]) * 0.0625f, chunk_dot_x16(qq[u], xr[u]), acc);
         acc = group_sum<16>(acc);
-        if (lk == 0) part[r * P + p] = acc;
+        if (lk == 0 && r < R) part[r * P + p] = acc;
     };
+
+    int p = t0 / Rm, r = t0 - p * Rm;
+    int xp = p;
+    load_x(p);
     u32x4 qa[UP], qb[UP];
     uint32_t sa[UP], sb[UP];
-    int r = q0;
-    load(r, qa, sa);
+    load(p, r, qa, sa);
+    int k = 0;
     while (true) {
-        load(r + Q < R ? r + Q : r, qb, sb);
-        finish(r, qa, sa);
-        r += Q;
-        if (r >= R) break;
-        load(r + Q < R ? r + Q : r, qa, sa);
-        finish(r, qb, sb);
-        r += Q;
-        if (r >= R) break;
+        // the next task (or this one again on the last step)
+        int pn = p, rn = r + 1;
+        if (rn == Rm) {
+            rn = 0;
+            ++pn;
+        }
+        const bool more = k + 1 < n;
+        load(more ? pn : p, more ? rn : r, qb, sb);
+        finish(p, r, qa, sa);
+        if (++k >= n) break;
+        p = pn;
+        r = rn;
+        if (p != xp) {
+            xp = p;
+            load_x(p);
+        }
+        pn = p;
+        rn = r + 1;
+        if (rn == Rm) {
+            rn = 0;
+            ++pn;
+        }
+        const bool more2 = k + 1 < n;
+        load(more2 ? pn : p, more2 ? rn : r, qa, sa);
+        finish(p, r, qb, sb);
+        if (++k >= n) break;
+        p = pn;
+        r = rn;
+        if (p != xp) {
+            xp = p;
+            load_x(p);
+        }
     }
 }
 
@@ -400,14 +436,15 @@ __device__ __forceinline__ void streamed_fast(const SweepOp& op, const uint8_t* 
 
 __device__ __forceinline__ void compute_op(const SweepOp& op, const uint8_t* smem,
                                            const uint8_t* slot, int rb, int re, int wave,
-                                           int lane) {
+                                           int lane, uint32_t entry) {
     if (op.res) {
+        if (wave >= kOrdDmaWave) return;
         const int R = re - rb;
         switch (op.UP) {
-            case 1: compute_resident<1>(op, smem, slot, R, wave, lane); break;
-            case 2: compute_resident<2>(op, smem, slot, R, wave, lane); break;
-            case 3: compute_resident<3>(op, smem, slot, R, wave, lane); break;
-            default: compute_resident<4>(op, smem, slot, R, wave, lane); break;
+            case 1: compute_resident<1>(op, smem, slot, R, lane, entry); break;
+            case 2: compute_resident<2>(op, smem, slot, R, lane, entry); break;
+            case 3: compute_resident<3>(op, smem, slot, R, lane, entry); break;
+            default: compute_resident<4>(op, smem, slot, R, lane, entry); break;
         }
     } else {
         if (op.L * op.U == op.C && (op.G & 1) == 0) {
@@ -467,6 +504,10 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
         const SweepOp op = ops[i];
         int rb, re;
         share_rows(op.N, w, G, rb, re);
+        // this lane's group's task run, read now so that the load's latency
+        // hides behind the handoff
+        uint32_t entry = 0;
+        if (op.res && wave < kOrdDmaWave) entry = op.plan[4 * wave + (lane >> 4)];
 
         if (wave == 0) {
             // wait for op i-1 (every workgroup has signalled it)
@@ -539,7 +580,7 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
             issue_share(nx, w, G, slot_at(nx_slot), lane);
             nx_slot = -1;
         }
-        compute_op(op, smem, slot, rb, re, wave, lane);
+        compute_op(op, smem, slot, rb, re, wave, lane, entry);
         // B: the compute waves (0..6 for a resident share, all 8 for a
         // streamed one) count themselves done in LDS, partial sums written
         // (resident) or outputs stored and complete (streamed); wave 0 waits

@@ -40,8 +40,12 @@ struct SweepOp {
     int res;                 // 1: every workgroup's share fits an LDS slot (DMA'd ahead)
     int slot;                // its slot (0 or 1)
     int next;                // resident op DMA'd into this op's slot after it (-1: none)
-    int P, Q, CP, UP;        // resident: parts per row, row stride, chunks per part and
-                             // per lane (P Q <= kOrdGroups, UP = ceil(CP / 16))
+    // resident (decode-ordered mode): tasks (part p, row r) of a share, p in
+    // [0, P) of CP chunks each (UP = ceil(CP / 16) per lane), r in [0, Rm),
+    // numbered t = p Rm + r; plan[g] = (first task << 16) | task count of
+    // 16-lane group g of waves 0..6
+    int P, CP, UP, Rm;
+    const uint32_t* plan;
 };
 
 // Tile shapes (L lanes per row, U chunks per lane, L * U == C) compiled into

@@ -65,49 +65,84 @@ static int persist_lanes(int C) {
     return 64;
 }
 
-// How a resident share is split over the workgroup's 16-lane groups: each
-// row's C chunks in P parts of CP chunks, Q = kOrdGroups / P groups per part;
-// group j takes part j % P of rows j / P, j / P + Q, ... and its lanes hold
-// UP = ceil(CP / 16) chunks each.  The cost of a plan is the issue time of
-// the busiest SIMD: waves w and w + 4 share one, a wave runs as long as its
-// busiest group, and a row costs UP chunk decodes (about 84 vector
-// instructions each) plus about 25 for the row sum and its write (waves
-// 0..6 compute, wave 7 only issues the DMA).  Picks the
-// cheapest plan (the smallest P on ties: fewer partial sums) with no empty
+// How a resident share is spread over the compute waves' 16-lane groups.
+// A task is one row's sum over one part of its chunks (the row's C chunks cut
+// into P parts of CP chunks, UP = ceil(CP / 16) chunks per lane), costing
+// about 84 vector instructions per chunk decode and 25 for the row sum and
+// its write.  Each group takes a contiguous run of tasks, numbered part by
+// part, so its lanes reload their activation chunks only when the part
+// changes.  Waves w and w + 4 share a SIMD (wave 7 issues the DMA, so wave 3
+// has SIMD 3 to itself); a wave alone on its SIMD issues a chunk in 1.13x the
+// time that two interleaved waves take per chunk (measured).  A wave runs as
+// long as its busiest group.  For each P, whole rounds of four tasks (one per
+// group of a wave) go one at a time to the wave that leaves the busiest SIMD
+// least busy; the P with the cheapest busiest SIMD wins
+// (the smallest P on ties: fewer partial sums), among those with no empty
 // part, at most kPwMaxU chunks per lane and R P partials within the LDS
-// buffer.
-static bool resident_split(int R, int C, SweepOp* t) {
+// buffer.  Fills plan[0 .. kOrdGroups) and returns false when no P fits.
+static bool resident_plan(int R, int C, SweepOp* t, uint32_t* plan) {
+    constexpr int kWaves = kOrdGroups / 4;
     int best = 0;
-    long long best_cost = 0;
+    double best_cost = 0.0;
+    int best_rounds[kWaves] = {};
     for (int P = 1; P <= kOrdGroups; ++P) {
-        const int Q = kOrdGroups / P;
         const int CP = (C + P - 1) / P;
         const int UP = (CP + 15) / 16;
         if ((P - 1) * CP >= C || UP > kPwMaxU || R * P > kOrdMaxPartials) continue;
-        long long cost = 0;
-        for (int simd = 0; simd < 4; ++simd) {
-            long long c = 0;
-            for (int w = simd; w < kOrdGroups / 4; w += 4) {
-                int rows = 0;
-                for (int j = 4 * w; j < 4 * w + 4 && j < P * Q; ++j) {
-                    const int q = j / P;
-                    const int n = q < R ? (R - q + Q - 1) / Q : 0;
-                    rows = n > rows ? n : rows;
+        const double c = 84.0 * UP + 25.0;
+        int rounds[kWaves] = {};
+        // issue time of SIMD s: while both of its waves have rounds left they
+        // interleave (one round each per 2 c); the longer one then runs alone
+        // at 1.13 c per round
+        auto simd_time = [&](int s) {
+            const int a = rounds[s], b = s + 4 < kWaves ? rounds[s + 4] : 0;
+            const int lo = a < b ? a : b, hi = a < b ? b : a;
+            return c * (2.0 * lo + 1.13 * (hi - lo));
+        };
+        for (int left = R * P; left > 0; left -= 4) {
+            int pick = 0;
+            double pick_t = 0.0;
+            for (int w = 0; w < kWaves; ++w) {
+                rounds[w] += 1;
+                double tt = 0.0;
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const double v = simd_time(s2);
+                    tt = v > tt ? v : tt;
                 }
-                c += (long long)rows * (84 * UP + 25);
+                rounds[w] -= 1;
+                if (w == 0 || tt < pick_t) {
+                    pick = w;
+                    pick_t = tt;
+                }
             }
-            cost = c > cost ? c : cost;
+            rounds[pick] += 1;
+        }
+        double cost = 0.0;
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const double v = simd_time(s2);
+            cost = v > cost ? v : cost;
         }
         if (best == 0 || cost < best_cost) {
             best = P;
             best_cost = cost;
+            for (int w = 0; w < kWaves; ++w) best_rounds[w] = rounds[w];
         }
     }
     if (best == 0) return false;
     t->P = best;
-    t->Q = kOrdGroups / best;
     t->CP = (C + best - 1) / best;
     t->UP = (t->CP + 15) / 16;
+    t->Rm = R;
+    int start = 0, left = R * best;
+    for (int w = 0; w < kWaves; ++w) {
+        const int n = best_rounds[w] * 4 < left ? best_rounds[w] * 4 : left;
+        left -= n;
+        for (int g = 0; g < 4; ++g) {
+            const int k = n / 4 + (g < n % 4 ? 1 : 0);
+            plan[4 * w + g] = ((uint32_t)start << 16) | (uint32_t)k;
+            start += k;
+        }
+    }
     return true;
 }
 
@@ -138,6 +173,7 @@ static int setup_persistent(w4_sweep* h) {
 
     const int n = (int)h->ops.size();
     std::vector<SweepOp> tab(n);
+    std::vector<uint32_t> plans((size_t)n * kOrdGroups, 0u);
     long long tiles_before = 0;
     for (int i = 0; i < n; ++i) {
         const w4_gemv_op& o = h->ops[i];
@@ -155,7 +191,8 @@ static int setup_persistent(w4_sweep* h) {
         t.res = 0;
         t.slot = 0;
         t.next = -1;
-        t.P = t.Q = t.CP = t.UP = 0;
+        t.P = t.CP = t.UP = t.Rm = 0;
+        t.plan = nullptr;
         if (dep) {
             t.L = persist_lanes(t.C);
             t.cfg = kCfgGeneric;
@@ -168,7 +205,8 @@ static int setup_persistent(w4_sweep* h) {
                     rows * (o.K / 2) <= kOrdCodeBytes &&
                     rows * (o.K / o.group) * 2 <= kOrdScaleBytes && rows <= kOrdMaxRows &&
                     (long long)o.N * (o.K / 2) < (1LL << 32);
-            if (t.res && !resident_split((int)rows, t.C, &t)) t.res = 0;
+            if (t.res && !resident_plan((int)rows, t.C, &t, &plans[(size_t)i * kOrdGroups]))
+                t.res = 0;
         } else {
             t.cfg = stream_cfg(t.C, &t.L);
             if (t.G & 1) {  // the tiled loop reads scales in dword pairs
@@ -251,14 +289,22 @@ static int setup_persistent(w4_sweep* h) {
 
     const size_t tab_bytes = align_up(sizeof(SweepOp) * (size_t)n, kAlign);
     const size_t range_bytes = align_up(sizeof(int) * range.size(), kAlign);
-    const size_t total = tab_bytes + range_bytes + sweep_ctl_bytes(h->grid);
+    const size_t plan_bytes = align_up(sizeof(uint32_t) * plans.size(), kAlign);
+    const size_t total = tab_bytes + range_bytes + plan_bytes + sweep_ctl_bytes(h->grid);
     st = hip_fail(hipMalloc(&h->dev, total), "sweep device buffer");
     if (st != W4_OK) {
         h->dev = nullptr;
         return W4_ERR_NOMEM;
     }
-    h->range = reinterpret_cast<int*>(static_cast<uint8_t*>(h->dev) + tab_bytes);
-    h->ctl = reinterpret_cast<SweepCtl*>(static_cast<uint8_t*>(h->dev) + tab_bytes + range_bytes);
+    uint8_t* base = static_cast<uint8_t*>(h->dev);
+    h->range = reinterpret_cast<int*>(base + tab_bytes);
+    uint32_t* plan_dev = reinterpret_cast<uint32_t*>(base + tab_bytes + range_bytes);
+    h->ctl = reinterpret_cast<SweepCtl*>(base + tab_bytes + range_bytes + plan_bytes);
+    for (int i = 0; i < n; ++i)
+        if (tab[i].res) tab[i].plan = plan_dev + (size_t)i * kOrdGroups;
+    st = hip_fail(hipMemcpy(plan_dev, plans.data(), sizeof(uint32_t) * plans.size(),
+                            hipMemcpyHostToDevice), "sweep plans");
+    if (st != W4_OK) return st;
     st = hip_fail(hipMemcpy(h->dev, tab.data(), sizeof(SweepOp) * (size_t)n,
                             hipMemcpyHostToDevice), "sweep op table");
     if (st != W4_OK) return st;
