@@ -126,43 +126,38 @@ __device__ __forceinline__ int share_dmas(const SweepOp& op, int w, int G) {
     return ((re - rb) * (op.C * 16) + 1023) / 1024 + ((re - rb) * (op.G * 2) + 1023) / 1024;
 }
 
-// Chunks c0 + 64 j (j = 0..3) of an activation as agent-scope 16-byte loads
-// (written by any CU; sc1 loads are coherent across XCDs, as the
-// compiler's own agent-scope loads are), all in flight at once; chunks at or
-// past C re-read chunk C - 1.  The caller has no other vector-memory access
-// in flight that it needs to overlap (one wait covers everything).
-__device__ __forceinline__ void load_x4_agent(const uint32_t* x, int c0, int C,
-                                              u32x4 (&v)[4][4]) {
-    const uint8_t* p[4];
+// The activation as 16-byte pieces, piece q = bytes [16 q, 16 q + 16): the
+// compute waves v = 0..6 load pieces v 64 + lane + 448 j (j = 0..2; at most
+// 1024 pieces, K <= 8192) with agent-scope loads (written by any CU; sc1
+// loads are coherent across XCDs, as the compiler's own agent-scope loads
+// are), all in flight at once, and store them to the workgroup's copy: piece
+// q is quarter q % 4 of chunk q / 4.  Pieces past the end re-read the last
+// one and are not stored.  The caller has no other vector-memory access in
+// flight that it needs to overlap (one wait covers everything).
+constexpr int kXPieceWaves = kOrdWaves - 1;
+__device__ __forceinline__ void load_x_pieces(const uint8_t* x, int npieces, int wave, int lane,
+                                              uint8_t* smem) {
+    const uint8_t* p[3];
+    int q[3];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = c0 + 64 * j < C ? c0 + 64 * j : C - 1;
-        p[j] = reinterpret_cast<const uint8_t*>(x + 16 * c);
+    for (int j = 0; j < 3; ++j) {
+        q[j] = wave * 64 + lane + 64 * kXPieceWaves * j;
+        p[j] = x + 16 * (q[j] < npieces ? q[j] : npieces - 1);
     }
+    u32x4 v[3];
     asm volatile(
-        "global_load_dwordx4 %0, %16, off sc1\n\t"
-        "global_load_dwordx4 %1, %16, off offset:16 sc1\n\t"
-        "global_load_dwordx4 %2, %16, off offset:32 sc1\n\t"
-        "global_load_dwordx4 %3, %16, off offset:48 sc1\n\t"
-        "global_load_dwordx4 %4, %17, off sc1\n\t"
-        "global_load_dwordx4 %5, %17, off offset:16 sc1\n\t"
-        "global_load_dwordx4 %6, %17, off offset:32 sc1\n\t"
-        "global_load_dwordx4 %7, %17, off offset:48 sc1\n\t"
-        "global_load_dwordx4 %8, %18, off sc1\n\t"
-        "global_load_dwordx4 %9, %18, off offset:16 sc1\n\t"
-        "global_load_dwordx4 %10, %18, off offset:32 sc1\n\t"
-        "global_load_dwordx4 %11, %18, off offset:48 sc1\n\t"
-        "global_load_dwordx4 %12, %19, off sc1\n\t"
-        "global_load_dwordx4 %13, %19, off offset:16 sc1\n\t"
-        "global_load_dwordx4 %14, %19, off offset:32 sc1\n\t"
-        "global_load_dwordx4 %15, %19, off offset:48 sc1\n\t"
+        "global_load_dwordx4 %0, %3, off sc1\n\t"
+        "global_load_dwordx4 %1, %4, off sc1\n\t"
+        "global_load_dwordx4 %2, %5, off sc1\n\t"
         "s_waitcnt vmcnt(0)"
-        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]),
-          "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[2][0]), "=&v"(v[2][1]),
-          "=&v"(v[2][2]), "=&v"(v[2][3]), "=&v"(v[3][0]), "=&v"(v[3][1]), "=&v"(v[3][2]),
-          "=&v"(v[3][3])
-        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2])
         : "memory");
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (q[j] < npieces)
+            *reinterpret_cast<u32x4*>(smem + kXbOff + (q[j] & 3) * kQStride + 16 * (q[j] >> 2)) =
+                v[j];
 }
 
 // One lane's activation slice for tile (L, U) of a streamed share: chunks
@@ -479,9 +474,14 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     const int w = blockIdx.x;
     // [i & 1] op i may run (by parity: a wave may still read op i's flag
     // while wave 0 writes op i + 1's, never op i - 1's); [2] compute waves
-    // that finished an op (running count)
+    // that finished an op (running count); [3] i + 1 once wave 0 has decided
+    // whether op i may run
     int* s_flags = reinterpret_cast<int*>(smem + kFlagOff);
-    if (tid == 0) s_flags[2] = 0;
+    if (tid == 0) {
+        s_flags[2] = 0;
+        s_flags[3] = 0;
+    }
+    __syncthreads();
     auto slot_at = [&](int sl) { return smem + sl * kSlotBytes; };
 
     // the first two resident ops' shares go to the slots at once
@@ -537,28 +537,28 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
                     if (e) break;
                 }
             }
-            // op i's activation (written by any CU): agent-scope loads into
-            // the workgroup's bf16 copy
-            if (ok && lane < op.C) {
-                u32x4 xg[4][4];
-                load_x4_agent(reinterpret_cast<const uint32_t*>(op.x), lane, op.C, xg);
-                uint32_t* xb = reinterpret_cast<uint32_t*>(smem + kXbOff);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = lane + 64 * j;
-                    if (c < op.C) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(xb) +
-                                                      q * kQStride + 16 * c) = xg[j][q];
-                    }
-                }
-            }
             if (lane == 0) {
                 if (!ok)
                     __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 s_flags[i & 1] = ok ? 1 : 0;
+                // the verdict, for the other compute waves
+                __hip_atomic_store(&s_flags[3], i + 1, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
             }
+        }
+        if (wave < kOrdDmaWave) {
+            // op i's activation (written by any CU), loaded by the compute
+            // waves once wave 0 has seen op i - 1 complete everywhere
+            if (wave != 0) {
+                for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
+                    if (__hip_atomic_load(&s_flags[3], __ATOMIC_ACQUIRE,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP) > i)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            if (s_flags[i & 1])
+                load_x_pieces(reinterpret_cast<const uint8_t*>(op.x), 4 * op.C, wave, lane, smem);
         }
         if (wave == kOrdDmaWave && op.res) {
             // this op's share has landed: only DMA loads issued after it
