@@ -49,6 +49,7 @@ EXPORTS = (
     "w4_attn_decode",
     "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy", "w4_probe_mfma",
     "w4a16_gemm_noalloc", "w4a16_gemm_noalloc_max_bytes",
+    "w4_config_reload", "w4_tile_table_load",
 )
 
 
@@ -111,6 +112,8 @@ def lib():
                                       ctypes.POINTER(i)], i),
             "w4_decode_sweep_destroy": ([vp], i),
             "w4_describe_dispatch": ([i, i, i, i, ctypes.c_char_p, sz], i),
+            "w4_config_reload": ([], i),
+            "w4_tile_table_load": ([ctypes.c_char_p], i),
             "w4_selftest": ([vp], i),
             "w4_gather": ([vp, i, i, i, vp, i, vp, i, i, vp], i),
             "w4_quantize": ([vp, i, i, i, i, i, i, vp, vp], i),
@@ -194,6 +197,17 @@ def describe_dispatch(M: int, N: int, K: int, group: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(lib().w4_describe_dispatch(M, N, K, group, buf, 256))
     return buf.value.decode()
+
+
+def config_reload() -> None:
+    """Re-read W4_TILE_TABLE, W4_FORCE_PATH, W4_LOG and the tuning indices from
+    the environment (call after changing them in-process)."""
+    _check(lib().w4_config_reload())
+
+
+def tile_table_load(path=None) -> None:
+    """Load a GEMV tile table file (None: remove the loaded table)."""
+    _check(lib().w4_tile_table_load(None if path is None else os.fsencode(path)))
 
 
 def gather(packed, N: int, K: int, group: int, ids, out_dtype: str = "bf16", out=None,

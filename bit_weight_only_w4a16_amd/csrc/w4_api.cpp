@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "w4_config.h"
 #include "w4_dispatch.h"
 
 namespace w4 {
@@ -39,8 +40,6 @@ static bool aligned(const void* p, size_t a) {
 }
 
 // Largest sizes served (indices stay far from overflow).
-constexpr int kMaxN = 1 << 26;
-constexpr int kMaxK = 1 << 20;
 
 static int check_weight_shape(int N, int K, int group) {
     if (group != 32 && group != 256 && group != 512)
@@ -80,6 +79,10 @@ using namespace w4;
         const int _st = (expr);      \
         if (_st != W4_OK) return _st; \
     } while (0)
+
+namespace w4 {
+void log_choice(int M, int N, int K, int group);
+}
 
 extern "C" {
 
@@ -168,7 +171,10 @@ int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
     W4_TRY(check_in16(packed, "packed"));
     W4_TRY(check_in16(x, "x"));
     W4_TRY(check_out_ptr(y, ydt, "y"));
-    const GemvTile t = pick_gemv_tile(N, K, group);
+    W4_TRY(config_status());
+    const char* src = nullptr;
+    const GemvTile t = pick_gemv_tile(N, K, group, &src);
+    log_choice(1, N, K, group);
     return launch_gemv(t, packed, N, K, group, x, y, ydt,
                        static_cast<hipStream_t>(stream));
 }
@@ -184,6 +190,8 @@ int w4a16_gemm_smallM(const void* packed, int N, int K, int group, int M,
     W4_TRY(check_in16(packed, "packed"));
     W4_TRY(check_in16(X, "X"));
     W4_TRY(check_out_ptr(Y, ydt, "Y"));
+    W4_TRY(config_status());
+    log_choice(M, N, K, group);
     return launch_smallm(packed, N, K, group, M, X, ldx, Y, ldy, ydt,
                          static_cast<hipStream_t>(stream));
 }
@@ -235,14 +243,33 @@ int check_gemm_args(const void* packed, int N, int K, int group, int M, const ui
     return W4_OK;
 }
 
+// W4_LOG: the kernel and tile each distinct (M, N, K, group) dispatches to,
+// printed once.
+void log_choice(int M, int N, int K, int group) {
+    const auto c = config();
+    if (!c->log) return;
+    char d[192];
+    if (w4_describe_dispatch(M, N, K, group, d, sizeof d) != W4_OK) return;
+    char line[256];
+    snprintf(line, sizeof line, "M=%d N=%d K=%d group=%d: %s", M, N, K, group, d);
+    log_dispatch(*c, line);
+}
+
 }  // namespace w4
 
 extern "C" {
+
+int w4_config_reload(void) { return reload_config(); }
+
+int w4_tile_table_load(const char* path) { return load_tile_table(path); }
+
 
 int w4a16_gemm(const void* packed, int N, int K, int group, int M,
                const uint16_t* X, int ldx, int had_block, void* workspace,
                size_t ws_bytes, void* Y, int ldy, int ydt, void* stream) {
     W4_TRY(check_gemm_args(packed, N, K, group, M, X, ldx, had_block, Y, ldy, ydt));
+    W4_TRY(config_status());
+    log_choice(M, N, K, group);
     const size_t need = w4a16_gemm_workspace_bytes(M, K, had_block);
     if (need) {
         if (ws_bytes < need)
@@ -368,6 +395,13 @@ int w4_gemm_i8(const int8_t* Xq, int ldx, const float* xs, const int8_t* Wq, int
         return fail(W4_ERR_ALIGN, "int8 gemm: ldx and ldw must be >= K and multiples of 16");
     W4_TRY(check_out_ptr(Y, ydt, "Y"));
     if (ldy < N) return fail(W4_ERR_SHAPE, "int8 gemm: ldy %d < N %d", ldy, N);
+    W4_TRY(config_status());
+    if (config()->log) {
+        char d[128], line[200];
+        describe_i8(M, N, K, d, sizeof d);
+        snprintf(line, sizeof line, "int8 M=%d N=%d K=%d: %s", M, N, K, d);
+        log_dispatch(*config(), line);
+    }
     return launch_gemm_i8(Xq, ldx, xs, Wq, ldw, ws, M, N, K, Y, ldy, ydt,
                           static_cast<hipStream_t>(stream));
 }
@@ -465,10 +499,13 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) 
     W4_TRY(check_weight_shape(N, K, group));
     if (!buf || len == 0) return fail(W4_ERR_ARG, "describe: empty buffer");
     if (M < 1) return fail(W4_ERR_SHAPE, "describe: M must be >= 1");
+    W4_TRY(config_status());
     if (M == 1) {
-        const GemvTile t = pick_gemv_tile(N, K, group);
-        snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d%s", t.generic ? "_generic" : "",
-                 t.L, t.U, t.waves, t.grid, t.contig ? " contiguous" : "");
+        const char* src = nullptr;
+        const GemvTile t = pick_gemv_tile(N, K, group, &src);
+        snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d stages=%d%s (%s)",
+                 t.generic ? "_generic" : "", t.L, t.U, t.waves, t.grid, t.stages,
+                 t.contig ? " contiguous" : "", src);
     } else if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group))) {
         describe_smallm(M, N, K, group, buf, len);
     } else {

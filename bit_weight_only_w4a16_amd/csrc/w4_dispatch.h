@@ -7,6 +7,8 @@ namespace w4 {
 
 constexpr int kNumCUs = 256;        // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxU = 8;            // 32-element chunks held per lane
+constexpr int kMaxN = 1 << 26;      // largest N the entry points accept
+constexpr int kMaxK = 1 << 20;      // largest K
 
 // Batch-1 GEMV tiling: L lanes share one row (each lane owns U chunks of K,
 // chunk index lane + L*u), a wave covers 64/L rows per step, `waves` waves per
@@ -15,12 +17,15 @@ struct GemvTile {
     int L = 16;
     int U = 3;
     int waves = 4;
-    int grid = 1;
+    int grid = 1;          // workgroups (0 in a table entry: chosen from the shape)
+    int stages = 2;        // row groups in flight + 1 (2 or 3; 3 for U <= 4)
     bool generic = false;
     bool contig = false;   // contiguous row-group ranges per wave (large N)
 };
 
-GemvTile pick_gemv_tile(int N, int K, int group);
+// The tile for a batch-1 GEMV: W4_FORCE_PATH, then the loaded tile table,
+// then the built-in table, then the heuristic; *source (if given) names which.
+GemvTile pick_gemv_tile(int N, int K, int group, const char** source = nullptr);
 
 // Argument validation of w4a16_gemm (no HIP call); W4_OK or a status.
 int check_gemm_args(const void* packed, int N, int K, int group, int M, const uint16_t* X,

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "w4_config.h"
 #include "w4_dispatch.h"
 #include "w4_ring.h"
 
@@ -517,20 +518,20 @@ constexpr int kI8NumRingCfgs = sizeof(kI8RingCfgs) / sizeof(kI8RingCfgs[0]);
 
 static I8Plan plan_i8(int M, int N, int K, int ldx, int ldw) {
     I8Plan p;
-    // W4_I8_RING=0 selects the register-staged kernel (comparison runs);
-    // W4_I8_RING=<cfg + 1> forces a ring configuration
-    const char* r = getenv("W4_I8_RING");
+    // W4_FORCE_PATH i8_regs selects the register-staged kernel (comparison
+    // runs); W4_I8_RING=<cfg + 1> forces a ring configuration
+    const auto c = config();
     // per-lane DMA offsets are 32-bit
     const bool fits = (size_t)(M - 1) * (size_t)ldx + (size_t)K < (1ull << 32) &&
                       (size_t)(N - 1) * (size_t)ldw + (size_t)K < (1ull << 32);
-    p.ring = fits && !(r && r[0] == '0' && r[1] == 0);
+    p.ring = fits && !(c->force & kForceI8Regs);
     if (p.ring) {
         p.cfg = M <= 256 ? 1 : 0;
         // one 64-row block (N / 64 workgroups, at most one per CU): split K
         const int st = K / kI8RingStage;
         if (p.cfg == 1 && (N + 63) / 64 * ((M + 63) / 64) <= kNumCUs)
             p.cfg = st % 6 == 0 ? 2 : (st % 4 == 0 ? 3 : 1);
-        if (r && r[0] >= '1' && r[0] < '1' + kI8NumRingCfgs && r[1] == 0) p.cfg = r[0] - '1';
+        if (c->i8_ring >= 1 && c->i8_ring <= kI8NumRingCfgs) p.cfg = c->i8_ring - 1;
         // each K group needs a whole number of two-stage steps
         if (st % (2 * kI8RingCfgs[p.cfg].ks) != 0) p.cfg = M <= 256 ? 1 : 0;
         p.MF = 4;
@@ -543,12 +544,9 @@ static I8Plan plan_i8(int M, int N, int K, int ldx, int ldw) {
         p.cfg = 0;
         p.MF = 2;
         p.NF = 2;
-        const char* e = getenv("W4_I8_TILE");  // tuning override "MF,NF" (2 or 4 each)
-        int mf = 0, nf = 0;
-        if (e && sscanf(e, "%d,%d", &mf, &nf) == 2 && (mf == 2 || mf == 4) &&
-            (nf == 2 || nf == 4)) {
-            p.MF = mf;
-            p.NF = nf;
+        if (c->i8_mf) {  // W4_I8_TILE "MF,NF": tuning override (2 or 4 each)
+            p.MF = c->i8_mf;
+            p.NF = c->i8_nf;
         }
         p.BM = 2 * p.MF * 16;
         p.BN = 2 * p.NF * 16;

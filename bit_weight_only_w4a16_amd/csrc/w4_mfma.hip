@@ -33,6 +33,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "w4_config.h"
 #include "w4_dispatch.h"
 
 namespace w4 {
@@ -246,8 +247,8 @@ static MfmaPlan plan_mfma(int M, int N) {
     // measured on MI355X at N = 12288, K = 1536: 64 x 64 blocks for short M,
     // 64 x 128 blocks (two workgroups per CU) beyond
     p.cfg = M <= 128 ? 0 : 2;
-    const char* e = getenv("W4_MFMA_CFG");  // tuning override: 0..3
-    if (e && *e >= '0' && *e <= '3' && e[1] == 0) p.cfg = *e - '0';
+    const int o = config()->mfma_cfg;  // W4_MFMA_CFG: tuning override 0..3
+    if (o >= 0 && o <= 3) p.cfg = o;
     p.BM = 32 * kMfmaCfgs[p.cfg].MF;
     p.BN = 32 * kMfmaCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -264,11 +265,10 @@ static void launch_cfg(bool super, dim3 g, hipStream_t s, const MfmaArgs& a) {
         mfma_gemm_kernel<WM, WN, MF, NF, false><<<g, dim3(256), 0, s>>>(a);
 }
 
-// W4_PREFILL=0 keeps every shape on the register-staged kernel below (A/B
-// comparisons); otherwise groups that are multiples of 64 take the DMA ring.
+// W4_FORCE_PATH prefill_regs keeps every shape on the register-staged kernel
+// below (A/B comparisons); otherwise the shapes the DMA ring serves take it.
 static bool use_ring(int M, int N, int K, int group, int ldx) {
-    const char* e = getenv("W4_PREFILL");
-    if (e && e[0] == '0' && e[1] == 0) return false;
+    if (config()->force & kForcePrefillRegs) return false;
     return prefill_supported(M, N, K, group, ldx);
 }
 

@@ -55,6 +55,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "w4_config.h"
 #include "w4_dispatch.h"
 #include "w4_ring.h"
 
@@ -469,8 +470,8 @@ PfPlan plan_prefill(int M, int N, int K, int group) {
     // against 35.7 us; equal at 256 and 512).
     if (p.cfg == 1 && (M + 63) / 64 * ((N + 63) / 64) <= kNumCUs)
         p.cfg = G % 3 == 0 && (group != 32 || G > kMaxG32) ? 4 : (G % 2 == 0 ? 5 : 1);
-    const char* e = getenv("W4_PREFILL_CFG");  // tuning override: a kPfCfgs index
-    if (e && *e >= '0' && *e < '0' + kPfNumCfgs && e[1] == 0) p.cfg = *e - '0';
+    const int o = config()->prefill_cfg;  // W4_PREFILL_CFG: a kPfCfgs index
+    if (o >= 0 && o < kPfNumCfgs) p.cfg = o;
     // a K split needs whole scale groups per wave group
     if (G % kPfCfgs[p.cfg].ks != 0) p.cfg = 1;   // the split entries are 64 x 64 blocks
     // group 32 beyond 48 groups: only the split workgroups hold the scale table

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include "w4_config.h"
 #include "w4_dispatch.h"
 #include "w4_fwht.h"
 
@@ -509,8 +510,7 @@ static SmqPlan plan_smq(int M, int N, int K, int group) {
 }
 
 bool smallm_mfma_applies(int M, int N, int K, int group) {
-    const char* e = getenv("W4_SMALLM_MFMA");
-    return plan_smq(M, N, K, group).ok && !(e && e[0] == '0' && e[1] == 0);
+    return plan_smq(M, N, K, group).ok && !(config()->force & kForceSmallmValu);
 }
 
 static size_t smallm_lds(int M, int K) {
@@ -611,7 +611,7 @@ int launch_smallm(const void* packed, int N, int K, int group, int M,
     a.ydt = ydt;
     a.K = K;
     const SmqPlan mp = plan_smq(M, N, K, group);
-    if (smallm_mfma_applies(M, N, K, group)) {   // W4_SMALLM_MFMA=0: vector ALU only
+    if (smallm_mfma_applies(M, N, K, group)) {   // W4_FORCE_PATH smallm_valu: vector ALU only
         SmqArgs b;
         b.codes = static_cast<const uint8_t*>(packed);
         b.scales = a.scales;

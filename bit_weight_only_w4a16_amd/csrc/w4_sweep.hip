@@ -10,6 +10,7 @@
 #include <new>
 #include <vector>
 
+#include "w4_config.h"
 #include "w4_persist.h"
 
 struct w4_sweep {
@@ -339,6 +340,10 @@ int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode, void* str
         return fail(W4_ERR_ARG, "sweep: unknown mode %d", mode);
     for (int i = 0; i < n_ops; ++i) {
         const int st = check_op(ops[i], i);
+        if (st != W4_OK) return st;
+    }
+    {
+        const int st = config_status();   // GRAPH mode picks each op's tile
         if (st != W4_OK) return st;
     }
     if (mode != W4_SWEEP_GRAPH) {

@@ -402,12 +402,56 @@ int w4_gather(const void* packed, int N, int K, int group, const int32_t* ids,
 
 /*
  * The kernel and tile the dispatcher picks for (M, N, K, group), as text
- * (e.g. "gemv L=16 U=3 W=4 grid=512"), written NUL-terminated into buf.
- * [P1] paragraph on the w4gemv.py kernel: each weight shape gets its own
- * fixed tiling.
+ * (e.g. "gemv L=16 U=3 W=4 grid=160 stages=2 (built-in table)"), written
+ * NUL-terminated into buf (truncated to len - 1 characters).  [P1] paragraph
+ * on the w4gemv.py kernel: each weight shape gets its own fixed tiling, found
+ * by searching tile sizes, warps and pipeline stages on the card.
  */
 int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
                          size_t len);
+
+/*
+ * Run-time dispatch configuration.  Read from the environment on the first
+ * dispatching call and again by w4_config_reload():
+ *  W4_TILE_TABLE=path   a batch-1 GEMV tile table (format below) whose
+ *                       entries replace the built-in table's for their
+ *                       shapes.  A file that cannot be read or has any bad
+ *                       line is rejected as a whole: every dispatching call
+ *                       then returns its status (W4_ERR_ARG or W4_ERR_SHAPE)
+ *                       with the file, line and reason in w4_last_error().
+ *  W4_FORCE_PATH=a,b    force kernel families wherever they apply:
+ *                       gemv_generic, gemv_tiled (heuristic tile, no table),
+ *                       gemv_contig (heuristic tile, contiguous row ranges
+ *                       where the tile allows), smallm_valu (vector-ALU
+ *                       small-M kernel), prefill_regs (register-staged
+ *                       matrix-core kernel), i8_regs (register-staged int8
+ *                       kernel).  An unknown name is W4_ERR_ARG.
+ *  W4_LOG=1             print each distinct dispatch decision once to stderr.
+ *  W4_PREFILL_CFG, W4_MFMA_CFG, W4_I8_RING (1..4), W4_I8_TILE ("MF,NF"):
+ *                       tiling indices of the prefill, register-staged
+ *                       matrix-core and int8 kernels, for tuning runs.
+ * Batch-1 GEMV tile order: W4_FORCE_PATH, the loaded table, the built-in
+ * table (searched on MI355X for the model's shapes), the heuristic.
+ *
+ * Tile table format: text, one entry per line, '#' starts a comment:
+ *   gemv N K group L U waves grid stages contig
+ *  L       lanes per row: 8, 16, 32 or 64
+ *  U       32-element chunks per lane, ceil(K / 32 / L) (the register-tiled
+ *          loop; needs an even K / group), or 0 for the generic loop
+ *  waves   waves per workgroup, 1..4
+ *  grid    workgroups, 1..65535, or 0 to derive it from the shape
+ *  stages  row groups in flight + 1: 2, or 3 with 1 <= U <= 4
+ *  contig  1: every wave streams one contiguous range of rows (needs
+ *          L >= 16, L U = K / 32, U <= 3 and 4 waves), 0: rows strided over
+ *          the grid
+ * A shape may appear once; at most 4096 entries, 1 MiB.
+ */
+int w4_config_reload(void);
+
+/* Replaces the loaded tile table with the file at `path` (validated as
+ * above; on error the previous table stays), or removes it (path NULL).
+ * Takes precedence over W4_TILE_TABLE until the next w4_config_reload(). */
+int w4_tile_table_load(const char* path);
 
 /*
  * Start-up check of the compute paths on the current device ([P2] probes its

@@ -84,3 +84,12 @@ def upload_packed(case_P, case_S, N, K, group):
     S = to_dev_u16(case_S)
     packed = w4.pack(P, S, N, K, group)
     return packed
+
+
+def set_dispatch_env(monkeypatch, **env):
+    """Set W4_* dispatch variables for this test and make the library re-read
+    them (the conftest fixture restores the configuration afterwards)."""
+    import bit_weight_only_w4a16_amd as w4
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    w4.config_reload()

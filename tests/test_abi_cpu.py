@@ -238,13 +238,20 @@ def test_probe_validation(L):
     assert L.w4_probe_mfma(8, A2, VP(0)) == -3
 
 
-def test_describe_dispatch_tile_table(L):
-    # one fixed tiling per weight shape
+def test_describe_dispatch_tile_table(L, monkeypatch):
+    # the model's shapes: the built-in (searched) table
+    for shape in [(12288, 1536, 32), (262144, 1536, 32), (1536, 6144, 32), (2560, 1536, 32),
+                  (1536, 2048, 32), (256, 512, 32)]:
+        assert w4.describe_dispatch(1, *shape).endswith("(built-in table)"), shape
+    # the heuristic for the same shapes: zero-waste lane splits
+    from _util import set_dispatch_env
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="gemv_tiled")
     assert w4.describe_dispatch(1, 12288, 1536, 32).startswith("gemv L=16 U=3")
     assert w4.describe_dispatch(1, 262144, 1536, 32).startswith("gemv L=16 U=3")
     assert w4.describe_dispatch(1, 1536, 6144, 32).startswith("gemv L=64 U=3")
     assert w4.describe_dispatch(1, 2560, 1536, 32).startswith("gemv L=16 U=3")
     assert w4.describe_dispatch(1, 256, 512, 32).startswith("gemv L=16 U=1")
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="")
     # K = 128: 4 chunks, 8 lanes per row with half of them masked
     assert w4.describe_dispatch(1, 100, 128, 32).startswith("gemv L=8 U=1")
     # an odd number of groups per row (3) takes the generic loop: the tiled

@@ -16,7 +16,7 @@ import pytest
 import bit_weight_only_w4a16_amd as w4
 from bit_weight_only_w4a16_amd import synth
 
-from _util import assert_within, device, from_dev, note, to_dev_bf16, upload_packed
+from _util import assert_within, device, from_dev, note, to_dev_bf16, upload_packed, set_dispatch_env
 
 pytestmark = pytest.mark.gpu
 
@@ -55,10 +55,12 @@ def test_gemv_near_zero_rows(oracle_mod, N, K, g):
         note("  %s worst err/bound %.3g" % (out_dtype, r))
 
 
-def test_gemv_near_zero_lm_head(oracle_mod):
-    """262144 x 1536: the contiguous-range loop."""
-    assert "contiguous" in w4.describe_dispatch(1, 262144, 1536, 32)
-    note("gemv near-zero lm_head")
+@pytest.mark.parametrize("path", ["", "gemv_contig"])
+def test_gemv_near_zero_lm_head(oracle_mod, monkeypatch, path):
+    """262144 x 1536: the searched tile and the contiguous-range loop."""
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH=path)
+    assert ("contiguous" in w4.describe_dispatch(1, 262144, 1536, 32)) == bool(path)
+    note("gemv near-zero lm_head path=%s" % (path or "default"))
     case = synth.sparse_case("near_zero_lm", 262144, 1536, 32, 1, 77, "f32")
     _gemv_check(oracle_mod, case, "f32")
 
@@ -149,7 +151,7 @@ def test_smallm_near_zero_rows(oracle_mod, M, N, K, g):
 
 @pytest.mark.parametrize("M", [2, 8])
 def test_smallm_vector_alu_near_zero(oracle_mod, monkeypatch, M):
-    monkeypatch.setenv("W4_SMALLM_MFMA", "0")
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="smallm_valu")
     N, K, g = 2048, 1536, 256
     note("smallM VALU near-zero M=%d" % M)
     case = synth.sparse_case("smallv0", N, K, g, M, 17 * M, "f32")

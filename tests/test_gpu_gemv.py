@@ -8,8 +8,8 @@ import pytest
 import bit_weight_only_w4a16_amd as w4
 from bit_weight_only_w4a16_amd import synth
 
-from _util import (assert_within, device, from_dev, note, to_dev_bf16, to_dev_u16,
-                   to_dev_u32, upload_packed)
+from _util import (assert_within, device, from_dev, note, set_dispatch_env, to_dev_bf16,
+                   to_dev_u16, to_dev_u32, upload_packed)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,13 +189,16 @@ def test_probes_run():
     assert out.item() == 7.0
 
 
-def test_one_hot_through_the_contiguous_kernel(oracle_mod):
-    """x = e_k through the 262144 x 1536 lm_head (the contiguous-range
-    kernel): every output is exactly (code - 8) * scale of column k."""
+@pytest.mark.parametrize("path", ["", "gemv_contig"])
+def test_one_hot_through_the_lm_head(oracle_mod, monkeypatch, path):
+    """x = e_k through the 262144 x 1536 lm_head (its searched tile, and the
+    contiguous-range kernel): every output is exactly (code - 8) * scale of
+    column k."""
     import torch
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH=path)
     case = synth.lm_head()
     N, K = case.N, case.K
-    assert "contiguous" in w4.describe_dispatch(1, N, K, 32)
+    assert ("contiguous" in w4.describe_dispatch(1, N, K, 32)) == bool(path)
     packed = upload_packed(case.P, case.S, N, K, 32)
     for k in (0, 1, 31, 32, 777, K - 1):
         x = torch.zeros(K, dtype=torch.bfloat16, device=device())
@@ -205,3 +208,45 @@ def test_one_hot_through_the_contiguous_kernel(oracle_mod):
         col = oracle_mod.dequant(np.ascontiguousarray(case.P[:, 4 * q:4 * q + 4]),
                                  np.ascontiguousarray(case.S[:, q:q + 1]), N, 32, 32)[:, k % 32]
         assert np.array_equal(y.view(np.uint32), col.astype(np.float32).view(np.uint32)), k
+
+
+# One table entry per tile feature the heuristic never picks: three stages
+# (strided and contiguous rows), one and two waves per workgroup, explicit
+# grids (one workgroup; more waves than row groups), 8 lanes per row, the
+# generic loop at 16 lanes, and the contiguous kernel on a ragged row count.
+TABLE_CASES = [
+    ("gemv 2560 1536 32 16 3 4 77 3 0", "bf16"),
+    ("gemv 1536 2048 32 32 2 1 0 3 0", "bf16"),
+    ("gemv 1000 6144 32 64 3 2 1 2 0", "f32"),
+    ("gemv 333 1536 32 8 6 4 4096 2 0", "f32"),
+    ("gemv 4097 2048 32 16 4 2 300 3 0", "bf16"),
+    ("gemv 777 1024 256 16 0 4 9 2 0", "f32"),
+    ("gemv 70001 1536 32 16 3 4 0 3 1", "f32"),
+    ("gemv 70001 1024 32 32 1 4 97 3 1", "bf16"),
+]
+
+
+@pytest.mark.parametrize("line,odt", TABLE_CASES)
+def test_table_tiles_parity(oracle_mod, tmp_path, line, odt):
+    """Every tile feature a table can ask for, through w4a16_gemv, against the
+    oracle; outputs past N untouched."""
+    import torch
+    f = tmp_path / "tiles.txt"
+    f.write_text(line + "\n")
+    N, K, g = (int(v) for v in line.split()[1:4])
+    w4.tile_table_load(str(f))
+    try:
+        assert "(table)" in w4.describe_dispatch(1, N, K, g)
+        note("table tile %s out=%s" % (line, odt))
+        case = synth.make_case("table", N, K, g, 1, N + K, odt)
+        packed = upload_packed(case.P, case.S, N, K, g)
+        x = to_dev_bf16(case.X[0])
+        dt = torch.float32 if odt == "f32" else torch.bfloat16
+        ybuf = torch.full((N + 64,), float("nan"), dtype=dt, device=device())
+        w4.gemv(packed, N, K, g, x, odt, out=ybuf[:N])
+        torch.cuda.synchronize()
+        Y, A = oracle_mod.gemm_bf16(case.P, case.S, N, K, g, case.X[0], threads=16)
+        assert_within(from_dev(ybuf[:N]), Y, A, odt, line)
+        assert np.isnan(from_dev(ybuf[N:])).all()
+    finally:
+        w4.tile_table_load(None)

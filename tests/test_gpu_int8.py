@@ -9,7 +9,7 @@ import pytest
 import bit_weight_only_w4a16_amd as w4
 from bit_weight_only_w4a16_amd import synth
 
-from _util import device, note, to_dev_bf16, upload_packed
+from _util import device, note, to_dev_bf16, upload_packed, set_dispatch_env
 
 pytestmark = pytest.mark.gpu
 
@@ -74,9 +74,9 @@ def test_gemm_i8_vs_exact(oracle_mod, M, N, K, out_dtype):
 
 @pytest.mark.parametrize("ring,K", [(r, 1536) for r in "01234"] + [("3", 1024), ("4", 1024)])
 def test_gemm_i8_every_tiling(oracle_mod, monkeypatch, ring, K):
-    """Every compiled int8 tiling (W4_I8_RING: 0 register-staged, 1 to 4 the
-    DMA-ring configurations, 3 and 4 splitting K over three or two wave
-    groups; at K = 1024 the three-way split falls back) on one ragged case,
+    """Every compiled int8 tiling (0: W4_FORCE_PATH=i8_regs, register-staged;
+    W4_I8_RING 1 to 4: the DMA-ring configurations, 3 and 4 splitting K over
+    three or two wave groups; at K = 1024 the three-way split falls back) on one ragged case,
     bitwise equal to the default dispatch and within the exact product's
     bound."""
     import torch
@@ -89,7 +89,10 @@ def test_gemm_i8_every_tiling(oracle_mod, monkeypatch, ring, K):
     ws = (rng.random(N) * 0.02 + 1e-3).astype(np.float32)
     note("int8 gemm tiling W4_I8_RING=%s M=%d N=%d K=%d" % (ring, M, N, K))
     Yd = w4.gemm_i8(_t(Xq), _t(xs), _t(Wq), _t(ws), "f32")
-    monkeypatch.setenv("W4_I8_RING", ring)
+    if ring == "0":
+        set_dispatch_env(monkeypatch, W4_FORCE_PATH="i8_regs")
+    else:
+        set_dispatch_env(monkeypatch, W4_I8_RING=ring)
     Y = w4.gemm_i8(_t(Xq), _t(xs), _t(Wq), _t(ws), "f32")
     torch.cuda.synchronize()
     got = Y.cpu().numpy().astype(np.float64)

@@ -8,8 +8,8 @@ import pytest
 import bit_weight_only_w4a16_amd as w4
 from bit_weight_only_w4a16_amd import synth
 
-from _util import (assert_within, bf16_ulp, device, from_dev, note, to_dev_bf16,
-                   upload_packed)
+from _util import (assert_within, bf16_ulp, device, from_dev, note, set_dispatch_env,
+                   to_dev_bf16, upload_packed)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,8 +106,8 @@ def test_smallm_largest_k(oracle_mod, M, N, g):
 @pytest.mark.parametrize("N,K,g", [(12288, 1536, 256), (129, 1536, 512), (12288, 1536, 32)])
 def test_smallm_vector_alu_path(oracle_mod, monkeypatch, M, N, K, g):
     """The vector-ALU small-M kernels on shapes the matrix-core small-M
-    kernel otherwise takes (W4_SMALLM_MFMA=0 keeps them)."""
-    monkeypatch.setenv("W4_SMALLM_MFMA", "0")
+    kernel otherwise takes (W4_FORCE_PATH=smallm_valu keeps them)."""
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="smallm_valu")
     note("smallM vector ALU M=%d N=%d K=%d g=%d" % (M, N, K, g))
     assert not w4.describe_dispatch(M, N, K, g).startswith("smallm mfma") or M > 8
     case = synth.make_case("smallv", N, K, g, M, 7 * M + N + K, "bf16")
@@ -241,15 +241,14 @@ def test_matrix_core_largest_m(oracle_mod):
 
 @pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(7)] +
                          [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(7)] +
-                         [({"W4_PREFILL": "0"}, 32)] +
+                         [({"W4_FORCE_PATH": "prefill_regs"}, 32)] +
                          [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
-                          ({"W4_PREFILL": "0"}, 256)])
+                          ({"W4_FORCE_PATH": "prefill_regs"}, 256)])
 def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
     """Every compiled matrix-core tiling (the tuning overrides select them,
     one per call) against the oracle on one ragged case; at group 512 the
     two-way K split falls back to an unsplit tiling (3 groups)."""
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+    set_dispatch_env(monkeypatch, **env)
     M, N, K = 70, 1000, 1536
     note("mfma tiling %s M=%d N=%d K=%d g=%d" % (env, M, N, K, g))
     case = synth.make_case("tile", N, K, g, M, 77, "bf16", outlier_frac=0.01)
@@ -269,7 +268,7 @@ def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     and 64 to 192 at group 32 (only the split tilings hold more than 48; the
     others are replaced by the two-way split), ragged M and N; a split that
     does not divide the groups falls back unsplit."""
-    monkeypatch.setenv("W4_PREFILL_CFG", str(cfg))
+    set_dispatch_env(monkeypatch, W4_PREFILL_CFG=str(cfg))
     M, N = 70, 1000
     assert "dma-ring" in w4.describe_dispatch(M, N, K, g)
     note("mfma many groups cfg=%d M=%d N=%d K=%d g=%d" % (cfg, M, N, K, g))
