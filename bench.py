@@ -10,14 +10,15 @@ weight bytes with 1 GB = 1e9 B, the accounting of the pages' own figures
 ([P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than llama.cpp",
 summary line of the w4gemv.py kernel).
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--mode persistent]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 50] [--mode auto]
 
 Prints one JSON line.  The headline respects decode order: op i + 1 starts
 only after every output of op i is written, as in a decode step ([P1],
 paragraph on the step captured once as a graph and replayed per token).
-Each step is one replay of a captured graph: by default the decode-ordered
-persistent kernel captured as a one-node graph ("persistent"); "graph" is the
-141 GEMV kernels captured in order; "auto" times both and reports the faster.
+Each step is one replay of a captured graph: the decode-ordered persistent
+kernel captured as a one-node graph ("persistent"), or the 141 GEMV kernels
+captured in order ("graph"); the default "auto" times both with the same
+steps and reports the faster, naming it in config.mode.
 ms_per_step is the median of five timed regions of --steps replays each.
 Reported under "extra", labelled: the other ordered mode, direct launches
 without a graph, and the 141 GEMVs with no ordering between them
@@ -452,10 +453,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--mode", choices=sorted(MODES) + ["auto"], default="persistent",
-                    help="headline mode: persistent (default) or graph, the two "
-                         "decode-ordered modes; auto = the faster of them; stream = the "
-                         "unordered upper bound (for counter runs)")
+    ap.add_argument("--mode", choices=sorted(MODES) + ["auto"], default="auto",
+                    help="headline mode: auto (default) = the faster of the two "
+                         "decode-ordered modes, persistent (one kernel) and graph (141 "
+                         "kernels); stream = the unordered upper bound (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
@@ -575,7 +576,8 @@ def main():
     # Roofline of the step's dominant kernel.  persistent: the step is one
     # kernel, so bytes per launch / replay time (HIP events on the stream the
     # graph is replayed on; the replay adds the graph launch to the kernel).
-    # graph: 141 kernels per step, none dominant; the step's rate is given.
+    # graph: 141 kernels per step (the largest, the lm_head GEMV, takes ~6 %
+    # of the step), none dominant: the step's bytes / step time.
     achieved = weight_bytes / (ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBPS,
