@@ -238,36 +238,20 @@ static int setup_persistent(w4_sweep* h) {
         h->first1 = res.size() > 1 ? res[1] : -1;
     }
 
-    // STREAM partition: contiguous tile ranges, wave b's share of the bytes
-    // set by its dispatch round (tiles of one op are equal-sized); then, for
-    // each wave, the index of the op that holds its first tile.
-    //
-    // The workgroups of round r = blockIdx / CUs are the r-th to arrive on
-    // their CU, and a SIMD issues the memory instructions of its older waves
-    // first: with equal shares the first round finished at 88 us of a 140 us
-    // sweep and the last at 130 us, with one wave per SIMD left for the final
-    // stretch.  With four workgroups per CU the rounds take 1.2 : 1.1 : 0.9 :
-    // 0.8 of an equal share (measured 137.5 -> 136.9 and 140.3 -> 138.4 us on two
-    // machines; steeper ratios and costing the 32-lane tiles higher were
-    // slower).
+    // STREAM partition: contiguous tile ranges, an equal share of the bytes
+    // per wave (tiles of one op are equal-sized); then, for each wave, the
+    // index of the op that holds its first tile.  (Shares weighted by a
+    // wave's dispatch round and by XCD parity, fitted on earlier machines,
+    // measured no better on later ones: 154.5 against 153.2 us, median of 15
+    // trials each, so the shares are equal.)
     const int parts = GW;
     std::vector<int> range(2 * (size_t)parts + 1);
     {
         double total_bytes = 0.0;
         for (const w4_gemv_op& o : h->ops)
             total_bytes += (double)o.N * o.K / 2 + (double)o.N * (o.K / o.group) * 2;
-        static const double kRoundWeight[4] = {1.2, 1.1, 0.9, 0.8};
-        const int per_round = ncu * kPwWaves;   // waves per dispatch round
         std::vector<double> cum((size_t)parts + 1, 0.0);
-        for (int w = 0; w < parts; ++w) {
-            // workgroup b runs on XCD b % 8; even-numbered XCDs streamed
-            // ~7% slower in every timestamped run, so their waves take 0.97
-            // of a share and the odd ones 1.03 (138.3 -> 136.7 us; 0.95 :
-            // 1.05 and the inverse were slower)
-            const int b = w / kPwWaves;
-            const double xw = (b & 1) ? 1.03 : 0.97;
-            cum[w + 1] = cum[w] + (bpc == 4 ? kRoundWeight[w / per_round] * xw : 1.0);
-        }
+        for (int w = 0; w < parts; ++w) cum[w + 1] = cum[w] + 1.0;
         int b = 0;
         double at = 0.0;  // byte offset of the current tile
         for (int i = 0; i < n && b <= parts; ++i) {
