@@ -14,11 +14,12 @@
 //    gives the exact fp16 pair (1024 + c, ...) (or (1024 + 16c, ...)), and one
 //    packed fp16 add (or multiply-add by 1/16) turns it into (c - 8, ...),
 //    exactly: every intermediate is an integer (or a sixteenth) inside fp16's
-//    exact range.  The activations are scaled per 32-element chunk by a power
-//    of two 2^s and rounded to fp16, which is exact whenever every nonzero
-//    element of the chunk is a normal bf16 within 2^29 of the chunk's largest
-//    magnitude; v_dot2_f32_f16 then forms exact products.  A chunk outside
-//    that range (or holding inf / NaN) sends its wave to the bf16 decode.
+//    exact range.  The activation elements a lane holds (its 32-element
+//    chunks) are scaled by one power of two 2^s and rounded to fp16, which is
+//    exact whenever every nonzero one is a normal bf16 within 2^29 of the
+//    largest of them; v_dot2_f32_f16 then forms exact products.  A lane whose
+//    elements fall outside that range (or hold inf / NaN) sends its wave to
+//    the bf16 decode.
 //  - bf16 (matrix cores, small M, and the fallback): the nibble is moved to
 //    the top of a byte and its offset bit flipped, so the byte read as a
 //    signed integer is 16 (c - 8); one byte-select convert per code and one

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(I8Args a) {
 }
 
 // DMA-ring int8 GEMM (the layout and pipeline of the int4 prefill ring in
-// w4_prefill.hip, without decode or offset chains).  Four waves side by side
+// w4_prefill.hip, without the decode).  Four waves side by side
 // along N share one 64-row activation tile; each wave owns 16*NF weight rows
 // and computes 64 x 16*NF outputs.  64-wide K stages (one MFMA step) are
 // DMA'd into an LDS ring of SLOTS slots, P stages per wait and barrier.  Rows
