@@ -34,7 +34,8 @@ unsigned parse_force(const char* e, std::string& bad) {
     static const struct { const char* name; unsigned bit; } kNames[] = {
         {"gemv_generic", kForceGemvGeneric}, {"gemv_tiled", kForceGemvTiled},
         {"gemv_contig", kForceGemvContig},   {"smallm_valu", kForceSmallmValu},
-        {"prefill_regs", kForcePrefillRegs}, {"i8_regs", kForceI8Regs}};
+        {"prefill_regs", kForcePrefillRegs}, {"i8_regs", kForceI8Regs},
+        {"ordered_inline", kForceOrderedInline}};
     unsigned f = 0;
     std::stringstream ss(e);
     std::string tok;

@@ -23,6 +23,7 @@ enum ForcePath : unsigned {
     kForceSmallmValu = 1u << 3,    // small M: the vector-ALU kernel
     kForcePrefillRegs = 1u << 4,   // M > 16: the register-staged matrix-core kernel
     kForceI8Regs = 1u << 5,        // int8 twin: the register-staged kernel
+    kForceOrderedInline = 1u << 6, // decode-ordered sweep: decode while multiplying
 };
 
 struct TileEntry {

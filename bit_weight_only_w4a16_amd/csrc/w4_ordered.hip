@@ -126,38 +126,29 @@ __device__ __forceinline__ int share_dmas(const SweepOp& op, int w, int G) {
     return ((re - rb) * (op.C * 16) + 1023) / 1024 + ((re - rb) * (op.G * 2) + 1023) / 1024;
 }
 
-// The activation as 16-byte pieces, piece q = bytes [16 q, 16 q + 16): the
-// compute waves v = 0..6 load pieces v 64 + lane + 448 j (j = 0..2; at most
-// 1024 pieces, K <= 8192) with agent-scope loads (written by any CU; sc1
-// loads are coherent across XCDs, as the compiler's own agent-scope loads
-// are), all in flight at once, and store them to the workgroup's copy: piece
-// q is quarter q % 4 of chunk q / 4.  Pieces past the end re-read the last
-// one and are not stored.  The caller has no other vector-memory access in
-// flight that it needs to overlap (one wait covers everything).
-constexpr int kXPieceWaves = kOrdWaves - 1;
-__device__ __forceinline__ void load_x_pieces(const uint8_t* x, int npieces, int wave, int lane,
-                                              uint8_t* smem) {
-    const uint8_t* p[3];
-    int q[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        q[j] = wave * 64 + lane + 64 * kXPieceWaves * j;
-        p[j] = x + 16 * (q[j] < npieces ? q[j] : npieces - 1);
+// The activation (K = 32 C bf16, written by any CU) into the workgroup's
+// quarter-major copy, by global-to-LDS DMA from one wave, then waited for:
+// instruction j moves quarter j % 4 of chunks 64 (j / 4) + lane (16 bytes per
+// lane, landing at consecutive LDS addresses).  The loads are agent scope
+// (sc1: coherent across XCDs, as the compiler's own agent-scope loads are).
+// Lanes past the last chunk re-read it into the unused tail of their quarter
+// (256 chunks each), which nothing reads.  The caller has no other
+// vector-memory access in flight that it needs to overlap.
+__device__ __forceinline__ void dma16_agent(uint32_t off, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void load_x_dma(const void* x, int C, int lane, uint8_t* smem) {
+    const int nj = 4 * ((C + 63) / 64);
+    for (int j = 0; j < nj; ++j) {
+        int c = 64 * (j >> 2) + lane;
+        c = c < C ? c : C - 1;
+        dma16_agent(64u * (uint32_t)c + 16u * (uint32_t)(j & 3), x,
+                    lds_addr(smem + kXbOff + (j & 3) * kQStride + 16 * 64 * (j >> 2)));
     }
-    u32x4 v[3];
-    asm volatile(
-        "global_load_dwordx4 %0, %3, off sc1\n\t"
-        "global_load_dwordx4 %1, %4, off sc1\n\t"
-        "global_load_dwordx4 %2, %5, off sc1\n\t"
-        "s_waitcnt vmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2])
-        : "v"(p[0]), "v"(p[1]), "v"(p[2])
-        : "memory");
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (q[j] < npieces)
-            *reinterpret_cast<u32x4*>(smem + kXbOff + (q[j] & 3) * kQStride + 16 * (q[j] >> 2)) =
-                v[j];
+    wait_vm<0>();
 }
 
 // One lane's activation slice for tile (L, U) of a streamed share: chunks
@@ -308,6 +299,114 @@ __device__ __forceinline__ void compute_resident(const SweepOp& op, const uint8_
     }
 }
 
+// Resident share decoded ahead (the same tasks, plan and arithmetic as
+// compute_resident, so the partial sums are bitwise the same): before the
+// activation is there, each lane of waves 1..6 decodes its group's tasks
+// (at most kOrdPreChunks / UP of them) from the slot into registers, as the
+// exact bf16 pairs 16 (c - 8) with the chunk's scale s / 16 beside them; the
+// task's part and row go to tpr (p | r << 16).  Once the activation is in
+// LDS, dot_predecoded multiplies.
+template <int UP>
+__device__ __forceinline__ void predecode(const SweepOp& op, const uint8_t* slot, int R, int lane,
+                                          uint32_t entry, uint32_t (&wd)[kOrdPreChunks][16],
+                                          float (&ws)[kOrdPreChunks], int (&tpr)[kOrdPreChunks]) {
+    constexpr int NT = kOrdPreChunks / UP;
+    const int n = (int)(entry & 0xFFFFu);
+    if (n == 0 || R <= 0) return;
+    const int lk = lane & 15;
+    const int CP = op.CP, Rm = op.Rm, C = op.C, G = op.G, gshift = op.gshift, rowb = 16 * C;
+    const int t0 = (int)(entry >> 16);
+    const uint16_t* sslot = reinterpret_cast<const uint16_t*>(slot + kOrdCodeBytes);
+    int p = t0 / Rm, r = t0 - p * Rm;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t < n) {
+            tpr[t] = p | (r << 16);
+            const int rr = r < R ? r : R - 1;
+            const int c0 = p * CP;
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+                // chunks past the part's end read the part's first chunk
+                // (multiplied by a zero activation)
+                const int c = c0 + lk + 16 * u;
+                const int cc = c < c0 + CP && c < C ? c : c0;
+                const u32x4 q = *reinterpret_cast<const u32x4*>(slot + (size_t)rr * rowb + 16 * cc);
+                ws[t * UP + u] = bf16_to_f32(sslot[rr * G + (cc >> gshift)]) * 0.0625f;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const u32x4 v = decode_x16(q[d]);
+                    wd[t * UP + u][4 * d + 0] = v[0];
+                    wd[t * UP + u][4 * d + 1] = v[1];
+                    wd[t * UP + u][4 * d + 2] = v[2];
+                    wd[t * UP + u][4 * d + 3] = v[3];
+                }
+            }
+            if (++r == Rm) {
+                r = 0;
+                ++p;
+            }
+        }
+    }
+}
+
+template <int UP>
+__device__ __forceinline__ void dot_predecoded(const SweepOp& op, const uint8_t* smem, int R,
+                                               int lane, uint32_t entry,
+                                               const uint32_t (&wd)[kOrdPreChunks][16],
+                                               const float (&ws)[kOrdPreChunks],
+                                               const int (&tpr)[kOrdPreChunks]) {
+    constexpr int NT = kOrdPreChunks / UP;
+    const int n = (int)(entry & 0xFFFFu);
+    if (n == 0 || R <= 0) return;
+    const int lk = lane & 15;
+    const int P = op.P, CP = op.CP, C = op.C;
+    float* part = reinterpret_cast<float*>(const_cast<uint8_t*>(smem) + kOutOff);
+    uint32_t xr[UP][16];
+    int xp = -1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t < n) {
+            const int p = tpr[t] & 0xFFFF, r = tpr[t] >> 16;
+            if (p != xp) {
+                xp = p;
+#pragma unroll
+                for (int u = 0; u < UP; ++u) {
+                    const int c0 = p * CP;
+                    const int c = c0 + lk + 16 * u;
+                    const bool in = c < c0 + CP && c < C;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        u32x4 v = {0u, 0u, 0u, 0u};
+                        if (in)
+                            v = *reinterpret_cast<const u32x4*>(smem + kXbOff + i * kQStride + 16 * c);
+                        xr[u][4 * i + 0] = v[0];
+                        xr[u][4 * i + 1] = v[1];
+                        xr[u][4 * i + 2] = v[2];
+                        xr[u][4 * i + 3] = v[3];
+                    }
+                }
+            }
+            // chunk_dot_x16's two chains in its order, then s / 16
+            float acc = 0.f;
+#pragma unroll
+            for (int u = 0; u < UP; ++u) {
+                const uint32_t* b = wd[t * UP + u];
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    a0 = dot2(b[4 * d + 0], xr[u][4 * d + 0], a0);
+                    a1 = dot2(b[4 * d + 1], xr[u][4 * d + 1], a1);
+                    a0 = dot2(b[4 * d + 2], xr[u][4 * d + 2], a0);
+                    a1 = dot2(b[4 * d + 3], xr[u][4 * d + 3], a1);
+                }
+                acc = fmaf(ws[t * UP + u], a0 + a1, acc);
+            }
+            acc = group_sum<16>(acc);
+            if (lk == 0 && r < R) part[r * P + p] = acc;
+        }
+    }
+}
+
 // Streamed share (larger than a slot): every wave streams a contiguous part
 // of the rows from HBM, the next row group's codes in flight while the
 // current one is multiplied; outputs stored at agent scope.
@@ -429,213 +528,296 @@ __device__ __forceinline__ void streamed_fast(const SweepOp& op, const uint8_t* 
     gemv_rows<L, U, true, 3, true, true>(a, g0, g1, 1, lane, k, LdsX{smem});
 }
 
-__device__ __forceinline__ void compute_op(const SweepOp& op, const uint8_t* smem,
-                                           const uint8_t* slot, int rb, int re, int wave,
-                                           int lane, uint32_t entry) {
-    if (op.res) {
-        if (wave >= kOrdDmaWave) return;
-        const int R = re - rb;
-        switch (op.UP) {
-            case 1: compute_resident<1>(op, smem, slot, R, lane, entry); break;
-            case 2: compute_resident<2>(op, smem, slot, R, lane, entry); break;
-            case 3: compute_resident<3>(op, smem, slot, R, lane, entry); break;
-            default: compute_resident<4>(op, smem, slot, R, lane, entry); break;
+// A streamed share, every wave of the workgroup; its outputs are stored and
+// complete when it returns.  (The wait sits on this path itself, so that the
+// compiler knows no load of it is still in flight afterwards.)
+__device__ __forceinline__ void compute_streamed_op(const SweepOp& op, const uint8_t* smem,
+                                                    int rb, int re, int wave, int lane) {
+    bool done = false;
+    if (op.L * op.U == op.C && (op.G & 1) == 0) {
+        done = true;
+        switch (op.L * 8 + op.U) {
+            case 16 * 8 + 3: streamed_fast<16, 3>(op, smem, rb, re, wave, lane); break;
+            case 16 * 8 + 4: streamed_fast<16, 4>(op, smem, rb, re, wave, lane); break;
+            case 32 * 8 + 3: streamed_fast<32, 3>(op, smem, rb, re, wave, lane); break;
+            case 32 * 8 + 4: streamed_fast<32, 4>(op, smem, rb, re, wave, lane); break;
+            case 64 * 8 + 3: streamed_fast<64, 3>(op, smem, rb, re, wave, lane); break;
+            case 64 * 8 + 4: streamed_fast<64, 4>(op, smem, rb, re, wave, lane); break;
+            default: done = false; break;
         }
-    } else {
-        if (op.L * op.U == op.C && (op.G & 1) == 0) {
-            switch (op.L * 8 + op.U) {
-                case 16 * 8 + 3: streamed_fast<16, 3>(op, smem, rb, re, wave, lane); return;
-                case 16 * 8 + 4: streamed_fast<16, 4>(op, smem, rb, re, wave, lane); return;
-                case 32 * 8 + 3: streamed_fast<32, 3>(op, smem, rb, re, wave, lane); return;
-                case 32 * 8 + 4: streamed_fast<32, 4>(op, smem, rb, re, wave, lane); return;
-                case 64 * 8 + 3: streamed_fast<64, 3>(op, smem, rb, re, wave, lane); return;
-                case 64 * 8 + 4: streamed_fast<64, 4>(op, smem, rb, re, wave, lane); return;
-                default: break;
-            }
-        }
+    }
+    if (!done) {
         switch (op.L) {
             case 16: compute_streamed<16>(op, smem, rb, re, wave, lane); break;
             case 32: compute_streamed<32>(op, smem, rb, re, wave, lane); break;
             default: compute_streamed<64>(op, smem, rb, re, wave, lane); break;
         }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+}
+
+// State of one workgroup across the ops of a replay.
+struct OrdCtx {
+    const SweepOp* ops;
+    SweepCtl* ctl;
+    uint8_t* smem;
+    int* s_flags;   // [i & 1] op i may run; [2] compute-wave completions; [3] (pre) slot landed
+    int w, G, wave, lane;
+    // DMA loads issued after those of the next resident op
+    int pend_next;
+    // the resident op whose share is DMA'd next (see ordered_kernel)
+    SweepOp nx;
+    int nx_slot;
+    // running count of compute-wave completions wave 0 waits for
+    unsigned arrived;
+    __device__ uint8_t* slot_at(int sl) const { return smem + sl * kSlotBytes; }
+};
+
+// Wave 0: wait until every workgroup has signalled op i - 1 (or the error
+// word is set), publish the verdict for op i in LDS and, if op i may run,
+// load its activation into LDS.
+__device__ __forceinline__ void handoff_in(OrdCtx& k, const SweepOp& op, int i) {
+    bool ok = true;
+    if (i > 0) {
+        ok = false;
+        const unsigned target = (unsigned)i * (unsigned)k.G;
+        for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
+            // one round trip per poll: lanes 0..7 read the counters, lane 8
+            // the error word
+            unsigned c = 0, e = 0;
+            if (k.lane < 8)
+                c = __hip_atomic_load(&k.ctl->cnt[32 * k.lane], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            else if (k.lane == 8)
+                e = __hip_atomic_load(&k.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            c += __shfl_xor(c, 1, 64);
+            c += __shfl_xor(c, 2, 64);
+            c += __shfl_xor(c, 4, 64);
+            c = __shfl(c, 0, 64);   // lane 0's total on every lane
+            e = __shfl(e, 8, 64);
+            if ((int)(c - target) >= 0) {
+                ok = true;
+                break;
+            }
+            if (e) break;
+        }
+    }
+    if (k.lane == 0) {
+        if (!ok) __hip_atomic_store(&k.ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        k.s_flags[i & 1] = ok ? 1 : 0;
+    }
+    if (ok) load_x_dma(op.x, op.C, k.lane, k.smem);
+}
+
+// After the compute: the compute waves (0..6 for a resident share, all 8
+// for a streamed one) count themselves done in LDS, partial sums written
+// (resident) or outputs stored and complete (streamed); wave 0 waits for the
+// count (not a workgroup barrier, so the DMA wave, whose copy may still be
+// issuing, holds nobody up), adds a resident share's partial sums, stores
+// the outputs, waits for them to complete and signals.
+__device__ __forceinline__ void handoff_out(OrdCtx& k, const SweepOp& op, int rb, int re) {
+    const bool computes = !op.res || k.wave != kOrdDmaWave;
+    k.arrived += op.res ? kOrdWaves - 1 : kOrdWaves;
+    if (computes && k.lane == 0)
+        __hip_atomic_fetch_add(&k.s_flags[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (k.wave != 0) return;
+    bool done = false;
+    for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
+        const unsigned c = (unsigned)__hip_atomic_load(&k.s_flags[2], __ATOMIC_ACQUIRE,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        if ((int)(c - k.arrived) >= 0) {
+            done = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    if (!done) {
+        // cannot happen unless a wave is lost; the next poll sees the error
+        // word and every workgroup leaves
+        if (k.lane == 0)
+            __hip_atomic_store(&k.ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (op.res) {
+        // a row's P partial sums, added in order
+        const float* part = reinterpret_cast<const float*>(k.smem + kOutOff);
+        for (int r = k.lane; r < re - rb; r += 64) {
+            float v = part[r * op.P];
+            for (int q = 1; q < op.P; ++q) v += part[r * op.P + q];
+            store_out_agent(op.y, (size_t)(rb + r), v, op.ydt);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the outputs are visible to every CU
+    asm volatile("" ::: "memory");
+    if (k.lane == 0)
+        __hip_atomic_fetch_add(&k.ctl->cnt[32 * (k.w & 7)], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One op decoded in the compute (streamed shares; resident shares unless
+// decoded ahead).  Returns false when the workgroup is to leave.
+__device__ __forceinline__ bool inline_op(OrdCtx& k, const SweepOp& op, int i, uint32_t entry) {
+    int rb, re;
+    share_rows(op.N, k.w, k.G, rb, re);
+    if (k.wave == kOrdDmaWave && op.res) {
+        // this op's share has landed once only the DMA loads issued after it
+        // are in flight
+        wait_vm_rt(k.pend_next);
+        k.pend_next = 0;
+    }
+    if (k.wave == 0) handoff_in(k, op, i);
+    __syncthreads();   // A: the verdict, the activation and the weights of op i
+    if (k.s_flags[i & 1] == 0) return false;
+    if (k.wave == kOrdDmaWave && op.res && k.nx_slot >= 0) {
+        // the previous resident op's slot is free: the resident op after this
+        // one goes in.  Issued here, not when that slot was freed, so that
+        // the DMA traffic overlaps this op's compute (which reads only LDS)
+        // instead of the handoff's stores, polls and loads.
+        issue_share(k.nx, k.w, k.G, k.slot_at(k.nx_slot), k.lane);
+        k.nx_slot = -1;
+    }
+    if (op.res) {
+        if (k.wave < kOrdDmaWave) {
+            const uint8_t* slot = k.slot_at(op.slot);
+            const int R = re - rb;
+            switch (op.UP) {
+                case 1: compute_resident<1>(op, k.smem, slot, R, k.lane, entry); break;
+                case 2: compute_resident<2>(op, k.smem, slot, R, k.lane, entry); break;
+                case 3: compute_resident<3>(op, k.smem, slot, R, k.lane, entry); break;
+                default: compute_resident<4>(op, k.smem, slot, R, k.lane, entry); break;
+            }
+        }
+    } else {
+        compute_streamed_op(op, k.smem, rb, re, k.wave, k.lane);
+    }
+    handoff_out(k, op, rb, re);
+    if (k.wave == kOrdDmaWave && op.res && op.next >= 0) {
+        // the slot is free once the compute waves are past this op (they are
+        // when the next op's barrier A opens): the resident op after the
+        // next one goes in once the next resident op starts computing
+        k.nx = k.ops[op.next];
+        k.nx_slot = k.nx.slot;
+    }
+    return true;
+}
+
+// One resident op decoded ahead: the DMA wave flags the share as landed;
+// waves 1..6 decode their tasks into registers while wave 0 waits for op
+// i - 1 and loads the activation; after barrier A the DMA wave sends op i's
+// successor-but-one into op i's slot (already decoded) and waves 1..6
+// multiply.  Returns false when the workgroup is to leave.
+template <int UP>
+__device__ __forceinline__ bool predecoded_op(OrdCtx& k, const SweepOp& op, int i,
+                                              uint32_t entry) {
+    int rb, re;
+    share_rows(op.N, k.w, k.G, rb, re);
+    const int R = re - rb;
+    uint32_t wd[kOrdPreChunks][16];
+    float ws[kOrdPreChunks];
+    int tpr[kOrdPreChunks];
+    if (k.wave == kOrdDmaWave) {
+        // the share is in LDS once only the DMA loads issued after it are in
+        // flight.  The flag is a relaxed store after that explicit wait: a
+        // release store would wait for every DMA load in flight, the next
+        // op's too.
+        wait_vm_rt(k.pend_next);
+        k.pend_next = 0;
+        asm volatile("" ::: "memory");
+        if (k.lane == 0)
+            __hip_atomic_store(&k.s_flags[3], i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (op.next >= 0) k.nx = k.ops[op.next];
+    } else if (k.wave != 0) {
+        bool landed = false;
+        for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
+            if (__hip_atomic_load(&k.s_flags[3], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) > i) {
+                landed = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (landed) {
+            predecode<UP>(op, k.slot_at(op.slot), R, k.lane, entry, wd, ws, tpr);
+        } else if (k.lane == 0) {
+            // cannot happen unless the DMA wave is lost; the next poll sees
+            // the error word and every workgroup leaves
+            __hip_atomic_store(&k.ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        handoff_in(k, op, i);
+    }
+    __syncthreads();   // A: the verdict and the activation of op i; op i's slot decoded
+    if (k.s_flags[i & 1] == 0) return false;
+    if (k.wave == kOrdDmaWave) {
+        if (op.next >= 0) {
+            issue_share(k.nx, k.w, k.G, k.slot_at(op.slot), k.lane);
+            k.pend_next = share_dmas(k.nx, k.w, k.G);
+        }
+    } else if (k.wave != 0) {
+        dot_predecoded<UP>(op, k.smem, R, k.lane, entry, wd, ws, tpr);
+    }
+    handoff_out(k, op, rb, re);
+    return true;
 }
 
 }  // namespace
 
+// pre: every resident op's share is decoded ahead (predecoded_op); the
+// host's plans then give wave 0 no tasks.
 __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __restrict__ ops,
                                                               int n_ops, SweepCtl* ctl,
-                                                              int first0, int first1) {
+                                                              int first0, int first1, int pre) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = gridDim.x;
-    const int w = blockIdx.x;
-    // [i & 1] op i may run (by parity: a wave may still read op i's flag
-    // while wave 0 writes op i + 1's, never op i - 1's); [2] compute waves
-    // that finished an op (running count); [3] i + 1 once wave 0 has decided
-    // whether op i may run
-    int* s_flags = reinterpret_cast<int*>(smem + kFlagOff);
+    OrdCtx k;
+    k.ops = ops;
+    k.ctl = ctl;
+    k.smem = smem;
+    k.s_flags = reinterpret_cast<int*>(smem + kFlagOff);
+    k.lane = tid & 63;
+    k.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    k.G = gridDim.x;
+    k.w = blockIdx.x;
+    k.nx_slot = -1;
+    k.arrived = 0;
     if (tid == 0) {
-        s_flags[2] = 0;
-        s_flags[3] = 0;
+        k.s_flags[2] = 0;
+        k.s_flags[3] = 0;
     }
     __syncthreads();
-    auto slot_at = [&](int sl) { return smem + sl * kSlotBytes; };
 
     // the first two resident ops' shares go to the slots at once
-    if (wave == kOrdDmaWave) {
-        if (first0 >= 0) issue_share(ops[first0], w, G, slot_at(ops[first0].slot), lane);
-        if (first1 >= 0) issue_share(ops[first1], w, G, slot_at(ops[first1].slot), lane);
+    if (k.wave == kOrdDmaWave) {
+        if (first0 >= 0) issue_share(ops[first0], k.w, k.G, k.slot_at(ops[first0].slot), k.lane);
+        if (first1 >= 0) issue_share(ops[first1], k.w, k.G, k.slot_at(ops[first1].slot), k.lane);
     }
-    // DMA loads issued after those of the next resident op (the second
-    // op's, until the first one has been waited for)
-    int pend_next = first1 >= 0 ? share_dmas(ops[first1], w, G) : 0;
-    // resident op whose share is to be DMA'd once the next resident op's
-    // compute starts (nx_slot < 0: none).  Its table entry is read when the
-    // slot is freed, so the scalar load's latency hides behind the handoff.
-    SweepOp nx;
-    int nx_slot = -1;
-    // running count of compute-wave completions wave 0 waits for
-    unsigned arrived = 0;
+    k.pend_next = first1 >= 0 ? share_dmas(ops[first1], k.w, k.G) : 0;
+    // this lane's group's task run of the next op, read one op ahead so that
+    // the load's latency hides behind the current op
+    // (a global-typed load: a generic one would also hold the LDS counter)
+    uint32_t entry_next = 0;
+    if (ops[0].res && k.wave < kOrdDmaWave)
+        entry_next = gload(ops[0].plan + 4 * k.wave + (k.lane >> 4));
 
     for (int i = 0; i < n_ops; ++i) {
         const SweepOp op = ops[i];
-        int rb, re;
-        share_rows(op.N, w, G, rb, re);
-        // this lane's group's task run, read now so that the load's latency
-        // hides behind the handoff
-        uint32_t entry = 0;
-        if (op.res && wave < kOrdDmaWave) entry = op.plan[4 * wave + (lane >> 4)];
-
-        if (wave == 0) {
-            // wait for op i-1 (every workgroup has signalled it)
-            bool ok = true;
-            if (i > 0) {
-                ok = false;
-                const unsigned target = (unsigned)i * (unsigned)G;
-                for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
-                    // one round trip per poll: lanes 0..7 read the counters,
-                    // lane 8 the error word
-                    unsigned c = 0, e = 0;
-                    if (lane < 8)
-                        c = __hip_atomic_load(&ctl->cnt[32 * lane], __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-                    else if (lane == 8)
-                        e = __hip_atomic_load(&ctl->error, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-                    c += __shfl_xor(c, 1, 64);
-                    c += __shfl_xor(c, 2, 64);
-                    c += __shfl_xor(c, 4, 64);
-                    c = __shfl(c, 0, 64);   // lane 0's total on every lane
-                    e = __shfl(e, 8, 64);
-                    if ((int)(c - target) >= 0) {
-                        ok = true;
-                        break;
-                    }
-                    if (e) break;
-                }
+        const uint32_t entry = entry_next;
+        if (i + 1 < n_ops && k.wave < kOrdDmaWave && ops[i + 1].res)
+            entry_next = gload(ops[i + 1].plan + 4 * k.wave + (k.lane >> 4));
+        bool go;
+        if (pre && op.res) {
+            switch (op.UP) {
+                case 1: go = predecoded_op<1>(k, op, i, entry); break;
+                case 2: go = predecoded_op<2>(k, op, i, entry); break;
+                case 3: go = predecoded_op<3>(k, op, i, entry); break;
+                default: go = predecoded_op<4>(k, op, i, entry); break;
             }
-            if (lane == 0) {
-                if (!ok)
-                    __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_flags[i & 1] = ok ? 1 : 0;
-                // the verdict, for the other compute waves
-                __hip_atomic_store(&s_flags[3], i + 1, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
+        } else {
+            go = inline_op(k, op, i, entry);
         }
-        if (wave < kOrdDmaWave) {
-            // op i's activation (written by any CU), loaded by the compute
-            // waves once wave 0 has seen op i - 1 complete everywhere
-            if (wave != 0) {
-                for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
-                    if (__hip_atomic_load(&s_flags[3], __ATOMIC_ACQUIRE,
-                                          __HIP_MEMORY_SCOPE_WORKGROUP) > i)
-                        break;
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            if (s_flags[i & 1])
-                load_x_pieces(reinterpret_cast<const uint8_t*>(op.x), 4 * op.C, wave, lane, smem);
-        }
-        if (wave == kOrdDmaWave && op.res) {
-            // this op's share has landed: only DMA loads issued after it
-            // (the second op's, at the start) may still be in flight
-            wait_vm_rt(pend_next);
-            pend_next = 0;
-        }
-        __syncthreads();   // A: activation and weights of op i visible
-        if (s_flags[i & 1] == 0) {
+        if (!go) {
             __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the workgroup
             return;
-        }
-        const uint8_t* slot = slot_at(op.slot);
-        if (wave == kOrdDmaWave && op.res && nx_slot >= 0) {
-            // the previous resident op's slot is free: the resident op after
-            // this one goes in.  Issued here, not when that slot was freed,
-            // so that the DMA traffic overlaps this op's compute (which reads
-            // only LDS) instead of the handoff's stores, polls and loads.
-            issue_share(nx, w, G, slot_at(nx_slot), lane);
-            nx_slot = -1;
-        }
-        compute_op(op, smem, slot, rb, re, wave, lane, entry);
-        // B: the compute waves (0..6 for a resident share, all 8 for a
-        // streamed one) count themselves done in LDS, partial sums written
-        // (resident) or outputs stored and complete (streamed); wave 0 waits
-        // for the count.  Not a workgroup barrier, so the DMA wave, whose
-        // copy may still be issuing, holds nobody up.
-        if (!op.res) {
-            __builtin_amdgcn_s_waitcnt(0);
-            asm volatile("" ::: "memory");
-        }
-        const bool computes = !op.res || wave != kOrdDmaWave;
-        arrived += op.res ? kOrdWaves - 1 : kOrdWaves;
-        if (computes && lane == 0)
-            __hip_atomic_fetch_add(&s_flags[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-
-        if (wave == 0) {
-            bool done = false;
-            for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
-                const unsigned c = (unsigned)__hip_atomic_load(&s_flags[2], __ATOMIC_ACQUIRE,
-                                                               __HIP_MEMORY_SCOPE_WORKGROUP);
-                if ((int)(c - arrived) >= 0) {
-                    done = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (!done) {
-                // cannot happen unless a wave is lost; the next poll sees the
-                // error word and every workgroup leaves
-                if (lane == 0)
-                    __hip_atomic_store(&ctl->error, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                continue;
-            }
-            if (op.res) {
-                // a row's P partial sums, added in order
-                const float* part = reinterpret_cast<const float*>(smem + kOutOff);
-                for (int r = lane; r < re - rb; r += 64) {
-                    float v = part[r * op.P];
-                    for (int q = 1; q < op.P; ++q) v += part[r * op.P + q];
-                    store_out_agent(op.y, (size_t)(rb + r), v, op.ydt);
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0);   // the outputs are visible to every CU
-            asm volatile("" ::: "memory");
-            if (lane == 0)
-                __hip_atomic_fetch_add(&ctl->cnt[32 * (w & 7)], 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        } else if (wave == kOrdDmaWave && op.res) {
-            // the slot is free once the compute waves are past this op (they
-            // are when the next op's barrier A opens): the resident op after
-            // the next one goes in once the next resident op starts computing
-            if (op.next >= 0) {
-                nx = ops[op.next];
-                nx_slot = nx.slot;
-            }
         }
     }
 
@@ -647,7 +829,7 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     if (tid == 0) {
         const unsigned done = __hip_atomic_fetch_add(&ctl->fin, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if (done == (unsigned)G - 1u) {
+        if (done == (unsigned)k.G - 1u) {
 #pragma unroll
             for (int x = 0; x < 8; ++x)
                 __hip_atomic_store(&ctl->cnt[32 * x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -23,6 +23,7 @@ constexpr int kOrdMaxK = 32 * kPwMaxC;                   // 8192
 constexpr int kOrdMaxRows = 512;                         // rows of a resident share
 constexpr int kOrdGroups = 16 * (kOrdWaves - 1) / 4;     // 16-lane groups of waves 0..6
 constexpr int kOrdMaxPartials = 1024;                    // rows x parts of a resident share
+constexpr int kOrdPreChunks = 6;                         // chunks per lane decoded ahead
 
 // One GEMV of the step, as the kernel reads it.
 struct SweepOp {
@@ -88,9 +89,10 @@ inline size_t sweep_ctl_bytes(int) { return sizeof(SweepCtl); }
 
 int persist_occupancy(bool dep, int* blocks_per_cu);
 int launch_persist(bool dep, const SweepOp* ops_dev, int n_ops, SweepCtl* ctl,
-                   const int* range, int grid, int first0, int first1, hipStream_t s);
+                   const int* range, int grid, int first0, int first1, int pre,
+                   hipStream_t s);
 int ordered_lds_bytes();
 __global__ void ordered_kernel(const SweepOp* __restrict__ ops, int n_ops, SweepCtl* ctl,
-                               int first0, int first1);
+                               int first0, int first1, int pre);
 
 }  // namespace w4

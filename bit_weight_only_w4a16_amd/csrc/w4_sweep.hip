@@ -6,6 +6,8 @@
 // paragraph on the decode step: hundreds of small kernels launched one at a
 // time cost more than running them, so the step is captured once as a graph
 // and replayed for every token.
+#include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <new>
 #include <vector>
@@ -25,6 +27,7 @@ struct w4_sweep {
     w4::SweepCtl* ctl = nullptr;
     int* range = nullptr;             // STREAM: first tile of each wave (waves + 1)
     int first0 = -1, first1 = -1;     // PERSISTENT: first two resident ops
+    int pre = 0;                      // PERSISTENT: resident shares decoded ahead
 };
 
 namespace w4 {
@@ -80,9 +83,14 @@ static int persist_lanes(int C) {
 // least busy; the P with the cheapest busiest SIMD wins
 // (the smallest P on ties: fewer partial sums), among those with no empty
 // part, at most kPwMaxU chunks per lane and R P partials within the LDS
-// buffer.  Fills plan[0 .. kOrdGroups) and returns false when no P fits.
-static bool resident_plan(int R, int C, SweepOp* t, uint32_t* plan) {
+// buffer.
+// pre: the tasks are decoded ahead into registers (kOrdPreChunks chunks per
+// lane at most) by waves 1..6 only (wave 0, the control wave, polls
+// meanwhile; it then has SIMD 0's second slot to itself, like wave 3).
+// Fills plan[0 .. kOrdGroups) and returns false when no P fits.
+static bool resident_plan(int R, int C, bool pre, SweepOp* t, uint32_t* plan) {
     constexpr int kWaves = kOrdGroups / 4;
+    const int w0 = pre ? 1 : 0;   // first computing wave
     int best = 0;
     double best_cost = 0.0;
     int best_rounds[kWaves] = {};
@@ -90,20 +98,23 @@ static bool resident_plan(int R, int C, SweepOp* t, uint32_t* plan) {
         const int CP = (C + P - 1) / P;
         const int UP = (CP + 15) / 16;
         if ((P - 1) * CP >= C || UP > kPwMaxU || R * P > kOrdMaxPartials) continue;
+        const int cap = pre ? kOrdPreChunks / UP : 1 << 20;   // tasks per group
         const double c = 84.0 * UP + 25.0;
         int rounds[kWaves] = {};
         // issue time of SIMD s: while both of its waves have rounds left they
         // interleave (one round each per 2 c); the longer one then runs alone
         // at 1.13 c per round
         auto simd_time = [&](int s) {
-            const int a = rounds[s], b = s + 4 < kWaves ? rounds[s + 4] : 0;
+            const int a = s >= w0 ? rounds[s] : 0, b = s + 4 < kWaves ? rounds[s + 4] : 0;
             const int lo = a < b ? a : b, hi = a < b ? b : a;
             return c * (2.0 * lo + 1.13 * (hi - lo));
         };
-        for (int left = R * P; left > 0; left -= 4) {
-            int pick = 0;
+        int left = R * P;
+        for (; left > 0; left -= 4) {
+            int pick = -1;
             double pick_t = 0.0;
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = w0; w < kWaves; ++w) {
+                if (rounds[w] + 1 > cap) continue;
                 rounds[w] += 1;
                 double tt = 0.0;
                 for (int s2 = 0; s2 < 4; ++s2) {
@@ -111,13 +122,15 @@ static bool resident_plan(int R, int C, SweepOp* t, uint32_t* plan) {
                     tt = v > tt ? v : tt;
                 }
                 rounds[w] -= 1;
-                if (w == 0 || tt < pick_t) {
+                if (pick < 0 || tt < pick_t) {
                     pick = w;
                     pick_t = tt;
                 }
             }
+            if (pick < 0) break;   // every wave at the cap
             rounds[pick] += 1;
         }
+        if (left > 0) continue;
         double cost = 0.0;
         for (int s2 = 0; s2 < 4; ++s2) {
             const double v = simd_time(s2);
@@ -206,7 +219,7 @@ static int setup_persistent(w4_sweep* h) {
                     rows * (o.K / 2) <= kOrdCodeBytes &&
                     rows * (o.K / o.group) * 2 <= kOrdScaleBytes && rows <= kOrdMaxRows &&
                     (long long)o.N * (o.K / 2) < (1LL << 32);
-            if (t.res && !resident_plan((int)rows, t.C, &t, &plans[(size_t)i * kOrdGroups]))
+            if (t.res && !resident_plan((int)rows, t.C, false, &t, &plans[(size_t)i * kOrdGroups]))
                 t.res = 0;
         } else {
             t.cfg = stream_cfg(t.C, &t.L);
@@ -236,6 +249,33 @@ static int setup_persistent(w4_sweep* h) {
         }
         h->first0 = res.size() > 0 ? res[0] : -1;
         h->first1 = res.size() > 1 ? res[1] : -1;
+        // decode the resident shares ahead into registers when every one of
+        // them fits (W4_FORCE_PATH ordered_inline: decode while multiplying)
+        bool pre = !res.empty() && !(config()->force & kForceOrderedInline);
+        std::vector<SweepOp> pt(res.size());
+        std::vector<uint32_t> pp(res.size() * (size_t)kOrdGroups, 0u);
+        for (size_t k = 0; k < res.size() && pre; ++k) {
+            const w4_gemv_op& o = h->ops[res[k]];
+            pt[k] = tab[res[k]];
+            pre = resident_plan((o.N + h->grid - 1) / h->grid, tab[res[k]].C, true, &pt[k],
+                                &pp[k * (size_t)kOrdGroups]);
+        }
+        if (pre) {
+            for (size_t k = 0; k < res.size(); ++k) {
+                tab[res[k]] = pt[k];
+                std::copy(pp.begin() + k * kOrdGroups, pp.begin() + (k + 1) * kOrdGroups,
+                          plans.begin() + (size_t)res[k] * kOrdGroups);
+            }
+        }
+        h->pre = pre ? 1 : 0;
+        {
+            const auto cfg = config();
+            char msg[160];
+            snprintf(msg, sizeof msg,
+                     "decode-ordered sweep: %d ops, %d resident, resident shares decoded %s",
+                     n, (int)res.size(), pre ? "ahead" : "inline");
+            log_dispatch(*cfg, msg);
+        }
     }
 
     // STREAM partition: contiguous tile ranges, an equal share of the bytes
@@ -384,7 +424,7 @@ int w4_decode_sweep_launch(w4_sweep* h, void* stream) {
     if (h->mode != W4_SWEEP_GRAPH)
         return launch_persist(h->mode == W4_SWEEP_PERSISTENT,
                               static_cast<const SweepOp*>(h->dev), (int)h->ops.size(), h->ctl,
-                              h->range, h->grid, h->first0, h->first1, s);
+                              h->range, h->grid, h->first0, h->first1, h->pre, s);
     if (!h->exec) return fail(W4_ERR_ARG, "sweep: bad handle");
     return hip_fail(hipGraphLaunch(h->exec, s), "graph launch");
 }

@@ -8,7 +8,8 @@ import pytest
 import bit_weight_only_w4a16_amd as w4
 from bit_weight_only_w4a16_amd import synth
 
-from _util import assert_within, device, from_dev, note, to_dev_bf16, upload_packed
+from _util import (assert_within, device, from_dev, note, set_dispatch_env, to_dev_bf16,
+                   upload_packed)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,8 +40,19 @@ def _check_all(oracle_mod, cases, ops, what):
     return worst
 
 
+# "persistent_inline": the decode-ordered kernel with every resident share
+# decoded while multiplying (W4_FORCE_PATH ordered_inline) instead of ahead
 MODES = [("graph", w4.W4_SWEEP_GRAPH), ("persistent", w4.W4_SWEEP_PERSISTENT),
-         ("stream", w4.W4_SWEEP_STREAM)]
+         ("persistent_inline", w4.W4_SWEEP_PERSISTENT), ("stream", w4.W4_SWEEP_STREAM)]
+
+
+@pytest.fixture(autouse=True)
+def _mode_env(request, monkeypatch):
+    """Selects the inline decode for the persistent_inline cases."""
+    cs = getattr(request.node, "callspec", None)
+    name = cs.params.get("name", "") if cs else ""
+    if name.endswith("_inline"):
+        set_dispatch_env(monkeypatch, W4_FORCE_PATH="ordered_inline")
 
 
 @pytest.mark.parametrize("name,mode", MODES)
@@ -186,7 +198,7 @@ def test_sweep_one_hot_is_bit_exact(oracle_mod, sweep_data, name, mode):
     sw.close()
 
 
-@pytest.mark.parametrize("name,mode", MODES[:2])
+@pytest.mark.parametrize("name,mode", MODES[:3])
 def test_chained_ops_read_the_previous_output(oracle_mod, name, mode):
     """Decode order: op i + 1 multiplies op i's bf16 output (square 1536 x
     1536 weights, x_{i+1} = y_i), outputs NaN-filled before every replay, so
@@ -223,3 +235,28 @@ def test_chained_ops_read_the_previous_output(oracle_mod, name, mode):
                           "%s rep %d op %d" % (name, rep, i))
             xin = got
     sw.close()
+
+
+def test_decoded_ahead_equals_inline(sweep_data, monkeypatch, capfd):
+    """The decode-ordered kernel's two ways of decoding a resident share
+    (ahead into registers, or while multiplying) run the same tasks in the
+    same order: all 141 outputs are bitwise equal.  W4_LOG names which way
+    each handle runs."""
+    import torch
+    cases, ops = sweep_data
+    got = {}
+    for name, force in (("ahead", ""), ("inline", "ordered_inline")):
+        set_dispatch_env(monkeypatch, W4_FORCE_PATH=force, W4_LOG="1")
+        note("persistent sweep, resident shares decoded %s" % name)
+        for op in ops:
+            op[5].fill_(float("nan"))
+        sw = w4.DecodeSweep(ops, w4.W4_SWEEP_PERSISTENT)
+        sw.launch()
+        sw.check()
+        torch.cuda.synchronize()
+        got[name] = [from_dev(op[5]).copy() for op in ops]
+        sw.close()
+        err = capfd.readouterr().err
+        assert ("resident shares decoded %s" % name) in err, err
+    for c, a, b in zip(cases, got["ahead"], got["inline"]):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), c.name
