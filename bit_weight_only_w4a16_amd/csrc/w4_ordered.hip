@@ -68,9 +68,15 @@ constexpr int kOutOff = kXbOff + kOrdMaxK * 2;          // the share's partial s
 constexpr int kFlagOff = kOutOff + kOrdMaxPartials * 4; // flags and the LDS count
 constexpr int kOrdLds = kFlagOff + 16;
 
+// Rows [w N / G, (w + 1) N / G) of workgroup w (floor division), in 32-bit
+// arithmetic: w N / G = w (N / G) + w (N % G) / G, and w (N % G) < G^2.
+__device__ __forceinline__ int share_start(int N, int w, int G) {
+    const unsigned q = (unsigned)N / (unsigned)G, r = (unsigned)N % (unsigned)G;
+    return (int)((unsigned)w * q + ((unsigned)w * r) / (unsigned)G);
+}
 __device__ __forceinline__ void share_rows(int N, int w, int G, int& rb, int& re) {
-    rb = (int)((long long)w * N / G);
-    re = (int)((long long)(w + 1) * N / G);
+    rb = share_start(N, w, G);
+    re = share_start(N, w + 1, G);
 }
 
 // wait until at most n of this wave's DMA loads are in flight (0 <= n < 64;
@@ -148,7 +154,6 @@ __device__ __forceinline__ void load_x_dma(const void* x, int C, int lane, uint8
         dma16_agent(64u * (uint32_t)c + 16u * (uint32_t)(j & 3), x,
                     lds_addr(smem + kXbOff + (j & 3) * kQStride + 16 * 64 * (j >> 2)));
     }
-    wait_vm<0>();
 }
 
 // One lane's activation slice for tile (L, U) of a streamed share: chunks
@@ -571,31 +576,32 @@ struct OrdCtx {
     int nx_slot;
     // running count of compute-wave completions wave 0 waits for
     unsigned arrived;
+    // (pre) ops below this index have been flagged as landed
+    int landed;
     __device__ uint8_t* slot_at(int sl) const { return smem + sl * kSlotBytes; }
 };
 
 // Wave 0: wait until every workgroup has signalled op i - 1 (or the error
 // word is set), publish the verdict for op i in LDS and, if op i may run,
-// load its activation into LDS.
+// load its activation into LDS.  One poll in flight at a time: more (four,
+// 130 ns apart) measured slower, the extra reads of the counters' lines
+// slowing the signals themselves (547 against 537 us per step).
 __device__ __forceinline__ void handoff_in(OrdCtx& k, const SweepOp& op, int i) {
     bool ok = true;
     if (i > 0) {
         ok = false;
+        // lanes 0..7 read the counters, lane 8 the error word (the others
+        // re-read counter 0 and are ignored)
+        const unsigned* p = k.lane < 8 ? &k.ctl->cnt[32 * k.lane]
+                                       : (k.lane == 8 ? &k.ctl->error : &k.ctl->cnt[0]);
         const unsigned target = (unsigned)i * (unsigned)k.G;
         for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
-            // one round trip per poll: lanes 0..7 read the counters, lane 8
-            // the error word
-            unsigned c = 0, e = 0;
-            if (k.lane < 8)
-                c = __hip_atomic_load(&k.ctl->cnt[32 * k.lane], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-            else if (k.lane == 8)
-                e = __hip_atomic_load(&k.ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            c += __shfl_xor(c, 1, 64);
-            c += __shfl_xor(c, 2, 64);
-            c += __shfl_xor(c, 4, 64);
-            c = __shfl(c, 0, 64);   // lane 0's total on every lane
-            e = __shfl(e, 8, 64);
+            const unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // lanes 0..7 summed and lane 8's word, read into scalar registers
+            unsigned c = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c += __builtin_amdgcn_readlane(v, j);
+            const unsigned e = __builtin_amdgcn_readlane(v, 8);
             if ((int)(c - target) >= 0) {
                 ok = true;
                 break;
@@ -608,6 +614,7 @@ __device__ __forceinline__ void handoff_in(OrdCtx& k, const SweepOp& op, int i) 
         k.s_flags[i & 1] = ok ? 1 : 0;
     }
     if (ok) load_x_dma(op.x, op.C, k.lane, k.smem);
+    wait_vm<0>();   // the activation has landed
 }
 
 // After the compute: the compute waves (0..6 for a resident share, all 8
@@ -702,6 +709,16 @@ __device__ __forceinline__ bool inline_op(OrdCtx& k, const SweepOp& op, int i, u
     return true;
 }
 
+// DMA wave: resident op i's share is in LDS (its DMA loads have been
+// waited for).  A relaxed store after that explicit wait: a release store
+// would also wait for every other DMA load in flight.
+__device__ __forceinline__ void flag_landed(OrdCtx& k, int i) {
+    asm volatile("" ::: "memory");
+    if (k.lane == 0)
+        __hip_atomic_store(&k.s_flags[3], i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    k.landed = i + 1;
+}
+
 // One resident op decoded ahead: the DMA wave flags the share as landed;
 // waves 1..6 decode their tasks into registers while wave 0 waits for op
 // i - 1 and loads the activation; after barrier A the DMA wave sends op i's
@@ -717,15 +734,14 @@ __device__ __forceinline__ bool predecoded_op(OrdCtx& k, const SweepOp& op, int 
     float ws[kOrdPreChunks];
     int tpr[kOrdPreChunks];
     if (k.wave == kOrdDmaWave) {
-        // the share is in LDS once only the DMA loads issued after it are in
-        // flight.  The flag is a relaxed store after that explicit wait: a
-        // release store would wait for every DMA load in flight, the next
-        // op's too.
-        wait_vm_rt(k.pend_next);
-        k.pend_next = 0;
-        asm volatile("" ::: "memory");
-        if (k.lane == 0)
-            __hip_atomic_store(&k.s_flags[3], i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (k.landed <= i) {
+            // the first resident op: its share is in LDS once only the DMA
+            // loads issued after it are in flight (later ones are flagged at
+            // the previous resident op's barrier A)
+            wait_vm_rt(k.pend_next);
+            k.pend_next = 0;
+            flag_landed(k, i);
+        }
         if (op.next >= 0) k.nx = k.ops[op.next];
     } else if (k.wave != 0) {
         bool landed = false;
@@ -749,10 +765,15 @@ __device__ __forceinline__ bool predecoded_op(OrdCtx& k, const SweepOp& op, int 
     __syncthreads();   // A: the verdict and the activation of op i; op i's slot decoded
     if (k.s_flags[i & 1] == 0) return false;
     if (k.wave == kOrdDmaWave) {
-        if (op.next >= 0) {
-            issue_share(k.nx, k.w, k.G, k.slot_at(op.slot), k.lane);
-            k.pend_next = share_dmas(k.nx, k.w, k.G);
+        // the next resident op's share, the only DMA in flight (issued at the
+        // previous barrier A), is flagged as soon as it has landed, so that
+        // its decode can start when this op's multiply ends; then the
+        // resident op after it goes into this op's slot (already decoded)
+        if (op.nres >= 0) {
+            wait_vm<0>();
+            flag_landed(k, op.nres);
         }
+        if (op.next >= 0) issue_share(k.nx, k.w, k.G, k.slot_at(op.slot), k.lane);
     } else if (k.wave != 0) {
         dot_predecoded<UP>(op, k.smem, R, k.lane, entry, wd, ws, tpr);
     }
@@ -780,6 +801,7 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     k.w = blockIdx.x;
     k.nx_slot = -1;
     k.arrived = 0;
+    k.landed = 0;
     if (tid == 0) {
         k.s_flags[2] = 0;
         k.s_flags[3] = 0;
@@ -793,8 +815,8 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     }
     k.pend_next = first1 >= 0 ? share_dmas(ops[first1], k.w, k.G) : 0;
     // this lane's group's task run of the next op, read one op ahead so that
-    // the load's latency hides behind the current op
-    // (a global-typed load: a generic one would also hold the LDS counter)
+    // the load's latency hides behind the current op (a global-typed load:
+    // a generic one would also hold the LDS counter)
     uint32_t entry_next = 0;
     if (ops[0].res && k.wave < kOrdDmaWave)
         entry_next = gload(ops[0].plan + 4 * k.wave + (k.lane >> 4));

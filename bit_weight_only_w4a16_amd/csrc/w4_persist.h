@@ -41,6 +41,7 @@ struct SweepOp {
     int res;                 // 1: every workgroup's share fits an LDS slot (DMA'd ahead)
     int slot;                // its slot (0 or 1)
     int next;                // resident op DMA'd into this op's slot after it (-1: none)
+    int nres;                // the next resident op (-1: none)
     // resident (decode-ordered mode): tasks (part p, row r) of a share, p in
     // [0, P) of CP chunks each (UP = ceil(CP / 16) per lane), r in [0, Rm),
     // numbered t = p Rm + r; plan[g] = (first task << 16) | task count of

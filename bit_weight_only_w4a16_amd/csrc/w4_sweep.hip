@@ -205,6 +205,7 @@ static int setup_persistent(w4_sweep* h) {
         t.res = 0;
         t.slot = 0;
         t.next = -1;
+        t.nres = -1;
         t.P = t.CP = t.UP = t.Rm = 0;
         t.plan = nullptr;
         if (dep) {
@@ -246,6 +247,7 @@ static int setup_persistent(w4_sweep* h) {
         for (size_t k = 0; k < res.size(); ++k) {
             tab[res[k]].slot = (int)(k & 1);
             tab[res[k]].next = k + 2 < res.size() ? res[k + 2] : -1;
+            tab[res[k]].nres = k + 1 < res.size() ? res[k + 1] : -1;
         }
         h->first0 = res.size() > 0 ? res[0] : -1;
         h->first1 = res.size() > 1 ? res[1] : -1;
