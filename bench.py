@@ -294,7 +294,8 @@ def time_mfma_probe(torch, w4):
 def time_prefill(torch, w4, synth, dev, mfma_tflops=None):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
-    cores); also the transform alone and the product without it."""
+    cores); also the transform alone, the product without it, and, for
+    context, torch's dense bf16 matmul of the same shape."""
     import numpy as np
     out = {}
     for M in (8, 64, 512):
@@ -320,8 +321,15 @@ def time_prefill(torch, w4, synth, dev, mfma_tflops=None):
         if mfma_tflops:
             res["gemm_pct_of_mfma_probe"] = flops / t / 1e12 / mfma_tflops * 100
         res["gemm_weight_GBps"] = c.weight_bytes / t / 1e9
+        # context, not a target: the vendor library's dense bf16 GEMM of the
+        # same shape (torch.matmul, hipBLASLt), with 16-bit weights (4x the
+        # bytes) and no decode
+        Wd = torch.randn(c.N, c.K, device=dev, dtype=torch.bfloat16)
+        us = time_calls(torch, lambda: torch.matmul(X, Wd.t(), out=Y))
+        res["dense_bf16_matmul_us"] = us
+        res["dense_bf16_matmul_pct_of_2.5PF"] = flops / (us * 1e-6) / 2.5e15 * 100
         out["M%d" % M] = res
-        del P, S, packed, X, Y, Xr, ws
+        del P, S, packed, X, Y, Xr, ws, Wd
     torch.cuda.empty_cache()
     return out
 

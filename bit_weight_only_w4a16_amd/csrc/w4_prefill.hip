@@ -101,7 +101,10 @@ struct PfShape {
     static_assert(B_DMA * 256 == WN * kBRow, "code tile: whole DMA rounds per wave");
     static_assert(LOADS * (SLOTS - 2) < 64, "vmcnt range");
     static constexpr int OUT_ROW = BN * 4 + 16;        // padded fp32 staging row (bytes)
-    static_assert(BM * OUT_ROW <= SLOTS * SLOT, "output staging fits in the ring");
+    // the output block is staged in the ring whole, or in two halves of rows
+    static constexpr int OUT_PARTS = BM * OUT_ROW <= SLOTS * SLOT ? 1 : 2;
+    static_assert(BM / OUT_PARTS * OUT_ROW <= SLOTS * SLOT, "output staging fits in the ring");
+    static_assert(MF % OUT_PARTS == 0, "whole fragments per staged part");
     static constexpr int PART = 4 * 64 * MF * NF * 16; // one K group's partial block (bytes)
     static_assert(KS == 1 || PART <= SLOTS * SLOT, "partial block fits in the group's ring");
     static constexpr int THREADS = 256 * KS;
@@ -115,8 +118,14 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
 
+// MF = 8 (128 activation rows per wave; groups of 64 or more, two stages per
+// barrier): one wave per SIMD with the registers of two, each decoded code
+// word feeding eight MFMAs instead of four (half the decode per MFMA), and
+// the activation fragments of the next 32-wide step read while the current
+// step's MFMAs run (compute_pair).
 template <int MF, int NF, int SLOTS, int P, int KS, bool G32>
-__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : 2)))
+__global__ __launch_bounds__(256 * KS)
+__attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : (MF * NF > 16 ? 1 : 2))))
 void prefill_kernel(PfArgs a) {
     using S = PfShape<MF, NF, SLOTS, KS>;
     static_assert(P == 1 || P == 2, "stages per barrier");
@@ -263,6 +272,47 @@ void prefill_kernel(PfArgs a) {
             }
         }
     };
+    // Two stages (slots SL0, SL0 + 1), four 32-wide steps, each step's
+    // activation fragments read one step ahead (MF = 8 only).
+    auto compute_pair = [&](auto slc, bool first) {
+        constexpr int SL0 = decltype(slc)::value;
+        const uint8_t* sa = ring + SL0 * S::SLOT;
+        const uint8_t* sb = ring + (SL0 + 1) * S::SLOT;
+        auto read_a = [&](const uint8_t* slot, int off, u32x4 (&xa)[MF]) {
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+                xa[mf] = *reinterpret_cast<const u32x4*>(slot + off + mf * 16 * kARow);
+        };
+        auto read_b = [&](const uint8_t* slot, u32x2 (&bw)[NF]) {
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+                bw[nf] = *reinterpret_cast<const u32x2*>(slot + boff + nf * 16 * kBRow);
+        };
+        auto mstep = [&](const u32x4 (&xa)[MF], const u32x2 (&bw)[NF], int t, bool zero_acc) {
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+                const u32x4 bv = decode_x16(bw[nf][t]);
+#pragma unroll
+                for (int mf = 0; mf < MF; ++mf)
+                    acc[mf][nf] = mfma(xa[mf], bv, zero_acc ? zero : acc[mf][nf]);
+            }
+        };
+        u32x4 xa0[MF], xa1[MF];
+        u32x2 bw0[NF], bw1[NF];
+        read_b(sa, bw0);
+        read_a(sa, aoff0, xa0);
+        read_a(sa, aoff1, xa1);
+        if (first)
+            mstep(xa0, bw0, 0, true);
+        else
+            mstep(xa0, bw0, 0, false);
+        read_b(sb, bw1);
+        read_a(sb, aoff0, xa0);
+        mstep(xa1, bw0, 1, false);
+        read_a(sb, aoff1, xa1);
+        mstep(xa0, bw1, 0, false);
+        mstep(xa1, bw1, 1, false);
+    };
     // fold the finished group g into the totals
     auto close_group = [&](int g) {
 #pragma unroll
@@ -291,14 +341,18 @@ void prefill_kernel(PfArgs a) {
             if (s0 + SLOTS - P + I < stages)
                 issue(s0 + SLOTS - P + I, (SL0 + SLOTS - P + I) % SLOTS);
         });
-        if (first)
-            compute(std::integral_constant<int, SL0>{}, std::true_type{}, s0);
-        else
-            compute(std::integral_constant<int, SL0>{}, std::false_type{}, s0);
-        static_for<P - 1>([&](auto ic) {
-            constexpr int I = 1 + decltype(ic)::value;
-            compute(std::integral_constant<int, SL0 + I>{}, std::false_type{}, s0 + I);
-        });
+        if constexpr (MF == 8 && P == 2 && !G32) {
+            compute_pair(std::integral_constant<int, SL0>{}, first);
+        } else {
+            if (first)
+                compute(std::integral_constant<int, SL0>{}, std::true_type{}, s0);
+            else
+                compute(std::integral_constant<int, SL0>{}, std::false_type{}, s0);
+            static_for<P - 1>([&](auto ic) {
+                constexpr int I = 1 + decltype(ic)::value;
+                compute(std::integral_constant<int, SL0 + I>{}, std::false_type{}, s0 + I);
+            });
+        }
     };
 
     // Scales of the workgroup's rows: rows n0 .. n0 + BN - 1 are one
@@ -360,45 +414,51 @@ void prefill_kernel(PfArgs a) {
     const bool f32 = a.ydt == W4_F32;
     const int esz = f32 ? 4 : 2;
     uint8_t* ostage = rings;   // K group 0's ring
-    if (kg == 0) {
+    constexpr int PMF = MF / S::OUT_PARTS;    // fragments of rows per staged part
+    constexpr int PBM = S::BM / S::OUT_PARTS;
+    static_for<S::OUT_PARTS>([&](auto hc) {
+        constexpr int H = decltype(hc)::value;
+        if (H > 0) __syncthreads();           // the previous part is stored
+        if (kg == 0) {
 #pragma unroll
-        for (int mf = 0; mf < MF; ++mf)
+            for (int mf = 0; mf < PMF; ++mf)
 #pragma unroll
-            for (int nf = 0; nf < NF; ++nf)
+                for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    uint8_t* p = ostage + (16 * mf + 4 * lk + r) * S::OUT_ROW +
-                                 (wave * S::WN + 16 * nf + li) * esz;
+                    for (int r = 0; r < 4; ++r) {
+                        uint8_t* p = ostage + (16 * mf + 4 * lk + r) * S::OUT_ROW +
+                                     (wave * S::WN + 16 * nf + li) * esz;
+                        const float v = tot[H * PMF + mf][nf][r];
+                        if (f32)
+                            *reinterpret_cast<float*>(p) = v;
+                        else
+                            *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(v);
+                    }
+        }
+        __syncthreads();
+        const int per = 16 / esz;                 // elements per 16-byte piece
+        const int cpr = S::BN / per;              // pieces per row
+        for (int e = tid; e < PBM * cpr; e += S::THREADS) {
+            const int row = e / cpr, c = e - row * cpr;
+            const int m = m0 + H * PBM + row;
+            if (m >= a.M) break;                  // rows only grow with e
+            const int n = n0 + c * per;
+            if (n >= a.N) continue;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + row * S::OUT_ROW + 16 * c);
+            uint8_t* dst = static_cast<uint8_t*>(a.Y) + ((size_t)m * a.ldy + n) * esz;
+            if (a.vec_out && n + per <= a.N) {
+                gstore(reinterpret_cast<u32x4*>(dst), v);
+            } else {
+                for (int i = 0; i < per && n + i < a.N; ++i) {
                     if (f32)
-                        *reinterpret_cast<float*>(p) = tot[mf][nf][r];
+                        gstore(reinterpret_cast<uint32_t*>(dst) + i, v[i]);
                     else
-                        *reinterpret_cast<uint16_t*>(p) =
-                            (uint16_t)f32_to_bf16_rne(tot[mf][nf][r]);
+                        gstore(reinterpret_cast<uint16_t*>(dst) + i,
+                               (uint16_t)(v[i >> 1] >> (16 * (i & 1))));
                 }
-    }
-    __syncthreads();
-    const int per = 16 / esz;                 // elements per 16-byte piece
-    const int cpr = S::BN / per;              // pieces per row
-    for (int e = tid; e < S::BM * cpr; e += S::THREADS) {
-        const int row = e / cpr, c = e - row * cpr;
-        const int m = m0 + row;
-        if (m >= a.M) break;                  // rows only grow with e
-        const int n = n0 + c * per;
-        if (n >= a.N) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + row * S::OUT_ROW + 16 * c);
-        uint8_t* dst = static_cast<uint8_t*>(a.Y) + ((size_t)m * a.ldy + n) * esz;
-        if (a.vec_out && n + per <= a.N) {
-            gstore(reinterpret_cast<u32x4*>(dst), v);
-        } else {
-            for (int i = 0; i < per && n + i < a.N; ++i) {
-                if (f32)
-                    gstore(reinterpret_cast<uint32_t*>(dst) + i, v[i]);
-                else
-                    gstore(reinterpret_cast<uint16_t*>(dst) + i,
-                           (uint16_t)(v[i >> 1] >> (16 * (i & 1))));
             }
         }
-    }
+    });
 }
 
 struct PfCfg {
@@ -412,7 +472,7 @@ struct PfCfg {
 // 5 split K over three or two wave groups.
 constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2, 1}, {4, 1, 6, 2, 1}, {4, 3, 5, 1, 1},
                              {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2},
-                             {4, 2, 4, 2, 1}};
+                             {4, 2, 4, 2, 1}, {8, 3, 6, 2, 1}, {8, 2, 3, 1, 1}};
 constexpr int kPfNumCfgs = sizeof(kPfCfgs) / sizeof(kPfCfgs[0]);
 
 struct PfPlan {
@@ -477,6 +537,7 @@ PfPlan plan_prefill(int M, int N, int K, int group) {
     // group 32 beyond 48 groups: only the split workgroups hold the scale table
     // (G is a multiple of 8 here, so the two-way split divides it)
     if (group == 32 && G > kMaxG32 && kPfCfgs[p.cfg].ks == 1) p.cfg = 5;
+    if (group == 32 && p.cfg >= 7) p.cfg = 6;   // the wide tiles are for groups of 64 or more
     p.BM = 16 * kPfCfgs[p.cfg].MF;
     p.BN = 64 * kPfCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -509,6 +570,18 @@ static void launch_cfg(int cfg, dim3 g, dim3 b, hipStream_t s, const PfArgs& a) 
         case 3: prefill_kernel<4, 1, 5, 1, 1, G32><<<g, b, 0, s>>>(a); break;
         case 4: prefill_kernel<4, 1, 4, 2, 3, G32><<<g, b, 0, s>>>(a); break;
         case 5: prefill_kernel<4, 1, 6, 2, 2, G32><<<g, b, 0, s>>>(a); break;
+        case 7:
+            if constexpr (!G32) {
+                prefill_kernel<8, 3, 6, 2, 1, false><<<g, b, 0, s>>>(a);
+                break;
+            }
+            [[fallthrough]];
+        case 8:
+            if constexpr (!G32) {
+                prefill_kernel<8, 2, 3, 1, 1, false><<<g, b, 0, s>>>(a);
+                break;
+            }
+            [[fallthrough]];
         default: prefill_kernel<4, 2, 4, 2, 1, G32><<<g, b, 0, s>>>(a); break;
     }
 }

@@ -239,11 +239,11 @@ def test_matrix_core_largest_m(oracle_mod):
     assert_within(Y[rows], Yr, A, "bf16", "largest M")
 
 
-@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(7)] +
-                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(7)] +
+@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(9)] +
+                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(9)] +
                          [({"W4_FORCE_PATH": "prefill_regs"}, 32)] +
                          [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
-                          ({"W4_FORCE_PATH": "prefill_regs"}, 256)])
+                          ({"W4_FORCE_PATH": "prefill_regs"}, 256), ({"W4_PREFILL_CFG": "7"}, 512)])
 def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
     """Every compiled matrix-core tiling (the tuning overrides select them,
     one per call) against the oracle on one ragged case; at group 512 the
@@ -259,8 +259,9 @@ def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
     assert_within(Y, Yr, A, "f32", "tiling %s" % env)
 
 
-@pytest.mark.parametrize("cfg,K,g", [(c, 6144, 256) for c in (0, 1, 4, 5, 6)] +
+@pytest.mark.parametrize("cfg,K,g", [(c, 6144, 256) for c in (0, 1, 4, 5, 6, 7, 8)] +
                          [(0, 8192, 256), (5, 8192, 256), (4, 8192, 256), (6, 6144, 512),
+                          (7, 8192, 256), (7, 6144, 512),
                           (5, 6144, 32), (1, 6144, 32), (4, 6144, 32), (0, 2048, 32)])
 def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     """The DMA-ring tilings with 12 to 32 scale groups per row at groups 256
@@ -283,7 +284,8 @@ def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
 @pytest.mark.parametrize("g", [256, 32])
 def test_matrix_core_code8_columns_exact_zero(g):
     """Columns whose codes are all 8 are exactly zero through the matrix-core
-    path (the offset MFMA goes through the same arithmetic)."""
+    path (every operand is the exact (c - 8), so such a column's products are
+    all exact zeros)."""
     M, N, K = 64, 128, 1536
     rng = np.random.default_rng(4)
     P, S = synth.draw_weights(rng, N, K, g)
