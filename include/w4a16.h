@@ -425,7 +425,9 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
  *                       where the tile allows), smallm_valu (vector-ALU
  *                       small-M kernel), prefill_regs (register-staged
  *                       matrix-core kernel), i8_regs (register-staged int8
- *                       kernel).  An unknown name is W4_ERR_ARG.
+ *                       kernel), ordered_inline (decode-ordered sweep:
+ *                       decode each share while multiplying instead of
+ *                       ahead).  An unknown name is W4_ERR_ARG.
  *  W4_LOG=1             print each distinct dispatch decision once to stderr.
  *  W4_PREFILL_CFG, W4_MFMA_CFG, W4_I8_RING (1..4), W4_I8_TILE ("MF,NF"):
  *                       tiling indices of the prefill, register-staged

@@ -131,6 +131,10 @@ def test_force_path(L, monkeypatch):
     set_dispatch_env(monkeypatch, W4_FORCE_PATH="smallm_valu,prefill_regs")
     assert not w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm mfma")
     assert "dma-ring" not in w4.describe_dispatch(64, 12288, 1536, 256)
+    # the decode-ordered sweep's inline decode is a known name (it applies
+    # when a sweep handle is created)
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="ordered_inline")
+    assert w4.describe_dispatch(1, 2560, 1536, 32).endswith("(built-in table)")
     monkeypatch.setenv("W4_FORCE_PATH", "gemv_fast")
     assert L.w4_config_reload() == -1
     assert "gemv_fast" in w4.last_error()
