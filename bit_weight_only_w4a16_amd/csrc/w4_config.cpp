@@ -74,6 +74,10 @@ std::shared_ptr<Config> from_env() {
     c->prefill_cfg = env_index("W4_PREFILL_CFG", 0, 63);
     c->mfma_cfg = env_index("W4_MFMA_CFG", 0, 63);
     c->i8_ring = env_index("W4_I8_RING", 1, 63);
+    if (const char* e = getenv("W4_SWEEP_POLL_LIMIT")) {
+        int v;
+        if (parse_int(e, 0, 1 << 30, v)) c->sweep_poll_limit = v;
+    }
     if (const char* e = getenv("W4_I8_TILE")) {
         int mf = 0, nf = 0;
         if (sscanf(e, "%d,%d", &mf, &nf) == 2 && (mf == 2 || mf == 4) && (nf == 2 || nf == 4)) {

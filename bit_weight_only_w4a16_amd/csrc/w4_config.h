@@ -38,6 +38,7 @@ struct Config {
     int mfma_cfg = -1;              // W4_MFMA_CFG: a register-staged tiling index
     int i8_ring = -1;               // W4_I8_RING: 1..4 a ring tiling (0 = W4_FORCE_PATH i8_regs)
     int i8_mf = 0, i8_nf = 0;       // W4_I8_TILE "MF,NF": register-staged int8 tile
+    long sweep_poll_limit = -1;     // W4_SWEEP_POLL_LIMIT: completion polls per op (-1: default)
     std::vector<TileEntry> table;   // W4_TILE_TABLE or w4_tile_table_load
     std::string table_source;       // its path, "" for none
     int status = 0;                 // W4_OK, or why W4_TILE_TABLE could not be used

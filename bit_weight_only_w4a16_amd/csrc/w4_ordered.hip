@@ -578,6 +578,8 @@ struct OrdCtx {
     unsigned arrived;
     // (pre) ops below this index have been flagged as landed
     int landed;
+    // completion polls per op before giving up
+    unsigned poll_limit;
     __device__ uint8_t* slot_at(int sl) const { return smem + sl * kSlotBytes; }
 };
 
@@ -595,7 +597,7 @@ __device__ __forceinline__ void handoff_in(OrdCtx& k, const SweepOp& op, int i) 
         const unsigned* p = k.lane < 8 ? &k.ctl->cnt[32 * k.lane]
                                        : (k.lane == 8 ? &k.ctl->error : &k.ctl->cnt[0]);
         const unsigned target = (unsigned)i * (unsigned)k.G;
-        for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
+        for (unsigned spin = 0; spin < k.poll_limit; ++spin) {
             const unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // lanes 0..7 summed and lane 8's word, read into scalar registers
             unsigned c = 0;
@@ -787,7 +789,8 @@ __device__ __forceinline__ bool predecoded_op(OrdCtx& k, const SweepOp& op, int 
 // host's plans then give wave 0 no tasks.
 __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __restrict__ ops,
                                                               int n_ops, SweepCtl* ctl,
-                                                              int first0, int first1, int pre) {
+                                                              int first0, int first1, int pre,
+                                                              unsigned poll_limit) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
     OrdCtx k;
@@ -802,6 +805,7 @@ __global__ __launch_bounds__(kOrdThreads) void ordered_kernel(const SweepOp* __r
     k.nx_slot = -1;
     k.arrived = 0;
     k.landed = 0;
+    k.poll_limit = poll_limit;
     if (tid == 0) {
         k.s_flags[2] = 0;
         k.s_flags[3] = 0;

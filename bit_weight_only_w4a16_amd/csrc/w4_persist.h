@@ -89,11 +89,14 @@ struct SweepCtl {
 inline size_t sweep_ctl_bytes(int) { return sizeof(SweepCtl); }
 
 int persist_occupancy(bool dep, int* blocks_per_cu);
+// poll_limit: the decode-ordered kernel's completion polls per op before it
+// gives up (kOrdPollLimit unless a test asks for fewer)
+constexpr unsigned kOrdPollLimit = 1u << 20;
 int launch_persist(bool dep, const SweepOp* ops_dev, int n_ops, SweepCtl* ctl,
                    const int* range, int grid, int first0, int first1, int pre,
-                   hipStream_t s);
+                   unsigned poll_limit, hipStream_t s);
 int ordered_lds_bytes();
 __global__ void ordered_kernel(const SweepOp* __restrict__ ops, int n_ops, SweepCtl* ctl,
-                               int first0, int first1, int pre);
+                               int first0, int first1, int pre, unsigned poll_limit);
 
 }  // namespace w4

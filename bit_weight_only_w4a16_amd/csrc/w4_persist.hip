@@ -105,10 +105,10 @@ int persist_occupancy(bool dep, int* blocks_per_cu) {
 
 int launch_persist(bool dep, const SweepOp* ops_dev, int n_ops, SweepCtl* ctl,
                    const int* range, int grid, int first0, int first1, int pre,
-                   hipStream_t s) {
+                   unsigned poll_limit, hipStream_t s) {
     if (dep)
         ordered_kernel<<<dim3(grid), dim3(kOrdThreads), ordered_lds_bytes(), s>>>(
-            ops_dev, n_ops, ctl, first0, first1, pre);
+            ops_dev, n_ops, ctl, first0, first1, pre, poll_limit);
     else
         stream_kernel<<<dim3(grid), dim3(kPwThreads), 0, s>>>(ops_dev, n_ops, range);
     return hip_fail(hipGetLastError(), "persistent sweep launch");

@@ -28,6 +28,7 @@ struct w4_sweep {
     int* range = nullptr;             // STREAM: first tile of each wave (waves + 1)
     int first0 = -1, first1 = -1;     // PERSISTENT: first two resident ops
     int pre = 0;                      // PERSISTENT: resident shares decoded ahead
+    unsigned poll_limit = 0;          // PERSISTENT: completion polls per op
 };
 
 namespace w4 {
@@ -271,6 +272,10 @@ static int setup_persistent(w4_sweep* h) {
         }
         h->pre = pre ? 1 : 0;
         {
+            const long lim = config()->sweep_poll_limit;
+            h->poll_limit = lim >= 0 ? (unsigned)lim : kOrdPollLimit;
+        }
+        {
             const auto cfg = config();
             char msg[160];
             snprintf(msg, sizeof msg,
@@ -426,7 +431,8 @@ int w4_decode_sweep_launch(w4_sweep* h, void* stream) {
     if (h->mode != W4_SWEEP_GRAPH)
         return launch_persist(h->mode == W4_SWEEP_PERSISTENT,
                               static_cast<const SweepOp*>(h->dev), (int)h->ops.size(), h->ctl,
-                              h->range, h->grid, h->first0, h->first1, h->pre, s);
+                              h->range, h->grid, h->first0, h->first1, h->pre,
+                              h->poll_limit, s);
     if (!h->exec) return fail(W4_ERR_ARG, "sweep: bad handle");
     return hip_fail(hipGraphLaunch(h->exec, s), "graph launch");
 }

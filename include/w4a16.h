@@ -429,6 +429,11 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
  *                       decode each share while multiplying instead of
  *                       ahead).  An unknown name is W4_ERR_ARG.
  *  W4_LOG=1             print each distinct dispatch decision once to stderr.
+ *  W4_SWEEP_POLL_LIMIT=n
+ *                       completion polls per op before a decode-ordered
+ *                       sweep handle created afterwards gives up (default
+ *                       2^20); 0 makes every replay give up at its second
+ *                       op, for tests of the W4_ERR_TIMEOUT path.
  *  W4_PREFILL_CFG, W4_MFMA_CFG, W4_I8_RING (1..4), W4_I8_TILE ("MF,NF"):
  *                       tiling indices of the prefill, register-staged
  *                       matrix-core and int8 kernels, for tuning runs.

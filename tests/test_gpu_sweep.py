@@ -260,3 +260,48 @@ def test_decoded_ahead_equals_inline(sweep_data, monkeypatch, capfd):
         assert ("resident shares decoded %s" % name) in err, err
     for c, a, b in zip(cases, got["ahead"], got["inline"]):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), c.name
+
+
+@pytest.mark.parametrize("force", ["", "ordered_inline"])
+def test_persistent_gives_up_and_recovers(oracle_mod, monkeypatch, force):
+    """The decode-ordered kernel's give-up path: with no completion polls
+    allowed (W4_SWEEP_POLL_LIMIT=0) every workgroup stops at its second op,
+    the kernel ends normally, and the check reports W4_ERR_TIMEOUT and resets
+    the counters; a handle created with the default limit then replays the
+    same ops correctly."""
+    import torch
+    device()
+    n_ops, N = 4, 1536
+    x0b = synth.draw_activations(np.random.default_rng(9), 1, N)[0]
+    x0 = to_dev_bf16(x0b)
+    cases, ys, ops = [], [], []
+    for i in range(n_ops):
+        c = synth.make_case("giveup%d" % i, N, N, 32, 1, 900 + i, "bf16")
+        y = torch.full((N,), float("nan"), dtype=torch.bfloat16, device=device())
+        ops.append((upload_packed(c.P, c.S, N, N, 32), N, N, 32, x0 if i == 0 else ys[-1], y))
+        cases.append(c)
+        ys.append(y)
+    set_dispatch_env(monkeypatch, W4_SWEEP_POLL_LIMIT="0", W4_FORCE_PATH=force)
+    note("persistent sweep give-up force=%r" % force)
+    sw = w4.DecodeSweep(ops, w4.W4_SWEEP_PERSISTENT)
+    sw.launch()
+    with pytest.raises(w4.W4Error) as err:
+        sw.check()
+    assert err.value.status == -9
+    sw.close()
+    monkeypatch.delenv("W4_SWEEP_POLL_LIMIT")
+    w4.config_reload()
+    sw = w4.DecodeSweep(ops, w4.W4_SWEEP_PERSISTENT)
+    for y in ys:
+        y.fill_(float("nan"))
+    torch.cuda.synchronize()
+    sw.launch()
+    sw.check()
+    torch.cuda.synchronize()
+    xin = x0b
+    for i, c in enumerate(cases):
+        got = ys[i].view(torch.int16).cpu().numpy().view(np.uint16)
+        Y, A = oracle_mod.gemm_bf16(c.P, c.S, N, N, 32, xin, threads=16)
+        assert_within(synth.bf16_bits_to_f32(got), Y, A, "bf16", "after give-up op %d" % i)
+        xin = got
+    sw.close()

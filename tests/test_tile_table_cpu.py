@@ -202,3 +202,11 @@ def test_tuner_candidates_are_all_accepted(L, tmp_path):
         for i, line in enumerate(lines):
             p = _table(tmp_path, line + "\n", "c%d.txt" % i)
             assert L.w4_tile_table_load(p.encode()) == 0, (line, w4.last_error())
+
+
+def test_sweep_poll_limit_is_read(L, monkeypatch):
+    """W4_SWEEP_POLL_LIMIT is read with the configuration; it is a test knob
+    and a value out of range is ignored (the default applies)."""
+    for v in ("0", "5", "junk", "-3"):
+        monkeypatch.setenv("W4_SWEEP_POLL_LIMIT", v)
+        assert L.w4_config_reload() == 0
