@@ -631,6 +631,7 @@ __device__ __forceinline__ void handoff_out(OrdCtx& k, const SweepOp& op, int rb
     if (computes && k.lane == 0)
         __hip_atomic_fetch_add(&k.s_flags[2], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (k.wave != 0) return;
+    // a tight spin (no sleep between the LDS reads: 3 us less per step)
     bool done = false;
     for (unsigned spin = 0; spin < kOrdSpin; ++spin) {
         const unsigned c = (unsigned)__hip_atomic_load(&k.s_flags[2], __ATOMIC_ACQUIRE,
@@ -639,7 +640,6 @@ __device__ __forceinline__ void handoff_out(OrdCtx& k, const SweepOp& op, int rb
             done = true;
             break;
         }
-        __builtin_amdgcn_s_sleep(1);
     }
     if (!done) {
         // cannot happen unless a wave is lost; the next poll sees the error
