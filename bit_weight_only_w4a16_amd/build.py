@@ -38,11 +38,20 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-file code generation options.  The split-K kernel holds its matrix
+# accumulators in ordinary VGPRs (it fits in 256 of them at one wave per
+# SIMD): with accumulation registers the compiler moves every accumulator
+# out and back for each scale step (~350 extra moves per wave).
+FILE_FLAGS = {
+    "w4_splitk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _compile(src: str, asm: bool) -> str:
     base = os.path.splitext(os.path.basename(src))[0]
     obj = os.path.join(BUILD, base + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + ["-x", "hip", "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc()] + COMMON_FLAGS + extra + ["-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
@@ -50,7 +59,7 @@ def _compile(src: str, asm: bool) -> str:
         adir = os.path.join(BUILD, "asm")
         os.makedirs(adir, exist_ok=True)
         out = os.path.join(adir, base + ".s")
-        cmd = ([hipcc()] + COMMON_FLAGS +
+        cmd = ([hipcc()] + COMMON_FLAGS + extra +
                ["-x", "hip", "--cuda-device-only", "-S", src, "-o", out])
         subprocess.run(cmd, check=True, capture_output=True)
     return obj

@@ -306,6 +306,8 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
         const GemvTile t = pick_gemv_tile(N, K, group);
         return launch_gemv(t, packed, N, K, group, Xin, Y, ydt, s);
     }
+    if (splitk_applies(M, N, K, group, ld_in))
+        return launch_splitk(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
     if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group)))
         return launch_smallm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
     return launch_mfma_gemm(packed, N, K, group, M, Xin, ld_in, Y, ldy, ydt, s);
@@ -506,7 +508,9 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf, size_t len) 
         snprintf(buf, len, "gemv%s L=%d U=%d W=%d grid=%d stages=%d%s (%s)",
                  t.generic ? "_generic" : "", t.L, t.U, t.waves, t.grid, t.stages,
                  t.contig ? " contiguous" : "", src);
-    } else if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group))) {
+    } else if (splitk_applies(M, N, K, group, K)) {
+        describe_splitk(M, N, K, group, K, buf, len);
+  } else if (M <= kGemmSmallMRows || (M <= 16 && smallm_mfma_applies(M, N, K, group))) {
         describe_smallm(M, N, K, group, buf, len);
     } else {
         if (K % 256 != 0) return fail(W4_ERR_SHAPE, "describe: gemm needs K % 256 == 0");

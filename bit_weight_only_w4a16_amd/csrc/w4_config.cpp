@@ -35,7 +35,7 @@ unsigned parse_force(const char* e, std::string& bad) {
         {"gemv_generic", kForceGemvGeneric}, {"gemv_tiled", kForceGemvTiled},
         {"gemv_contig", kForceGemvContig},   {"smallm_valu", kForceSmallmValu},
         {"prefill_regs", kForcePrefillRegs}, {"i8_regs", kForceI8Regs},
-        {"ordered_inline", kForceOrderedInline}};
+        {"ordered_inline", kForceOrderedInline}, {"no_splitk", kForceNoSplitK}};
     unsigned f = 0;
     std::stringstream ss(e);
     std::string tok;

@@ -24,6 +24,7 @@ enum ForcePath : unsigned {
     kForcePrefillRegs = 1u << 4,   // M > 16: the register-staged matrix-core kernel
     kForceI8Regs = 1u << 5,        // int8 twin: the register-staged kernel
     kForceOrderedInline = 1u << 6, // decode-ordered sweep: decode while multiplying
+    kForceNoSplitK = 1u << 7,      // 2..64 rows: not the split-K matrix-core kernel
 };
 
 struct TileEntry {

@@ -45,6 +45,12 @@ void describe_smallm(int M, int N, int K, int group, char* buf, size_t len);
 // the matrix-core small-M kernel takes this shape (rotated groups, M <= 16)
 bool smallm_mfma_applies(int M, int N, int K, int group);
 
+// The split-K matrix-core kernel for 2..64 rows (w4_splitk.hip).
+bool splitk_applies(int M, int N, int K, int group, int ldx);
+int launch_splitk(const void* packed, int N, int K, int group, int M, const uint16_t* X, int ldx,
+                  void* Y, int ldy, int ydt, hipStream_t s);
+void describe_splitk(int M, int N, int K, int group, int ldx, char* buf, size_t len);
+
 int launch_fwht(const uint16_t* X, int ldx, uint16_t* Xo, int ldo, int M,
                 int K, int block, hipStream_t s);
 

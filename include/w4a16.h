@@ -185,9 +185,13 @@ size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block);
  * scale / 16.
  *  group must be 256 or 512 (the rotated prefill format of [P2]) or 32.
  *  M >= 1, K % 256 == 0.  Decode-shaped row counts take the decode kernels
- *  after the same transform: M = 1 the GEMV; 2..8 the small-M product, and
- *  9..16 too where it runs on the matrix cores (see w4a16_gemm_smallM).
- *  Larger row counts run on the tiled matrix-core kernels.
+ *  after the same transform: M = 1 the GEMV.  2..32 rows (8..32 at group
+ *  32) of a matrix of at least 128 tiles of 48 rows with K a multiple of
+ *  512 up to 2048 run on the split-K matrix-core kernel (K in four slices
+ *  per workgroup, the sum of the slices in a fixed order).  Otherwise 2..8
+ *  rows take the small-M product, and 9..16 too where it runs on the
+ *  matrix cores (see w4a16_gemm_smallM); larger row counts run on the tiled
+ *  matrix-core kernels.
  *  X: device, stride ldx (% 8 == 0).  Y: device, stride ldy.
  *  workspace: device, >= w4a16_gemm_workspace_bytes(M, K, had_block) bytes,
  *  16-byte aligned (may be NULL when that size is 0).
@@ -427,7 +431,10 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
  *                       matrix-core kernel), i8_regs (register-staged int8
  *                       kernel), ordered_inline (decode-ordered sweep:
  *                       decode each share while multiplying instead of
- *                       ahead).  An unknown name is W4_ERR_ARG.
+ *                       ahead), no_splitk (w4a16_gemm: not the split-K
+ *                       kernel; smallm_valu and prefill_regs also keep it
+ *                       off the row counts they name).  An unknown name is
+ *                       W4_ERR_ARG.
  *  W4_LOG=1             print each distinct dispatch decision once to stderr.
  *  W4_SWEEP_POLL_LIMIT=n
  *                       completion polls per op before a decode-ordered

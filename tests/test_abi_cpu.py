@@ -259,11 +259,28 @@ def test_describe_dispatch_tile_table(L, monkeypatch):
     assert w4.describe_dispatch(1, 100, 96, 32).startswith("gemv_generic")
     assert w4.describe_dispatch(1, 100, 768, 256).startswith("gemv_generic")
     assert w4.describe_dispatch(1, 100, 20000, 32).startswith("gemv_generic")
-    assert w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm")
+    # 2..32 rows (8..32 at group 32) of a matrix of >= 128 48-row tiles with
+    # K a multiple of 512 up to 2048: the split-K kernel, one or two
+    # activation tiles
+    assert w4.describe_dispatch(2, 12288, 1536, 256).startswith("splitk mfma 16x16x32 rows 48 x 1 ")
+    assert w4.describe_dispatch(16, 12288, 1536, 256).startswith("splitk mfma 16x16x32 rows 48 x 1 ")
+    assert w4.describe_dispatch(17, 12288, 1536, 256).startswith("splitk mfma 16x16x32 rows 48 x 2 ")
+    assert w4.describe_dispatch(32, 12288, 1536, 512).startswith("splitk mfma 16x16x32 rows 48 x 2 ")
+    assert w4.describe_dispatch(8, 12288, 1536, 32).startswith("splitk")
+    assert w4.describe_dispatch(32, 12288, 1536, 32).startswith("splitk")
+    assert "(512 each)" in w4.describe_dispatch(8, 6144, 2048, 256)
+    # fewer than 128 tiles, or K past 2048: the small-M kernels
+    assert w4.describe_dispatch(8, 2560, 1536, 256).startswith("smallm")
+    assert w4.describe_dispatch(9, 2560, 1536, 256).startswith("smallm mfma")
+    assert w4.describe_dispatch(16, 2560, 1536, 256).startswith("smallm mfma")
+    assert w4.describe_dispatch(8, 2560, 1536, 32).startswith("smallm mfma")
+    assert w4.describe_dispatch(8, 12288, 3072, 256).startswith("smallm mfma")
+    # W4_FORCE_PATH=no_splitk: the kernels those shapes take otherwise
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="no_splitk")
     assert w4.describe_dispatch(9, 12288, 1536, 256).startswith("smallm mfma")
-    assert w4.describe_dispatch(16, 12288, 1536, 256).startswith("smallm mfma")
-    assert w4.describe_dispatch(8, 12288, 1536, 32).startswith("smallm mfma")
     assert w4.describe_dispatch(16, 12288, 1536, 32).startswith("smallm mfma")
+    assert w4.describe_dispatch(17, 12288, 1536, 256).startswith("mfma")
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="")
     # group 32 below 5 rows, and K not a multiple of 128: vector ALU
     assert w4.describe_dispatch(4, 12288, 1536, 32).startswith("smallm MT=4")
     assert w4.describe_dispatch(8, 97, 288, 32).startswith("smallm MT=8")
@@ -272,7 +289,7 @@ def test_describe_dispatch_tile_table(L, monkeypatch):
     assert w4.describe_dispatch(8, 1536, 6144, 32).startswith("smallm mfma")
     assert w4.describe_dispatch(16, 1536, 2048, 32).startswith("smallm mfma")
     assert w4.describe_dispatch(16, 1536, 6144, 32).startswith("mfma")
-    assert w4.describe_dispatch(17, 12288, 1536, 256).startswith("mfma")
+    assert w4.describe_dispatch(33, 12288, 1536, 256).startswith("mfma")
     assert w4.describe_dispatch(64, 12288, 1536, 256).startswith("mfma")
     # DMA ring: block shape by workgroup rounds, K split for one-block grids,
     # up to 32 scale groups per row

@@ -129,8 +129,11 @@ def test_force_path(L, monkeypatch):
     set_dispatch_env(monkeypatch, W4_FORCE_PATH="gemv_tiled")
     assert "contiguous" not in w4.describe_dispatch(1, 262144, 1536, 32)
     set_dispatch_env(monkeypatch, W4_FORCE_PATH="smallm_valu,prefill_regs")
-    assert not w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm mfma")
+    assert w4.describe_dispatch(8, 12288, 1536, 256).startswith("smallm MT=")
+    assert w4.describe_dispatch(24, 12288, 1536, 256).startswith("mfma 16x16x32 block")
     assert "dma-ring" not in w4.describe_dispatch(64, 12288, 1536, 256)
+    set_dispatch_env(monkeypatch, W4_FORCE_PATH="no_splitk")
+    assert w4.describe_dispatch(24, 12288, 1536, 256).startswith("mfma 16x16x32 dma-ring")
     # the decode-ordered sweep's inline decode is a known name (it applies
     # when a sweep handle is created)
     set_dispatch_env(monkeypatch, W4_FORCE_PATH="ordered_inline")
