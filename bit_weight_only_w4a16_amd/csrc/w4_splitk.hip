@@ -17,6 +17,9 @@
 //   the DMA reads them as whole 256-byte row spans, four rows per load,
 //   where loads in the MFMA operand layout would touch 16 rows per 16
 //   lanes (measured: 11.0 against 8.7 us at 64 rows, 7.8 against 6.7 at 32);
+// - waits: group 32 starts each block once its own activations and codes
+//   are in, groups 256 and 512 once every first load is in (each faster for
+//   its group, by 0.5-0.7 and 0.2-0.3 us);
 // - the four slice sums meet in LDS and are added in slice order 0..3, so
 //   the result is deterministic.
 //
@@ -90,11 +93,29 @@ __device__ __forceinline__ u32x4 sk_transpose(u32x4 v, int lk) {
     return v;
 }
 
+// Wait until block b's activation DMA has landed: NB blocks of DB loads,
+// followed by W code-word loads.  b is a constant once the block loop is
+// unrolled, so one wait remains.
+template <int NB, int DB, int W, int I = 0>
+__device__ __forceinline__ void sk_wait_block(int b) {
+    if constexpr (I < NB) {
+        if (b == I)
+            ring::wait_vm<(NB - 1 - I) * DB + W>();
+        else
+            sk_wait_block<NB, DB, W, I + 1>(b);
+    }
+}
+
 // MF activation tiles, NB 128-K blocks per wave.
 template <int MF, int NB, bool G32>
 __global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void splitk_kernel(SkArgs a) {
     constexpr int NF = kSkNF;
+    // group 32 starts each block once its own operands are in (measured
+    // faster: 6.5 against 7.2 us at 8 rows); groups 256 and 512 start once
+    // every first load is in (5.3 against 5.5 us at 16 rows, 6.7 against
+    // 7.0 at 32)
+    constexpr bool PRECISE = G32;
     constexpr int DB = 4 * MF;                  // DMA loads per activation block
     constexpr int AB = 16 * MF * 256;           // bytes of one activation block
     extern __shared__ __align__(16) uint8_t sk_lds[];
@@ -142,38 +163,56 @@ void splitk_kernel(SkArgs a) {
                                                16 * (p ^ li));
     };
 
-    // code words: all of the wave's blocks, issued first
-    u32x4 q[NB][NF];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf)
-            q[b][nf] = nt_load(reinterpret_cast<const u32x4*>(crow[nf] + 64 * b));
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int b = 0; b < NB; ++b) dma_block(b, b);
-
-    // scales: groups of 32, the block's four as one 8-byte load; otherwise
-    // the aligned dword that holds the block's group scale
+    // Everything the wave reads is issued at its start.  The compiler's own
+    // waits (for codes and scales) do not count the DMA loads, and would
+    // wait for any issued after what they need, so with per-block waits
+    // (group 32) the order is scales, activation blocks (DMA), code words;
+    // otherwise code words, activation blocks, scales (measured 0.2-0.3 us
+    // faster than scales first at 2..16 rows).
     uint32_t sw[NB][NF][G32 ? 2 : 1];
     uint32_t ssel[NB][NF];
+    auto load_scales = [&]() {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int nf = 0; nf < NF; ++nf) {
-            if constexpr (G32) {
-                const u32x2 v = gload(reinterpret_cast<const u32x2*>(
-                    a.scales + srow[nf] + (k0 + 128 * b) / 32));
-                sw[b][nf][0] = v[0];
-                sw[b][nf][1] = v[1];
-                ssel[b][nf] = 0;
-            } else {
-                const int e = srow[nf] + (k0 + 128 * b) / a.group;
-                sw[b][nf][0] = gload(reinterpret_cast<const uint32_t*>(a.scales + (e & ~1)));
-                ssel[b][nf] = (e & 1) ? kScaleSelHi : kScaleSelLo;
+            for (int nf = 0; nf < NF; ++nf) {
+                // groups of 32: the block's four scales as one 8-byte load;
+                // otherwise the aligned dword that holds the block's group
+                // scale
+                if constexpr (G32) {
+                    const u32x2 v = gload(reinterpret_cast<const u32x2*>(
+                        a.scales + srow[nf] + (k0 + 128 * b) / 32));
+                    sw[b][nf][0] = v[0];
+                    sw[b][nf][1] = v[1];
+                    ssel[b][nf] = 0;
+                } else {
+                    const int e = srow[nf] + (k0 + 128 * b) / a.group;
+                    sw[b][nf][0] = gload(reinterpret_cast<const uint32_t*>(a.scales + (e & ~1)));
+                    ssel[b][nf] = (e & 1) ? kScaleSelHi : kScaleSelLo;
+                }
             }
-        }
+        asm volatile("" ::: "memory");
+    };
+    u32x4 q[NB][NF];
+    auto load_codes = [&]() {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+                q[b][nf] = nt_load(reinterpret_cast<const u32x4*>(crow[nf] + 64 * b));
+        asm volatile("" ::: "memory");
+    };
+    if constexpr (PRECISE)
+        load_scales();
+    else
+        load_codes();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dma_block(b, b);
     asm volatile("" ::: "memory");
+    if constexpr (PRECISE)
+        load_codes();
+    else
+        load_scales();
 
     const sk_f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     sk_f32x4 acc[MF][NF], tot[MF][NF];
@@ -188,12 +227,13 @@ void splitk_kernel(SkArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int buf = b;
-        if (b == 0) {
-            // every load has landed: the activations (DMA, not seen by the
-            // compiler's own waits), codes and scales
+        // block b's activations have landed (per block: at most the loads
+        // issued after them are in flight; otherwise every load has, once)
+        if constexpr (PRECISE)
+            sk_wait_block<NB, DB, NB * NF>(b);
+        else if (b == 0)
             ring::wait_vm<0>();
-            asm volatile("" ::: "memory");
-        }
+        asm volatile("" ::: "memory");
         if constexpr (G32) {
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf) q[b][nf] = sk_transpose(q[b][nf], lk);
@@ -293,12 +333,14 @@ struct SkPlan {
 // multiple of 512 up to 2048 (a quarter of K, NB <= 4 blocks of 128, per
 // wave), matrices of at least 128 workgroups of 48 rows, and activations
 // addressable with 32-bit offsets (the DMA loads').  Measured at N = 12288,
-// K = 1536 against the kernels these shapes took before: group 256 5.2-5.4 us
-// at 2..16 rows (5.6-6.9 on the matrix-core small-M kernel), 6.1-6.7 us at
-// 17..32 (8.3-8.4 on the DMA ring); group 32 7.0 us at 8..16 (7.1-7.9),
-// 7.9-8.4 at 17..32 (10.3); below 8 rows of group 32 the vector-ALU small-M
-// kernel is faster (5.2-6.2 us at 2..4 against 6.8-7.0), and from 33 rows on
-// (four activation tiles) the DMA ring (8.4 against 8.4-8.7 us at group 256).
+// K = 1536 against the kernels these shapes took before: group 256 5.2-5.3 us
+// at 2..16 rows (5.6-6.9 on the matrix-core small-M kernel), 6.2-6.7 us at
+// 17..32 (8.3-8.4 on the DMA ring); group 32 6.5-6.7 us at 8..16 (7.2-8.1),
+// 7.5-8.3 at 17..32 (10.2-10.3).  Below 8 rows of group 32 the vector-ALU
+// small-M kernel is as fast or faster (4.9-5.8 us at 2..4), and from 33 rows
+// on, with four activation tiles per workgroup (two 16 KB blocks in LDS per
+// wave), this kernel measured 8.5-8.9 us at 64 rows against the DMA ring's
+// 8.4.
 static SkPlan plan_splitk(int M, int N, int K, int group, int ldx) {
     SkPlan p{};
     p.ok = false;
