@@ -399,21 +399,26 @@ def time_single_gemv(torch, w4, synth, dev, cases, ops):
 
 def time_smallm_g32(torch, w4, synth, dev):
     """A few rows through the decode-format (group 32) gate+up weight,
-    12288 x 1536: the small-M product at 2, 8 and 16 rows, bf16 out."""
+    12288 x 1536, at 2, 8, 16 and 32 rows, bf16 out: w4a16_gemm (whatever it
+    dispatches to, named in "kernel") and, to 16 rows, the small-M entry
+    point (w4a16_gemm_smallM, its own kernels)."""
     import numpy as np
-    c = synth.make_case("smallm_g32", 12288, 1536, 32, 16, 16, "bf16")
+    c = synth.make_case("smallm_g32", 12288, 1536, 32, 32, 16, "bf16")
     P = torch.from_numpy(c.P.view(np.int32)).to(dev)
     S = torch.from_numpy(c.S.view(np.int16)).to(dev)
     packed = w4.pack(P, S, c.N, c.K, c.group)
     X16 = torch.from_numpy(c.X.view(np.int16)).to(dev).view(torch.bfloat16)
     out = {}
-    for M in (2, 8, 16):
+    for M in (2, 8, 16, 32):
         X = X16[:M]
         Y = torch.empty((M, c.N), dtype=torch.bfloat16, device=dev)
-        us = time_calls(torch, lambda: w4.gemm_smallM(packed, c.N, c.K, c.group, X, "bf16",
-                                                        out=Y))
-        out["M%d" % M] = {"kernel": w4.describe_dispatch(M, c.N, c.K, c.group), "us": us,
-                          "weight_GBps": c.weight_bytes / us / 1e3}
+        us = time_calls(torch, lambda: w4.gemm(packed, c.N, c.K, c.group, X, 0, "bf16", out=Y))
+        r = {"kernel": w4.describe_dispatch(M, c.N, c.K, c.group), "us": us,
+             "weight_GBps": c.weight_bytes / us / 1e3}
+        if M <= 16:
+            r["smallM_entry_us"] = time_calls(torch, lambda: w4.gemm_smallM(
+                packed, c.N, c.K, c.group, X, "bf16", out=Y))
+        out["M%d" % M] = r
     del P, S, packed, X16
     return out
 
