@@ -28,13 +28,11 @@ struct GemvArgs {
     int N, C, G, gshift, ydt;
 };
 
-// Loads this lane's activation slice, converts it to fp16 pairs in place and
-// sets xv to its inverse scale (zero slices for chunks past the row end).
-// Returns whether the conversion was exact.
+// Issues the loads of this lane's activation slice (bf16 pairs; zero slices
+// for chunks past the row end).  x_slice_to_f16 converts it once it is in.
 template <int L, int U>
-__device__ __forceinline__ bool load_x_slice(const uint32_t* x, int C, int lk,
-                                             uint32_t (&xr)[U][16], float& xv) {
-    bool ok = true;
+__device__ __forceinline__ void load_x_slice(const uint32_t* x, int C, int lk,
+                                             uint32_t (&xr)[U][16]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = lk + L * u;
@@ -53,6 +51,13 @@ __device__ __forceinline__ bool load_x_slice(const uint32_t* x, int C, int lk,
             for (int i = 0; i < 16; ++i) xr[u][i] = 0u;
         }
     }
+}
+
+// Converts a lane's activation slice to fp16 pairs in place and sets xv to
+// its inverse scale; returns whether the conversion was exact.
+template <int U>
+__device__ __forceinline__ bool x_slice_to_f16(uint32_t (&xr)[U][16], float& xv) {
+    bool ok = true;
     xv = chunks_to_f16<U>(xr, ok);
     return ok;
 }
@@ -71,9 +76,8 @@ __device__ __forceinline__ void gemv_rows_generic(const struct GemvArgs& a, int 
 // memory (written before the launch), the exact bf16 loop as fallback.
 struct GlobalX {
     template <int L, int U>
-    __device__ __forceinline__ bool load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16],
-                                         float& xv) const {
-        return load_x_slice<L, U>(a.x, a.C, lk, xr, xv);
+    __device__ __forceinline__ void load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16]) const {
+        load_x_slice<L, U>(a.x, a.C, lk, xr);
     }
     template <int L>
     __device__ __forceinline__ void fallback(const GemvArgs& a, int rg0, int rg1, int step,
@@ -113,12 +117,11 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
     const int lk = lane % L;
     const int lr = lane / L;
 
+    // the activation slice's loads go first, then (below) the first row
+    // groups' codes; the conversion waits for the slice only
     uint32_t xr[U][16];
     float xv;
-    if (!BATCH && wave_any_inexact(xs.template load<L, U>(a, lk, xr, xv))) {
-        xs.template fallback<L>(a, rg0, rg1, step, lane);
-        return;
-    }
+    xs.template load<L, U>(a, lk, xr);
 
     // chunk offsets, scale dword offsets and scale half selectors per chunk
     int coff[U], soff[U];
@@ -203,10 +206,6 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         }
     };
 
-    // Load order at the start of a range: a stand-alone grid-stride walk loads
-    // the activation slice first, so its offset terms are computed while the
-    // codes arrive; a BATCH walk (one of several ranges a wave runs in a row)
-    // issues the first row group's codes first, which measured faster there.
     // The prefetch is never skipped: on the last row group it re-reads the
     // current one (lines just fetched, so a cache hit) instead of branching.
     // A load issued under a branch that rejoins would leave the wait-count
@@ -218,7 +217,7 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         u32x4 qa[U], qb[U];
         uint32_t sa[U], sb[U];
         load(rg, qa, sa);
-        if (BATCH && wave_any_inexact(xs.template load<L, U>(a, lk, xr, xv))) {
+        if (wave_any_inexact(x_slice_to_f16<U>(xr, xv))) {
             xs.template fallback<L>(a, rg0, rg1, step, lane);
             return;
         }
@@ -239,7 +238,7 @@ __device__ __forceinline__ void gemv_rows(const GemvArgs& a, int rg0, int rg1, i
         uint32_t sa[U], sb[U], sc[U];
         load(rg, qa, sa);
         load(next(rg, step), qb, sb);
-        if (BATCH && wave_any_inexact(xs.template load<L, U>(a, lk, xr, xv))) {
+        if (wave_any_inexact(x_slice_to_f16<U>(xr, xv))) {
             xs.template fallback<L>(a, rg0, rg1, step, lane);
             return;
         }

@@ -477,17 +477,13 @@ __device__ __forceinline__ void compute_streamed(const SweepOp& op, const uint8_
 struct LdsX {
     const uint8_t* smem;
     template <int L, int U>
-    __device__ __forceinline__ bool load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16],
-                                         float& xv) const {
+    __device__ __forceinline__ void load(const GemvArgs& a, int lk, uint32_t (&xr)[U][16]) const {
         uint32_t t[kPwMaxU][16];
         slice_from_lds<L, U>(smem, a.C, U, lk, t);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int i = 0; i < 16; ++i) xr[u][i] = t[u][i];
-        bool ok = true;
-        xv = chunks_to_f16<U>(xr, ok);
-        return ok;
     }
     template <int L>
     __device__ __forceinline__ void fallback(const GemvArgs&, int, int, int, int) const {}
