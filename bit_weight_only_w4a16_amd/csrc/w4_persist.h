@@ -52,8 +52,8 @@ struct SweepOp {
 
 // Tile shapes (L lanes per row, U chunks per lane, L * U == C) compiled into
 // the STREAM kernel; any other K runs a generic loop.
-// At most 3 chunks per lane keeps the kernel at <= 128 VGPRs (4 waves per
-// SIMD); shapes are tried in order, so K = 2048 takes 32 x 2.
+// At most 3 chunks per lane (the activation slice, 16 registers per chunk,
+// stays in registers); shapes are tried in order, so K = 2048 takes 32 x 2.
 enum {
     kCfgGeneric = 0,
     kCfg16x1, kCfg16x2, kCfg16x3,

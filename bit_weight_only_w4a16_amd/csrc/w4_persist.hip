@@ -17,8 +17,11 @@ namespace w4 {
 #ifndef W4_STREAM_STAGES
 #define W4_STREAM_STAGES 2
 #endif
+// Two waves per SIMD (8 per CU, 256 VGPRs each, no spills): measured
+// 150.4-151.2 us per graph-replayed step against 153.8-154.0 with four
+// (128 VGPRs, 34 spilled outside the loops); three stages per wave 152-158.
 #ifndef W4_STREAM_WAVES_PER_EU
-#define W4_STREAM_WAVES_PER_EU 4
+#define W4_STREAM_WAVES_PER_EU 2
 #endif
 constexpr int kStreamStages = W4_STREAM_STAGES;  // register stages per wave
 
@@ -52,7 +55,7 @@ __device__ __forceinline__ void stream_rows(const SweepOp& op, int rg0, int rg1,
         gemv_rows_generic<L>(a, rg0, rg1, 1, lane);
 }
 
-// (register budget for W4_STREAM_WAVES_PER_EU waves per SIMD: 4 -> 128 VGPRs)
+// (register budget for W4_STREAM_WAVES_PER_EU waves per SIMD: 2 -> 256 VGPRs)
 __global__ __launch_bounds__(kPwThreads)
 __attribute__((amdgpu_waves_per_eu(W4_STREAM_WAVES_PER_EU)))
 void stream_kernel(const SweepOp* __restrict__ ops, int n_ops, const int* __restrict__ range) {
