@@ -461,6 +461,53 @@ def cpu_baseline(cases, max_threads=None, min_seconds=10.0, max_passes=40):
                       % (passes, total // passes, dt, threads, os.cpu_count())}
 
 
+def cpu_oracle_per_config(synth, cases, threads):
+    """The fp64 oracle on each workload, one host thread and `threads`
+    threads, median of three wall times (perf_counter) per entry: the
+    256 x 512 GEMV, decoder layer 0's four GEMVs, the lm_head GEMV, and the
+    prefill product with its 512-point transform at 8 rows (64 and 512 rows
+    given as that time scaled, the oracle being linear in the rows)."""
+    import oracle
+    oracle.build()
+    import numpy as np
+
+    def med3(fn):
+        t = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+        return sorted(t)[1]
+
+    out = {"threads": threads, "nproc": os.cpu_count(), "timing": "median of 3, perf_counter"}
+    c1 = synth.make_case("single", 256, 512, 32, 1, 0, "f32")
+    gemv_sets = (("256x512_g32", [c1]), ("decoder_layer_4_gemvs", cases[:4]),
+                 ("lm_head_262144x1536", [cases[-1]]))
+    for name, cs in gemv_sets:
+        wb = sum(c.weight_bytes for c in cs)
+        r = {"weight_bytes": wb}
+        for label, th in (("one_thread", 1), ("all_threads", threads)):
+            dt = med3(lambda: [oracle.gemm_bf16(c.P, c.S, c.N, c.K, c.group, c.X[0], threads=th)
+                               for c in cs])
+            r[label + "_ms"] = dt * 1e3
+            r[label + "_GBps"] = wb / dt / 1e9
+        out[name] = r
+    # the oracle's time is linear in the rows: the 8-row product is timed,
+    # 64 and 512 rows are that time scaled
+    c = synth.prefill_g256(8)
+    x = oracle.bf16_to_f64(c.X)
+    flops = 2.0 * 8 * c.N * c.K
+    r = {"rows_timed": 8}
+    for label, th in (("one_thread", 1), ("all_threads", threads)):
+        dt = med3(lambda: oracle.gemm(c.P, c.S, c.N, c.K, c.group, oracle.fwht(x, 512),
+                                      threads=th))
+        r[label + "_GFLOPs"] = flops / dt / 1e9
+        for M in (8, 64, 512):
+            r[label + "_ms_M%d" % M] = dt * 1e3 * M / 8
+    out["prefill_g256_N12288_K1536"] = r
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -609,6 +656,8 @@ def main():
                 "GBps": one["value"], "sample": one["sample"].replace(
                     "full decode-step sweep(s) (141 GEMVs", "pass(es) over decoder layer 0 (4 GEMVs"),
                 "ms_per_sweep_scaled": weight_bytes / one["value"] / 1e6}
+            log("timing the CPU oracle on each workload")
+            extra["cpu_oracle_per_config"] = cpu_oracle_per_config(synth, cases, cpu["cores"])
 
     out = {
         "metric": METRIC,
