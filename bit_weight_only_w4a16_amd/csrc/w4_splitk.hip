@@ -144,22 +144,22 @@ void splitk_kernel(SkArgs a) {
     uint8_t* region = sk_lds + ks * NB * AB;
     const uint32_t region_lds = ring::lds_addr(region);
     const int dr = lane >> 4, dc = lane & 15;
-    auto dma_block = [&](int b, int buf) {
+    auto dma_block = [&](int b) {
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
             const int r = 4 * j + dr;
             const int m = min(r, a.M - 1);
             const uint32_t off = (uint32_t)m * (uint32_t)a.ldx * 2u + (uint32_t)(k0 + 128 * b) * 2u +
                                  16u * (uint32_t)(dc ^ (r & 15));
-            ring::dma16(off, a.X, region_lds + buf * AB + 1024 * j);
+            ring::dma16(off, a.X, region_lds + b * AB + 1024 * j);
         }
     };
     // activation fragment of step t for tile mf: lane group lk's 8 elements
     // are piece 4 lk + t of the row's block (groups >= 128) or piece 4 t +
     // lk (group 32)
-    auto frag = [&](int buf, int mf, int t) {
+    auto frag = [&](int b, int mf, int t) {
         const int p = G32 ? 4 * t + lk : 4 * lk + t;
-        return *reinterpret_cast<const u32x4*>(region + buf * AB + (16 * mf + li) * 256 +
+        return *reinterpret_cast<const u32x4*>(region + b * AB + (16 * mf + li) * 256 +
                                                16 * (p ^ li));
     };
 
@@ -207,7 +207,7 @@ void splitk_kernel(SkArgs a) {
     else
         load_codes();
 #pragma unroll
-    for (int b = 0; b < NB; ++b) dma_block(b, b);
+    for (int b = 0; b < NB; ++b) dma_block(b);
     asm volatile("" ::: "memory");
     if constexpr (PRECISE)
         load_codes();
@@ -226,7 +226,6 @@ void splitk_kernel(SkArgs a) {
 
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const int buf = b;
         // block b's activations have landed (per block: at most the loads
         // issued after them are in flight; otherwise every load has, once)
         if constexpr (PRECISE)
@@ -241,7 +240,7 @@ void splitk_kernel(SkArgs a) {
             for (int t = 0; t < 4; ++t) {
                 u32x4 x[MF];
 #pragma unroll
-                for (int mf = 0; mf < MF; ++mf) x[mf] = frag(buf, mf, t);
+                for (int mf = 0; mf < MF; ++mf) x[mf] = frag(b, mf, t);
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
                     const u32x4 bv = decode_x16(q[b][nf][t]);
@@ -263,7 +262,7 @@ void splitk_kernel(SkArgs a) {
             for (int t = 0; t < 4; ++t) {
                 u32x4 x[MF];
 #pragma unroll
-                for (int mf = 0; mf < MF; ++mf) x[mf] = frag(buf, mf, t);
+                for (int mf = 0; mf < MF; ++mf) x[mf] = frag(b, mf, t);
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
                     const u32x4 bv = decode_x16(q[b][nf][t]);
