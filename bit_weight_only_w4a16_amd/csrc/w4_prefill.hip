@@ -461,6 +461,273 @@ void prefill_kernel(PfArgs a) {
     });
 }
 
+// Shared decode (groups of 64 or more): WM x WN waves, each computing
+// 64 x 48 outputs (MF = 4, NF = 3) of a (64 WM) x (48 WN) block.  Above, each
+// wave decodes the code words of its own 48 weight rows, so the WM waves of
+// a block that share those rows would decode every word WM times; here the
+// workgroup decodes each word of a stage once, into an LDS buffer of bf16
+// values laid out like an activation tile, and every wave reads its B
+// fragments from there.  Per 64-wide K stage:
+//   - each wave's DMA fills its share of the stage's activation tile (16-byte
+//     loads) and of its code tile (4-byte loads, U per wave); lane i of a
+//     code load brings exactly the word that lane i decodes, so a lane needs
+//     only its own wave's loads to have landed before decoding;
+//   - stage s + 1 is decoded (into one of two buffers) while stage s is
+//     multiplied from the other: one barrier per stage publishes the decoded
+//     words and the stage's activation tile, and frees the slot and buffer
+//     that the next DMA and decode overwrite;
+//   - the products, their K permutation (step t of lane group j takes words
+//     2j + t) and the per-group scaling are those of prefill_kernel, so the
+//     two give the same bits.
+// Decoded row i: 128 bytes, position p holds word p ^ g(i) (the activation
+// swizzle), so both the 16-byte decode writes (16 rows, one word each per
+// lane group) and the fragment reads are free of bank conflicts.
+template <int WM, int WN, int SLOTS>
+struct SdShape {
+    static constexpr int NW = WM * WN;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int BM = 64 * WM;
+    static constexpr int BN = 48 * WN;
+    static constexpr int A_BYTES = BM * kARow;
+    static constexpr int B_BYTES = BN * kBRow;
+    static constexpr int SLOT = A_BYTES + B_BYTES;
+    static constexpr int DEC = BN * kARow;               // one decoded stage
+    static constexpr int A_DMA = A_BYTES / 1024 / NW;    // 16-byte DMA per wave per stage
+    static constexpr int U = B_BYTES / 256 / NW;         // 4-byte DMA per wave per stage
+    static constexpr int LOADS = A_DMA + U;
+    static_assert(A_DMA * NW * 1024 == A_BYTES, "activation tile: whole DMA rounds per wave");
+    static_assert(U * NW * 256 == B_BYTES, "code tile: whole DMA rounds per wave");
+    static_assert(SLOTS >= 3 && SLOTS % 2 == 0, "a stage decoded ahead; buffer parity constant");
+    static_assert(LOADS * (SLOTS - 1) < 64, "vmcnt range");
+    static constexpr int LDS = SLOTS * SLOT + 2 * DEC;
+    static constexpr int OUT_ROW = BN * 4 + 16;          // padded fp32 staging row (bytes)
+    static_assert(BM * OUT_ROW <= LDS, "output block staged whole");
+};
+
+// s_waitcnt lgkmcnt(0), vmcnt and expcnt left alone: this wave's LDS writes
+// are done (the raw barrier does not wait for them)
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int WM, int WN, int SLOTS>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2)))
+void shared_decode_kernel(PfArgs a) {
+    using S = SdShape<WM, WN, SLOTS>;
+    constexpr int MF = 4, NF = 3;
+    __shared__ __align__(16) uint8_t lds[S::LDS];
+    __shared__ __align__(16) uint16_t sc[S::BN * kMaxG];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM, wn = wave / WM;
+    const int li = lane & 15, lk = lane >> 4;
+
+    // XCD x = blockIdx % 8 runs every M block of N blocks x, x + 8, ...
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int mb = j % a.m_blocks;
+    const int nb = (j / a.m_blocks) * 8 + xcd;
+    if (nb >= a.n_blocks) return;
+    const int m0 = mb * S::BM, n0 = nb * S::BN;
+    const int KW = a.K / 8;
+    const int stages = a.K / kStage;
+
+    uint32_t aoffs[S::A_DMA];
+#pragma unroll
+    for (int d = 0; d < S::A_DMA; ++d) {
+        const int r = 8 * (wave * S::A_DMA + d) + (lane >> 3);
+        const int q = (lane & 7) ^ swz_a(r);
+        const int m = min(m0 + r, a.M - 1);
+        aoffs[d] = (uint32_t)(((size_t)m * a.ldx + 8 * q) * 2);
+    }
+    // decode unit q (U per wave): rows 16 (q / 2) .. + 15, words 4 (q % 2) + lk
+    uint32_t boffs[S::U];
+    int doff[S::U];
+#pragma unroll
+    for (int u = 0; u < S::U; ++u) {
+        const int q = wave * S::U + u;
+        const int row = 16 * (q >> 1) + li;
+        const int word = 4 * (q & 1) + lk;
+        const int n = min(n0 + row, a.N - 1);
+        boffs[u] = (uint32_t)(((size_t)n * KW + word) * 4);
+        doff[u] = row * kARow + 16 * (word ^ swz_a(row));
+    }
+    const uint32_t lds0 = lds_addr(lds);
+    const uint32_t adst = lds0 + 1024 * (wave * S::A_DMA);
+    const uint32_t bdst = lds0 + S::A_BYTES + 256 * (wave * S::U);
+    const int bsrc = S::A_BYTES + 256 * (wave * S::U) + 4 * lane;   // this lane's code word
+    auto issue = [&](int st, int slot) {
+        const uint8_t* ab = reinterpret_cast<const uint8_t*>(a.X) + (size_t)st * kStage * 2;
+        const uint8_t* bb = reinterpret_cast<const uint8_t*>(a.codes) + (size_t)st * kStage / 2;
+#pragma unroll
+        for (int d = 0; d < S::A_DMA; ++d) dma16(aoffs[d], ab, adst + slot * S::SLOT + 1024 * d);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u) dma4(boffs[u], bb, bdst + slot * S::SLOT + 256 * u);
+    };
+    uint8_t* const dec = lds + SLOTS * S::SLOT;
+    auto decode = [&](auto slc, auto bufc) {
+        constexpr int SL = decltype(slc)::value, BUF = decltype(bufc)::value;
+        uint32_t w[S::U];
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+            w[u] = *reinterpret_cast<const uint32_t*>(lds + SL * S::SLOT + bsrc + 256 * u);
+#pragma unroll
+        for (int u = 0; u < S::U; ++u)
+            *reinterpret_cast<u32x4*>(dec + BUF * S::DEC + doff[u]) = decode_x16(w[u]);
+    };
+
+    // fragment offsets: step t of lane group lk reads word 2 lk + t of row li
+    const int gl = swz_a(li);
+    const int foff0 = li * kARow + 16 * ((2 * lk) ^ gl);
+    const int foff1 = li * kARow + 16 * ((2 * lk + 1) ^ gl);
+    const int arow = 64 * wm * kARow, brow = 48 * wn * kARow;
+    const uint16_t* scrow = sc + (48 * wn + li) * a.G;
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 tot[MF][NF], acc[MF][NF];
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) tot[mf][nf] = zero;
+
+    // one 32-wide step's fragments: MF activation, NF decoded weight
+    struct Frags {
+        u32x4 a[MF], b[NF];
+    };
+    auto read_frags = [&](auto slc, auto bufc, int fo, Frags& f) {
+        constexpr int SL = decltype(slc)::value, BUF = decltype(bufc)::value;
+        const uint8_t* sa = lds + SL * S::SLOT + arow;
+        const uint8_t* sb = dec + BUF * S::DEC + brow;
+#pragma unroll
+        for (int mf = 0; mf < MF; ++mf)
+            f.a[mf] = *reinterpret_cast<const u32x4*>(sa + fo + mf * 16 * kARow);
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+            f.b[nf] = *reinterpret_cast<const u32x4*>(sb + fo + nf * 16 * kARow);
+    };
+    // a group's first step starts its MFMA chains from a zero operand
+    auto mstep = [&](const Frags& f, auto zc) {
+        constexpr bool Z = decltype(zc)::value;
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+                acc[mf][nf] = mfma(f.a[mf], f.b[nf], Z ? zero : acc[mf][nf]);
+    };
+    auto close_group = [&](int g) {
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf) {
+            const float sv = bf16_to_f32(scrow[nf * 16 * a.G + g]) * 0.0625f;
+#pragma unroll
+            for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tot[mf][nf][r] = fmaf(sv, acc[mf][nf][r], tot[mf][nf][r]);
+        }
+    };
+
+    // scales of the block's rows, ahead of stage 0 (as in prefill_kernel)
+    {
+        const int ndw = (min(S::BN, a.N - n0) * a.G + 1) / 2;
+        const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.scales + (size_t)n0 * a.G);
+        const uint32_t sl = lds_addr(sc);
+        for (int i = wave; i < (ndw + 63) / 64; i += S::NW)
+            dma4((uint32_t)(4 * min(64 * i + lane, ndw - 1)), sb, sl + 256 * i);
+    }
+    const int pro = stages < SLOTS ? stages : SLOTS;
+    for (int st = 0; st < pro; ++st) issue(st, st);
+    // this wave's loads of stage 0 (and of the scales) have landed
+    wait_stage<S::LOADS, SLOTS - 1>(stages - 1);
+    asm volatile("" ::: "memory");
+    decode(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+    wait_lgkm0();
+    ring_barrier();
+    Frags f0, f1;
+    read_frags(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, foff0, f0);
+
+    // Stage s lives in slot s % SLOTS and is decoded into buffer s % 2
+    // (unrolled by SLOTS so that both are constants).  Software pipeline, per
+    // stage: read step 1's fragments; multiply step 0; decode stage s + 1
+    // (this wave's loads of it have landed); one barrier publishes every
+    // wave's decode and activation tile of stage s + 1 and proves stage s
+    // read by all, so its slot is refilled with stage s + SLOTS; read stage
+    // s + 1's step 0 fragments; multiply step 1.  The step-0 products are
+    // still in the matrix cores across the decode and the barrier.
+    const int spg = a.group / kStage;   // stages per scale group
+    int gs = 0, gi = 0;                 // stage within its group, group index
+    for (int st0 = 0; st0 < stages; st0 += SLOTS)
+        static_for<SLOTS>([&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            constexpr int NX = (I + 1) % SLOTS, BX = (I + 1) % 2;
+            const int s = st0 + I;
+            if (s >= stages) return;
+            read_frags(ic, std::integral_constant<int, I % 2>{}, foff1, f1);
+            if (gs == 0)
+                mstep(f0, std::true_type{});
+            else
+                mstep(f0, std::false_type{});
+            if (s + 1 < stages) {
+                // stages issued after s + 1 may still be in flight
+                wait_stage<S::LOADS, SLOTS - 2>(stages - s - 2);
+                asm volatile("" ::: "memory");
+                decode(std::integral_constant<int, NX>{}, std::integral_constant<int, BX>{});
+            }
+            wait_lgkm0();
+            ring_barrier();
+            if (s + SLOTS < stages) issue(s + SLOTS, I);
+            if (s + 1 < stages)
+                read_frags(std::integral_constant<int, NX>{}, std::integral_constant<int, BX>{},
+                           foff0, f0);
+            mstep(f1, std::false_type{});
+            if (++gs == spg) {
+                close_group(gi++);
+                gs = 0;
+            }
+        });
+
+    // Output through LDS as whole 16-byte row pieces (every DMA was waited
+    // for; past the barrier no wave reads the ring)
+    const bool f32 = a.ydt == W4_F32;
+    const int esz = f32 ? 4 : 2;
+    __syncthreads();
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < NF; ++nf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint8_t* p = lds + (64 * wm + 16 * mf + 4 * lk + r) * S::OUT_ROW +
+                             (48 * wn + 16 * nf + li) * esz;
+                const float v = tot[mf][nf][r];
+                if (f32)
+                    *reinterpret_cast<float*>(p) = v;
+                else
+                    *reinterpret_cast<uint16_t*>(p) = (uint16_t)f32_to_bf16_rne(v);
+            }
+    __syncthreads();
+    const int per = 16 / esz;
+    const int cpr = S::BN / per;
+    for (int e = tid; e < S::BM * cpr; e += S::THREADS) {
+        const int row = e / cpr, c = e - row * cpr;
+        const int m = m0 + row;
+        if (m >= a.M) break;
+        const int n = n0 + c * per;
+        if (n >= a.N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * S::OUT_ROW + 16 * c);
+        uint8_t* dst = static_cast<uint8_t*>(a.Y) + ((size_t)m * a.ldy + n) * esz;
+        if (a.vec_out && n + per <= a.N) {
+            gstore(reinterpret_cast<u32x4*>(dst), v);
+        } else {
+            for (int i = 0; i < per && n + i < a.N; ++i) {
+                if (f32)
+                    gstore(reinterpret_cast<uint32_t*>(dst) + i, v[i]);
+                else
+                    gstore(reinterpret_cast<uint16_t*>(dst) + i,
+                           (uint16_t)(v[i >> 1] >> (16 * (i & 1))));
+            }
+        }
+    }
+}
+
 struct PfCfg {
     int MF, NF, slots, per_barrier, ks;
 };
@@ -469,10 +736,14 @@ struct PfCfg {
 // one (the per-barrier latency chain, not the DMA depth, bounds the loop).
 // Entries 0, 6 and 1 are the unsplit block shapes chosen below; entries 2
 // and 3 are the one-stage variants, kept for comparison runs; entries 4 and
-// 5 split K over three or two wave groups.
+// 5 split K over three or two wave groups.  Entry 9 is the shared-decode
+// kernel (128 x 192 blocks of eight waves; its MF and NF give the block as
+// for the others: 16 MF rows, 64 NF columns).
 constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2, 1}, {4, 1, 6, 2, 1}, {4, 3, 5, 1, 1},
                              {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2},
-                             {4, 2, 4, 2, 1}, {8, 3, 6, 2, 1}, {8, 2, 3, 1, 1}};
+                             {4, 2, 4, 2, 1}, {8, 3, 6, 2, 1}, {8, 2, 3, 1, 1},
+                             {8, 3, 4, 1, 1}};
+constexpr int kPfShared = 9;
 constexpr int kPfNumCfgs = sizeof(kPfCfgs) / sizeof(kPfCfgs[0]);
 
 struct PfPlan {
@@ -582,6 +853,12 @@ static void launch_cfg(int cfg, dim3 g, dim3 b, hipStream_t s, const PfArgs& a) 
                 break;
             }
             [[fallthrough]];
+        case kPfShared:
+            if constexpr (!G32) {
+                shared_decode_kernel<2, 4, 4><<<g, dim3(SdShape<2, 4, 4>::THREADS), 0, s>>>(a);
+                break;
+            }
+            [[fallthrough]];
         default: prefill_kernel<4, 2, 4, 2, 1, G32><<<g, b, 0, s>>>(a); break;
     }
 }
@@ -617,6 +894,13 @@ int launch_prefill(const void* packed, int N, int K, int group, int M, const uin
 
 void describe_prefill(int M, int N, int K, int group, char* buf, size_t len) {
     const PfPlan p = plan_prefill(M, N, K, group);
+    if (p.cfg == kPfShared) {
+        snprintf(buf, len,
+                 "mfma 16x16x32 dma-ring shared-decode block %dx%d waves 2x4 slots %d stage %d "
+                 "grid=%d (K=%d g=%d)",
+                 p.BM, p.BN, kPfCfgs[p.cfg].slots, kStage, p.grid, K, group);
+        return;
+    }
     snprintf(buf, len,
              "mfma 16x16x32 dma-ring block %dx%d waves %dx4 slots %d stage %d x%d grid=%d (K=%d g=%d)",
              p.BM, p.BN, kPfCfgs[p.cfg].ks, kPfCfgs[p.cfg].slots, kStage,

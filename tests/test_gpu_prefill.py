@@ -239,8 +239,8 @@ def test_matrix_core_largest_m(oracle_mod):
     assert_within(Y[rows], Yr, A, "bf16", "largest M")
 
 
-@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(9)] +
-                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(9)] +
+@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(10)] +
+                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(10)] +
                          [({"W4_FORCE_PATH": "prefill_regs"}, 32)] +
                          [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
                           ({"W4_FORCE_PATH": "prefill_regs"}, 256), ({"W4_PREFILL_CFG": "7"}, 512)])
@@ -261,7 +261,8 @@ def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
 
 @pytest.mark.parametrize("cfg,K,g", [(c, 6144, 256) for c in (0, 1, 4, 5, 6, 7, 8)] +
                          [(0, 8192, 256), (5, 8192, 256), (4, 8192, 256), (6, 6144, 512),
-                          (7, 8192, 256), (7, 6144, 512),
+                          (7, 8192, 256), (7, 6144, 512), (9, 6144, 256), (9, 8192, 256),
+                          (9, 6144, 512),
                           (5, 6144, 32), (1, 6144, 32), (4, 6144, 32), (0, 2048, 32)])
 def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     """The DMA-ring tilings with 12 to 32 scale groups per row at groups 256
@@ -279,6 +280,28 @@ def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, oracle_mod.bf16_to_f64(case.X), threads=16)
     Y = from_dev(w4.gemm(packed, N, K, g, X, out_dtype="f32"))
     assert_within(Y, Yr, A, "f32", "cfg %d K %d g %d" % (cfg, K, g))
+
+
+@pytest.mark.parametrize("M,N,K,g", [(512, 12288, 1536, 256), (300, 1000, 1536, 512),
+                                     (129, 12288, 256, 256), (1024, 1536, 6144, 256)])
+def test_shared_decode_matches_per_wave_decode_bitwise(monkeypatch, M, N, K, g):
+    """The shared-decode tiling forms the same products in the same order as
+    the per-wave-decode tiling (same K permutation, groups accumulated from
+    zero and scaled into the totals in group order): their outputs agree bit
+    for bit, in fp32 and bf16, including ragged blocks and a K of four stages."""
+    rng = np.random.default_rng(M + N + K)
+    P, S = synth.draw_weights(rng, N, K, g)
+    packed = upload_packed(P, S, N, K, g)
+    X = to_dev_bf16(synth.draw_activations(rng, M, K, outlier_frac=0.01))
+    note("shared decode bitwise M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    for out_dtype in ("f32", "bf16"):
+        outs = []
+        for cfg in ("0", "9"):
+            set_dispatch_env(monkeypatch, W4_PREFILL_CFG=cfg)
+            d = w4.describe_dispatch(M, N, K, g)
+            assert ("shared-decode" in d) == (cfg == "9"), d
+            outs.append(from_dev(w4.gemm(packed, N, K, g, X, out_dtype=out_dtype)))
+        assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8)), out_dtype
 
 
 @pytest.mark.parametrize("g", [256, 32])
