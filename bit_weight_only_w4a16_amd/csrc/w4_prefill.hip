@@ -125,7 +125,7 @@ __device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
 // step's MFMAs run (compute_pair).
 template <int MF, int NF, int SLOTS, int P, int KS, bool G32>
 __global__ __launch_bounds__(256 * KS)
-__attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : (MF * NF > 16 ? 1 : 2))))
+__attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : (MF * NF > 16 ? 1 : (MF * NF <= 8 && SLOTS == 3 ? 3 : 2)))))
 void prefill_kernel(PfArgs a) {
     using S = PfShape<MF, NF, SLOTS, KS>;
     static_assert(P == 1 || P == 2, "stages per barrier");
@@ -734,7 +734,8 @@ struct PfCfg {
 // 64 x 192, 64 x 128 or 64 x 64 blocks; ring slots; stages per barrier; K
 // groups.  Measured at N = 12288, K = 1536, g256: two stages per barrier beat
 // one (the per-barrier latency chain, not the DMA depth, bounds the loop).
-// Entries 0, 6 and 1 are the unsplit block shapes chosen below; entries 2
+// Entries 0, 10, 6 and 1 are the unsplit block shapes chosen below (10: the
+// 64 x 128 block with a three-slot ring, three workgroups per CU); entries 2
 // and 3 are the one-stage variants, kept for comparison runs; entries 4 and
 // 5 split K over three or two wave groups.  Entry 9 is the shared-decode
 // kernel (128 x 192 blocks of eight waves; its MF and NF give the block as
@@ -742,7 +743,7 @@ struct PfCfg {
 constexpr PfCfg kPfCfgs[] = {{4, 3, 4, 2, 1}, {4, 1, 6, 2, 1}, {4, 3, 5, 1, 1},
                              {4, 1, 5, 1, 1}, {4, 1, 4, 2, 3}, {4, 1, 6, 2, 2},
                              {4, 2, 4, 2, 1}, {8, 3, 6, 2, 1}, {8, 2, 3, 1, 1},
-                             {8, 3, 4, 1, 1}};
+                             {8, 3, 4, 1, 1}, {4, 2, 3, 1, 1}};
 constexpr int kPfShared = 9;
 constexpr int kPfNumCfgs = sizeof(kPfCfgs) / sizeof(kPfCfgs[0]);
 
@@ -750,32 +751,37 @@ struct PfPlan {
     int cfg, BM, BN, m_blocks, n_blocks, grid;
 };
 
-// Unsplit block shape: all three keep two workgroups per CU, so a launch runs
-// in rounds of 2 * CUs workgroups.  Choose the fewest rounds times the
-// measured time of one full round (N = 12288, K = 1536, g256: 64 x 64 blocks
-// 14.1 us, 64 x 128 20.9 us, 64 x 192 27.6 us), wider blocks on ties.  This
-// picks, at N = 12288, 64 x 64 for 65..128 rows, 64 x 128 for 129..320 and
-// 513..640, 64 x 192 for 321..512 and from 641: the measured best at every
-// row count tried from 80 to 1024.  Group 32 (a scale per MFMA step: more
-// registers and ALU work per block) has no 64 x 192 entry, which spills, and
-// its own round times (64 x 128 26 us, 64 x 64 17.5 us): 64 x 64 up to 128
-// rows, 64 x 128 above (28.1 against 32.0 us at 256 rows, 51.3 against 55.4
-// at 512, 86.8 against 105.4 at 1024).
+// Unsplit block shape.  Each candidate holds a fixed number of workgroups
+// per CU (LDS and registers), so a launch runs in rounds of that many times
+// the CUs; choose the fewest rounds times the measured time of one full
+// round, wider blocks on ties.  Groups of 64 or more, N = 12288, K = 1536,
+// g256: 64 x 192 blocks two per CU 27.6 us; 64 x 128 three per CU (a
+// three-slot ring, three waves per SIMD) 26.5 us, the same outputs per round
+// as 64 x 192 (M = 512: 29.1 against 30.3 us, M = 1024: 53.1 against 56.0,
+// measured side by side); 64 x 128 two per CU 20.9 us; 64 x 64 two per CU
+// 14.1 us.  At N = 12288 this gives 64 x 64 for 65..128 rows, 64 x 128 two
+// per CU for 129..320 and 513..640, three per CU for 321..512 and from 641.
+// Group 32 (a scale per MFMA step: more registers and ALU work per block)
+// has no 64 x 192 entry, which spills, and its own round times (64 x 128
+// three per CU 35.5 us, two per CU 26 us, 64 x 64 17.5 us): 64 x 64 up to
+// 128 rows, 64 x 128 two per CU for 129..320, three per CU above (512 rows
+// 35.5 against 39.7 us two per CU, 1024 rows 65.1 against 70.5).
 struct PfCand {
-    int cfg, BN;
+    int cfg, BN, per_cu;
     double t_round;
 };
 static int pick_block_cfg(int M, int N, int group) {
-    static const PfCand kCand[3] = {{0, 192, 27.6}, {6, 128, 20.9}, {1, 64, 14.1}};
-    static const PfCand kCand32[2] = {{6, 128, 26.0}, {1, 64, 17.5}};
+    static const PfCand kCand[4] = {
+        {0, 192, 2, 27.6}, {10, 128, 3, 26.5}, {6, 128, 2, 20.9}, {1, 64, 2, 14.1}};
+    static const PfCand kCand32[3] = {{10, 128, 3, 35.5}, {6, 128, 2, 26.0}, {1, 64, 2, 17.5}};
     const PfCand* cand = group == 32 ? kCand32 : kCand;
-    const int ncand = group == 32 ? 2 : 3;
-    const long long slots = 2LL * kNumCUs;
+    const int ncand = group == 32 ? 3 : 4;
     const long long mb = (M + 63) / 64;
     int best = 0;
     double best_t = 1e300;
     for (int i = 0; i < ncand; ++i) {
         const PfCand& c = cand[i];
+        const long long slots = (long long)c.per_cu * kNumCUs;
         const long long wgs = mb * ((N + c.BN - 1) / c.BN);
         const double t = (double)((wgs + slots - 1) / slots) * c.t_round;
         if (t < best_t - 1e-9) {   // candidates in decreasing width: ties keep the wider
@@ -808,7 +814,8 @@ PfPlan plan_prefill(int M, int N, int K, int group) {
     // group 32 beyond 48 groups: only the split workgroups hold the scale table
     // (G is a multiple of 8 here, so the two-way split divides it)
     if (group == 32 && G > kMaxG32 && kPfCfgs[p.cfg].ks == 1) p.cfg = 5;
-    if (group == 32 && p.cfg >= 7) p.cfg = 6;   // the wide tiles are for groups of 64 or more
+    // the wide tiles and the shared decode are for groups of 64 or more
+    if (group == 32 && (p.cfg == 7 || p.cfg == 8 || p.cfg == kPfShared)) p.cfg = 6;
     p.BM = 16 * kPfCfgs[p.cfg].MF;
     p.BN = 64 * kPfCfgs[p.cfg].NF;
     p.m_blocks = (M + p.BM - 1) / p.BM;
@@ -853,6 +860,7 @@ static void launch_cfg(int cfg, dim3 g, dim3 b, hipStream_t s, const PfArgs& a) 
                 break;
             }
             [[fallthrough]];
+        case 10: prefill_kernel<4, 2, 3, 1, 1, G32><<<g, b, 0, s>>>(a); break;
         case kPfShared:
             if constexpr (!G32) {
                 shared_decode_kernel<2, 4, 4><<<g, dim3(SdShape<2, 4, 4>::THREADS), 0, s>>>(a);

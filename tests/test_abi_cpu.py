@@ -295,17 +295,21 @@ def test_describe_dispatch_tile_table(L, monkeypatch):
     # up to 32 scale groups per row
     ring = lambda M, N, K, g: w4.describe_dispatch(M, N, K, g).split("block ")[1]
     assert ring(128, 12288, 1536, 256).startswith("64x64 waves 1x4")
-    assert ring(320, 12288, 1536, 256).startswith("64x128 waves 1x4")
-    assert ring(384, 12288, 1536, 256).startswith("64x192 waves 1x4")
-    assert ring(640, 12288, 1536, 256).startswith("64x128 waves 1x4")
-    assert ring(1024, 12288, 1536, 256).startswith("64x192 waves 1x4")
+    assert ring(320, 12288, 1536, 256).startswith("64x128 waves 1x4 slots 4")
+    # three workgroups per CU (three-slot ring) where a round of them fits
+    assert ring(384, 12288, 1536, 256).startswith("64x128 waves 1x4 slots 3")
+    assert ring(512, 12288, 1536, 256).startswith("64x128 waves 1x4 slots 3")
+    assert ring(640, 12288, 1536, 256).startswith("64x128 waves 1x4 slots 4")
+    assert ring(1024, 12288, 1536, 256).startswith("64x128 waves 1x4 slots 3")
+    assert ring(1984, 6336, 1536, 256).startswith("64x192 waves 1x4")  # fewer rounds
     assert ring(64, 1536, 6144, 256).startswith("64x64 waves 3x4")
     assert ring(256, 4096, 1536, 256).startswith("64x64 waves 3x4")
     assert ring(64, 1536, 8192, 256).startswith("64x64 waves 2x4")
     assert "dma-ring" not in w4.describe_dispatch(64, 1536, 1 << 14, 256)  # 64 groups
     assert ring(64, 12288, 1536, 32).startswith("64x64 waves 2x4")
     assert ring(128, 12288, 1536, 32).startswith("64x64 waves 1x4")
-    assert ring(512, 12288, 1536, 32).startswith("64x128 waves 1x4")
+    assert ring(512, 12288, 1536, 32).startswith("64x128 waves 1x4 slots 3")
+    assert ring(256, 12288, 1536, 32).startswith("64x128 waves 1x4 slots 4")
     assert ring(64, 1536, 6144, 32).startswith("64x64 waves 3x4")      # 192 groups
     assert ring(1024, 1536, 6144, 32).startswith("64x64 waves 2x4")
     assert "dma-ring" not in w4.describe_dispatch(64, 1536, 6400, 32)  # 200 groups

@@ -239,8 +239,8 @@ def test_matrix_core_largest_m(oracle_mod):
     assert_within(Y[rows], Yr, A, "bf16", "largest M")
 
 
-@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(10)] +
-                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(10)] +
+@pytest.mark.parametrize("env,g", [({"W4_PREFILL_CFG": str(c)}, 256) for c in range(11)] +
+                         [({"W4_PREFILL_CFG": str(c)}, 32) for c in range(11)] +
                          [({"W4_FORCE_PATH": "prefill_regs"}, 32)] +
                          [({"W4_PREFILL_CFG": "4"}, 512), ({"W4_PREFILL_CFG": "5"}, 512),
                           ({"W4_FORCE_PATH": "prefill_regs"}, 256), ({"W4_PREFILL_CFG": "7"}, 512)])
@@ -262,7 +262,7 @@ def test_matrix_core_every_tiling(oracle_mod, monkeypatch, env, g):
 @pytest.mark.parametrize("cfg,K,g", [(c, 6144, 256) for c in (0, 1, 4, 5, 6, 7, 8)] +
                          [(0, 8192, 256), (5, 8192, 256), (4, 8192, 256), (6, 6144, 512),
                           (7, 8192, 256), (7, 6144, 512), (9, 6144, 256), (9, 8192, 256),
-                          (9, 6144, 512),
+                          (9, 6144, 512), (10, 8192, 256), (10, 1536, 32),
                           (5, 6144, 32), (1, 6144, 32), (4, 6144, 32), (0, 2048, 32)])
 def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     """The DMA-ring tilings with 12 to 32 scale groups per row at groups 256
