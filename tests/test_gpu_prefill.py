@@ -282,6 +282,26 @@ def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     assert_within(Y, Yr, A, "f32", "cfg %d K %d g %d" % (cfg, K, g))
 
 
+@pytest.mark.parametrize("cfg,K,g", [(c, K, g) for c in (9, 10) for K, g in ((256, 256), (512, 512),
+                                                                          (512, 256))] +
+                         [(10, 256, 32), (10, 512, 32)])
+def test_matrix_core_short_k(oracle_mod, monkeypatch, cfg, K, g):
+    """The three-slot and shared-decode tilings at their shortest K (four
+    and eight 64-wide stages: the ring never wraps, or wraps twice), one
+    and two scale groups, ragged M and N, against the oracle."""
+    set_dispatch_env(monkeypatch, W4_PREFILL_CFG=str(cfg))
+    M, N = 133, 1100
+    assert "dma-ring" in w4.describe_dispatch(M, N, K, g)
+    note("mfma short K cfg=%d M=%d N=%d K=%d g=%d" % (cfg, M, N, K, g))
+    case = synth.make_case("shortk", N, K, g, M, 300 + cfg + K + g, "bf16", outlier_frac=0.01)
+    packed = upload_packed(case.P, case.S, N, K, g)
+    X = to_dev_bf16(case.X)
+    Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, oracle_mod.bf16_to_f64(case.X), threads=16)
+    for out_dtype in ("f32", "bf16"):
+        Y = from_dev(w4.gemm(packed, N, K, g, X, out_dtype=out_dtype))
+        assert_within(Y, Yr, A, out_dtype, "short K cfg %d K %d g %d" % (cfg, K, g))
+
+
 @pytest.mark.parametrize("M,N,K,g", [(512, 12288, 1536, 256), (300, 1000, 1536, 512),
                                      (129, 12288, 256, 256), (1024, 1536, 6144, 256)])
 def test_shared_decode_matches_per_wave_decode_bitwise(monkeypatch, M, N, K, g):
