@@ -282,6 +282,27 @@ def test_matrix_core_many_scale_groups(oracle_mod, monkeypatch, cfg, K, g):
     assert_within(Y, Yr, A, "f32", "cfg %d K %d g %d" % (cfg, K, g))
 
 
+@pytest.mark.parametrize("M,g,slots", [(320, 256, "slots 4"), (321, 256, "slots 3"),
+                                       (640, 256, "slots 4"), (641, 256, "slots 3"),
+                                       (320, 32, "slots 4"), (321, 32, "slots 3")])
+def test_ring_block_shape_boundaries(oracle_mod, M, g, slots):
+    """Row counts on both sides of a block-shape change at N = 12288,
+    K = 1536 (64 x 128 blocks, two workgroups per CU on a four-slot ring or
+    three on a three-slot ring), on sampled rows including the last."""
+    N, K = 12288, 1536
+    desc = w4.describe_dispatch(M, N, K, g)
+    assert "block 64x128" in desc and slots in desc, desc
+    note("ring boundary M=%d g=%d -> %s" % (M, g, desc))
+    rng = np.random.default_rng(M + g)
+    P, S = synth.draw_weights(rng, N, K, g)
+    X = synth.draw_activations(rng, M, K, outlier_frac=0.01)
+    packed = upload_packed(P, S, N, K, g)
+    rows = np.concatenate([[0, M - 1], rng.choice(M, 14, replace=False)])
+    Yr, A = oracle_mod.gemm(P, S, N, K, g, oracle_mod.bf16_to_f64(X[rows]), threads=16)
+    Y = from_dev(w4.gemm(packed, N, K, g, to_dev_bf16(X), out_dtype="bf16"))
+    assert_within(Y[rows], Yr, A, "bf16", "boundary M=%d g=%d" % (M, g))
+
+
 @pytest.mark.parametrize("cfg,K,g", [(c, K, g) for c in (9, 10) for K, g in ((256, 256), (512, 512),
                                                                           (512, 256))] +
                          [(10, 256, 32), (10, 512, 32)])
