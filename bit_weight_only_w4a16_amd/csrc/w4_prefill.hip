@@ -30,7 +30,9 @@
 // the groups' partial blocks are added in LDS in group order at the end: the
 // same weight and activation bytes per workgroup, KS times the waves to hide
 // each stage's latency, and 1/KS of the stages per wave (few-row products,
-// whose workgroups do not fill the chip).  Workgroups are numbered so that every M block of an N block runs on
+// whose workgroups do not fill the chip).  The block shapes hold two or
+// three workgroups per CU (LDS and registers), and the host counts launch
+// rounds at each one's occupancy.  Workgroups are numbered so that every M block of an N block runs on
 // one XCD (workgroups go round-robin to the 8 XCDs): the weights are read from
 // HBM once per XCD and the activations stay in that XCD's L2.
 //
@@ -123,6 +125,9 @@ __device__ __forceinline__ int swz_b(int i) { return ((i & 15) >> 2) & 3; }
 // word feeding eight MFMAs instead of four (half the decode per MFMA), and
 // the activation fragments of the next 32-wide step read while the current
 // step's MFMAs run (compute_pair).
+// Waves per SIMD the registers are sized for: KS for K splits of three or
+// more groups; one for 128 x 48 per wave; three for 64 x 32 per wave on a
+// three-slot ring (44-48 KB of LDS: three workgroups per CU); two otherwise.
 template <int MF, int NF, int SLOTS, int P, int KS, bool G32>
 __global__ __launch_bounds__(256 * KS)
 __attribute__((amdgpu_waves_per_eu(KS > 2 ? KS : (MF * NF > 16 ? 1 : (MF * NF <= 8 && SLOTS == 3 ? 3 : 2)))))
