@@ -291,6 +291,43 @@ def time_mfma_probe(torch, w4):
             "pct_of_2.5PF_bf16": flops / us / 1e6 / 2500 * 100}
 
 
+def time_handoff_probe(torch, w4):
+    """The decode-ordered sweep's per-op handoff without weights
+    (w4_probe_handoff): us per round from two round counts (launched
+    directly, HIP events, median of five each), the difference over the extra
+    rounds.  rows bf16 outputs per workgroup per round, and 256 * rows * 2
+    bytes loaded by every workgroup: 6 rows = the 3 KB input of the K = 1536
+    ops, 24 = the 12 KB input of the down projection, 48 = the gate+up output
+    rows per workgroup.  handoff_floor_us: the handoffs of one step at these
+    sizes (106 at 6 rows: three per layer and the lm_head's; 35 at 24)."""
+    r1, r2 = 64, 1088
+    work = w4.probe_handoff(1, 0)
+    res = {"rounds": [r1, r2]}
+
+    def once(rounds, rows):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        w4.probe_handoff(rounds, rows, work)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    for rows in (0, 6, 24, 48):
+        once(r1, rows)
+        t = {}
+        for r in (r1, r2):
+            v = sorted(once(r, rows) for _ in range(5))
+            t[r] = v[2]
+        if int(work[:4].view(torch.int32).item()) != 0:
+            raise RuntimeError("handoff probe: a poll gave up")
+        res["rows%d_us_per_round" % rows] = (t[r2] - t[r1]) / (r2 - r1)
+    res["handoff_floor_us"] = (106 * res["rows6_us_per_round"] +
+                               35 * res["rows24_us_per_round"])
+    return res
+
+
 def time_prefill(torch, w4, synth, dev, mfma_tflops=None):
     """The prefill-shaped product, group 256, N=12288, K=1536 with the 512-point
     run-time Hadamard transform, at M = 8 (small-M kernel), 64 and 512 (matrix
@@ -616,6 +653,7 @@ def main():
                                        "unordered, so it bounds what ordering costs",
             "single_gemv": time_single_gemv(torch, w4, synth, dev, cases, ops),
             "mfma_probe": mfma,
+            "handoff_probe": time_handoff_probe(torch, w4),
             "prefill_g256_N12288_K1536": time_prefill(torch, w4, synth, dev, mfma["TFLOPs"]),
             "prefill_down_g256_N1536_K6144": time_gemm_shapes(torch, w4, synth, dev, 1536,
                                                               6144, 256, (64, 512)),

@@ -48,6 +48,7 @@ EXPORTS = (
     "w4a16_gemm_twin_workspace_bytes", "w4a16_gemm_twin", "w4_attn_workspace_bytes",
     "w4_attn_decode",
     "w4_attn_pack_v", "w4_attn_store_kv", "w4_describe_dispatch", "w4_selftest", "w4_probe_read", "w4_probe_copy", "w4_probe_mfma",
+    "w4_probe_handoff", "w4_probe_handoff_bytes",
     "w4a16_gemm_noalloc", "w4a16_gemm_noalloc_max_bytes",
     "w4_config_reload", "w4_tile_table_load",
 )
@@ -130,6 +131,8 @@ def lib():
             "w4_probe_read": ([vp, sz, vp, vp], i),
             "w4_probe_copy": ([vp, vp, sz, vp], i),
             "w4_probe_mfma": ([i, vp, vp], i),
+            "w4_probe_handoff": ([vp, i, i, vp], i),
+            "w4_probe_handoff_bytes": ([], sz),
             "w4a16_gemm_noalloc": ([vp, i, i, i, i, vp, i, i, vp, i, i, vp], i),
             "w4a16_gemm_noalloc_max_bytes": ([], sz),
         }
@@ -500,6 +503,18 @@ def probe_mfma(iters: int, out=None, stream=None):
         out = torch.zeros(1, dtype=torch.float32, device="cuda")
     _check(lib().w4_probe_mfma(int(iters), _ptr(out), _stream(stream)))
     return out
+
+
+def probe_handoff(rounds: int, rows: int, work=None, stream=None):
+    """Grid-wide handoff probe (``rounds`` rounds, ``rows`` bf16 values per
+    workgroup per round); returns the work buffer (uint8), whose first
+    32-bit word is nonzero if a poll gave up."""
+    import torch
+    if work is None:
+        work = torch.empty(int(lib().w4_probe_handoff_bytes()), dtype=torch.uint8,
+                           device="cuda")
+    _check(lib().w4_probe_handoff(_ptr(work), int(rounds), int(rows), _stream(stream)))
+    return work
 
 
 def probe_copy(src, dst, nbytes: int = None, stream=None):

@@ -536,6 +536,18 @@ int w4_probe_mfma(int iters, float* out, void* stream) {
     return launch_probe_mfma(iters, out, static_cast<hipStream_t>(stream));
 }
 
+size_t w4_probe_handoff_bytes(void) { return probe_handoff_bytes(); }
+
+int w4_probe_handoff(void* work, int rounds, int rows, void* stream) {
+    if (!work) return fail(W4_ERR_ARG, "probe handoff: work is NULL");
+    if (!aligned(work, 256)) return fail(W4_ERR_ALIGN, "probe handoff: work must be 256-byte aligned");
+    if (rounds < 1 || rounds > (1 << 20))
+        return fail(W4_ERR_SHAPE, "probe handoff: rounds must be in 1..2^20 (got %d)", rounds);
+    if (rows < 0 || rows > 64)
+        return fail(W4_ERR_SHAPE, "probe handoff: rows must be in 0..64 (got %d)", rows);
+    return launch_probe_handoff(work, rounds, rows, static_cast<hipStream_t>(stream));
+}
+
 int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
     W4_TRY(check_in16(src, "src"));
     W4_TRY(check_in16(dst, "dst"));

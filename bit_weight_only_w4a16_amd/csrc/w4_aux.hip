@@ -10,8 +10,12 @@
 //
 // Probes: [P1] "Gemma 4 E2B on a 4 GB GPU with plain PyTorch, faster than
 // llama.cpp", the summary line of the w4gemv.py kernel compares the kernel
-// with a plain sum over memory; the copy kernel calibrates byte counters.
+// with a plain sum over memory; the copy kernel calibrates byte counters; the
+// handoff probe measures the fixed cost of one op of a decode step whose ops
+// each read the whole previous output (the paragraph on the decode step
+// captured once as a graph).
 #include "w4_dispatch.h"
+#include "w4_ring.h"
 
 namespace w4 {
 
@@ -137,6 +141,92 @@ int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
     probe_copy_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
     return hip_fail(hipGetLastError(), "probe copy launch");
+}
+
+// Grid-wide handoff probe: the per-op handoff of the decode-ordered sweep
+// kernel with no weights, so that its cost is measured apart from any GEMV.
+// One workgroup of one wave per CU.  Round r: every workgroup stores `rows`
+// bf16 values (its share of a vector of G * rows elements, buffer r mod 2) at
+// agent scope, waits for them to complete and adds one to its XCD's counter
+// (workgroup w counts in counter w mod 8, each counter in its own 128-byte
+// line); lanes 0..7 then poll the eight counters (lane 8 the error word) until
+// they sum to (r + 1) G, and the wave loads the whole vector into LDS with
+// agent-scope 16-byte global-to-LDS loads and waits for them, as the sweep
+// kernel's control wave does before every op.  rows = 0 is the bare
+// signal-and-poll round.  A poll that gives up sets the error word and every
+// workgroup leaves.
+namespace {
+constexpr int kHoCtlWords = 512;                       // error word, 8 counters
+constexpr int kHoMaxRows = 64;
+constexpr size_t kHoVecBytes = (size_t)kNumCUs * kHoMaxRows * 2;
+constexpr unsigned kHoPollLimit = 1u << 20;
+
+__device__ __forceinline__ void dma16_agent_probe(uint32_t off, const void* base, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+}  // namespace
+
+__global__ __launch_bounds__(64) void probe_handoff_kernel(unsigned* ctl, uint16_t* y0,
+                                                           uint16_t* y1, int rounds, int rows) {
+    __shared__ __align__(16) uint8_t xs[kHoVecBytes];
+    const int lane = threadIdx.x;
+    const int w = blockIdx.x;
+    const unsigned G = gridDim.x;
+    // 16-byte pieces of the vector; lanes past the last re-read it into the
+    // part of xs past the vector (xs holds kHoVecBytes / 16 pieces, a
+    // multiple of 64 at or above every piece count)
+    const int n16 = ((int)G * rows * 2 + 15) / 16;
+    const unsigned* p = lane < 8 ? &ctl[32 + 32 * lane] : &ctl[0];
+    for (int r = 0; r < rounds; ++r) {
+        uint16_t* y = (r & 1) ? y1 : y0;
+        if (lane < rows)
+            __hip_atomic_store(y + (size_t)w * rows + lane, (uint16_t)(r + lane),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // the stores are visible to every CU
+        asm volatile("" ::: "memory");
+        if (lane == 0)
+            __hip_atomic_fetch_add(&ctl[32 + 32 * (w & 7)], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned target = (unsigned)(r + 1) * G;
+        bool ok = false;
+        for (unsigned spin = 0; spin < kHoPollLimit; ++spin) {
+            const unsigned v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            unsigned c = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c += __builtin_amdgcn_readlane(v, j);
+            const unsigned e = __builtin_amdgcn_readlane(v, 8);
+            if ((int)(c - target) >= 0) {
+                ok = true;
+                break;
+            }
+            if (e) break;
+        }
+        if (!ok) {
+            if (lane == 0) __hip_atomic_store(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        for (int j = 0; j < n16; j += 64) {
+            const int q = j + lane < n16 ? j + lane : n16 - 1;
+            dma16_agent_probe(16u * (uint32_t)q, y, ring::lds_addr(xs + 16 * j));
+        }
+        ring::wait_vm<0>();
+    }
+}
+
+size_t probe_handoff_bytes() { return (size_t)kHoCtlWords * 4 + 2 * kHoVecBytes; }
+
+int launch_probe_handoff(void* work, int rounds, int rows, hipStream_t s) {
+    uint8_t* base = static_cast<uint8_t*>(work);
+    unsigned* ctl = reinterpret_cast<unsigned*>(base);
+    uint16_t* y0 = reinterpret_cast<uint16_t*>(base + kHoCtlWords * 4);
+    uint16_t* y1 = reinterpret_cast<uint16_t*>(base + kHoCtlWords * 4 + kHoVecBytes);
+    int st = hip_fail(hipMemsetAsync(ctl, 0, kHoCtlWords * 4, s), "probe handoff clear");
+    if (st != W4_OK) return st;
+    probe_handoff_kernel<<<dim3(kNumCUs), dim3(64), 0, s>>>(ctl, y0, y1, rounds, rows);
+    return hip_fail(hipGetLastError(), "probe handoff launch");
 }
 
 }  // namespace w4

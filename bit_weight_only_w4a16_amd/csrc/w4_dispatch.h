@@ -90,5 +90,7 @@ int launch_probe_read(const void* buf, size_t bytes, uint32_t* out,
                       hipStream_t s);
 int launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 int launch_probe_mfma(int iters, float* out, hipStream_t s);
+size_t probe_handoff_bytes();
+int launch_probe_handoff(void* work, int rounds, int rows, hipStream_t s);
 
 }  // namespace w4

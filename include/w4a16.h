@@ -504,6 +504,30 @@ int w4_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
  */
 int w4_probe_mfma(int iters, float* out, void* stream);
 
+/*
+ * Grid-wide handoff probe: the fixed cost each op of the decode-ordered sweep
+ * pays because it reads the whole output of the op before it ([P1], paragraph
+ * on the decode step captured once as a graph: every GEMV of a step reads
+ * what the previous one wrote), measured with no weights.  One workgroup of
+ * one wave per CU (256) runs `rounds` rounds; in each, every workgroup
+ * stores `rows` bf16 values (its share of a vector of 256 * rows elements)
+ * at agent scope, waits for them to complete, adds one to its XCD's
+ * completion counter, polls the eight counters until every workgroup has
+ * signalled, then loads the whole vector into LDS (agent scope, 16-byte
+ * global-to-LDS loads) and waits for it, as the sweep kernel's control wave
+ * does before each op.  rows = 0 times the bare signal-and-poll round.  The
+ * caller times the call (two round counts, the difference over the extra
+ * rounds, removes the launch).  Round r writes the value r + j (as a 16-bit
+ * integer) at element w * rows + j of buffer r mod 2.
+ *  work: device, >= w4_probe_handoff_bytes() bytes, 256-byte aligned.
+ *  Layout: 512 control words (word 0 is nonzero afterwards if a poll gave
+ *  up), then the two vectors of 256 * 64 elements each.  The call clears the
+ *  control words with hipMemsetAsync first, so it is not for graph capture.
+ *  rounds in 1..2^20, rows in 0..64.
+ */
+size_t w4_probe_handoff_bytes(void);
+int w4_probe_handoff(void* work, int rounds, int rows, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -236,6 +236,13 @@ def test_probe_validation(L):
     assert L.w4_probe_mfma((1 << 20) + 1, A16, VP(0)) == -2
     assert L.w4_probe_mfma(8, VP(0), VP(0)) == -1
     assert L.w4_probe_mfma(8, A2, VP(0)) == -3
+    assert L.w4_probe_handoff_bytes() >= 2048 + 2 * 256 * 64 * 2
+    assert L.w4_probe_handoff(VP(0), 1, 6, VP(0)) == -1
+    assert L.w4_probe_handoff(VP(0x10010), 1, 6, VP(0)) == -3
+    assert L.w4_probe_handoff(VP(0x10000), 0, 6, VP(0)) == -2
+    assert L.w4_probe_handoff(VP(0x10000), (1 << 20) + 1, 6, VP(0)) == -2
+    assert L.w4_probe_handoff(VP(0x10000), 1, -1, VP(0)) == -2
+    assert L.w4_probe_handoff(VP(0x10000), 1, 65, VP(0)) == -2
 
 
 def test_describe_dispatch_tile_table(L, monkeypatch):

@@ -189,6 +189,29 @@ def test_probes_run():
     assert out.item() == 7.0
 
 
+@pytest.mark.parametrize("rows", [0, 1, 6, 24, 64])
+def test_handoff_probe(rows):
+    """The handoff probe completes every round (no poll gave up) and leaves
+    in each of its two vectors what its last round on that vector wrote:
+    r + j at element w * rows + j (r the round, w the workgroup)."""
+    import torch
+    device()
+    rounds = 7
+    work = w4.probe_handoff(rounds, rows)
+    torch.cuda.synchronize()
+    h = work.cpu().numpy()
+    assert int(h[:4].view(np.uint32)[0]) == 0
+    if rows == 0:
+        return
+    n = 256 * rows
+    vec = 256 * 64 * 2
+    for buf, last in ((0, rounds - 1 if (rounds - 1) % 2 == 0 else rounds - 2),
+                      (1, rounds - 1 if (rounds - 1) % 2 == 1 else rounds - 2)):
+        y = h[2048 + buf * vec: 2048 + buf * vec + 2 * n].view(np.uint16)
+        expect = (last + np.tile(np.arange(rows), 256)).astype(np.uint16)
+        assert np.array_equal(y, expect), buf
+
+
 @pytest.mark.parametrize("path", ["", "gemv_contig"])
 def test_one_hot_through_the_lm_head(oracle_mod, monkeypatch, path):
     """x = e_k through the 262144 x 1536 lm_head (its searched tile, and the
