@@ -189,14 +189,11 @@ def test_prefill_g256_hadamard(oracle_mod, M):
         if e.status == -5:
             pytest.skip("matrix-core tile not built: %s" % e)
         raise
+    # every row, also at 512 (9.7 G multiply-adds: a few seconds of the
+    # oracle on 16 threads)
     xr = oracle_mod.fwht(oracle_mod.bf16_to_f64(case.X), 512)
-    if M > 64:
-        rows = np.random.default_rng(0).choice(M, 48, replace=False)
-        Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr[rows], threads=16)
-        assert_within(Y[rows], Yr, A, "bf16", "prefill M=%d (sampled rows)" % M)
-    else:
-        Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr, threads=16)
-        assert_within(Y, Yr, A, "bf16", "prefill M=%d" % M)
+    Yr, A = oracle_mod.gemm(case.P, case.S, N, K, g, xr, threads=16)
+    assert_within(Y, Yr, A, "bf16", "prefill M=%d" % M)
 
 
 @pytest.mark.parametrize("M,N,K,g,had", [(17, 100, 256, 32, 0), (64, 12288, 1536, 32, 0),
