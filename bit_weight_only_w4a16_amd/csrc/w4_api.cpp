@@ -70,6 +70,21 @@ static int check_in16(const void* p, const char* name) {
     return W4_OK;
 }
 
+// The output of a product may share no byte with its activations or its
+// weights: other workgroups still read them while outputs are written.
+static int check_out_disjoint(const void* packed, int N, int K, int group, const void* X,
+                              size_t x_bytes, const void* Y, size_t y_bytes, const char* who) {
+    if (ranges_overlap(Y, y_bytes, X, x_bytes))
+        return fail(W4_ERR_ARG, "%s: the output overlaps the activations", who);
+    if (ranges_overlap(Y, y_bytes, packed, w4_packed_bytes(N, K, group)))
+        return fail(W4_ERR_ARG, "%s: the output overlaps the weights", who);
+    return W4_OK;
+}
+
+static size_t rows_bytes(int M, int ld, int n, size_t es) {
+    return ((size_t)(M - 1) * (size_t)ld + (size_t)n) * es;
+}
+
 }  // namespace w4
 
 using namespace w4;
@@ -175,6 +190,8 @@ int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
     const char* src = nullptr;
     const GemvTile t = pick_gemv_tile(N, K, group, &src);
     log_choice(1, N, K, group);
+    W4_TRY(check_out_disjoint(packed, N, K, group, x, (size_t)K * 2, y,
+                              (size_t)N * (ydt == W4_F32 ? 4 : 2), "gemv"));
     return launch_gemv(t, packed, N, K, group, x, y, ydt,
                        static_cast<hipStream_t>(stream));
 }
@@ -192,6 +209,8 @@ int w4a16_gemm_smallM(const void* packed, int N, int K, int group, int M,
     W4_TRY(check_out_ptr(Y, ydt, "Y"));
     W4_TRY(config_status());
     log_choice(M, N, K, group);
+    W4_TRY(check_out_disjoint(packed, N, K, group, X, rows_bytes(M, ldx, K, 2), Y,
+                              rows_bytes(M, ldy, N, ydt == W4_F32 ? 4 : 2), "smallM"));
     return launch_smallm(packed, N, K, group, M, X, ldx, Y, ldy, ydt,
                          static_cast<hipStream_t>(stream));
 }
@@ -243,6 +262,12 @@ int check_gemm_args(const void* packed, int N, int K, int group, int M, const ui
     return W4_OK;
 }
 
+int check_gemm_disjoint(const void* packed, int N, int K, int group, int M, const uint16_t* X,
+                        int ldx, const void* Y, int ldy, int ydt) {
+    return check_out_disjoint(packed, N, K, group, X, rows_bytes(M, ldx, K, 2), Y,
+                              rows_bytes(M, ldy, N, ydt == W4_F32 ? 4 : 2), "gemm");
+}
+
 // W4_LOG: the kernel and tile each distinct (M, N, K, group) dispatches to,
 // printed once.
 void log_choice(int M, int N, int K, int group) {
@@ -277,6 +302,7 @@ int w4a16_gemm(const void* packed, int N, int K, int group, int M,
                         ws_bytes);
         W4_TRY(check_in16(workspace, "workspace"));
     }
+    W4_TRY(check_gemm_disjoint(packed, N, K, group, M, X, ldx, Y, ldy, ydt));
     hipStream_t s = static_cast<hipStream_t>(stream);
     // The 512-block transform of up to 4 rows runs inside the matrix-core
     // small-M kernel, on the rows it stages anyway (bitwise the same rows the

@@ -27,9 +27,18 @@ struct GemvTile {
 // then the built-in table, then the heuristic; *source (if given) names which.
 GemvTile pick_gemv_tile(int N, int K, int group, const char** source = nullptr);
 
+// True when the byte ranges [a, a + na) and [b, b + nb) share a byte.
+inline bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
 // Argument validation of w4a16_gemm (no HIP call); W4_OK or a status.
 int check_gemm_args(const void* packed, int N, int K, int group, int M, const uint16_t* X,
                     int ldx, int had_block, const void* Y, int ldy, int ydt);
+// The output span of w4a16_gemm shares no byte with X's span or the weights.
+int check_gemm_disjoint(const void* packed, int N, int K, int group, int M, const uint16_t* X,
+                        int ldx, const void* Y, int ldy, int ydt);
 int launch_gemv(const GemvTile& t, const void* packed, int N, int K, int group,
                 const uint16_t* x, void* y, int ydt, hipStream_t s);
 

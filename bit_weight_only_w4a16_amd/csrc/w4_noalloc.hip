@@ -60,6 +60,8 @@ int w4a16_gemm_noalloc(const void* packed, int N, int K, int group, int M, const
                     "gemm_noalloc: the transform needs %zu bytes, beyond the %zu-byte static "
                     "scratch (M * K * 2 <= %zu)",
                     need, kScratchBytes, kScratchBytes);
+    const int dst = check_gemm_disjoint(packed, N, K, group, M, X, ldx, Y, ldy, y_dtype);
+    if (dst != W4_OK) return dst;
     void* ws = nullptr;
     if (need) {
         const int st = scratch_ptr(&ws);

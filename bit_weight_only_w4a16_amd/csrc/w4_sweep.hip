@@ -35,6 +35,10 @@ namespace w4 {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+static size_t out_bytes(const w4_gemv_op& op) {
+    return (size_t)op.N * (op.y_dtype == W4_F32 ? 4 : 2);
+}
+
 static int check_op(const w4_gemv_op& op, int i) {
     if (op.group != 32 && op.group != 256 && op.group != 512)
         return fail(W4_ERR_SHAPE, "sweep op %d: group must be 32, 256 or 512", i);
@@ -48,6 +52,23 @@ static int check_op(const w4_gemv_op& op, int i) {
         return fail(W4_ERR_ALIGN, "sweep op %d: packed and x must be 16-byte aligned", i);
     if ((reinterpret_cast<uintptr_t>(op.y) & (op.y_dtype == W4_F32 ? 3 : 1)) != 0)
         return fail(W4_ERR_ALIGN, "sweep op %d: y misaligned", i);
+    return W4_OK;
+}
+
+// No op's output may share a byte with its own activation (other workgroups
+// still read it while outputs are written) or with any op's weights (the
+// persistent kernel reads a later op's weights ahead, and every replay reads
+// them all again).
+static int check_outputs_spare_inputs(const std::vector<w4_gemv_op>& ops) {
+    for (size_t i = 0; i < ops.size(); ++i)
+        if (ranges_overlap(ops[i].y, out_bytes(ops[i]), ops[i].x, (size_t)ops[i].K * 2))
+            return fail(W4_ERR_ARG, "sweep op %d: y overlaps its own x", (int)i);
+    for (size_t i = 0; i < ops.size(); ++i)
+        for (size_t j = 0; j < ops.size(); ++j)
+            if (ranges_overlap(ops[i].y, out_bytes(ops[i]), ops[j].packed,
+                               w4_packed_bytes(ops[j].N, ops[j].K, ops[j].group)))
+                return fail(W4_ERR_ARG, "sweep op %d: y overlaps the weights of op %d", (int)i,
+                            (int)j);
     return W4_OK;
 }
 
@@ -375,6 +396,10 @@ int w4_decode_sweep_create(const w4_gemv_op* ops, int n_ops, int mode, void* str
     }
     {
         const int st = config_status();   // GRAPH mode picks each op's tile
+        if (st != W4_OK) return st;
+    }
+    {
+        const int st = check_outputs_spare_inputs(std::vector<w4_gemv_op>(ops, ops + n_ops));
         if (st != W4_OK) return st;
     }
     if (mode != W4_SWEEP_GRAPH) {

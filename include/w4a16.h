@@ -135,7 +135,8 @@ int w4_unpack_host(const void* packed, int N, int K, int group,
  * [P1] paragraph on the w4gemv.py kernel.
  *  packed: device layout of W (N x K, group 32, 256 or 512), 16-byte aligned.
  *  x: device, K bf16, 16-byte aligned.
- *  y: device, N elements of y_dtype (4-byte aligned for fp32, 2 for bf16).
+ *  y: device, N elements of y_dtype (4-byte aligned for fp32, 2 for bf16);
+ *     sharing no byte with x or packed (W4_ERR_ARG otherwise).
  * N >= 1; K >= 32 and K % group == 0.
  */
 int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
@@ -150,7 +151,8 @@ int w4a16_gemv(const void* packed, int N, int K, int group, const uint16_t* x,
  * the vector ALU.
  *  X: device, M rows of K bf16, row stride ldx >= K elements (ldx % 8 == 0),
  *     16-byte aligned.
- *  Y: device, M rows of N y_dtype elements, row stride ldy >= N elements.
+ *  Y: device, M rows of N y_dtype elements, row stride ldy >= N elements;
+ *     its span shares no byte with X's span or packed (W4_ERR_ARG otherwise).
  */
 int w4a16_gemm_smallM(const void* packed, int N, int K, int group, int M,
                       const uint16_t* X, int ldx, void* Y, int ldy,
@@ -192,7 +194,8 @@ size_t w4a16_gemm_workspace_bytes(int M, int K, int had_block);
  *  rows take the small-M product, and 9..16 too where it runs on the
  *  matrix cores (see w4a16_gemm_smallM); larger row counts run on the tiled
  *  matrix-core kernels.
- *  X: device, stride ldx (% 8 == 0).  Y: device, stride ldy.
+ *  X: device, stride ldx (% 8 == 0).  Y: device, stride ldy; its span
+ *  shares no byte with X's span or packed (W4_ERR_ARG otherwise).
  *  workspace: device, >= w4a16_gemm_workspace_bytes(M, K, had_block) bytes,
  *  16-byte aligned (may be NULL when that size is 0).
  */
@@ -227,7 +230,9 @@ size_t w4a16_gemm_noalloc_max_bytes(void);
  * Each op is one w4a16_gemv (M = 1).  The handle owns its graph, its
  * executable graph and a small device buffer (op table, counters, flags); it
  * BORROWS every pointer in `ops`, which must stay valid while the handle
- * lives.  Ops run in array order.
+ * lives.  Ops run in array order.  No op's y may share a byte with its own
+ * x or with any op's weights (W4_ERR_ARG); an op's x may be an earlier op's
+ * y (the decode-ordered mode orders them).
  * Modes:
  *  W4_SWEEP_GRAPH      one GEMV kernel per op captured into a hipGraph;
  *                      op i+1 starts after op i has finished (stream order).

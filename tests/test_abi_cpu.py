@@ -227,6 +227,36 @@ def test_sweep_validation(L):
     assert L.w4_decode_sweep_destroy(VP(0)) == -1
 
 
+def test_outputs_must_not_overlap_inputs(L):
+    """An output that shares a byte with the activations or the weights of
+    its product is refused before any HIP call (other workgroups still read
+    them while outputs are written)."""
+    if L.w4_device_check() != -6:
+        pytest.skip("a HIP device is present: the fake-pointer calls would launch")
+    P, X, Y = VP(0x100000), VP(0x200000), VP(0x300000)   # disjoint fake buffers
+    nb = L.w4_packed_bytes(256, 512, 32)
+    assert L.w4a16_gemv(P, 256, 512, 32, X, Y, 0, VP(0)) == -6          # validates, no device
+    assert L.w4a16_gemv(P, 256, 512, 32, X, X, 0, VP(0)) == -1          # y on x
+    assert L.w4a16_gemv(P, 256, 512, 32, X, VP(0x200000 + 1022), 1, VP(0)) == -1  # last byte
+    assert L.w4a16_gemv(P, 256, 512, 32, X, VP(0x200000 + 1024), 1, VP(0)) == -6  # adjacent
+    assert L.w4a16_gemv(P, 256, 512, 32, X, VP(0x100000 + nb - 4), 0, VP(0)) == -1  # on weights
+    assert L.w4a16_gemm_smallM(P, 256, 512, 32, 4, X, 512, VP(0x200000 + 3 * 1024), 256, 1,
+                               VP(0)) == -1                              # Y on X's last row
+    assert L.w4a16_gemm(P, 256, 512, 32, 64, X, 512, 0, VP(0), 0, VP(0x200000 + 64 * 1024 - 2),
+                        256, 1, VP(0)) == -1                             # Y on X's last element
+    assert L.w4a16_gemm_noalloc(P, 256, 512, 32, 64, X, 512, 0, X, 256, 1, VP(0)) == -1
+    ops = (w4.GemvOp * 2)()
+    ops[0] = w4.GemvOp(0x100000, 256, 512, 32, 0x200000, 0x300000, 0)
+    ops[1] = w4.GemvOp(0x400000, 256, 512, 32, 0x300000, 0x200000, 1)   # x = y of op 0: allowed
+    h = ctypes.c_void_p()
+    ops[1] = w4.GemvOp(0x400000, 256, 512, 32, 0x300000, 0x300000, 1)   # y on its own x
+    assert L.w4_decode_sweep_create(ops, 2, 1, VP(0), ctypes.byref(h)) == -1
+    assert "op 1" in w4.last_error()
+    ops[1] = w4.GemvOp(0x400000, 256, 512, 32, 0x300000, 0x100000 + 64, 1)  # on op 0's weights
+    assert L.w4_decode_sweep_create(ops, 2, 1, VP(0), ctypes.byref(h)) == -1
+    assert "weights of op 0" in w4.last_error()
+
+
 def test_probe_validation(L):
     assert L.w4_probe_read(A16, 0, A16, VP(0)) == -2
     assert L.w4_probe_read(A16, 24, A16, VP(0)) == -2

@@ -152,7 +152,7 @@ def test_log_prints_each_choice_once(L, monkeypatch, capfd):
         pytest.skip("a HIP device is present: the fake-pointer call would launch")
     set_dispatch_env(monkeypatch, W4_LOG="1")
     for _ in range(3):
-        assert L.w4a16_gemv(A16, 256, 512, 32, A16, A16, 0, VP(0)) == -6
+        assert L.w4a16_gemv(A16, 256, 512, 32, A16, VP(0x7F000000), 0, VP(0)) == -6
     err = capfd.readouterr().err
     line = "w4a16: M=1 N=256 K=512 group=32: " + w4.describe_dispatch(1, 256, 512, 32)
     assert line.endswith("(built-in table)")
