@@ -556,6 +556,8 @@ def main():
                          "kernels); stream = the unordered upper bound (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--handoff-only", action="store_true",
+                    help="time only the grid-wide handoff probe and print its JSON")
     ap.add_argument("--kernel-only", action="store_true",
                     help="for hardware-counter runs: only --steps replays of the timed "
                          "mode, then three 1 GiB probe copies (the calibration kernel); "
@@ -576,6 +578,9 @@ def main():
 
     dev = torch.device("cuda:0")
     w4.device_check()
+    if args.handoff_only:
+        print(json.dumps(time_handoff_probe(torch, w4)))
+        return
     if args.prefill_only:
         import numpy as np
         c = synth.prefill_g256(args.prefill_only)
