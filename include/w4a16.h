@@ -446,6 +446,11 @@ int w4_describe_dispatch(int M, int N, int K, int group, char* buf,
  *                       sweep handle created afterwards gives up (default
  *                       2^20); 0 makes every replay give up at its second
  *                       op, for tests of the W4_ERR_TIMEOUT path.
+ *  W4_SWEEP_BLOCKS_PER_CU=n (1..16)
+ *                       workgroups per CU of an unordered (STREAM) sweep
+ *                       handle created afterwards (default 5, capped at what
+ *                       fits a CU at once), for tuning runs; read when the
+ *                       handle is created.
  *  W4_PREFILL_CFG, W4_MFMA_CFG, W4_I8_RING (1..4), W4_I8_TILE ("MF,NF"):
  *                       tiling indices of the prefill, register-staged
  *                       matrix-core and int8 kernels, for tuning runs.
