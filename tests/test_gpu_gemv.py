@@ -189,6 +189,33 @@ def test_probes_run():
     assert out.item() == 7.0
 
 
+def test_output_on_input_is_refused():
+    """An output that shares bytes with the activation or the weights is
+    refused with W4_ERR_ARG before anything is launched, and the buffers are
+    left as they were."""
+    import torch
+    case = synth.single_gemv_small()
+    packed = w4.pack(torch.from_numpy(case.P.view(np.int32)).to(device()),
+                     torch.from_numpy(case.S.view(np.int16)).to(device()),
+                     case.N, case.K, case.group)
+    buf = torch.zeros(case.K + case.N, dtype=torch.bfloat16, device=device())
+    buf[:case.K] = torch.from_numpy(case.X[0].view(np.int16)).to(device()).view(torch.bfloat16)
+    before = buf.clone()
+    with pytest.raises(w4.W4Error) as e:
+        w4.gemv(packed, case.N, case.K, case.group, buf[:case.K], "bf16", out=buf[8:8 + case.N])
+    assert e.value.status == -1
+    with pytest.raises(w4.W4Error) as e:
+        w4.gemv(packed, case.N, case.K, case.group, buf[:case.K], "bf16",
+                out=packed.view(torch.bfloat16)[:case.N])
+    assert e.value.status == -1
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    # adjacent, not overlapping: runs
+    y = w4.gemv(packed, case.N, case.K, case.group, buf[:case.K], "bf16", out=buf[case.K:])
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+
+
 @pytest.mark.parametrize("rows", [0, 1, 6, 24, 64])
 def test_handoff_probe(rows):
     """The handoff probe completes every round (no poll gave up) and leaves
